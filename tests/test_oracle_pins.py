@@ -1,0 +1,458 @@
+"""Pins of the fp64 oracle to facts outside itself (CPU only).
+
+Each check ties the oracle to something the pages print, a closed form, an
+invariant of the mathematics, or a 50-digit brute force of the literal
+definition.  The planted-mistake tests at the end swap one step of the oracle
+for a plausible wrong version (dropped term, wrong sign, wrong index,
+transposed operand) and show that the pin suite then fails.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from oracle import attention as A
+from oracle import brute
+import workloads
+
+RNG = np.random.default_rng(12345)
+
+
+def _golden(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------- printed examples
+
+def check_worked_example(gold):
+    s = np.array(gold["scores_reading"])
+    _, traj = A.online_softmax(s, gold["block_size"])
+    pr, tol = gold["printed"], gold["printed_tolerance"]
+    assert abs(traj[0]["l"] - pr["block1_denominator"]) <= tol
+    assert traj[1]["m"] == pr["running_max_after_block2"]
+    assert abs(traj[1]["l"] - pr["denominator_after_block2"]) <= tol
+    assert traj[2]["m"] == pr["running_max_after_block3"]
+    assert abs(traj[2]["alpha"] - math.exp(pr["rescale_factor_exponent_at_block3"])) <= 1e-15
+    assert abs(traj[2]["l"] - pr["final_denominator"]) <= tol
+
+
+def test_worked_example_trajectory(golden_dir):
+    check_worked_example(_golden(golden_dir, "online_softmax_worked_example.json"))
+
+
+def test_worked_example_online_equals_one_shot(golden_dir):
+    gold = _golden(golden_dir, "online_softmax_worked_example.json")
+    s = np.array(gold["scores_reading"])
+    vals = RNG.standard_normal((6, 5))
+    online, _ = A.online_softmax(s, 2, vals)
+    p, _, _ = A.safe_softmax(s[None, :])
+    np.testing.assert_allclose(online, p[0] @ vals, rtol=0, atol=1e-12)
+    w, _ = A.online_softmax(s, 2)
+    exact = [float(x) for x in brute.softmax_decimal(s)]
+    np.testing.assert_allclose(w, exact, rtol=0, atol=1e-14)
+
+
+def test_appendix_safe_softmax(golden_dir):
+    gold = _golden(golden_dir, "safe_softmax_appendix.json")
+    s = np.array(gold["scores"])
+    assert abs(math.exp(12.0) - gold["printed_exp12"]) <= gold["printed_exp12_tolerance"]
+    # the direct form overflows in fp16, the max-subtracted form does not
+    with np.errstate(over="ignore"):
+        e12_16 = np.float16(np.exp(np.float32(12.0)))
+    assert np.isinf(e12_16) and np.float16(gold["printed_fp16_max"]) == np.finfo(np.float16).max
+    sub16 = np.exp((s - s.max()).astype(np.float16))
+    assert np.all(np.isfinite(sub16))
+    p, m, l = A.safe_softmax(s[None, :])
+    exact = [float(x) for x in brute.softmax_decimal(s)]
+    np.testing.assert_allclose(p[0], exact, rtol=0, atol=1e-15)
+    assert m[0] == 12.0
+
+
+def test_numpy_exercise_three_chunks_vs_scipy():
+    """CMU notes, self-study section: online softmax over a long vector in three chunks vs scipy."""
+    x = RNG.standard_normal(3001) * 6.0
+    w, traj = A.online_softmax(x, 1001)
+    assert len(traj) == 3
+    np.testing.assert_allclose(w, scipy.special.softmax(x), rtol=1e-12, atol=1e-300)
+
+
+def test_online_equals_one_shot_every_block_size():
+    for n in (1, 2, 7, 16):
+        x = RNG.standard_normal(n) * 4.0
+        vals = RNG.standard_normal((n, 3))
+        p, _, _ = A.safe_softmax(x[None, :])
+        for b in range(1, n + 1):
+            res, traj = A.online_softmax(x, b, vals)
+            np.testing.assert_allclose(res, p[0] @ vals, rtol=0, atol=1e-13)
+            assert traj[-1]["m"] == x.max()
+
+
+def test_blockwise_softmaxes_cannot_simply_be_added():
+    """HPC notes, long-context section: per-block softmaxes do not sum to the global one."""
+    x = np.array([1.0, 2.0, 5.0, 0.5])
+    naive = np.concatenate([A.safe_softmax(x[None, :2])[0][0], A.safe_softmax(x[None, 2:])[0][0]])
+    p, _, _ = A.safe_softmax(x[None, :])
+    assert np.max(np.abs(naive - p[0])) > 0.1
+    w, _ = A.online_softmax(x, 2)
+    np.testing.assert_allclose(w, p[0], atol=1e-15)
+
+
+# ------------------------------------------------------- forward: brute force
+
+def check_forward_vs_decimal(seed=0):
+    rng = np.random.default_rng(seed)
+    for (n, d, causal) in ((1, 1, False), (3, 2, True), (5, 3, False), (6, 3, True), (4, 2, False)):
+        q, k, v = (rng.standard_normal((n, d)) * 1.5 for _ in range(3))
+        v = rng.standard_normal((n, d + 1))
+        scale = 1.0 / math.sqrt(d)
+        o, lse = A.attention_forward_head(q, k, v, scale, causal)
+        Od, Ld = brute.attention_decimal(q, k, v, scale, causal)
+        np.testing.assert_allclose(o, np.array(Od, dtype=float), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse, np.array(Ld, dtype=float), rtol=0, atol=1e-13)
+
+
+def test_forward_vs_decimal_brute_force():
+    check_forward_vs_decimal()
+
+
+def check_forward_large_scores():
+    """Scores far beyond exp's float64 range: max subtraction keeps the result exact."""
+    q = np.array([[30.0, 0.0], [0.0, 30.0]])
+    k = np.array([[30.0, 0.0], [0.0, 29.0]])
+    v = np.array([[1.0, 2.0], [3.0, 4.0]])
+    o, lse = A.attention_forward_head(q, k, v, 1.0, False)
+    # row 0: scores (900, 0) -> weight 1 on key 0; row 1: scores (0, 870) -> key 1
+    np.testing.assert_allclose(o, [[1.0, 2.0], [3.0, 4.0]], atol=1e-300)
+    np.testing.assert_allclose(lse, [900.0, 870.0], rtol=1e-15)
+
+
+def test_forward_large_scores_stay_finite():
+    check_forward_large_scores()
+
+
+# ----------------------------------------------------------- forward invariants
+
+def check_forward_invariants(seed=1):
+    rng = np.random.default_rng(seed)
+    n, d = 37, 8
+    scale = 1.0 / math.sqrt(d)
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    for causal in (False, True):
+        rows = np.arange(n)
+        s = np.where(A.visible(rows, n, causal), A.scores(q, k, scale), -np.inf)
+        p, m, l = A.safe_softmax(s)
+        np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+        o, lse = A.attention_forward_head(q, k, v, scale, causal)
+        for i in range(n):
+            vis = np.arange(n) <= i if causal else np.ones(n, bool)
+            lo, hi = v[vis].min(axis=0), v[vis].max(axis=0)
+            assert np.all(o[i] >= lo - 1e-13) and np.all(o[i] <= hi + 1e-13)
+            si = scale * q[i] @ k[vis].T
+            assert lse[i] >= si.max() - 1e-13
+            assert lse[i] <= si.max() + math.log(vis.sum()) + 1e-13
+    # key permutation invariance (non-causal): permute K and V rows together
+    perm = rng.permutation(n)
+    o1, l1 = A.attention_forward_head(q, k, v, scale, False)
+    o2, l2 = A.attention_forward_head(q, k[perm], v[perm], scale, False)
+    np.testing.assert_allclose(o1, o2, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, atol=1e-13)
+    # Q = 0: uniform weights over visible keys
+    z = np.zeros_like(q)
+    oc, lc = A.attention_forward_head(z, k, v, scale, True)
+    np.testing.assert_allclose(oc, np.cumsum(v, axis=0) / np.arange(1, n + 1)[:, None], atol=1e-13)
+    np.testing.assert_allclose(lc, np.log(np.arange(1, n + 1)), atol=1e-13)
+    on, ln_ = A.attention_forward_head(z, k, v, scale, False)
+    np.testing.assert_allclose(on, np.broadcast_to(v.mean(axis=0), on.shape), atol=1e-13)
+    np.testing.assert_allclose(ln_, math.log(n), atol=1e-13)
+    # causal row 0 sees only key 0: O_0 = V_0, LSE_0 = scale q0.k0
+    oc, lc = A.attention_forward_head(q, k, v, scale, True)
+    np.testing.assert_array_equal(oc[0], v[0])
+    np.testing.assert_allclose(lc[0], scale * q[0] @ k[0], rtol=1e-15)
+    # causal last row sees every key: equals the non-causal last row
+    onc, lnc = A.attention_forward_head(q, k, v, scale, False)
+    np.testing.assert_allclose(oc[-1], onc[-1], atol=1e-14)
+    # N = 1: O = V
+    o1, l1 = A.attention_forward_head(q[:1], k[:1], v[:1], scale, False)
+    np.testing.assert_array_equal(o1, v[:1])
+    # a row subset equals the same rows of the full result
+    sub = np.array([0, 5, 36, 17])
+    os_, ls_ = A.attention_forward_head(q, k, v, scale, True, rows=sub)
+    np.testing.assert_allclose(os_, oc[sub], atol=0)
+    np.testing.assert_allclose(ls_, lc[sub], atol=0)
+
+
+def test_forward_invariants():
+    check_forward_invariants()
+
+
+def test_forward_batched_matches_per_head():
+    x = workloads.attention_inputs(2, 3, 19, 8, "bf16", seed=5)
+    res = A.attention_forward(x["q"], x["k"], x["v"], 0.3, True, workers=4)
+    for (b, h), (o, lse) in res.items():
+        q, k, v = (A.to_f64(x[n][b, h]) for n in "qkv")
+        o2, l2 = A.attention_forward_head(q, k, v, 0.3, True)
+        np.testing.assert_array_equal(o, o2)
+        np.testing.assert_array_equal(lse, l2)
+
+
+def test_bf16_inputs_converted_exactly():
+    x = workloads.attention_inputs(1, 1, 4, 8, "bf16", seed=9)
+    f = A.to_f64(x["q"])
+    assert np.array_equal(f, x["q"].float().double().numpy())
+    assert f.dtype == np.float64
+
+
+# --------------------------------------------------------------------- backward
+
+def check_backward_vs_fd(seed=2):
+    rng = np.random.default_rng(seed)
+    for (n, d, causal) in ((3, 2, True), (4, 3, False), (5, 2, True)):
+        q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+        scale = 1.0 / math.sqrt(d)
+        g = A.attention_backward_head(q, k, v, do, scale, causal)
+        fd = brute.grads_fd_decimal(q, k, v, do, scale, causal)
+        for name in ("dq", "dk", "dv"):
+            np.testing.assert_allclose(g[name], fd[name], rtol=0, atol=1e-9)
+
+
+def test_backward_vs_decimal_finite_differences():
+    check_backward_vs_fd()
+
+
+def check_backward_invariants(seed=3):
+    rng = np.random.default_rng(seed)
+    n, d = 23, 8
+    scale = 1.0 / math.sqrt(d)
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    for causal in (False, True):
+        g = A.attention_backward_head(q, k, v, do, scale, causal)
+        np.testing.assert_allclose(g["dv"].sum(axis=0), do.sum(axis=0), atol=1e-12)
+        np.testing.assert_allclose(g["dk"].sum(axis=0), 0.0, atol=1e-12)
+        o, lse = A.attention_forward_head(q, k, v, scale, causal)
+        np.testing.assert_allclose(g["o"], o, atol=1e-14)
+        np.testing.assert_allclose(g["lse"], lse, atol=1e-14)
+        if causal:
+            assert np.all(np.abs(g["dq"][0]) <= 1e-15)
+            # the last key is seen only by the last query
+            p_last = 1.0 / np.exp(lse[-1] - scale * q[-1] @ k[-1])
+            np.testing.assert_allclose(g["dv"][-1], p_last * do[-1], atol=1e-14)
+
+
+def test_backward_invariants():
+    check_backward_invariants()
+
+
+# ------------------------------------------------------------------ paged decode
+
+def _scatter_to_pool(Kc, Vc, lens, block_size, H, d, seed):
+    """Build a paged pool from contiguous per-sequence K/V by an independent route."""
+    rng = np.random.default_rng(seed)
+    nblk = [-(-L // block_size) for L in lens]
+    total = sum(nblk) + 3
+    perm = rng.permutation(total)
+    kp = rng.standard_normal((total, block_size, H, d))
+    vp = rng.standard_normal((total, block_size, H, d))
+    table = -np.ones((len(lens), max(nblk)), dtype=np.int32)
+    off = 0
+    for s, L in enumerate(lens):
+        for t in range(L):
+            b, slot = divmod(t, block_size)
+            if slot == 0:
+                table[s, b] = perm[off]
+                off += 1
+            kp[table[s, b], slot] = Kc[s][t]
+            vp[table[s, b], slot] = Vc[s][t]
+    return kp, vp, table
+
+
+def check_decode(seed=4):
+    rng = np.random.default_rng(seed)
+    H, d, bs = 3, 4, 4
+    lens = [1, 4, 5, 11]
+    Kc = [rng.standard_normal((L, H, d)) for L in lens]
+    Vc = [rng.standard_normal((L, H, d)) for L in lens]
+    q = rng.standard_normal((len(lens), H, d))
+    scale = 0.5
+    kp, vp, table = _scatter_to_pool(Kc, Vc, lens, bs, H, d, seed)
+    o, lse = A.paged_decode(q, kp, vp, table, np.array(lens), bs, scale)
+    for s, L in enumerate(lens):
+        for h in range(H):
+            Od, Ld = brute.attention_decimal(q[s, h][None], Kc[s][:, h], Vc[s][:, h], scale, False)
+            np.testing.assert_allclose(o[s, h], np.array(Od[0], dtype=float), atol=1e-13)
+            np.testing.assert_allclose(lse[s, h], float(Ld[0]), atol=1e-13)
+    np.testing.assert_array_equal(o[0], Vc[0][0])     # seq_len 1: o = v_0
+    # a second, different placement gives the same result
+    kp2, vp2, table2 = _scatter_to_pool(Kc, Vc, lens, bs, H, d, seed + 100)
+    o2, lse2 = A.paged_decode(q, kp2, vp2, table2, np.array(lens), bs, scale)
+    np.testing.assert_allclose(o2, o, atol=1e-15)
+    # equals the last row of a causal forward whose final query is q
+    s = 3
+    for h in range(H):
+        qq = np.concatenate([rng.standard_normal((lens[s] - 1, d)), q[s, h][None]])
+        of, lf = A.attention_forward_head(qq, Kc[s][:, h], Vc[s][:, h], scale, True)
+        np.testing.assert_allclose(of[-1], o[s, h], atol=1e-14)
+        np.testing.assert_allclose(lf[-1], lse[s, h], atol=1e-14)
+    # pad slots past the length never enter the result
+    kp_nan, vp_nan = kp.copy(), vp.copy()
+    for s, L in enumerate(lens):
+        if L % bs:
+            p = table[s, L // bs]
+            kp_nan[p, L % bs:] = np.nan
+            vp_nan[p, L % bs:] = np.nan
+    o3, lse3 = A.paged_decode(q, kp_nan, vp_nan, table, np.array(lens), bs, scale)
+    np.testing.assert_array_equal(o3, o)
+    np.testing.assert_array_equal(lse3, lse)
+
+
+def test_paged_decode_pins():
+    check_decode()
+
+
+def test_paged_decode_on_generated_pool_with_nan_pads():
+    p = workloads.paged_inputs(5, 2, 8, 16, 1, 40, seed=11, pad_value=float("nan"))
+    o, lse = A.paged_decode(p["q"], p["k_pool"], p["v_pool"], p["block_table"], p["seq_lens"],
+                            16, 0.35)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+# ---------------------------------------------------------- planted mistakes
+
+def _all_forward_pins(golden_dir):
+    check_forward_vs_decimal()
+    check_forward_large_scores()
+    check_forward_invariants()
+
+
+def _all_backward_pins():
+    check_backward_vs_fd()
+    check_backward_invariants()
+
+
+_orig = {n: getattr(A, n) for n in ("scores", "visible", "safe_softmax", "attend", "lse_of",
+                                      "grad_v", "grad_p", "row_dot", "grad_s", "grad_q",
+                                      "grad_k", "gather_tokens", "online_softmax")}
+
+
+def _bad_safe_softmax_axis(s):
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    l = np.sum(e, axis=0, keepdims=True)   # normalises the wrong axis
+    return e / l, m[..., 0], np.sum(e, axis=-1)
+
+
+def _bad_safe_softmax_nomax(s):
+    e = np.exp(s)                          # no max subtraction
+    l = np.sum(e, axis=-1, keepdims=True)
+    return e / l, np.zeros(s.shape[:-1]), l[..., 0]
+
+
+FORWARD_MUTANTS = {
+    "scale_dropped": ("scores", lambda q, k, scale: q @ k.T),
+    "scale_squared": ("scores", lambda q, k, scale: scale * scale * (q @ k.T)),
+    "transposed_scores": ("scores", lambda q, k, scale: scale * (k @ q.T) if q.shape == k.shape
+                          else scale * (q @ k.T)[:, ::-1]),
+    "causal_strict": ("visible", lambda rows, nk, causal: (np.arange(nk)[None, :] < np.asarray(rows)[:, None])
+                      | (not causal) | (np.asarray(rows)[:, None] == 0) & (np.arange(nk)[None, :] == 0)),
+    "causal_reversed": ("visible", lambda rows, nk, causal: (np.arange(nk)[None, :] >= np.asarray(rows)[:, None])
+                        | (not causal)),
+    "causal_ignored": ("visible", lambda rows, nk, causal: np.ones((len(rows), nk), bool)),
+    "softmax_wrong_axis": ("safe_softmax", _bad_safe_softmax_axis),
+    "softmax_no_max": ("safe_softmax", _bad_safe_softmax_nomax),
+    "values_reversed": ("attend", lambda p, v: p @ v[::-1]),
+    "lse_sign": ("lse_of", lambda m, l: m - np.log(l)),
+    "lse_no_max": ("lse_of", lambda m, l: np.log(l)),
+}
+
+BACKWARD_MUTANTS = {
+    "dv_untransposed": ("grad_v", lambda p, do: p @ do),
+    "dp_wrong_operand": ("grad_p", lambda do, v: do @ v[::-1].T),
+    "D_dropped": ("grad_s", lambda p, dp, D: p * dp),
+    "D_sign": ("grad_s", lambda p, dp, D: p * (dp + D[:, None])),
+    "D_from_wrong_axis": ("row_dot", lambda do, o: np.sum(do * o, axis=1)[::-1]),
+    "dq_scale_dropped": ("grad_q", lambda ds, k, scale: ds @ k),
+    "dq_transposed": ("grad_q", lambda ds, k, scale: scale * (ds.T @ k)),
+    "dk_untransposed": ("grad_k", lambda ds, q, scale: scale * (ds @ q)),
+}
+
+
+def _gather_off_by_one(pool, table_row, length, block_size):
+    t = np.arange(length)
+    tbl = np.asarray(table_row).astype(np.int64)
+    return A.to_f64(np.asarray(pool)[tbl[(t + 1) // block_size % max(1, (length + block_size - 1) // block_size)],
+                                     (t + 1) % block_size])
+
+
+def _gather_logical(pool, table_row, length, block_size):
+    t = np.arange(length)
+    return A.to_f64(np.asarray(pool)[t // block_size, t % block_size])
+
+
+def _gather_one_extra(pool, table_row, length, block_size):
+    return _orig["gather_tokens"](pool, table_row, min(length + 1, block_size * int(np.sum(np.asarray(table_row) >= 0))),
+                                  block_size)
+
+
+DECODE_MUTANTS = {
+    "slot_off_by_one": ("gather_tokens", _gather_off_by_one),
+    "logical_block_ids": ("gather_tokens", _gather_logical),
+    "reads_pad_slot": ("gather_tokens", _gather_one_extra),
+}
+
+
+def test_pins_pass_on_unmodified_oracle(golden_dir):
+    _all_forward_pins(golden_dir)
+    _all_backward_pins()
+    check_decode()
+
+
+@pytest.mark.parametrize("mutant", sorted(FORWARD_MUTANTS))
+def test_forward_pins_catch_planted_mistake(mutant, monkeypatch, golden_dir):
+    name, fn = FORWARD_MUTANTS[mutant]
+    monkeypatch.setattr(A, name, fn)
+    with pytest.raises((AssertionError, ValueError, FloatingPointError)):
+        with np.errstate(all="ignore"):
+            _all_forward_pins(golden_dir)
+
+
+@pytest.mark.parametrize("mutant", sorted(BACKWARD_MUTANTS))
+def test_backward_pins_catch_planted_mistake(mutant, monkeypatch):
+    name, fn = BACKWARD_MUTANTS[mutant]
+    monkeypatch.setattr(A, name, fn)
+    with pytest.raises((AssertionError, ValueError)):
+        _all_backward_pins()
+
+
+@pytest.mark.parametrize("mutant", sorted(DECODE_MUTANTS))
+def test_decode_pins_catch_planted_mistake(mutant, monkeypatch):
+    name, fn = DECODE_MUTANTS[mutant]
+    monkeypatch.setattr(A, name, fn)
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        with np.errstate(all="ignore"):
+            check_decode()
+
+
+def _online_no_rescale(s, block, values=None):
+    s = np.asarray(s, dtype=np.float64)
+    n = s.shape[0]
+    vals = np.eye(n) if values is None else np.asarray(values, dtype=np.float64)
+    m, l, acc, traj = -math.inf, 0.0, np.zeros(vals.shape[1:]), []
+    for start in range(0, n, block):
+        blk = s[start:start + block]
+        m = max(m, float(np.max(blk)))
+        e = np.exp(blk - m)
+        l = l + float(np.sum(e))           # forgets to rescale the old state
+        acc = acc + e @ vals[start:start + block]
+        traj.append({"m": m, "l": l, "alpha": 1.0})
+    return acc / l, traj
+
+
+def test_worked_example_catches_missing_rescale(monkeypatch, golden_dir):
+    monkeypatch.setattr(A, "online_softmax", _online_no_rescale)
+    with pytest.raises(AssertionError):
+        check_worked_example(_golden(golden_dir, "online_softmax_worked_example.json"))
