@@ -1,0 +1,237 @@
+"""Benchmark of the libfa hot path on one MI355X.
+
+One step = one pass of the whole hot path over synthetic inputs of the
+benchmark shapes:
+  * fa_fwd   causal bf16 B=1 H=32 N=8192 d=128   (the headline: TFLOP/s, % MFMA peak)
+  * fa_fwd   causal bf16 B=8 H=12 N=1024 d=64
+  * fa_fwd + fa_bwd causal bf16 B=4 H=16 N=2048 d=128
+  * fa_paged_decode bf16 64 seqs x H=32 x d=128, lengths U[128,4096], 16-token blocks
+Inputs are resident in HBM before timing starts.  Each call is bracketed by
+HIP events on the stream it runs on; `value` is the headline forward's
+algorithmic TFLOP/s (causal pairs only) over its average kernel time.
+
+The CPU baseline times the fp64 oracle on a bounded sample of the headline
+workload on the host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak (published)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def causal_flops(B, H, N, d):
+    return 4 * B * H * d * (N * (N + 1) // 2)
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "exact_attention_70_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, src_hash):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(kernel_key)
+    except Exception:
+        return None
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="", help="comma list of parts to run (profiling aid)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the kernels run on a single MI355X; see DESIGN.md for how the path would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    from exact_attention_70_amd import binding
+
+    binding.load_library()
+    dev = torch.device("cuda:0")
+    only = set(x for x in args.only.split(",") if x)
+
+    def want(name):
+        return not only or name in only
+
+    # ------------------------------------------------------------ inputs (untimed)
+    c3, c2, c4, c5 = (workloads.CONFIGS[i] for i in (3, 2, 4, 5))
+    parts = {}
+    if want("fwd_c3"):
+        x = workloads.attention_inputs(c3.B, c3.H, c3.N, c3.d, "bf16", seed=workloads.seed_for(3))
+        q, k, v = (x[n].to(dev) for n in "qkv")
+        o = torch.empty_like(q)
+        lse = torch.empty(c3.B, c3.H, c3.N, device=dev)
+        parts["fwd_c3"] = dict(fn=lambda: binding.fwd(q, k, v, causal=True, scale=c3.scale, out=o,
+                                                       lse=lse),
+                               flops=causal_flops(c3.B, c3.H, c3.N, c3.d))
+    if want("fwd_c2"):
+        x2 = workloads.attention_inputs(c2.B, c2.H, c2.N, c2.d, "bf16", seed=workloads.seed_for(2),
+                                        in_scale=c2.in_scale)
+        q2, k2, v2 = (x2[n].to(dev) for n in "qkv")
+        o2 = torch.empty_like(q2)
+        lse2 = torch.empty(c2.B, c2.H, c2.N, device=dev)
+        parts["fwd_c2"] = dict(fn=lambda: binding.fwd(q2, k2, v2, causal=True, scale=c2.scale,
+                                                       out=o2, lse=lse2),
+                               flops=causal_flops(c2.B, c2.H, c2.N, c2.d))
+    if want("fwd_c4") or want("bwd_c4"):
+        x4 = workloads.attention_inputs(c4.B, c4.H, c4.N, c4.d, "bf16", seed=workloads.seed_for(4),
+                                        with_do=True)
+        q4, k4, v4, do4 = (x4[n].to(dev) for n in ("q", "k", "v", "do"))
+        o4 = torch.empty_like(q4)
+        lse4 = torch.empty(c4.B, c4.H, c4.N, device=dev)
+        grads = tuple(torch.empty(q4.shape, dtype=torch.float32, device=dev) for _ in range(3))
+        ws4 = torch.empty(binding.bwd_workspace_size(c4.B, c4.H, c4.N, c4.d), dtype=torch.uint8,
+                          device=dev)
+        f4 = causal_flops(c4.B, c4.H, c4.N, c4.d)
+        parts["fwd_c4"] = dict(fn=lambda: binding.fwd(q4, k4, v4, causal=True, scale=c4.scale,
+                                                       out=o4, lse=lse4), flops=f4)
+        parts["bwd_c4"] = dict(fn=lambda: binding.bwd(q4, k4, v4, o4, do4, lse4, causal=True,
+                                                       scale=c4.scale, workspace=ws4, grads=grads),
+                               flops=int(2.5 * f4), flops_2x=2 * f4)
+    if want("decode_c5"):
+        p = workloads.paged_inputs(c5.num_seqs, c5.H, c5.d, c5.block_size, c5.min_len, c5.max_len,
+                                   seed=workloads.seed_for(5))
+        pd = {kk: (vv.to(dev) if isinstance(vv, torch.Tensor) else vv) for kk, vv in p.items()}
+        od = torch.empty_like(pd["q"])
+        lsed = torch.empty(c5.num_seqs, c5.H, device=dev)
+        wsd = torch.empty(binding.paged_decode_workspace_size(c5.num_seqs, c5.H, c5.d,
+                                                              p["max_blocks_per_seq"], 16),
+                          dtype=torch.uint8, device=dev)
+        tokens = int(p["seq_lens"].long().sum())
+        kv_bytes = tokens * c5.H * c5.d * 2 * 2
+        parts["decode_c5"] = dict(fn=lambda: binding.paged_decode(
+            pd["q"], pd["k_pool"], pd["v_pool"], pd["block_table"], pd["seq_lens"], block_size=16,
+            scale=c5.scale, workspace=wsd, out=od, lse=lsed), bytes=kv_bytes, tokens=tokens)
+    torch.cuda.synchronize()
+    log(f"inputs ready: {list(parts)}")
+
+    order = [n for n in ("fwd_c3", "fwd_c2", "fwd_c4", "bwd_c4", "decode_c5") if n in parts]
+    for _ in range(args.warmup):
+        for n in order:
+            parts[n]["fn"]()
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    evs = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)] for n in order}
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for s in range(args.steps):
+        for n in order:
+            a, b = evs[n][s]
+            a.record()
+            parts[n]["fn"]()
+            b.record()
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    log("timed steps done")
+
+    res = {}
+    for n in order:
+        ts = sorted(a.elapsed_time(b) for a, b in evs[n])
+        avg = sum(ts) / len(ts)
+        r = {"avg_ms": round(avg, 5), "median_ms": round(ts[len(ts) // 2], 5),
+             "min_ms": round(ts[0], 5)}
+        if "flops" in parts[n]:
+            r["tflops"] = round(parts[n]["flops"] / (avg * 1e-3) / 1e12, 2)
+            r["frac_mfma_peak"] = round(r["tflops"] / PEAK_BF16_TFLOPS, 4)
+            if "flops_2x" in parts[n]:
+                r["tflops_2x_convention"] = round(parts[n]["flops_2x"] / (avg * 1e-3) / 1e12, 2)
+        if "bytes" in parts[n]:
+            r["gbs"] = round(parts[n]["bytes"] / (avg * 1e-3) / 1e9, 1)
+            r["frac_hbm_peak"] = round(r["gbs"] / PEAK_HBM_GBS, 4)
+        res[n] = r
+        log(n, r)
+
+    cpu = None
+    if not args.no_cpu_baseline and "fwd_c3" in parts:
+        import numpy as np
+        import oracle
+        workers = min(os.cpu_count() or 1, 16)
+        heads = [(0, h) for h in range(0, 32, 2)]          # 16 of the 32 heads, every row
+        t0 = time.perf_counter()
+        oracle.attention_forward(x["q"], x["k"], x["v"], c3.scale, True, heads=heads,
+                                 workers=workers)
+        dt = time.perf_counter() - t0
+        fl = causal_flops(1, len(heads), c3.N, c3.d)
+        cpu = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": workers,
+               "kind": "oracle",
+               "sample": f"fp64 oracle forward on 16 of 32 heads (all 8192 rows) of the causal "
+                         f"B=1 H=32 N=8192 d=128 workload; {dt:.1f} s wall"}
+        log("cpu baseline", cpu)
+
+    head = res.get("fwd_c3")
+    src = source_hash("fa_fwd.hip", "fa_device.h")
+    roof = None
+    if head is not None:
+        traffic = load_traffic("fwd_bf16_d128_causal_b1h32n8192", src)
+        roof = {"bound": "mfma", "achieved": head["tflops"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": head["frac_mfma_peak"], "traffic": traffic,
+                "kernel": "fwd_bf16_kernel<128,causal>", "source_hash": src}
+    dec = res.get("decode_c5")
+    roof_dec = None
+    if dec is not None:
+        roof_dec = {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": dec["frac_hbm_peak"],
+                    "traffic": load_traffic("decode_partial_c5", source_hash("fa_decode.hip")),
+                    "kernel": "decode_partial_kernel + decode_merge_kernel"}
+    out = {
+        "metric": "fwd attention TFLOP/s (causal bf16, % of MFMA dense bf16 peak); "
+                  "paged-decode GB/s in parts.decode_c5",
+        "value": head["tflops"] if head else None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1))",
+        "config": {"workload": "causal bf16 attention forward B=1 H=32 N=8192 d=128 "
+                               "(one step also runs fwd B=8 H=12 N=1024 d=64, fwd+bwd "
+                               "B=4 H=16 N=2048 d=128, paged decode 64x32x128)",
+                   "global_batch": 1, "seq_len": 8192, "parallelism": "single-gpu"},
+        "roofline": roof,
+        "roofline_decode": roof_dec,
+        "parts": res,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,159 @@
+"""Thin ctypes binding of libfa.
+
+Argument marshalling only: every step of the attention computation runs in
+the HIP kernels behind the C ABI declared in include/fa.h.  torch is used for
+device memory (output and workspace allocation) and for the current HIP
+stream.  If the shared library is missing or fails to load, every entry point
+raises; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_DT_F32 = 0
+FA_DT_BF16 = 1
+
+EXPORTED = ("fa_status_string", "fa_version", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd",
+            "fa_paged_decode_workspace_size", "fa_paged_decode")
+
+_lib = None
+
+
+class LibfaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libfa.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libfa shared library not found at {p}; build it with "
+                           "`python -m exact_attention_70_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(p)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = i
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
+    lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_bwd.argtypes = [vp] * 9 + [i, i, i, i, f, i, i, vp, sz, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_paged_decode_workspace_size.argtypes = [i, i, i, i, i]
+    lib.fa_paged_decode_workspace_size.restype = sz
+    lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, i, vp, sz, vp]
+    lib.fa_paged_decode.restype = i
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise LibfaError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FA_DT_BF16
+    if t.dtype == torch.float32:
+        return FA_DT_F32
+    raise TypeError(f"libfa supports bf16 and fp32 tensors, got {t.dtype}")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous()):
+            raise ValueError("libfa expects contiguous device tensors")
+
+
+def fwd(q, k, v, *, causal: bool, scale: float | None = None, out=None, lse=None):
+    """O, LSE = attention(q, k, v) for [B, H, N, d] device tensors (bf16 or fp32)."""
+    _need_cuda(q, k, v)
+    B, H, N, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape [B, H, N, d] and dtype")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, N, d, scale,
+                               int(bool(causal)), _dtype_code(q), _stream(q.device))
+    _check(st, "fa_fwd")
+    return o, l
+
+
+def bwd_workspace_size(B, H, N, d) -> int:
+    return int(load_library().fa_bwd_workspace_size(B, H, N, d))
+
+
+def bwd(q, k, v, o, do, lse, *, causal: bool, scale: float | None = None, workspace=None,
+        grads=None):
+    """dQ, dK, dV (fp32) of attention given the forward's O and LSE and dO."""
+    _need_cuda(q, k, v, o, do, lse)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if grads is None:
+        grads = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+                      for _ in range(3))
+    dq, dk, dv = grads
+    ws_bytes = bwd_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    st = load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                               _ptr(dk), _ptr(dv), B, H, N, d, scale, int(bool(causal)),
+                               _dtype_code(q), _ptr(workspace), workspace.numel(),
+                               _stream(q.device))
+    _check(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def paged_decode_workspace_size(num_seqs, H, d, max_blocks_per_seq, block_size) -> int:
+    return int(load_library().fa_paged_decode_workspace_size(num_seqs, H, d, max_blocks_per_seq,
+                                                             block_size))
+
+
+def paged_decode(q, k_pool, v_pool, block_table, seq_lens, *, block_size: int,
+                 scale: float | None = None, workspace=None, out=None, lse=None):
+    """o [S, H, d] bf16 and lse [S, H] fp32 of one decode step over a paged KV pool."""
+    _need_cuda(q, k_pool, v_pool, block_table, seq_lens)
+    S, H, d = q.shape
+    num_blocks = k_pool.shape[0]
+    mbps = block_table.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((S, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    ws_bytes = paged_decode_workspace_size(S, H, d, mbps, block_size)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    st = load_library().fa_paged_decode(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), block_size, S, H,
+        d, mbps, num_blocks, scale, _ptr(o), _ptr(l), _dtype_code(q), _ptr(workspace),
+        workspace.numel(), _stream(q.device))
+    _check(st, "fa_paged_decode")
+    return o, l

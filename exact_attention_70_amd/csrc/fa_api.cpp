@@ -1,0 +1,157 @@
+// C-ABI entry points of libfa: argument validation, workspace sizing and
+// dispatch to the kernel launchers.  Nothing here computes attention; every
+// arithmetic step runs in the HIP kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int kMaxN = 1 << 20;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+bool debug_checks() {
+  const char* s = std::getenv("FA_DEBUG");
+  return s != nullptr && s[0] != '\0' && s[0] != '0';
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Per-head byte sizes must fit the 32-bit range of a buffer resource.
+bool head_fits(long long N, long long d, long long elem) { return N * d * elem < (1LL << 31); }
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid size";
+    case FA_ERR_DTYPE: return "FA_ERR_DTYPE: unknown dtype code";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: configuration not implemented";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointer not 16-byte aligned";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+    case FA_ERR_INVALID: return "FA_ERR_INVALID: block_table or seq_lens contents invalid";
+    case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error";
+    default: return "unknown libfa status";
+  }
+}
+
+int fa_version(void) { return 100; }
+
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N,
+           int d, float scale, int causal, int dtype, void* stream) {
+  if (dtype != FA_DT_F32 && dtype != FA_DT_BF16) return FA_ERR_DTYPE;
+  if (B < 0 || H < 1 || N < 1 || N > kMaxN || d < 1) return FA_ERR_SHAPE;
+  if (!std::isfinite(scale)) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!head_fits(N, d, dtype == FA_DT_F32 ? 4 : 2)) return FA_ERR_SHAPE;
+  if ((long long)B * H * ((N + 31) / 32) >= (1LL << 31)) return FA_ERR_SHAPE;
+  if (B == 0) return FA_OK;
+  if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
+    return FA_ERR_ALIGN;
+  fa::FwdArgs a{Q, K, V, O, LSE, B, H, N, d, scale, causal != 0, dtype,
+                reinterpret_cast<hipStream_t>(stream)};
+  return hip_status(fa::launch_fwd(a));
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+  (void)d;
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  return round_up((size_t)B * H * N * sizeof(float), 256);
+}
+
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+           const float* LSE, float* dQ, float* dK, float* dV, int B, int H, int N, int d,
+           float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+           void* stream) {
+  if (dtype != FA_DT_F32 && dtype != FA_DT_BF16) return FA_ERR_DTYPE;
+  if (B < 0 || H < 1 || N < 1 || N > kMaxN || d < 1) return FA_ERR_SHAPE;
+  if (!std::isfinite(scale)) return FA_ERR_SHAPE;
+  if (dtype != FA_DT_BF16) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!head_fits(N, d, 4)) return FA_ERR_SHAPE;
+  if (B == 0) return FA_OK;
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL;
+  if (!workspace || workspace_bytes < fa_bwd_workspace_size(B, H, N, d)) return FA_ERR_WORKSPACE;
+  const void* ptrs[] = {Q, K, V, O, dO, LSE, dQ, dK, dV, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  fa::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, static_cast<float*>(workspace),
+                B, H, N, d, scale, causal != 0, reinterpret_cast<hipStream_t>(stream)};
+  return hip_status(fa::launch_bwd(a));
+}
+
+size_t fa_paged_decode_workspace_size(int num_seqs, int H, int d, int max_blocks_per_seq,
+                                      int block_size) {
+  if (num_seqs <= 0 || H <= 0 || d <= 0 || max_blocks_per_seq <= 0 || block_size <= 0) return 0;
+  const size_t parts = (size_t)fa::decode_n_parts(max_blocks_per_seq, block_size);
+  // per (seq, partition, head): m, l, then d output values
+  return round_up((size_t)num_seqs * parts * H * (size_t)(d + 2) * sizeof(float), 256);
+}
+
+int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_table, const int32_t* seq_lens, int block_size,
+                    int num_seqs, int H, int d, int max_blocks_per_seq, int num_blocks,
+                    float scale, void* o, float* lse, int dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (dtype != FA_DT_F32 && dtype != FA_DT_BF16) return FA_ERR_DTYPE;
+  if (num_seqs < 0 || H < 1 || d < 1 || max_blocks_per_seq < 1 || num_blocks < 1 ||
+      block_size < 1)
+    return FA_ERR_SHAPE;
+  if (!std::isfinite(scale)) return FA_ERR_SHAPE;
+  if (dtype != FA_DT_BF16 || block_size != 16 || d != 128 || (H % 4) != 0)
+    return FA_ERR_UNSUPPORTED;
+  const long long block_bytes = (long long)block_size * H * d * 2;
+  if (block_bytes >= (1LL << 31)) return FA_ERR_SHAPE;
+  if ((long long)max_blocks_per_seq * block_size > kMaxN) return FA_ERR_SHAPE;
+  if (num_seqs == 0) return FA_OK;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !o || !lse)
+    return FA_ERR_NULL;
+  const size_t need =
+      fa_paged_decode_workspace_size(num_seqs, H, d, max_blocks_per_seq, block_size);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const void* ptrs[] = {q, k_pool, v_pool, o, lse, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return FA_ERR_ALIGN;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    std::vector<int32_t> tbl((size_t)num_seqs * max_blocks_per_seq), lens(num_seqs);
+    if (hipMemcpyAsync(lens.data(), seq_lens, lens.size() * 4, hipMemcpyDeviceToHost, st) !=
+            hipSuccess ||
+        hipMemcpyAsync(tbl.data(), block_table, tbl.size() * 4, hipMemcpyDeviceToHost, st) !=
+            hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return FA_ERR_HIP;
+    for (int s = 0; s < num_seqs; ++s) {
+      const int L = lens[s];
+      if (L < 1 || (long long)L > (long long)max_blocks_per_seq * block_size) return FA_ERR_INVALID;
+      const int nb = (L + block_size - 1) / block_size;
+      for (int b = 0; b < nb; ++b) {
+        const int32_t p = tbl[(size_t)s * max_blocks_per_seq + b];
+        if (p < 0 || p >= num_blocks) return FA_ERR_INVALID;
+      }
+    }
+  }
+  fa::DecodeArgs a{q, k_pool, v_pool, block_table, seq_lens, block_size, num_seqs, H, d,
+                   max_blocks_per_seq, num_blocks, scale, o, lse,
+                   static_cast<float*>(workspace), fa::kDecodePartTokens,
+                   fa::decode_n_parts(max_blocks_per_seq, block_size), st};
+  return hip_status(fa::launch_decode(a));
+}
+
+}  // extern "C"

@@ -1,0 +1,199 @@
+// Paged single-token decode for gfx950.
+//
+// Method: CMU 10-423 L17-L18 notes, section "Decoding: PagedAttention" (the KV
+// cache is cut into fixed-size token blocks stored non-contiguously; a block
+// table maps logical to physical blocks; the kernel computes block by block)
+// and HPC notes "07-16 afternoon", section "Prefill, Decode and inference
+// scheduling" (a decode step feeds one token whose query reads every cached
+// K/V of its sequence, so the step is bound by memory bandwidth).  The split
+// over KV partitions is merged with the rescaling rule of the online softmax
+// (HPC notes, section "Long context and sequence parallelism").
+//
+// Pool layout [num_blocks, block_size = 16, H, d = 128]: one physical block is
+// a contiguous 16 * H * 256-byte chunk, so a workgroup that reads all heads of
+// a block streams contiguous memory.
+//
+// Partial kernel: workgroup = (sequence, KV partition of 256 tokens, group of
+//   16 heads); wave = 4 heads; 16 lanes per head, each lane owning 8 of the
+//   128 head-dim values.  Per 16-token block: 16-byte loads of K and V rows
+//   through a buffer resource over that physical block (an out-of-range
+//   block id therefore reads zeros instead of faulting), q.k partial dot
+//   products reduced across the 16 lanes with DPP, one online-softmax update
+//   per block, and the P V accumulation.  Writes (m, l, unnormalised o).
+// Merge kernel: one wave per (sequence, head) combines its partitions.
+//   Throughput is bound by HBM: the flops per byte are ~1.
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kDecD = 128;
+constexpr int kDecBS = 16;
+constexpr int kDecThreads = 256;
+constexpr int kHeadsPerWave = 4;
+constexpr int kHeadsPerGroup = 16;
+
+__global__ __launch_bounds__(kDecThreads, 2) void decode_partial_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k_pool,
+    const __bf16* __restrict__ v_pool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, int H, int max_blocks_per_seq, int num_blocks,
+    float scale_log2, float* __restrict__ part_o, float* __restrict__ part_ml, int part_tokens,
+    int n_parts) {
+  const int p = blockIdx.x;
+  const int hg = blockIdx.y;
+  const int s = blockIdx.z;
+  const int len = min(seq_lens[s], max_blocks_per_seq * kDecBS);
+  const int t_begin = p * part_tokens;
+  if (t_begin >= len) return;                       // partition past this sequence's end
+  const int t_end = min(len, t_begin + part_tokens);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int head = hg * kHeadsPerGroup + wave * kHeadsPerWave + (lane >> 4);
+  const int ch = lane & 15;                          // which 8 of the 128 d values
+  const bool head_ok = head < H;
+  const int hh = head_ok ? head : 0;
+
+  const uint32_t blk_bytes = (uint32_t)kDecBS * H * kDecD * 2;
+  const uint32_t row_off = (uint32_t)(hh * kDecD + ch * 8) * 2;    // within one token row
+  const uint32_t tok_stride = (uint32_t)H * kDecD * 2;
+
+  // this lane's 8 query values, fp32
+  float qv[8];
+  {
+    const auto rq = make_rsrc(q + (size_t)s * H * kDecD, (uint32_t)H * kDecD * 2);
+    const u32x4 w = bload16(rq, row_off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qv[2 * e] = bf16lo(w[e]);
+      qv[2 * e + 1] = bf16hi(w[e]);
+    }
+  }
+
+  float m_run = kNegInf, l_run = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+
+  const int32_t* table = block_table + (size_t)s * max_blocks_per_seq;
+  for (int t0 = t_begin; t0 < t_end; t0 += kDecBS) {
+    const int32_t phys = table[t0 / kDecBS];
+    const bool phys_ok = (uint32_t)phys < (uint32_t)num_blocks;
+    const size_t boff = (size_t)(phys_ok ? phys : 0) * kDecBS * H * kDecD;
+    const auto rk = make_rsrc(k_pool + boff, phys_ok ? blk_bytes : 0u);
+    const auto rv = make_rsrc(v_pool + boff, phys_ok ? blk_bytes : 0u);
+    u32x4 kr[kDecBS], vr[kDecBS];
+#pragma unroll
+    for (int u = 0; u < kDecBS; ++u) kr[u] = bload16(rk, u * tok_stride + row_off);
+#pragma unroll
+    for (int u = 0; u < kDecBS; ++u) vr[u] = bload16(rv, u * tok_stride + row_off);
+
+    const int n_valid = min(kDecBS, t_end - t0);    // tokens of this block inside the range
+    float sc[kDecBS];
+    float mx = kNegInf;
+#pragma unroll
+    for (int u = 0; u < kDecBS; ++u) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        part = fmaf(qv[2 * e], bf16lo(kr[u][e]), part);
+        part = fmaf(qv[2 * e + 1], bf16hi(kr[u][e]), part);
+      }
+      float x = group_sum<16>(part) * scale_log2;
+      if (u >= n_valid) x = kNegInf;
+      sc[u] = x;
+      mx = fmaxf(mx, x);
+    }
+    const float m_new = fmaxf(m_run, mx);            // finite: token t0 is always valid
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float rs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int u = 0; u < kDecBS; ++u) {
+      const float pu = fast_exp2(sc[u] - m_new);
+      rs += pu;
+      if (u < n_valid) {                             // pad slots never enter the sum
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] = fmaf(pu, bf16lo(vr[u][e]), acc[2 * e]);
+          acc[2 * e + 1] = fmaf(pu, bf16hi(vr[u][e]), acc[2 * e + 1]);
+        }
+      }
+    }
+    l_run = l_run * alpha + rs;
+  }
+
+  if (!head_ok) return;
+  const size_t entry = ((size_t)s * n_parts + p) * H + head;
+  u32x4 w0, w1;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    w0[e] = as_u32(acc[e]);
+    w1[e] = as_u32(acc[4 + e]);
+  }
+  *(u32x4*)(part_o + entry * kDecD + ch * 8) = w0;
+  *(u32x4*)(part_o + entry * kDecD + ch * 8 + 4) = w1;
+  if (ch == 0) {
+    part_ml[entry * 2] = m_run;
+    part_ml[entry * 2 + 1] = l_run;
+  }
+}
+
+// One wave per (sequence, head): rescale every partition's (m, l, o) to the
+// common maximum and sum.  Each lane owns 2 of the 128 output values.
+__global__ __launch_bounds__(256) void decode_merge_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const int32_t* __restrict__ seq_lens, int num_seqs, int H, int part_tokens, int n_parts,
+    __bf16* __restrict__ o, float* __restrict__ lse) {
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (gw >= num_seqs * H) return;
+  const int lane = threadIdx.x & 63;
+  const int s = gw / H, head = gw % H;
+  const int len = seq_lens[s];
+  if (len <= 0) {   // invalid length: defined output, nothing read
+    *(uint32_t*)(o + ((size_t)s * H + head) * kDecD + 2 * lane) = 0u;
+    if (lane == 0) lse[(size_t)s * H + head] = kNegInf;
+    return;
+  }
+  const int np = min(n_parts, (len + part_tokens - 1) / part_tokens);
+  const size_t base = (size_t)s * n_parts * H + head;
+  float m_star = kNegInf;
+  for (int p = 0; p < np; ++p) m_star = fmaxf(m_star, part_ml[(base + (size_t)p * H) * 2]);
+  float L = 0.f, a0 = 0.f, a1 = 0.f;
+  for (int p = 0; p < np; ++p) {
+    const size_t e = base + (size_t)p * H;
+    const float w = fast_exp2(part_ml[e * 2] - m_star);
+    L = fmaf(w, part_ml[e * 2 + 1], L);
+    a0 = fmaf(w, part_o[e * kDecD + 2 * lane], a0);
+    a1 = fmaf(w, part_o[e * kDecD + 2 * lane + 1], a1);
+  }
+  const float inv = 1.f / L;
+  *(uint32_t*)(o + ((size_t)s * H + head) * kDecD + 2 * lane) = pack_bf16(a0 * inv, a1 * inv);
+  if (lane == 0) lse[(size_t)s * H + head] = (m_star + fast_log2(L)) * kLn2;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a) {
+  const size_t n_entries = (size_t)a.num_seqs * a.n_parts * a.H;
+  float* part_o = a.part;
+  float* part_ml = a.part + n_entries * kDecD;
+  dim3 grid(a.n_parts, (a.H + kHeadsPerGroup - 1) / kHeadsPerGroup, a.num_seqs);
+  hipLaunchKernelGGL(decode_partial_kernel, grid, dim3(kDecThreads), 0, a.stream,
+                     (const __bf16*)a.q, (const __bf16*)a.k_pool, (const __bf16*)a.v_pool,
+                     a.block_table, a.seq_lens, a.H, a.max_blocks_per_seq, a.num_blocks,
+                     a.scale * kLog2e, part_o, part_ml, a.part_tokens, a.n_parts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int waves = a.num_seqs * a.H;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3((waves + 3) / 4), dim3(256), 0, a.stream, part_o,
+                     part_ml, a.seq_lens, a.num_seqs, a.H, a.part_tokens, a.n_parts,
+                     (__bf16*)a.o, a.lse);
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,0 +1,173 @@
+// Device-side helpers shared by the libfa kernels (gfx950 / CDNA4, wave64).
+//
+// Matrix-core conventions used throughout (v_mfma_f32_32x32x16_bf16):
+//   A operand (32 x 16): lane l supplies row (l % 32), eight k values (slot j, half l / 32)
+//   B operand (16 x 32): lane l supplies column (l % 32), eight k values (slot j, half l / 32)
+//   C/D (32 x 32 fp32):  lane l, register i holds column (l % 32),
+//                        row 8*(i/4) + 4*(l/32) + (i%4)
+// The contraction pairs A's (half, slot) with B's (half, slot), so any
+// relabelling of k applied identically to both operands gives the same
+// product; the kernels use this to feed a C-layout tile back in as a B
+// operand without moving data between lanes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Bit reinterpretation goes through these by-value helpers only.  hipcc
+// miscompiles __builtin_bit_cast whose operand is an element of a vector
+// (e.g. bit_cast<float>(v[i])): it reads the wrong element, and the
+// optimizer then narrows the vector load feeding it.
+__device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Buffer resource word 3 for raw (untyped, stride 0) buffers on gfx9-family parts.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// A buffer resource over [base, base + bytes).  Loads outside the range return
+// zero and stores outside it are dropped, which is how ragged tails are handled
+// (and why an indexing slip cannot touch memory outside the tensor).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ float bload4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return as_f32(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void bstore16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void bstore8(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void bstore4f(float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b32(as_u32(v), r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// fp32 -> packed bf16 pair, round-to-nearest-even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2 h = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t u) { return as_f32(u << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t u) { return as_f32(u & 0xffff0000u); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Exchange with the lane 32 positions away (the other half of the wave).
+__device__ __forceinline__ float swap_half(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+// Map the hardware workgroup id to a logical tile id so that consecutive
+// logical tiles land on the same XCD: the dispatcher hands workgroups to the
+// 8 XCDs round-robin, so hardware id b runs on XCD b % 8.  The map is a
+// bijection on [0, n) for any n.
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  const int q = n >> 3, r = n & 7;
+  const int xcd = b & 7, slot = b >> 3;
+  return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+// --------------------------------------------------------------------------
+// LDS tile layouts.  Rows are stored unpadded; 16-byte chunks are XOR-swizzled
+// so that the matrix-operand reads (eight consecutive rows, same chunk) hit
+// distinct banks.
+
+// Row-major [rows][D] bf16 tile: byte offset of 16-byte chunk `c` of row `r`.
+template <int D>
+__device__ __forceinline__ uint32_t rm_off(int r, int c) {
+  return (uint32_t)(r * (D * 2) + ((c ^ (r & 7)) << 4));
+}
+
+// Transposed [D][BN] bf16 tile holding a BN = 64 key tile column-wise.  Keys
+// are stored in a permuted order inside every group of 16: key k sits at
+// position k with bits 2 and 3 swapped, which makes the eight keys a lane
+// needs for one P V matrix step (keys 8a + 4h + c, a,c in {0,1}x{0..3}, see
+// the C-layout above) contiguous.  Returns the byte offset of the 8-byte
+// piece holding positions [4p, 4p + 4) of row d.
+__device__ __forceinline__ int kpos(int k) {
+  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+__device__ __forceinline__ uint32_t tr_chunk_off(int d, int c) {   // 16-byte chunk c of row d
+  return (uint32_t)(d * 128 + ((c ^ ((d ^ (d >> 3)) & 7)) << 4));
+}
+__device__ __forceinline__ uint32_t tr_piece_off(int d, int p) {   // 8-byte piece p of row d
+  return tr_chunk_off(d, p >> 1) + ((p & 1) << 3);
+}
+
+// Transposed [D][32] bf16 tile (32 keys or queries per row, 64-byte rows, four
+// 16-byte chunks, same key permutation as above).
+__device__ __forceinline__ uint32_t tr32_chunk_off(int d, int c) {
+  return (uint32_t)(d * 64 + ((c ^ ((d >> 1) & 3)) << 4));
+}
+__device__ __forceinline__ uint32_t tr32_piece_off(int d, int p) {
+  return tr32_chunk_off(d, p >> 1) + ((p & 1) << 3);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                            0xF, 0xF, true));
+}
+
+// Sum over groups of N lanes (N = 4, 8 or 16, aligned) with DPP; every lane of
+// a group receives the group total.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp_f32<0xB1>(x);                       // quad_perm [1,0,3,2]
+  x += dpp_f32<0x4E>(x);                       // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x += dpp_f32<0x141>(x);    // row_half_mirror
+  if constexpr (N >= 16) x += dpp_f32<0x140>(x);   // row_mirror
+  return x;
+}
+
+// Transpose a 4 (keys) x 8 (d) bf16 block held as four 16-byte rows into
+// eight 8-byte columns: out[j] holds keys 0..3 of column j.
+__device__ __forceinline__ void transpose4x8(const u32x4 (&in)[4], u32x2 (&out)[8]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    // column 2w takes the low halves, column 2w+1 the high halves
+    out[2 * w][0] = __builtin_amdgcn_perm(in[1][w], in[0][w], 0x05040100u);
+    out[2 * w][1] = __builtin_amdgcn_perm(in[3][w], in[2][w], 0x05040100u);
+    out[2 * w + 1][0] = __builtin_amdgcn_perm(in[1][w], in[0][w], 0x07060302u);
+    out[2 * w + 1][1] = __builtin_amdgcn_perm(in[3][w], in[2][w], 0x07060302u);
+  }
+}
+
+}  // namespace fa

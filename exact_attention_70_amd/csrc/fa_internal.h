@@ -1,0 +1,68 @@
+// Internal launch interface between the C-ABI layer (fa_api.cpp) and the
+// kernel translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  float* LSE;
+  int B, H, N, d;
+  float scale;
+  bool causal;
+  int dtype;  // 0 = fp32, 1 = bf16
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const float* LSE;
+  float* dQ;
+  float* dK;
+  float* dV;
+  float* Dvec;  // workspace: [B, H, N] fp32
+  int B, H, N, d;
+  float scale;
+  bool causal;
+  hipStream_t stream;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int block_size, num_seqs, H, d, max_blocks_per_seq, num_blocks;
+  float scale;
+  void* o;
+  float* lse;
+  float* part;      // workspace: partial (m, l, o[d]) per (seq, partition, head)
+  int part_tokens;  // tokens per KV partition
+  int n_parts;      // partitions per sequence (max)
+  hipStream_t stream;
+};
+
+hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_bwd(const BwdArgs& a);
+hipError_t launch_decode(const DecodeArgs& a);
+
+// Decode partitioning shared by the workspace query and the launcher.
+constexpr int kDecodePartTokens = 256;
+inline int decode_n_parts(int max_blocks_per_seq, int block_size) {
+  const long long max_tokens = (long long)max_blocks_per_seq * block_size;
+  return (int)((max_tokens + kDecodePartTokens - 1) / kDecodePartTokens);
+}
+
+}  // namespace fa

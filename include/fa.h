@@ -1,0 +1,172 @@
+/*
+ * libfa -- exact scaled-dot-product attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every tensor argument is a DEVICE pointer owned by the caller; the
+ * library never allocates, frees or retains caller memory and keeps no device
+ * state between calls.  Scratch memory comes only through an explicit
+ * workspace argument whose minimum size the *_workspace_size queries return.
+ *
+ * Synchrony: each call validates its arguments on the host, enqueues its
+ * kernels on `stream` (a hipStream_t passed as void*, NULL = the null stream)
+ * and returns without synchronising.  Outputs are valid once the caller has
+ * synchronised that stream.  Calls are stateless and may be made from several
+ * host threads at once.
+ *
+ * Errors: status codes only; no C++ exception crosses this boundary.  Shapes,
+ * dtypes, null pointers, alignment and workspace size are validated BEFORE
+ * anything is launched, so a call that fails validation writes nothing.  A
+ * launch failure reported by the HIP runtime maps to FA_ERR_HIP.  B == 0 or
+ * num_seqs == 0 is a no-op that returns FA_OK.
+ *
+ * Layouts (row-major, contiguous): Q, K, V, O, dO and the fp32 gradients are
+ * [B, H, N, d]; LSE is [B, H, N] fp32.  This is the [batch, heads, seq,
+ * head_dim] order of the HPC notes "07-16 afternoon: distributed LLM training
+ * and inference", section "Autoregressive language model inference" (the
+ * tensor-shape walk-through, where Q K^T gives [B, heads, S, S] scores and
+ * the softmax-weighted V gives [B, heads, S, head_dim]).  Every tensor
+ * pointer must be 16-byte aligned.
+ *
+ * Score convention: s_ij = scale * (q_i . k_j).  With causal != 0, key j is
+ * visible to query i iff j <= i (each position sees itself and the tokens
+ * before it; same notes and section, on the causal mask).  LSE_i is the
+ * natural log of sum over visible j of exp(s_ij).
+ */
+#ifndef LIBFA_FA_H
+#define LIBFA_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,        /* a required pointer is NULL                          */
+  FA_ERR_SHAPE = -2,       /* a size is negative, zero where not allowed, or too big */
+  FA_ERR_DTYPE = -3,       /* dtype code is not one of fa_dtype                    */
+  FA_ERR_UNSUPPORTED = -4, /* valid but not implemented (head_dim, block_size, ...) */
+  FA_ERR_ALIGN = -5,       /* a tensor pointer is not 16-byte aligned             */
+  FA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than the query returns */
+  FA_ERR_INVALID = -7,     /* block_table / seq_lens contents invalid (FA_DEBUG=1) */
+  FA_ERR_HIP = -8          /* the HIP runtime reported an error                   */
+} fa_status;
+
+typedef enum { FA_DT_F32 = 0, FA_DT_BF16 = 1 } fa_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fa_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int fa_version(void);
+
+/*
+ * fa_fwd -- attention forward, FlashAttention-style.
+ *
+ * Computes O = softmax(scale * Q K^T [masked]) V and LSE per query row, as
+ * defined in the dcwnkz.com GPU/FlashAttention explainer, section
+ * "FlashAttention" (scores Q K^T, softmax, weighted sum of V), by scanning
+ * K/V in tiles with an online softmax: a running maximum and running
+ * denominator per row, with the partial output rescaled by
+ * exp(m_old - m_new) whenever the maximum grows (same section, worked
+ * example; CMU 10-423 L17-L18 notes, sections "Prerequisite 2: online
+ * softmax" and "FlashAttention itself").  The N x N matrix never reaches
+ * memory.
+ *
+ *   Q, K, V  in   [B,H,N,d], dtype `dtype` (FA_DT_BF16 or FA_DT_F32)
+ *   O        out  [B,H,N,d], same dtype as the inputs (bf16: round-to-nearest-even)
+ *   LSE      out  [B,H,N] fp32, natural-log log-sum-exp of the visible scaled scores
+ *   B, H, N  >= 0, >= 1, >= 1 (B == 0 is a no-op); N <= 1<<20
+ *   d        64 or 128 (else FA_ERR_UNSUPPORTED)
+ *   scale    finite; multiplies the raw scores (1/sqrt(d) in the usual setting)
+ *   causal   0 = every key visible; non-zero = key j visible to query i iff j <= i
+ *
+ * bf16 inputs are multiplied on the matrix cores with fp32 accumulation; the
+ * softmax weights are rounded to bf16 before the P V product.  fp32 inputs are
+ * multiplied with fp32 matrix instructions throughout.
+ */
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+           int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_bwd_workspace_size -- bytes of workspace fa_bwd needs for this shape
+ * (the per-row D_i = sum_d dO_id O_id vector, fp32 [B,H,N], rounded up).
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * fa_bwd -- attention backward with recomputation.
+ *
+ * Gradients of a loss L through O = softmax(S) V, S = scale * Q K^T, given
+ * dO = dL/dO.  Following the recomputation principle of the CMU 10-423
+ * L17-L18 notes (section "FlashAttention itself": never store the attention
+ * matrix, recompute the needed block in the backward pass), each tile of
+ * P = exp(S - LSE) is rebuilt from Q, K and the forward's LSE; nothing of
+ * size N x N is stored.  The chain rule written out:
+ *   dV = P^T dO;  dP = dO V^T;  D_i = sum_d dO_id O_id;  dS = P o (dP - D);
+ *   dQ = scale dS K;  dK = scale dS^T Q.
+ *
+ *   Q, K, V, O, dO  in   [B,H,N,d] bf16 (O is the forward's output)
+ *   LSE             in   [B,H,N] fp32 from fa_fwd with the same scale/causal
+ *   dQ, dK, dV      out  [B,H,N,d] fp32 (fully overwritten)
+ *   d               64 or 128; dtype must be FA_DT_BF16
+ *   workspace       device buffer of >= fa_bwd_workspace_size() bytes, 16-B aligned
+ * The result is deterministic (no atomics).
+ */
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+           const float* LSE, float* dQ, float* dK, float* dV,
+           int B, int H, int N, int d, float scale, int causal, int dtype,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_paged_decode_workspace_size -- bytes of workspace fa_paged_decode needs:
+ * per (sequence, head, KV partition) partial results (running max, running
+ * denominator and unnormalised output row, fp32).
+ */
+size_t fa_paged_decode_workspace_size(int num_seqs, int H, int d, int max_blocks_per_seq,
+                                      int block_size);
+
+/*
+ * fa_paged_decode -- one decode step over a paged KV cache.
+ *
+ * The KV cache is cut into fixed-size token blocks stored non-contiguously in
+ * a shared pool; a per-sequence block table maps logical block b to a
+ * physical block, and the attention kernel computes block by block (CMU
+ * 10-423 L17-L18 notes, section "Decoding: PagedAttention").  Each sequence
+ * feeds one new query token, which attends to all of its cached tokens,
+ * itself included (HPC notes, section "Prefill, Decode and inference
+ * scheduling").  Token t of sequence s is slot t % block_size of physical
+ * block block_table[s, t / block_size].  Long sequences are split into KV
+ * partitions whose partial (max, denominator, output) triples are merged by
+ * the rescaling rule of the online softmax (HPC notes, section "Long context
+ * and sequence parallelism").
+ *
+ *   q            in   [num_seqs, H, d] bf16
+ *   k_pool/v_pool in  [num_blocks, block_size, H, d] bf16
+ *   block_table  in   [num_seqs, max_blocks_per_seq] int32 physical block ids;
+ *                     entries past a sequence's last block are never read
+ *   seq_lens     in   [num_seqs] int32, 1 <= seq_lens[s] <= max_blocks_per_seq*block_size
+ *   o            out  [num_seqs, H, d] bf16
+ *   lse          out  [num_seqs, H] fp32 (natural log)
+ *   block_size   16 (else FA_ERR_UNSUPPORTED); d 128 (else FA_ERR_UNSUPPORTED)
+ *   H            a multiple of 4
+ *   workspace    >= fa_paged_decode_workspace_size() bytes, 16-B aligned
+ * The contents of block_table and seq_lens are trusted like a page table.
+ * With the environment variable FA_DEBUG=1 they are copied to the host and
+ * checked first (0 <= entry < num_blocks for every block a sequence uses,
+ * 1 <= seq_len <= max_blocks_per_seq*block_size); a violation returns
+ * FA_ERR_INVALID and launches nothing.  Without FA_DEBUG an out-of-range
+ * entry reads zeros instead of faulting.
+ */
+int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_table, const int32_t* seq_lens, int block_size,
+                    int num_seqs, int H, int d, int max_blocks_per_seq, int num_blocks,
+                    float scale, void* o, float* lse, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBFA_FA_H */

@@ -1,0 +1,130 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fa.h declares, and rejects invalid arguments on the host before any
+launch (these calls return before touching the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_attention_70_amd import binding as libfa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_UNSUP, ERR_ALIGN, ERR_WS, ERR_INVALID, ERR_HIP = \
+    0, -1, -2, -3, -4, -5, -6, -7, -8
+
+# fake but 16-byte aligned, non-null addresses: every call below fails host
+# validation before anything could dereference them
+P = ctypes.c_void_p(0x10000)
+P2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10008)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return libfa.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("fa_fwd", "fa_bwd", "fa_paged_decode", "fa_bwd_workspace_size",
+              "fa_paged_decode_workspace_size", "fa_status_string", "fa_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(libfa.EXPORTED)
+
+
+def test_status_strings(lib):
+    for code in (OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_UNSUP, ERR_ALIGN, ERR_WS, ERR_INVALID,
+                 ERR_HIP):
+        s = libfa.status_string(code)
+        assert s.startswith("FA_") or code == OK
+    assert libfa.status_string(12345) == "unknown libfa status"
+    assert lib.fa_version() >= 100
+
+
+def fwd(lib, q=P, k=P, v=P, o=P2, lse=P2, B=1, H=1, N=64, d=64, scale=0.125, causal=1, dt=1):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dt, None)
+
+
+def test_fwd_validation(lib):
+    assert fwd(lib, dt=7) == ERR_DTYPE
+    assert fwd(lib, H=0) == ERR_SHAPE
+    assert fwd(lib, N=0) == ERR_SHAPE
+    assert fwd(lib, B=-1) == ERR_SHAPE
+    assert fwd(lib, N=(1 << 20) + 1) == ERR_SHAPE
+    assert fwd(lib, scale=float("nan")) == ERR_SHAPE
+    assert fwd(lib, scale=float("inf")) == ERR_SHAPE
+    assert fwd(lib, d=96) == ERR_UNSUP
+    assert fwd(lib, d=256) == ERR_UNSUP
+    assert fwd(lib, q=None) == ERR_NULL
+    assert fwd(lib, lse=None) == ERR_NULL
+    assert fwd(lib, v=MIS) == ERR_ALIGN
+    assert fwd(lib, o=MIS) == ERR_ALIGN
+    # B == 0 is a no-op (nothing is touched, so even NULL pointers are fine)
+    assert fwd(lib, B=0, q=None, k=None, v=None, o=None, lse=None) == OK
+
+
+def test_bwd_validation(lib):
+    ws = lib.fa_bwd_workspace_size(2, 3, 100, 128)
+    assert ws >= 2 * 3 * 100 * 4 and ws % 256 == 0
+    assert lib.fa_bwd_workspace_size(0, 3, 100, 128) == 0
+
+    def bwd(dt=1, d=128, N=100, ws_ptr=P2, ws_bytes=ws, dq=P2, B=2, scale=0.1):
+        return lib.fa_bwd(P, P, P, P, P, P, dq, P2, P2, B, 3, N, d, scale, 1, dt, ws_ptr,
+                          ws_bytes, None)
+    assert bwd(dt=0) == ERR_UNSUP          # fp32 backward not provided
+    assert bwd(dt=5) == ERR_DTYPE
+    assert bwd(d=80) == ERR_UNSUP
+    assert bwd(N=0) == ERR_SHAPE
+    assert bwd(ws_ptr=None) == ERR_WS
+    assert bwd(ws_bytes=ws - 1) == ERR_WS
+    assert bwd(dq=None) == ERR_NULL
+    assert bwd(dq=MIS) == ERR_ALIGN
+    assert bwd(scale=float("nan")) == ERR_SHAPE
+    assert bwd(B=0) == OK
+
+
+def test_decode_validation(lib):
+    ws = lib.fa_paged_decode_workspace_size(64, 32, 128, 256, 16)
+    assert ws >= 64 * 32 * (4096 // 256) * 130 * 4
+    assert lib.fa_paged_decode_workspace_size(0, 32, 128, 256, 16) == 0
+
+    def dec(bs=16, S=4, H=32, d=128, mbps=8, nb=40, dt=1, ws_ptr=P2, ws_bytes=None,
+            table=P, q=P):
+        wsb = lib.fa_paged_decode_workspace_size(max(S, 1), H, d, mbps, bs) if ws_bytes is None \
+            else ws_bytes
+        return lib.fa_paged_decode(q, P, P, table, P, bs, S, H, d, mbps, nb, 0.1, P2, P2, dt,
+                                   ws_ptr, wsb, None)
+    assert dec(bs=32) == ERR_UNSUP
+    assert dec(d=64) == ERR_UNSUP
+    assert dec(H=6) == ERR_UNSUP
+    assert dec(dt=0) == ERR_UNSUP
+    assert dec(dt=3) == ERR_DTYPE
+    assert dec(nb=0) == ERR_SHAPE
+    assert dec(mbps=0) == ERR_SHAPE
+    assert dec(ws_ptr=None) == ERR_WS
+    assert dec(ws_bytes=16) == ERR_WS
+    assert dec(table=None) == ERR_NULL
+    assert dec(q=MIS) == ERR_ALIGN
+    assert dec(table=ctypes.c_void_p(0x10002)) == ERR_ALIGN
+    assert dec(S=0) == OK
+
+
+def test_python_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        libfa.fwd(x, x, x, causal=True)
