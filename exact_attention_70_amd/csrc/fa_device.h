@@ -29,6 +29,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -113,6 +114,37 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 template <int D>
 __device__ __forceinline__ uint32_t rm_off(int r, int c) {
   return (uint32_t)(r * (D * 2) + ((c ^ (r & 7)) << 4));
+}
+
+// Row-major [rows][D] bf16 tile read through the LDS transpose instruction
+// (V tiles): chunk c of row r sits at chunk c ^ f(r), f(r) = 2(r & 3) ^ ((r >> 2) & 1).
+// A transpose read takes 8 bytes from each of 4 consecutive rows per 16-lane
+// group (two adjacent chunks per row); f sends those 8 (row, chunk) pairs to 8
+// distinct chunk positions.
+template <int D>
+__device__ __forceinline__ uint32_t vt_off(int r, int c) {
+  return (uint32_t)(r * (D * 2) + ((c ^ (((r & 3) << 1) ^ ((r >> 2) & 1))) << 4));
+}
+
+// LDS address-space pointers for the direct global->LDS and transpose-read
+// instructions.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Direct buffer -> LDS copy: lane i's 16 bytes (at byte offset `off` inside the
+// resource; zeros when out of range) land at lds_base + 16 * i.  lds_base must
+// be wave-uniform.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, (int)off, 0, 0, 0);
+}
+
+// Transpose read (ds_read_b64_tr_b16).  Within each 16-lane group, lane j
+// receives element (j mod 4) of the four 16-bit values addressed by lanes
+// 4k + j/4, for k = 0..3.
+__device__ __forceinline__ u32x2 ds_read_tr16(const void* lds_addr) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_addr);
+  return __builtin_bit_cast(u32x2, v);
 }
 
 // Transposed [D][BN] bf16 tile holding a BN = 64 key tile column-wise.  Keys

@@ -39,24 +39,40 @@ constexpr int kBM = 128;   // query rows per workgroup
 constexpr int kBN = 64;    // keys per K/V tile
 constexpr int kThreads = 256;
 
+// Copy rows [row0, row0 + ROWS) of a [N][D] bf16 tensor into an LDS tile by
+// direct buffer->LDS transfers.  Each instruction moves 1 KiB (64 lanes x 16
+// bytes) into consecutive LDS bytes; the lane->source mapping applies the tile's
+// chunk swizzle, so the LDS image is the swizzled row-major layout.
+template <int D, int ROWS, bool VSWZ>
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int row0,
+                                         int wave, int lane) {
+  constexpr int DCH = D / 8;
+  constexpr int RPI = 64 / DCH;             // rows per instruction
+  constexpr int NI = ROWS / RPI;            // instructions per tile
+  static_assert(NI % (kThreads / 64) == 0, "tile rows must split evenly over the waves");
+#pragma unroll
+  for (int ii = 0; ii < NI / (kThreads / 64); ++ii) {
+    const int ins = ii * (kThreads / 64) + wave;
+    const int rr = ins * RPI + lane / DCH;  // LDS row written by this lane
+    const int pc = lane % DCH;              // physical chunk written by this lane
+    const int c = VSWZ ? (pc ^ (((rr & 3) << 1) ^ ((rr >> 2) & 1))) : (pc ^ (rr & 7));
+    dma16(r, lds + ins * 1024, (uint32_t)((row0 + rr) * D + c * 8) * 2);
+  }
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int N, float scale_log2, int n_qtiles) {
-  constexpr int DCH = D / 8;             // 16-byte chunks per row
+  // scale_log2 = scale * log2(e): scores are handled in base 2
   constexpr int KSTEPS = D / 16;         // matrix k-steps over the head dim
   constexpr int DT = D / 32;             // 32-row tiles of O^T
-  constexpr int Q_ROUNDS = kBM * DCH / kThreads;
-  constexpr int K_ROUNDS = kBN * DCH / kThreads;
-  constexpr int V_ITEMS = (kBN / 4) * DCH;          // (4-key group, d chunk) items
-  constexpr int V_ROUNDS = (V_ITEMS + kThreads - 1) / kThreads;
-  constexpr int K_BYTES = kBN * D * 2;
-  constexpr int V_BYTES = D * kBN * 2;
-  constexpr int Q_BYTES = kBM * D * 2;
-  constexpr int SMEM = (Q_BYTES > K_BYTES + V_BYTES) ? Q_BYTES : (K_BYTES + V_BYTES);
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-  unsigned char* const sK = smem;
-  unsigned char* const sV = smem + K_BYTES;
+  constexpr int TILE = kBN * D * 2;      // bytes of one K or V tile
+  static_assert(kBM * D * 2 <= 2 * TILE, "query staging must fit one K/V buffer");
+  // Two K/V buffers, declared as separate objects so that reads of one are not
+  // made to wait for transfers into the other.
+  __shared__ __attribute__((aligned(1024))) unsigned char buf0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf1[2 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -77,146 +93,127 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const auto rO = make_rsrc(O + head_off, head_bytes);
   const auto rL = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
 
-  // ---- stage the query tile through LDS, keep this wave's rows in registers
-  {
-    u32x4 qv[Q_ROUNDS];
-#pragma unroll
-    for (int r = 0; r < Q_ROUNDS; ++r) {
-      const int row = r * (kThreads / DCH) + tid / DCH, c = tid % DCH;
-      qv[r] = bload16(rQ, (uint32_t)((q0 + row) * D + c * 8) * 2);
-    }
-#pragma unroll
-    for (int r = 0; r < Q_ROUNDS; ++r) {
-      const int row = r * (kThreads / DCH) + tid / DCH, c = tid % DCH;
-      *(u32x4*)(smem + rm_off<D>(row, c)) = qv[r];
-    }
-  }
+  const int kv_end = CAUSAL ? min(N, q0 + kBM) : N;
+  const int n_kv = (kv_end + kBN - 1) / kBN;
+
+  // ---- stage the query tile (buffer 1) and the first K/V tile (buffer 0)
+  dma_rows<D, kBM, false>(rQ, buf1, q0, wave, lane);
+  dma_rows<D, kBN, false>(rK, buf0, 0, wave, lane);
+  dma_rows<D, kBN, true>(rV, buf0 + TILE, 0, wave, lane);
   __syncthreads();
   bf16x8 qf[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s)
-    qf[s] = *(const bf16x8*)(smem + rm_off<D>(wave * 32 + l32, 2 * s + half));
+    qf[s] = *(const bf16x8*)(buf1 + rm_off<D>(wave * 32 + l32, 2 * s + half));
+  // The softmax takes its maximum over raw scores and folds the scale into one
+  // multiply-add, which needs a positive multiplier: for a negative scale,
+  // negate Q once (exact in bf16) and use |scale|.
+  if (scale_log2 < 0.f) {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(as_u32x4(qf[s]) ^ 0x80008000u);
+    scale_log2 = -scale_log2;
+  }
+  __syncthreads();                                  // buffer 1 free for K/V tile 1
 
-  const int kv_end = CAUSAL ? min(N, q0 + kBM) : N;
-  const int n_kv = (kv_end + kBN - 1) / kBN;
-  const int my_q = q0 + wave * 32 + l32;          // this lane's query row
-  const int wave_qlast = q0 + wave * 32 + 31;     // last query row of this wave
-
-  // ---- K/V prefetch registers (one tile ahead)
-  u32x4 kreg[K_ROUNDS];
-  u32x4 vreg[V_ROUNDS][4];
-  auto load_kv = [&](int kb) {
-#pragma unroll
-    for (int r = 0; r < K_ROUNDS; ++r) {
-      const int row = r * (kThreads / DCH) + tid / DCH, c = tid % DCH;
-      kreg[r] = bload16(rK, (uint32_t)((kb + row) * D + c * 8) * 2);
-    }
-#pragma unroll
-    for (int r = 0; r < V_ROUNDS; ++r) {
-      const int item = r * kThreads + tid;
-      const int c = item % DCH, g = item / DCH;
-      if (item < V_ITEMS) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          vreg[r][i] = bload16(rV, (uint32_t)((kb + 4 * g + i) * D + c * 8) * 2);
-      }
-    }
-  };
-  auto store_kv = [&]() {
-#pragma unroll
-    for (int r = 0; r < K_ROUNDS; ++r) {
-      const int row = r * (kThreads / DCH) + tid / DCH, c = tid % DCH;
-      *(u32x4*)(sK + rm_off<D>(row, c)) = kreg[r];
-    }
-#pragma unroll
-    for (int r = 0; r < V_ROUNDS; ++r) {
-      const int item = r * kThreads + tid;
-      const int c = item % DCH, g = item / DCH;
-      if (item < V_ITEMS) {
-        u32x2 cols[8];
-        transpose4x8(vreg[r], cols);
-        const int p = kpos(4 * g) >> 2;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) *(u32x2*)(sV + tr_piece_off(c * 8 + j, p)) = cols[j];
-      }
-    }
-  };
+  const int my_q = q0 + wave * 32 + l32;            // this lane's query row
+  const int wave_qlast = q0 + wave * 32 + 31;       // last query row of this wave
+  // transpose-read geometry of the V^T operand (see vt_off / ds_read_tr16)
+  const int tr_row = 4 * half + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   f32x16 o[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) o[t] = zero16();
   float m_run = kNegInf;   // running max of scale*log2(e)*score
   float l_run = 0.f;       // this lane's share of the running denominator
+  const float one = 1.0f;
+  const bf16x2 ones = {(__bf16)one, (__bf16)one};
 
-  load_kv(0);
-  for (int j = 0; j < n_kv; ++j) {
+  // One step of the tile loop: tile j is read from `cur` while tile j+1 streams
+  // into `nxt`.  The loop below is unrolled by two so that each step names its
+  // buffers statically and the compiler can tell the transfer target apart from
+  // the buffer being read.
+  auto step = [&](unsigned char* const cur, unsigned char* const nxt, const int j) {
     const int kb = j * kBN;
-    __syncthreads();                 // previous tile fully consumed
-    store_kv();
-    __syncthreads();
-    if (j + 1 < n_kv) load_kv(kb + kBN);
-
-    if (CAUSAL && kb > wave_qlast) continue;   // whole tile above this wave's diagonal
-
-    // S^T = K Q^T for two 32-key sub-tiles
-    f32x16 s[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      s[t] = zero16();
-#pragma unroll
-      for (int k = 0; k < KSTEPS; ++k) {
-        const bf16x8 a = *(const bf16x8*)(sK + rm_off<D>(t * 32 + l32, 2 * k + half));
-        s[t] = mfma_bf16(a, qf[k], s[t]);
-      }
+    if (j + 1 < n_kv) {
+      dma_rows<D, kBN, false>(rK, nxt, kb + kBN, wave, lane);
+      dma_rows<D, kBN, true>(rV, nxt + TILE, kb + kBN, wave, lane);
     }
-
-    // online softmax over this lane's 32 scores (one query row)
-    const bool need_mask = (CAUSAL && kb + kBN - 1 > q0 + wave * 32) || (kb + kBN > N);
-    float mx = kNegInf;
+    if (!(CAUSAL && kb > wave_qlast)) {          // else: whole tile above this wave's diagonal
+      const unsigned char* const sK = cur;
+      const unsigned char* const sV = cur + TILE;
+      // S^T = K Q^T for two 32-key sub-tiles (raw scores)
+      f32x16 s[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t) {
+        s[t] = zero16();
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s[t][i] * scale_log2;
-        if (need_mask) {
-          const int key = kb + t * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          if ((CAUSAL && key > my_q) || key >= N) x = kNegInf;
+        for (int k = 0; k < KSTEPS; ++k) {
+          const bf16x8 a = *(const bf16x8*)(sK + rm_off<D>(t * 32 + l32, 2 * k + half));
+          s[t] = mfma_bf16(a, qf[k], s[t]);
         }
-        s[t][i] = x;
-        mx = fmaxf(mx, x);
       }
-    mx = fmaxf(mx, swap_half(mx));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    float rs = 0.f;
-    bf16x8 pb[4];
+      // online softmax over this lane's 32 scores (one query row)
+      const bool need_mask = (CAUSAL && kb + kBN - 1 > q0 + wave * 32) || (kb + kBN > N);
+      if (need_mask) {
+        // key offset within the tile that this lane may still see
+        const int lim = min(CAUSAL ? my_q : N - 1, N - 1) - kb - 4 * half;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const float p0 = fast_exp2(s[t][i] - m_use);
-        const float p1 = fast_exp2(s[t][i + 1] - m_use);
-        rs += p0 + p1;
-        const bf16x2 pk = {(__bf16)p0, (__bf16)p1};
-        pb[2 * t + (i >> 3)][i & 7] = pk[0];
-        pb[2 * t + (i >> 3)][(i & 7) + 1] = pk[1];
+          for (int i = 0; i < 16; ++i)
+            if (t * 32 + 8 * (i >> 2) + (i & 3) > lim) s[t][i] = kNegInf;
       }
-    l_run = l_run * alpha + rs;
+      float mx = kNegInf;
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
-
-    // O^T += V^T P^T
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[t][i], s[t][i + 1]));
+      mx = fmaxf(mx, swap_half(mx));
+      const float m_new = fmaxf(m_run, mx * scale_log2);
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+        // some row's maximum grew: scale its numerator and denominator by
+        // exp(m_old - m_new) (rows whose maximum did not grow get exactly 1)
+        const float alpha = fast_exp2(m_run - ((m_new == kNegInf) ? 0.f : m_new));
+        l_run *= alpha;
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+        for (int t = 0; t < DT; ++t)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bf16x8 a = *(const bf16x8*)(sV + tr_chunk_off(t * 32 + l32, 2 * u + half));
-        o[t] = mfma_bf16(a, pb[u], o[t]);
+          for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+        m_run = m_new;
       }
+      const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
+      bf16x8 pb[4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const float p0 = fast_exp2(fmaf(s[t][i], scale_log2, neg_m));
+          const float p1 = fast_exp2(fmaf(s[t][i + 1], scale_log2, neg_m));
+          const bf16x2 pk = {(__bf16)p0, (__bf16)p1};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l_run, false);
+          pb[2 * t + (i >> 3)][i & 7] = pk[0];
+          pb[2 * t + (i >> 3)][(i & 7) + 1] = pk[1];
+        }
+      // O^T += V^T P^T; the V^T operand (lane: one d, 8 keys) comes from two
+      // transpose reads of the row-major V tile (4 keys each)
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int row = 16 * u + tr_row;
+          const int col = t * 32 + tr_col;
+          const u32x2 lo = ds_read_tr16(sV + vt_off<D>(row, col >> 3) + (col & 7) * 2);
+          const u32x2 hi = ds_read_tr16(sV + vt_off<D>(row + 8, col >> 3) + (col & 7) * 2);
+          const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+          o[t] = mfma_bf16(as_bf16x8(a), pb[u], o[t]);
+        }
+    }
+    __syncthreads();      // tile j consumed by every wave; tile j+1 landed
+  };
+  for (int j = 0; j < n_kv; j += 2) {
+    step(buf0, buf1, j);
+    if (j + 1 < n_kv) step(buf1, buf0, j + 1);
   }
 
   // ---- epilogue: O = O^T / l, LSE = ln(sum exp) = (m + log2 l) ln 2
