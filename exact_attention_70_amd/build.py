@@ -20,6 +20,10 @@ LIB = os.path.join(PKG, "libfa.so")
 ARCH = os.environ.get("FA_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip"]
+# Per-source extra flags.  The attention kernels never test for NaN, so they
+# are built without NaN-preserving semantics; that lets max() compile to a
+# single v_max/v_max3 instead of canonicalize + max.
+EXTRA = {"fa_fwd.hip": ["-fno-honor-nans"], "fa_bwd.hip": ["-fno-honor-nans"]}
 
 # Packed fp32 VALU forms are disabled for all device code; hipcc's host pass
 # warns that it does not know the feature, which is harmless.
@@ -38,7 +42,7 @@ def hipcc() -> str:
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-c", os.path.join(CSRC, src),
-           "-o", obj] + COMMON + DEVICE_FLAGS
+           "-o", obj] + COMMON + DEVICE_FLAGS + EXTRA.get(src, [])
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

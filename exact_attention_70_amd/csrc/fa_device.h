@@ -95,6 +95,18 @@ __device__ __forceinline__ float swap_half(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// Workgroup barriers for LDS producer/consumer phases.  barrier_lds() waits
+// only for this wave's LDS accesses (so buffer->LDS transfers it issued may
+// still be in flight); barrier_all() also waits for its outstanding vector
+// memory operations, which includes those transfers.  The "memory" clobber
+// keeps the compiler from moving memory accesses across either barrier.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ void barrier_all() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Map the hardware workgroup id to a logical tile id so that consecutive
 // logical tiles land on the same XCD: the dispatcher hands workgroups to the
 // 8 XCDs round-robin, so hardware id b runs on XCD b % 8.  The map is a
@@ -106,45 +118,33 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 }
 
 // --------------------------------------------------------------------------
-// LDS tile layouts.  Rows are stored unpadded; 16-byte chunks are XOR-swizzled
-// so that the matrix-operand reads (eight consecutive rows, same chunk) hit
-// distinct banks.
+// LDS tile layouts.  gfx950's LDS serves 256 bytes per clock as 64 banks of 4
+// bytes.  Rows are stored unpadded and 16-byte chunks are XOR-swizzled so that
+// each clock's worth of a matrix-operand read touches 64 distinct banks.
 
-// Row-major [rows][D] bf16 tile: byte offset of 16-byte chunk `c` of row `r`.
+// Row-major [rows][D] bf16 tile read as 16-byte A/B operands: a 16-lane clock
+// reads one chunk from each of 16 consecutive rows, so those 16 rows must put
+// that chunk at 16 distinct 16-byte positions of the bank space.
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+  return (D == 128) ? (r & 15) : ((r >> 1) & 7);     // D = 64: two rows per 256 bytes
+}
 template <int D>
 __device__ __forceinline__ uint32_t rm_off(int r, int c) {
-  return (uint32_t)(r * (D * 2) + ((c ^ (r & 7)) << 4));
+  return (uint32_t)(r * (D * 2) + ((c ^ k_swz<D>(r)) << 4));
 }
 
 // Row-major [rows][D] bf16 tile read through the LDS transpose instruction
-// (V tiles): chunk c of row r sits at chunk c ^ f(r), f(r) = 2(r & 3) ^ ((r >> 2) & 1).
-// A transpose read takes 8 bytes from each of 4 consecutive rows per 16-lane
-// group (two adjacent chunks per row); f sends those 8 (row, chunk) pairs to 8
-// distinct chunk positions.
+// (V tiles): a 32-lane clock reads a 64-byte span (two chunks per 16-lane
+// group) from each of 4 consecutive rows; the swizzle moves those 4 spans to 4
+// different 64-byte windows of the bank space.
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {
+  return (D == 128) ? (4 * (r & 3)) : (4 * ((r >> 1) & 1));
+}
 template <int D>
 __device__ __forceinline__ uint32_t vt_off(int r, int c) {
-  return (uint32_t)(r * (D * 2) + ((c ^ (((r & 3) << 1) ^ ((r >> 2) & 1))) << 4));
-}
-
-// LDS address-space pointers for the direct global->LDS and transpose-read
-// instructions.
-typedef __attribute__((address_space(3))) void lds_void;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// Direct buffer -> LDS copy: lane i's 16 bytes (at byte offset `off` inside the
-// resource; zeros when out of range) land at lds_base + 16 * i.  lds_base must
-// be wave-uniform.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, (int)off, 0, 0, 0);
-}
-
-// Transpose read (ds_read_b64_tr_b16).  Within each 16-lane group, lane j
-// receives element (j mod 4) of the four 16-bit values addressed by lanes
-// 4k + j/4, for k = 0..3.
-__device__ __forceinline__ u32x2 ds_read_tr16(const void* lds_addr) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_addr);
-  return __builtin_bit_cast(u32x2, v);
+  return (uint32_t)(r * (D * 2) + ((c ^ v_swz<D>(r)) << 4));
 }
 
 // Transposed [D][BN] bf16 tile holding a BN = 64 key tile column-wise.  Keys
@@ -170,6 +170,27 @@ __device__ __forceinline__ uint32_t tr32_chunk_off(int d, int c) {
 }
 __device__ __forceinline__ uint32_t tr32_piece_off(int d, int p) {
   return tr32_chunk_off(d, p >> 1) + ((p & 1) << 3);
+}
+
+// LDS address-space pointers for the direct global->LDS and transpose-read
+// instructions.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Direct buffer -> LDS copy: lane i's 16 bytes (at byte offset `off` inside the
+// resource; zeros when out of range) land at lds_base + 16 * i.  lds_base must
+// be wave-uniform.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, (int)off, 0, 0, 0);
+}
+
+// Transpose read (ds_read_b64_tr_b16).  Within each 16-lane group, lane j
+// receives element (j mod 4) of the four 16-bit values addressed by lanes
+// 4k + j/4, for k = 0..3.
+__device__ __forceinline__ u32x2 ds_read_tr16(const void* lds_addr) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_addr);
+  return __builtin_bit_cast(u32x2, v);
 }
 
 template <int CTRL>

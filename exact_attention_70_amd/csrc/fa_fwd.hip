@@ -55,7 +55,7 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, unsigned char
     const int ins = ii * (kThreads / 64) + wave;
     const int rr = ins * RPI + lane / DCH;  // LDS row written by this lane
     const int pc = lane % DCH;              // physical chunk written by this lane
-    const int c = VSWZ ? (pc ^ (((rr & 3) << 1) ^ ((rr >> 2) & 1))) : (pc ^ (rr & 7));
+    const int c = pc ^ (VSWZ ? v_swz<D>(rr) : k_swz<D>(rr));
     dma16(r, lds + ins * 1024, (uint32_t)((row0 + rr) * D + c * 8) * 2);
   }
 }
@@ -68,11 +68,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   constexpr int KSTEPS = D / 16;         // matrix k-steps over the head dim
   constexpr int DT = D / 32;             // 32-row tiles of O^T
   constexpr int TILE = kBN * D * 2;      // bytes of one K or V tile
-  static_assert(kBM * D * 2 <= 2 * TILE, "query staging must fit one K/V buffer");
-  // Two K/V buffers, declared as separate objects so that reads of one are not
-  // made to wait for transfers into the other.
-  __shared__ __attribute__((aligned(1024))) unsigned char buf0[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char buf1[2 * TILE];
+  static_assert(kBM == 2 * kBN, "the query tile is staged in two K/V-sized halves");
+  // Two-slot rings for K and for V, four separate objects so that reads of one
+  // slot are never made to wait for transfers into another.
+  __shared__ __attribute__((aligned(1024))) unsigned char sK0[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char sK1[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char sV0[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char sV1[TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -95,16 +97,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   const int kv_end = CAUSAL ? min(N, q0 + kBM) : N;
   const int n_kv = (kv_end + kBN - 1) / kBN;
+  // tiles [0, n_full) need no masking for any row of this workgroup
+  const int n_full = min(CAUSAL ? q0 / kBN : n_kv, N / kBN);
 
-  // ---- stage the query tile (buffer 1) and the first K/V tile (buffer 0)
-  dma_rows<D, kBM, false>(rQ, buf1, q0, wave, lane);
-  dma_rows<D, kBN, false>(rK, buf0, 0, wave, lane);
-  dma_rows<D, kBN, true>(rV, buf0 + TILE, 0, wave, lane);
+  // ---- stage the query tile (two halves in slot 1 of each ring) and K_0, V_0
+  dma_rows<D, kBN, false>(rQ, sK1, q0, wave, lane);
+  dma_rows<D, kBN, false>(rQ, sV1, q0 + kBN, wave, lane);
+  dma_rows<D, kBN, false>(rK, sK0, 0, wave, lane);
+  dma_rows<D, kBN, true>(rV, sV0, 0, wave, lane);
   __syncthreads();
   bf16x8 qf[KSTEPS];
+  {
+    const unsigned char* const sQ = (wave < 2) ? sK1 : sV1;
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s)
-    qf[s] = *(const bf16x8*)(buf1 + rm_off<D>(wave * 32 + l32, 2 * s + half));
+    for (int s = 0; s < KSTEPS; ++s)
+      qf[s] = *(const bf16x8*)(sQ + rm_off<D>((wave & 1) * 32 + l32, 2 * s + half));
+  }
   // The softmax takes its maximum over raw scores and folds the scale into one
   // multiply-add, which needs a positive multiplier: for a negative scale,
   // negate Q once (exact in bf16) and use |scale|.
@@ -113,10 +121,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(as_u32x4(qf[s]) ^ 0x80008000u);
     scale_log2 = -scale_log2;
   }
-  __syncthreads();                                  // buffer 1 free for K/V tile 1
+  __syncthreads();                                  // slot 1 of both rings free again
 
   const int my_q = q0 + wave * 32 + l32;            // this lane's query row
-  const int wave_qlast = q0 + wave * 32 + 31;       // last query row of this wave
   // transpose-read geometry of the V^T operand (see vt_off / ds_read_tr16)
   const int tr_row = 4 * half + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -124,97 +131,133 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   f32x16 o[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) o[t] = zero16();
-  float m_run = kNegInf;   // running max of scale*log2(e)*score
+  float m_run = kNegInf;   // running max of scale*log2(e)*score (through the last reduced tile)
   float l_run = 0.f;       // this lane's share of the running denominator
+  float alpha = 1.f;       // exp2(m_old - m_new) of the last reduced tile
+  bool grew = false;       // did any row's maximum grow in the last reduced tile
   const float one = 1.0f;
   const bf16x2 ones = {(__bf16)one, (__bf16)one};
+  f32x16 s[2];             // raw scores of the last tile whose S was computed
 
-  // One step of the tile loop: tile j is read from `cur` while tile j+1 streams
-  // into `nxt`.  The loop below is unrolled by two so that each step names its
-  // buffers statically and the compiler can tell the transfer target apart from
-  // the buffer being read.
-  auto step = [&](unsigned char* const cur, unsigned char* const nxt, const int j) {
-    const int kb = j * kBN;
-    if (j + 1 < n_kv) {
-      dma_rows<D, kBN, false>(rK, nxt, kb + kBN, wave, lane);
-      dma_rows<D, kBN, true>(rV, nxt + TILE, kb + kBN, wave, lane);
+  // -- the four stages of one tile ------------------------------------------
+  // S = K_j Q^T for two 32-key sub-tiles
+  auto qk = [&](const unsigned char* sK) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      s[t] = zero16();
+#pragma unroll
+      for (int k = 0; k < KSTEPS; ++k) {
+        const bf16x8 a = *(const bf16x8*)(sK + rm_off<D>(t * 32 + l32, 2 * k + half));
+        s[t] = mfma_bf16(a, qf[k], s[t]);
+      }
     }
-    if (!(CAUSAL && kb > wave_qlast)) {          // else: whole tile above this wave's diagonal
-      const unsigned char* const sK = cur;
-      const unsigned char* const sV = cur + TILE;
-      // S^T = K Q^T for two 32-key sub-tiles (raw scores)
-      f32x16 s[2];
+  };
+  // keys beyond this lane's row (causal) or beyond N become -inf
+  auto mask = [&](int kb) {
+    const int lim = min(CAUSAL ? my_q : N - 1, N - 1) - kb - 4 * half;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        s[t] = zero16();
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int k = 0; k < KSTEPS; ++k) {
-          const bf16x8 a = *(const bf16x8*)(sK + rm_off<D>(t * 32 + l32, 2 * k + half));
-          s[t] = mfma_bf16(a, qf[k], s[t]);
-        }
+      for (int i = 0; i < 16; ++i)
+        if (t * 32 + 8 * (i >> 2) + (i & 3) > lim) s[t][i] = kNegInf;
+  };
+  // row max of the new tile, updated running max, rescale factor
+  auto reduce = [&]() {
+    float mx = kNegInf;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[t][i], s[t][i + 1]));
+    mx = fmaxf(mx, swap_half(mx));
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    grew = __builtin_amdgcn_ballot_w64(m_new > m_run) != 0;
+    alpha = fast_exp2(m_run - ((m_new == kNegInf) ? 0.f : m_new));   // 1 where m did not grow
+    m_run = m_new;
+  };
+  // probabilities P = exp2(c*s - m) rounded to bf16 and packed as the B
+  // operands of the P V product; accumulates the denominator
+  auto probs = [&](u32x4 (&pb)[4]) {
+    const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
+    float rs = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float p0 = fast_exp2(fmaf(s[t][i], scale_log2, neg_m));
+        const float p1 = fast_exp2(fmaf(s[t][i + 1], scale_log2, neg_m));
+        const uint32_t pk = pack_bf16(p0, p1);
+        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, rs, false);
+        pb[2 * t + (i >> 3)][(i & 7) >> 1] = pk;
       }
-      // online softmax over this lane's 32 scores (one query row)
-      const bool need_mask = (CAUSAL && kb + kBN - 1 > q0 + wave * 32) || (kb + kBN > N);
-      if (need_mask) {
-        // key offset within the tile that this lane may still see
-        const int lim = min(CAUSAL ? my_q : N - 1, N - 1) - kb - 4 * half;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (t * 32 + 8 * (i >> 2) + (i & 3) > lim) s[t][i] = kNegInf;
-      }
-      float mx = kNegInf;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[t][i], s[t][i + 1]));
-      mx = fmaxf(mx, swap_half(mx));
-      const float m_new = fmaxf(m_run, mx * scale_log2);
-      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
-        // some row's maximum grew: scale its numerator and denominator by
-        // exp(m_old - m_new) (rows whose maximum did not grow get exactly 1)
-        const float alpha = fast_exp2(m_run - ((m_new == kNegInf) ? 0.f : m_new));
-        l_run *= alpha;
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
-        m_run = m_new;
-      }
-      const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
-      bf16x8 pb[4];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const float p0 = fast_exp2(fmaf(s[t][i], scale_log2, neg_m));
-          const float p1 = fast_exp2(fmaf(s[t][i + 1], scale_log2, neg_m));
-          const bf16x2 pk = {(__bf16)p0, (__bf16)p1};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l_run, false);
-          pb[2 * t + (i >> 3)][i & 7] = pk[0];
-          pb[2 * t + (i >> 3)][(i & 7) + 1] = pk[1];
-        }
-      // O^T += V^T P^T; the V^T operand (lane: one d, 8 keys) comes from two
-      // transpose reads of the row-major V tile (4 keys each)
+    l_run = fmaf(l_run, alpha, rs);
+  };
+  // exp(m_old - m_new) rescale of the accumulated output (only when some row grew)
+  auto rescale = [&]() {
+    if (grew) {
 #pragma unroll
       for (int t = 0; t < DT; ++t)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int row = 16 * u + tr_row;
-          const int col = t * 32 + tr_col;
-          const u32x2 lo = ds_read_tr16(sV + vt_off<D>(row, col >> 3) + (col & 7) * 2);
-          const u32x2 hi = ds_read_tr16(sV + vt_off<D>(row + 8, col >> 3) + (col & 7) * 2);
-          const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-          o[t] = mfma_bf16(as_bf16x8(a), pb[u], o[t]);
-        }
+        for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
     }
-    __syncthreads();      // tile j consumed by every wave; tile j+1 landed
   };
-  for (int j = 0; j < n_kv; j += 2) {
-    step(buf0, buf1, j);
-    if (j + 1 < n_kv) step(buf1, buf0, j + 1);
+  // O^T += V^T P^T; the V^T operand (lane: one d, 8 keys) comes from two
+  // transpose reads of the row-major V tile (4 keys each)
+  auto pv = [&](const unsigned char* sV, const u32x4 (&pb)[4]) {
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = 16 * u + tr_row;
+        const int col = t * 32 + tr_col;
+        const u32x2 lo = ds_read_tr16(sV + vt_off<D>(row, col >> 3) + (col & 7) * 2);
+        const u32x2 hi = ds_read_tr16(sV + vt_off<D>(row + 8, col >> 3) + (col & 7) * 2);
+        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+        o[t] = mfma_bf16(as_bf16x8(a), as_bf16x8(pb[u]), o[t]);
+      }
+  };
+  auto need_mask = [&](int j) { return j >= n_full; };
+
+  // -- software pipeline over the K/V tiles ------------------------------------
+  // Iteration j overlaps the matrix-core work of tile j (S_j = K_j Q^T) with
+  // the exponentials of tile j-1, then the P_{j-1} V_{j-1} product with the row
+  // reduction of tile j.  K_j sits in ring slot j&1; V_{j-1} in slot (j-1)&1;
+  // K_{j+1} and V_j stream into the other slots meanwhile.
+  // prologue: tile 0
+  if (n_kv > 1) dma_rows<D, kBN, false>(rK, sK1, kBN, wave, lane);
+  qk(sK0);
+  if (need_mask(0)) mask(0);
+  reduce();
+  __syncthreads();
+  auto iter = [&](const int j, const unsigned char* kcur, unsigned char* knxt,
+                  const unsigned char* vprev, unsigned char* vcur) {
+    if (j + 1 < n_kv) dma_rows<D, kBN, false>(rK, knxt, (j + 1) * kBN, wave, lane);
+    dma_rows<D, kBN, true>(rV, vcur, j * kBN, wave, lane);
+    u32x4 pb[4];
+    probs(pb);            // P_{j-1}  (overlaps S_j below)
+    qk(kcur);             // S_j
+    rescale();            // by tile j-1's factor, before P_{j-1} V_{j-1} is added
+    if (need_mask(j)) mask(j * kBN);
+    pv(vprev, pb);        // P_{j-1} V_{j-1}
+    reduce();             // tile j's max (overlaps the P V product above)
+    __syncthreads();
+  };
+  int j = 1;
+  for (; j + 1 < n_kv; j += 2) {
+    iter(j, sK1, sK0, sV0, sV1);
+    iter(j + 1, sK0, sK1, sV1, sV0);
   }
+  if (j < n_kv) {
+    iter(j, sK1, sK0, sV0, sV1);
+    ++j;
+  }
+  // epilogue: P V of the last tile (its V sits in slot (n_kv-1)&1)
+  {
+    u32x4 pb[4];
+    probs(pb);
+    rescale();
+    pv(((n_kv - 1) & 1) ? sV1 : sV0, pb);
+  }
+  // (the V slot chosen at run time above is only read; nothing is in flight)
 
   // ---- epilogue: O = O^T / l, LSE = ln(sum exp) = (m + log2 l) ln 2
   const float l_tot = l_run + swap_half(l_run);
@@ -378,3 +421,4 @@ hipError_t launch_fwd(const FwdArgs& a) {
 }
 
 }  // namespace fa
+
