@@ -19,6 +19,7 @@ namespace fa {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -122,29 +123,24 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 // bytes.  Rows are stored unpadded and 16-byte chunks are XOR-swizzled so that
 // each clock's worth of a matrix-operand read touches 64 distinct banks.
 
-// Row-major [rows][D] bf16 tile read as 16-byte A/B operands: a 16-lane clock
-// reads one chunk from each of 16 consecutive rows, so those 16 rows must put
-// that chunk at 16 distinct 16-byte positions of the bank space.
+// Every bf16 tile is stored row-major [rows][D] with one swizzle that serves
+// both kinds of operand read:
+//   * 16-byte reads (A/B operands): a 16-lane clock reads the same chunk of 16
+//     consecutive rows, which must land on 16 distinct 16-byte bank positions;
+//   * transpose reads (ds_read_b64_tr_b16, for V^T, dO^T, Q^T, K^T operands): a
+//     32-lane clock reads a 64-byte span (four chunks, 4-aligned) of each of 4
+//     consecutive rows, which must land in 4 distinct 64-byte bank windows.
+// D = 128 (16 chunks = 256 bytes per row): f(r) = (r & 3) << 2 | (r >> 2) & 3.
+// D = 64 (8 chunks; two rows share the 256-byte bank space):
+//   f(r) = ((r >> 1) & 1) << 2 | (r >> 2) & 3.
 template <int D>
-__device__ __forceinline__ int k_swz(int r) {
-  return (D == 128) ? (r & 15) : ((r >> 1) & 7);     // D = 64: two rows per 256 bytes
+__device__ __forceinline__ int tile_swz(int r) {
+  return (D == 128) ? (((r & 3) << 2) | ((r >> 2) & 3))
+                    : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 template <int D>
-__device__ __forceinline__ uint32_t rm_off(int r, int c) {
-  return (uint32_t)(r * (D * 2) + ((c ^ k_swz<D>(r)) << 4));
-}
-
-// Row-major [rows][D] bf16 tile read through the LDS transpose instruction
-// (V tiles): a 32-lane clock reads a 64-byte span (two chunks per 16-lane
-// group) from each of 4 consecutive rows; the swizzle moves those 4 spans to 4
-// different 64-byte windows of the bank space.
-template <int D>
-__device__ __forceinline__ int v_swz(int r) {
-  return (D == 128) ? (4 * (r & 3)) : (4 * ((r >> 1) & 1));
-}
-template <int D>
-__device__ __forceinline__ uint32_t vt_off(int r, int c) {
-  return (uint32_t)(r * (D * 2) + ((c ^ v_swz<D>(r)) << 4));
+__device__ __forceinline__ uint32_t tile_off(int r, int c) {       // 16-byte chunk c of row r
+  return (uint32_t)(r * (D * 2) + ((c ^ tile_swz<D>(r)) << 4));
 }
 
 // Transposed [D][BN] bf16 tile holding a BN = 64 key tile column-wise.  Keys
@@ -191,6 +187,27 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds_base, 
 __device__ __forceinline__ u32x2 ds_read_tr16(const void* lds_addr) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_addr);
   return __builtin_bit_cast(u32x2, v);
+}
+
+// Copy rows [row0, row0 + ROWS) of a [N][D] bf16 tensor into an LDS tile by
+// direct buffer->LDS transfers.  Each instruction moves 1 KiB (64 lanes x 16
+// bytes) into consecutive LDS bytes; the lane->source mapping applies the tile's
+// chunk swizzle, so the LDS image is the swizzled row-major layout.
+template <int D, int ROWS, int NWAVES>
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int row0,
+                                         int wave, int lane) {
+  constexpr int DCH = D / 8;
+  constexpr int RPI = 64 / DCH;             // rows per instruction
+  constexpr int NI = ROWS / RPI;            // instructions per tile
+  static_assert(NI % (NWAVES) == 0, "tile rows must split evenly over the waves");
+#pragma unroll
+  for (int ii = 0; ii < NI / (NWAVES); ++ii) {
+    const int ins = ii * (NWAVES) + wave;
+    const int rr = ins * RPI + lane / DCH;  // LDS row written by this lane
+    const int pc = lane % DCH;              // physical chunk written by this lane
+    const int c = pc ^ tile_swz<D>(rr);
+    dma16(r, lds + ins * 1024, (uint32_t)((row0 + rr) * D + c * 8) * 2);
+  }
 }
 
 template <int CTRL>

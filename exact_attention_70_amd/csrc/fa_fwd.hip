@@ -39,27 +39,6 @@ constexpr int kBM = 128;   // query rows per workgroup
 constexpr int kBN = 64;    // keys per K/V tile
 constexpr int kThreads = 256;
 
-// Copy rows [row0, row0 + ROWS) of a [N][D] bf16 tensor into an LDS tile by
-// direct buffer->LDS transfers.  Each instruction moves 1 KiB (64 lanes x 16
-// bytes) into consecutive LDS bytes; the lane->source mapping applies the tile's
-// chunk swizzle, so the LDS image is the swizzled row-major layout.
-template <int D, int ROWS, bool VSWZ>
-__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int row0,
-                                         int wave, int lane) {
-  constexpr int DCH = D / 8;
-  constexpr int RPI = 64 / DCH;             // rows per instruction
-  constexpr int NI = ROWS / RPI;            // instructions per tile
-  static_assert(NI % (kThreads / 64) == 0, "tile rows must split evenly over the waves");
-#pragma unroll
-  for (int ii = 0; ii < NI / (kThreads / 64); ++ii) {
-    const int ins = ii * (kThreads / 64) + wave;
-    const int rr = ins * RPI + lane / DCH;  // LDS row written by this lane
-    const int pc = lane % DCH;              // physical chunk written by this lane
-    const int c = pc ^ (VSWZ ? v_swz<D>(rr) : k_swz<D>(rr));
-    dma16(r, lds + ins * 1024, (uint32_t)((row0 + rr) * D + c * 8) * 2);
-  }
-}
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
@@ -101,17 +80,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int n_full = min(CAUSAL ? q0 / kBN : n_kv, N / kBN);
 
   // ---- stage the query tile (two halves in slot 1 of each ring) and K_0, V_0
-  dma_rows<D, kBN, false>(rQ, sK1, q0, wave, lane);
-  dma_rows<D, kBN, false>(rQ, sV1, q0 + kBN, wave, lane);
-  dma_rows<D, kBN, false>(rK, sK0, 0, wave, lane);
-  dma_rows<D, kBN, true>(rV, sV0, 0, wave, lane);
+  dma_rows<D, kBN, kThreads / 64>(rQ, sK1, q0, wave, lane);
+  dma_rows<D, kBN, kThreads / 64>(rQ, sV1, q0 + kBN, wave, lane);
+  dma_rows<D, kBN, kThreads / 64>(rK, sK0, 0, wave, lane);
+  dma_rows<D, kBN, kThreads / 64>(rV, sV0, 0, wave, lane);
   __syncthreads();
   bf16x8 qf[KSTEPS];
   {
     const unsigned char* const sQ = (wave < 2) ? sK1 : sV1;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
-      qf[s] = *(const bf16x8*)(sQ + rm_off<D>((wave & 1) * 32 + l32, 2 * s + half));
+      qf[s] = *(const bf16x8*)(sQ + tile_off<D>((wave & 1) * 32 + l32, 2 * s + half));
   }
   // The softmax takes its maximum over raw scores and folds the scale into one
   // multiply-add, which needs a positive multiplier: for a negative scale,
@@ -124,7 +103,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   __syncthreads();                                  // slot 1 of both rings free again
 
   const int my_q = q0 + wave * 32 + l32;            // this lane's query row
-  // transpose-read geometry of the V^T operand (see vt_off / ds_read_tr16)
+  // transpose-read geometry of the V^T operand (see tile_off / ds_read_tr16)
   const int tr_row = 4 * half + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
@@ -147,7 +126,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       s[t] = zero16();
 #pragma unroll
       for (int k = 0; k < KSTEPS; ++k) {
-        const bf16x8 a = *(const bf16x8*)(sK + rm_off<D>(t * 32 + l32, 2 * k + half));
+        const bf16x8 a = *(const bf16x8*)(sK + tile_off<D>(t * 32 + l32, 2 * k + half));
         s[t] = mfma_bf16(a, qf[k], s[t]);
       }
     }
@@ -209,8 +188,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       for (int u = 0; u < 4; ++u) {
         const int row = 16 * u + tr_row;
         const int col = t * 32 + tr_col;
-        const u32x2 lo = ds_read_tr16(sV + vt_off<D>(row, col >> 3) + (col & 7) * 2);
-        const u32x2 hi = ds_read_tr16(sV + vt_off<D>(row + 8, col >> 3) + (col & 7) * 2);
+        const u32x2 lo = ds_read_tr16(sV + tile_off<D>(row, col >> 3) + (col & 7) * 2);
+        const u32x2 hi = ds_read_tr16(sV + tile_off<D>(row + 8, col >> 3) + (col & 7) * 2);
         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
         o[t] = mfma_bf16(as_bf16x8(a), as_bf16x8(pb[u]), o[t]);
       }
@@ -223,15 +202,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   // reduction of tile j.  K_j sits in ring slot j&1; V_{j-1} in slot (j-1)&1;
   // K_{j+1} and V_j stream into the other slots meanwhile.
   // prologue: tile 0
-  if (n_kv > 1) dma_rows<D, kBN, false>(rK, sK1, kBN, wave, lane);
+  if (n_kv > 1) dma_rows<D, kBN, kThreads / 64>(rK, sK1, kBN, wave, lane);
   qk(sK0);
   if (need_mask(0)) mask(0);
   reduce();
   __syncthreads();
   auto iter = [&](const int j, const unsigned char* kcur, unsigned char* knxt,
                   const unsigned char* vprev, unsigned char* vcur) {
-    if (j + 1 < n_kv) dma_rows<D, kBN, false>(rK, knxt, (j + 1) * kBN, wave, lane);
-    dma_rows<D, kBN, true>(rV, vcur, j * kBN, wave, lane);
+    if (j + 1 < n_kv) dma_rows<D, kBN, kThreads / 64>(rK, knxt, (j + 1) * kBN, wave, lane);
+    dma_rows<D, kBN, kThreads / 64>(rV, vcur, j * kBN, wave, lane);
     u32x4 pb[4];
     probs(pb);            // P_{j-1}  (overlaps S_j below)
     qk(kcur);             // S_j
