@@ -68,7 +68,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of parts to run (profiling aid)")
+    ap.add_argument("--only", default="",
+                    help="comma list of parts to run: fwd_c3, fwd_c2, fwd_c4, bwd_c4, decode_c5, "
+                         "copy_calib (a 1 GiB device copy used to scale the HBM-traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -136,10 +138,18 @@ def main():
         parts["decode_c5"] = dict(fn=lambda: binding.paged_decode(
             pd["q"], pd["k_pool"], pd["v_pool"], pd["block_table"], pd["seq_lens"], block_size=16,
             scale=c5.scale, workspace=wsd, out=od, lse=lsed), bytes=kv_bytes, tokens=tokens)
+    if "copy_calib" in only:
+        # plain device copy of known size: the HBM-traffic counters of the kernels
+        # are scaled by what the same counters read for this copy
+        src = torch.empty(256 << 20, dtype=torch.float32, device=dev)      # 1 GiB
+        src.fill_(1.0)
+        dst = torch.empty_like(src)
+        parts["copy_calib"] = dict(fn=lambda: dst.copy_(src), bytes=2 * src.numel() * 4)
     torch.cuda.synchronize()
     log(f"inputs ready: {list(parts)}")
 
-    order = [n for n in ("fwd_c3", "fwd_c2", "fwd_c4", "bwd_c4", "decode_c5") if n in parts]
+    order = [n for n in ("fwd_c3", "fwd_c2", "fwd_c4", "bwd_c4", "decode_c5", "copy_calib")
+             if n in parts]
     for _ in range(args.warmup):
         for n in order:
             parts[n]["fn"]()
@@ -201,7 +211,7 @@ def main():
     src = source_hash("fa_fwd.hip", "fa_device.h")
     roof = None
     if head is not None:
-        traffic = load_traffic("fwd_bf16_d128_causal_b1h32n8192", src)
+        traffic = load_traffic("fwd_c3", src)
         roof = {"bound": "mfma", "achieved": head["tflops"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": head["frac_mfma_peak"], "traffic": traffic,
                 "kernel": "fwd_bf16_kernel<128,causal>", "source_hash": src}
@@ -210,7 +220,8 @@ def main():
     if dec is not None:
         roof_dec = {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": dec["frac_hbm_peak"],
-                    "traffic": load_traffic("decode_partial_c5", source_hash("fa_decode.hip")),
+                    "traffic": load_traffic("decode_c5",
+                                            source_hash("fa_decode.hip", "fa_device.h")),
                     "kernel": "decode_partial_kernel + decode_merge_kernel"}
     out = {
         "metric": "fwd attention TFLOP/s (causal bf16, % of MFMA dense bf16 peak); "
