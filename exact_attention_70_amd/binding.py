@@ -33,11 +33,15 @@ class LibfaError(RuntimeError):
 
 
 def load_library(path: str | None = None) -> ctypes.CDLL:
-    """Load libfa.so (once) and declare the C signatures."""
+    """Load libfa.so (once) and declare the C signatures.
+
+    The in-tree library is used unless ``path`` or the LIBFA_PATH environment
+    variable names another build of the same C ABI.
+    """
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("LIBFA_PATH") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"libfa shared library not found at {p}; build it with "
                            "`python -m exact_attention_70_amd.build` (hipcc, gfx950)")

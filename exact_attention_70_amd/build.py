@@ -39,10 +39,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: libfa needs the ROCm toolchain to build")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, verbose: bool, objdir: str = OBJDIR, extra=()) -> str:
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-c", os.path.join(CSRC, src),
-           "-o", obj] + COMMON + DEVICE_FLAGS + EXTRA.get(src, [])
+           "-o", obj] + COMMON + DEVICE_FLAGS + EXTRA.get(src, []) + list(extra)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -55,19 +55,22 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile every source and link ``out``; ``defines`` are extra -D flags."""
+    objdir = OBJDIR if out == LIB else out + ".objs"
+    os.makedirs(objdir, exist_ok=True)
+    extra = [f"-D{d}" for d in defines]
     with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, objdir, extra), SOURCES))
+    tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}", flush=True)
-    return LIB
+        print(f"built {out}", flush=True)
+    return out
 
 
 if __name__ == "__main__":

@@ -36,18 +36,19 @@ namespace fa {
 namespace {
 
 constexpr int kBM = 128;   // query rows per workgroup
-constexpr int kBN = 64;    // keys per K/V tile
+constexpr int kBNDefault = 64;   // keys per K/V tile
 constexpr int kThreads = 256;
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
+template <int D, bool CAUSAL, int BN, int OCC>
+__global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int N, float scale_log2, int n_qtiles) {
   // scale_log2 = scale * log2(e): scores are handled in base 2
   constexpr int KSTEPS = D / 16;         // matrix k-steps over the head dim
   constexpr int DT = D / 32;             // 32-row tiles of O^T
-  constexpr int TILE = kBN * D * 2;      // bytes of one K or V tile
-  static_assert(kBM == 2 * kBN, "the query tile is staged in two K/V-sized halves");
+  constexpr int TILE = BN * D * 2;       // bytes of one K or V tile
+  constexpr int NSUB = BN / 32;          // 32-key sub-tiles per tile
+  constexpr int NU = BN / 16;            // 16-key matrix k-steps of the P V product
   // Two-slot rings for K and for V, four separate objects so that reads of one
   // slot are never made to wait for transfers into another.
   __shared__ __attribute__((aligned(1024))) unsigned char sK0[TILE];
@@ -75,23 +76,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const auto rL = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
 
   const int kv_end = CAUSAL ? min(N, q0 + kBM) : N;
-  const int n_kv = (kv_end + kBN - 1) / kBN;
+  const int n_kv = (kv_end + BN - 1) / BN;
   // tiles [0, n_full) need no masking for any row of this workgroup
-  const int n_full = min(CAUSAL ? q0 / kBN : n_kv, N / kBN);
+  const int n_full = min(CAUSAL ? q0 / BN : n_kv, N / BN);
 
-  // ---- stage the query tile (two halves in slot 1 of each ring) and K_0, V_0
-  dma_rows<D, kBN, kThreads / 64>(rQ, sK1, q0, wave, lane);
-  dma_rows<D, kBN, kThreads / 64>(rQ, sV1, q0 + kBN, wave, lane);
-  dma_rows<D, kBN, kThreads / 64>(rK, sK0, 0, wave, lane);
-  dma_rows<D, kBN, kThreads / 64>(rV, sV0, 0, wave, lane);
-  __syncthreads();
+  // ---- this wave's query rows, straight from HBM into B-operand registers;
+  //      K_0 and V_0 into ring slot 0
+  dma_rows<D, BN, kThreads / 64>(rK, sK0, 0, wave, lane);
+  dma_rows<D, BN, kThreads / 64>(rV, sV0, 0, wave, lane);
+  const int my_q_row = q0 + wave * 32 + l32;
   bf16x8 qf[KSTEPS];
-  {
-    const unsigned char* const sQ = (wave < 2) ? sK1 : sV1;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
-      qf[s] = *(const bf16x8*)(sQ + tile_off<D>((wave & 1) * 32 + l32, 2 * s + half));
-  }
+  for (int s = 0; s < KSTEPS; ++s)
+    qf[s] = as_bf16x8(bload16(rQ, (uint32_t)(my_q_row * D + 16 * s + 8 * half) * 2));
   // The softmax takes its maximum over raw scores and folds the scale into one
   // multiply-add, which needs a positive multiplier: for a negative scale,
   // negate Q once (exact in bf16) and use |scale|.
@@ -100,7 +97,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(as_u32x4(qf[s]) ^ 0x80008000u);
     scale_log2 = -scale_log2;
   }
-  __syncthreads();                                  // slot 1 of both rings free again
+  barrier_all();                                    // K_0, V_0 landed
 
   const int my_q = q0 + wave * 32 + l32;            // this lane's query row
   // transpose-read geometry of the V^T operand (see tile_off / ds_read_tr16)
@@ -116,13 +113,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   bool grew = false;       // did any row's maximum grow in the last reduced tile
   const float one = 1.0f;
   const bf16x2 ones = {(__bf16)one, (__bf16)one};
-  f32x16 s[2];             // raw scores of the last tile whose S was computed
+  f32x16 s[NSUB];             // raw scores of the last tile whose S was computed
 
   // -- the four stages of one tile ------------------------------------------
   // S = K_j Q^T for two 32-key sub-tiles
   auto qk = [&](const unsigned char* sK) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < NSUB; ++t) {
       s[t] = zero16();
 #pragma unroll
       for (int k = 0; k < KSTEPS; ++k) {
@@ -135,7 +132,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   auto mask = [&](int kb) {
     const int lim = min(CAUSAL ? my_q : N - 1, N - 1) - kb - 4 * half;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < NSUB; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (t * 32 + 8 * (i >> 2) + (i & 3) > lim) s[t][i] = kNegInf;
@@ -144,7 +141,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   auto reduce = [&]() {
     float mx = kNegInf;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < NSUB; ++t)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[t][i], s[t][i + 1]));
     mx = fmaxf(mx, swap_half(mx));
@@ -155,11 +152,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   };
   // probabilities P = exp2(c*s - m) rounded to bf16 and packed as the B
   // operands of the P V product; accumulates the denominator
-  auto probs = [&](u32x4 (&pb)[4]) {
+  auto probs = [&](u32x4 (&pb)[NU]) {
     const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
     float rs = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < NSUB; ++t)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         const float p0 = fast_exp2(fmaf(s[t][i], scale_log2, neg_m));
@@ -181,11 +178,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   };
   // O^T += V^T P^T; the V^T operand (lane: one d, 8 keys) comes from two
   // transpose reads of the row-major V tile (4 keys each)
-  auto pv = [&](const unsigned char* sV, const u32x4 (&pb)[4]) {
+  auto pv = [&](const unsigned char* sV, const u32x4 (&pb)[NU]) {
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < NU; ++u) {
         const int row = 16 * u + tr_row;
         const int col = t * 32 + tr_col;
         const u32x2 lo = ds_read_tr16(sV + tile_off<D>(row, col >> 3) + (col & 7) * 2);
@@ -202,20 +199,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   // reduction of tile j.  K_j sits in ring slot j&1; V_{j-1} in slot (j-1)&1;
   // K_{j+1} and V_j stream into the other slots meanwhile.
   // prologue: tile 0
-  if (n_kv > 1) dma_rows<D, kBN, kThreads / 64>(rK, sK1, kBN, wave, lane);
+  if (n_kv > 1) dma_rows<D, BN, kThreads / 64>(rK, sK1, BN, wave, lane);
   qk(sK0);
   if (need_mask(0)) mask(0);
   reduce();
   __syncthreads();
   auto iter = [&](const int j, const unsigned char* kcur, unsigned char* knxt,
                   const unsigned char* vprev, unsigned char* vcur) {
-    if (j + 1 < n_kv) dma_rows<D, kBN, kThreads / 64>(rK, knxt, (j + 1) * kBN, wave, lane);
-    dma_rows<D, kBN, kThreads / 64>(rV, vcur, j * kBN, wave, lane);
-    u32x4 pb[4];
+    if (j + 1 < n_kv) dma_rows<D, BN, kThreads / 64>(rK, knxt, (j + 1) * BN, wave, lane);
+    dma_rows<D, BN, kThreads / 64>(rV, vcur, j * BN, wave, lane);
+    u32x4 pb[NU];
     probs(pb);            // P_{j-1}  (overlaps S_j below)
     qk(kcur);             // S_j
     rescale();            // by tile j-1's factor, before P_{j-1} V_{j-1} is added
-    if (need_mask(j)) mask(j * kBN);
+    if (need_mask(j)) mask(j * BN);
     pv(vprev, pb);        // P_{j-1} V_{j-1}
     reduce();             // tile j's max (overlaps the P V product above)
     __syncthreads();
@@ -231,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   }
   // epilogue: P V of the last tile (its V sits in slot (n_kv-1)&1)
   {
-    u32x4 pb[4];
+    u32x4 pb[NU];
     probs(pb);
     rescale();
     pv(((n_kv - 1) & 1) ? sV1 : sV0, pb);
@@ -369,11 +366,11 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(
   if (half == 0) bstore4f((m_run + fast_log2(l_tot)) * kLn2, rL, (uint32_t)my_q * 4);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int BN = kBNDefault, int OCC = 2>
 hipError_t launch_bf16(const FwdArgs& a) {
   const int n_qtiles = (a.N + kBM - 1) / kBM;
   const int grid = a.B * a.H * n_qtiles;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, a.stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, BN, OCC>), dim3(grid), dim3(kThreads), 0, a.stream,
                      (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (__bf16*)a.O,
                      a.LSE, a.N, a.scale * kLog2e, n_qtiles);
   return hipGetLastError();

@@ -59,7 +59,10 @@ hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 
 // Decode partitioning shared by the workspace query and the launcher.
-constexpr int kDecodePartTokens = 256;
+#ifndef FA_DECODE_PART_TOKENS
+#define FA_DECODE_PART_TOKENS 256
+#endif
+constexpr int kDecodePartTokens = FA_DECODE_PART_TOKENS;
 inline int decode_n_parts(int max_blocks_per_seq, int block_size) {
   const long long max_tokens = (long long)max_blocks_per_seq * block_size;
   return (int)((max_tokens + kDecodePartTokens - 1) / kDecodePartTokens);
