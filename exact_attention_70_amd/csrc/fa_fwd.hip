@@ -12,24 +12,31 @@
 //
 // Work decomposition (bf16 kernel)
 //   * one workgroup = 4 waves = a 128-row query tile of one (batch, head);
-//     wave w owns query rows [32w, 32w + 32) of the tile.
-//   * the query tile is staged once through LDS with coalesced 16-byte loads,
-//     then each wave keeps its rows in registers as matrix B operands.
-//   * K/V are streamed in 64-key tiles: 16-byte coalesced global loads into
-//     registers one tile ahead, then written to LDS (K row-major, V
-//     transposed) for the four waves to share.
+//     wave w owns query rows [32w, 32w + 32) of the tile and keeps them in
+//     registers as the B operands of S^T = K Q^T (loaded once from HBM).
+//   * K/V stream through LDS in 64-key tiles by buffer-to-LDS DMA, one tile
+//     ahead of use, in two-slot rings (V one tile behind K).  Rows are stored
+//     with an XOR swizzle of their 16-byte chunks so that both the K operand
+//     reads and the transposing V reads (ds_read_b64_tr_b16) are free of LDS
+//     bank conflicts.
 //   * each wave computes S^T = K Q^T (keys x its 32 queries) so that every
 //     lane holds the scores of ONE query: the row max and row sum are
 //     in-lane reductions plus one exchange with the other half-wave.
 //   * the probabilities P^T are rounded to bf16 and fed straight back as the
-//     B operand of O^T += V^T P^T; V is stored transposed with the key order
-//     permuted to match the C-layout of the score tile.
+//     B operand of O^T += V^T P^T, whose A operand (V^T) comes from transpose
+//     reads of the row-major V tile.
+//   * software pipeline: iteration j runs the matrix ops of S_j interleaved
+//     with the exponentials of tile j-1, then P_{j-1} V_{j-1} interleaved with
+//     the row maximum of S_j.  The accumulated output is rescaled only when a
+//     row's maximum grows by more than a fixed slack (see kSlack).
 //   * causal: key tiles entirely above the diagonal are never visited; only
-//     tiles that straddle the diagonal (or the ragged end) are masked.
+//     tiles that straddle the diagonal (or the ragged end) are masked, in a
+//     separate tail of the loop.
 //   * workgroups are ordered heaviest-first within each head and mapped so
 //     that one head's query tiles share an XCD (and its L2).
 #include "fa_device.h"
 #include "fa_internal.h"
+#include <type_traits>
 
 namespace fa {
 
@@ -38,6 +45,11 @@ namespace {
 constexpr int kBM = 128;   // query rows per workgroup
 constexpr int kBNDefault = 64;   // keys per K/V tile
 constexpr int kThreads = 256;
+constexpr int kKLead = 3;        // K operand reads in flight ahead of their matrix op
+constexpr int kVLead = 2;        // V operand read pairs in flight ahead of their matrix op
+// The running reference maximum moves only when a tile's row maximum exceeds
+// it by more than this (base-2 exponent): probabilities stay <= 2^kSlack.
+constexpr float kSlack = 8.f;
 
 template <int D, bool CAUSAL, int BN, int OCC>
 __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
@@ -110,26 +122,50 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
   float m_run = kNegInf;   // running max of scale*log2(e)*score (through the last reduced tile)
   float l_run = 0.f;       // this lane's share of the running denominator
   float alpha = 1.f;       // exp2(m_old - m_new) of the last reduced tile
-  bool grew = false;       // did any row's maximum grow in the last reduced tile
   const float one = 1.0f;
   const bf16x2 ones = {(__bf16)one, (__bf16)one};
-  f32x16 s[NSUB];             // raw scores of the last tile whose S was computed
+  constexpr int NQ = NSUB * KSTEPS;     // matrix ops of S = K Q^T per tile
+  constexpr int NP = DT * NU;           // matrix ops of O^T += V^T P^T per tile
+  constexpr int KLEAD = kKLead;
+  constexpr int VLEAD = kVLead;
+  static_assert(2 * NSUB * 16 / NQ >= 1 && (NSUB * 16) % NQ == 0, "probs split");
+  constexpr int PPER = NSUB * 16 / NQ;  // probabilities per S matrix op
+  static_assert((NSUB * 16) % NP == 0, "reduce split");
+  constexpr int RPER = NSUB * 16 / NP;  // scores per P V matrix op in the row max
 
-  // -- the four stages of one tile ------------------------------------------
-  // S = K_j Q^T for two 32-key sub-tiles
-  auto qk = [&](const unsigned char* sK) {
+  // Per-lane byte offsets of the operand reads inside a tile.  The swizzle
+  // makes them differ per k-step (K) and per column block (V); sub-tile,
+  // row-block and ring-slot offsets are compile-time constants added on top,
+  // which the LDS instructions take as immediates.  The offsets are re-pinned
+  // every iteration so they stay the only live copies.
+  uint32_t kofs[KSTEPS], vofs[DT][2];
 #pragma unroll
-    for (int t = 0; t < NSUB; ++t) {
-      s[t] = zero16();
+  for (int k = 0; k < KSTEPS; ++k) kofs[k] = tile_off<D>(l32, 2 * k + half);
 #pragma unroll
-      for (int k = 0; k < KSTEPS; ++k) {
-        const bf16x8 a = *(const bf16x8*)(sK + tile_off<D>(t * 32 + l32, 2 * k + half));
-        s[t] = mfma_bf16(a, qf[k], s[t]);
-      }
-    }
+  for (int t = 0; t < DT; ++t) {
+    const int col = t * 32 + tr_col;
+    vofs[t][0] = tile_off<D>(tr_row, col >> 3) + (col & 7) * 2;
+    vofs[t][1] = tile_off<D>(tr_row + 8, col >> 3) + (col & 7) * 2;
+  }
+  auto pin_offsets = [&]() {
+#pragma unroll
+    for (int k = 0; k < KSTEPS; ++k) asm volatile("" : "+v"(kofs[k]));
+#pragma unroll
+    for (int t = 0; t < DT; ++t) asm volatile("" : "+v"(vofs[t][0]), "+v"(vofs[t][1]));
+  };
+  auto k_operand = [&](const unsigned char* sK, int idx) {
+    const int t = idx / KSTEPS, k = idx % KSTEPS;
+    return *(const bf16x8*)(sK + kofs[k] + t * 32 * D * 2);
+  };
+  auto v_operand = [&](const unsigned char* sV, int idx) {
+    const int t = idx / NU, u = idx % NU;
+    const u32x2 lo = ds_read_tr16(sV + vofs[t][0] + u * 16 * D * 2);
+    const u32x2 hi = ds_read_tr16(sV + vofs[t][1] + u * 16 * D * 2);
+    const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+    return a;
   };
   // keys beyond this lane's row (causal) or beyond N become -inf
-  auto mask = [&](int kb) {
+  auto mask = [&](f32x16 (&s)[NSUB], int kb) {
     const int lim = min(CAUSAL ? my_q : N - 1, N - 1) - kb - 4 * half;
 #pragma unroll
     for (int t = 0; t < NSUB; ++t)
@@ -137,103 +173,143 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
       for (int i = 0; i < 16; ++i)
         if (t * 32 + 8 * (i >> 2) + (i & 3) > lim) s[t][i] = kNegInf;
   };
-  // row max of the new tile, updated running max, rescale factor
-  auto reduce = [&]() {
+  // Reference maximum from a tile's raw row max.  The reference moves only
+  // when the tile's maximum exceeds it by more than kSlack (base 2), so the
+  // probabilities stay <= 2^kSlack and the accumulated output is rescaled
+  // rarely; numerator and denominator share the reference, so their ratio
+  // and the log-sum-exp are unchanged.  Returns whether any row moved.
+  auto update_max = [&](float mx) {
+    mx = fmaxf(mx, swap_half(mx));
+    const float cand = mx * scale_log2;
+    const bool up = cand > m_run + kSlack;            // always true while m_run = -inf
+    const float m_new = up ? cand : m_run;
+    alpha = up ? fast_exp2(m_run - m_new) : 1.f;     // exp2(-inf) = 0 on the first tile
+    m_run = m_new;
+    return __builtin_amdgcn_ballot_w64(up) != 0;
+  };
+  auto rescale = [&]() {
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+  };
+
+  // prologue: S_0, its max; K_1 streams meanwhile
+  f32x16 sa[NSUB], sb[NSUB];
+  if (n_kv > 1) dma_rows<D, BN, kThreads / 64>(rK, sK1, BN, wave, lane);
+  {
+#pragma unroll
+    for (int t = 0; t < NSUB; ++t) sa[t] = zero16();
+#pragma unroll
+    for (int idx = 0; idx < NQ; ++idx)
+      sa[idx / KSTEPS] = mfma_bf16(k_operand(sK0, idx), qf[idx % KSTEPS], sa[idx / KSTEPS]);
+    if (0 >= n_full) mask(sa, 0);
     float mx = kNegInf;
 #pragma unroll
     for (int t = 0; t < NSUB; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[t][i], s[t][i + 1]));
-    mx = fmaxf(mx, swap_half(mx));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    grew = __builtin_amdgcn_ballot_w64(m_new > m_run) != 0;
-    alpha = fast_exp2(m_run - ((m_new == kNegInf) ? 0.f : m_new));   // 1 where m did not grow
-    m_run = m_new;
-  };
-  // probabilities P = exp2(c*s - m) rounded to bf16 and packed as the B
-  // operands of the P V product; accumulates the denominator
-  auto probs = [&](u32x4 (&pb)[NU]) {
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sa[t][i], sa[t][i + 1]));
+    update_max(mx);   // O is still zero: no rescale needed
+  }
+  __syncthreads();
+
+  // Iteration j: S_j = K_j Q^T on the matrix cores interleaved with the
+  // probabilities P_{j-1} (exponentials), then O^T += V_{j-1}^T P_{j-1}^T
+  // interleaved with the row max of S_j; O is rescaled (rarely) at the end so
+  // the next P V product adds onto the right base.  K_j is in slot j&1,
+  // V_{j-1} in slot (j-1)&1; K_{j+1} and V_j stream into the other slots.
+  auto iter = [&](const int j, const unsigned char* kcur, unsigned char* knxt,
+                  const unsigned char* vprev, unsigned char* vcur, f32x16 (&so)[NSUB],
+                  f32x16 (&sn)[NSUB], auto masked) {
+    pin_offsets();
+    if (j + 1 < n_kv) dma_rows<D, BN, kThreads / 64>(rK, knxt, (j + 1) * BN, wave, lane);
+    dma_rows<D, BN, kThreads / 64>(rV, vcur, j * BN, wave, lane);
     const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
+    u32x4 pb[NU];
+    float rs = 0.f;
+    bf16x8 ka[KLEAD];
+#pragma unroll
+    for (int x = 0; x < KLEAD; ++x) ka[x] = k_operand(kcur, x);
+#pragma unroll
+    for (int t = 0; t < NSUB; ++t) sn[t] = zero16();
+#pragma unroll
+    for (int idx = 0; idx < NQ; ++idx) {
+      const bf16x8 a = ka[idx % KLEAD];
+      if (idx + KLEAD < NQ) ka[idx % KLEAD] = k_operand(kcur, idx + KLEAD);
+      sn[idx / KSTEPS] = mfma_bf16(a, qf[idx % KSTEPS], sn[idx / KSTEPS]);
+#pragma unroll
+      for (int e = 0; e < PPER; e += 2) {
+        const int flat = idx * PPER + e;
+        const int t = flat / 16, i = flat % 16;
+        const float p0 = fast_exp2(fmaf(so[t][i], scale_log2, neg_m));
+        const float p1 = fast_exp2(fmaf(so[t][i + 1], scale_log2, neg_m));
+        const uint32_t pk = pack_bf16(p0, p1);
+        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, rs, false);
+        pb[2 * t + (i >> 3)][(i & 7) >> 1] = pk;
+      }
+    }
+    l_run = fmaf(l_run, alpha, rs);
+    if constexpr (decltype(masked)::value) mask(sn, j * BN);
+    u32x4 va[VLEAD];
+#pragma unroll
+    for (int x = 0; x < VLEAD; ++x) va[x] = v_operand(vprev, x);
+    float mx = kNegInf;
+#pragma unroll
+    for (int idx = 0; idx < NP; ++idx) {
+      const u32x4 a = va[idx % VLEAD];
+      if (idx + VLEAD < NP) va[idx % VLEAD] = v_operand(vprev, idx + VLEAD);
+      o[idx / NU] = mfma_bf16(as_bf16x8(a), as_bf16x8(pb[idx % NU]), o[idx / NU]);
+#pragma unroll
+      for (int e = 0; e < RPER; e += 2) {
+        const int flat = idx * RPER + e;
+        mx = fmaxf(mx, fmaxf(sn[flat / 16][flat % 16], sn[flat / 16][flat % 16 + 1]));
+      }
+    }
+    if (update_max(mx)) rescale();
+    __syncthreads();
+  };
+  using Plain = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+  int j = 1;
+  const int n_plain = max(1, min(n_full, n_kv));   // iterations [1, n_plain) need no mask
+  for (; j + 1 < n_plain; j += 2) {
+    iter(j, sK1, sK0, sV0, sV1, sa, sb, Plain{});
+    iter(j + 1, sK0, sK1, sV1, sV0, sb, sa, Plain{});
+  }
+  // epilogue: P V of the last tile (its V sits in slot (n_kv-1)&1, its
+  // scores in sa when n_kv-1 is even, else sb)
+  auto last_pv = [&](const f32x16 (&sl)[NSUB], const unsigned char* vl) {
+    const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
+    u32x4 pb[NU];
     float rs = 0.f;
 #pragma unroll
     for (int t = 0; t < NSUB; ++t)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
-        const float p0 = fast_exp2(fmaf(s[t][i], scale_log2, neg_m));
-        const float p1 = fast_exp2(fmaf(s[t][i + 1], scale_log2, neg_m));
+        const float p0 = fast_exp2(fmaf(sl[t][i], scale_log2, neg_m));
+        const float p1 = fast_exp2(fmaf(sl[t][i + 1], scale_log2, neg_m));
         const uint32_t pk = pack_bf16(p0, p1);
         rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, rs, false);
         pb[2 * t + (i >> 3)][(i & 7) >> 1] = pk;
       }
     l_run = fmaf(l_run, alpha, rs);
-  };
-  // exp(m_old - m_new) rescale of the accumulated output (only when some row grew)
-  auto rescale = [&]() {
-    if (grew) {
 #pragma unroll
-      for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
-    }
+    for (int idx = 0; idx < NP; ++idx)
+      o[idx / NU] = mfma_bf16(as_bf16x8(v_operand(vl, idx)), as_bf16x8(pb[idx % NU]), o[idx / NU]);
   };
-  // O^T += V^T P^T; the V^T operand (lane: one d, 8 keys) comes from two
-  // transpose reads of the row-major V tile (4 keys each)
-  auto pv = [&](const unsigned char* sV, const u32x4 (&pb)[NU]) {
-#pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const int row = 16 * u + tr_row;
-        const int col = t * 32 + tr_col;
-        const u32x2 lo = ds_read_tr16(sV + tile_off<D>(row, col >> 3) + (col & 7) * 2);
-        const u32x2 hi = ds_read_tr16(sV + tile_off<D>(row + 8, col >> 3) + (col & 7) * 2);
-        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-        o[t] = mfma_bf16(as_bf16x8(a), as_bf16x8(pb[u]), o[t]);
-      }
-  };
-  auto need_mask = [&](int j) { return j >= n_full; };
-
-  // -- software pipeline over the K/V tiles ------------------------------------
-  // Iteration j overlaps the matrix-core work of tile j (S_j = K_j Q^T) with
-  // the exponentials of tile j-1, then the P_{j-1} V_{j-1} product with the row
-  // reduction of tile j.  K_j sits in ring slot j&1; V_{j-1} in slot (j-1)&1;
-  // K_{j+1} and V_j stream into the other slots meanwhile.
-  // prologue: tile 0
-  if (n_kv > 1) dma_rows<D, BN, kThreads / 64>(rK, sK1, BN, wave, lane);
-  qk(sK0);
-  if (need_mask(0)) mask(0);
-  reduce();
-  __syncthreads();
-  auto iter = [&](const int j, const unsigned char* kcur, unsigned char* knxt,
-                  const unsigned char* vprev, unsigned char* vcur) {
-    if (j + 1 < n_kv) dma_rows<D, BN, kThreads / 64>(rK, knxt, (j + 1) * BN, wave, lane);
-    dma_rows<D, BN, kThreads / 64>(rV, vcur, j * BN, wave, lane);
-    u32x4 pb[NU];
-    probs(pb);            // P_{j-1}  (overlaps S_j below)
-    qk(kcur);             // S_j
-    rescale();            // by tile j-1's factor, before P_{j-1} V_{j-1} is added
-    if (need_mask(j)) mask(j * BN);
-    pv(vprev, pb);        // P_{j-1} V_{j-1}
-    reduce();             // tile j's max (overlaps the P V product above)
-    __syncthreads();
-  };
-  int j = 1;
+  // The rest (at most one unmasked tile plus the tiles that straddle the
+  // diagonal or the ragged end) runs with the mask on.  j is odd here, so
+  // pairs keep the ring slots and score arrays static.
   for (; j + 1 < n_kv; j += 2) {
-    iter(j, sK1, sK0, sV0, sV1);
-    iter(j + 1, sK0, sK1, sV1, sV0);
+    iter(j, sK1, sK0, sV0, sV1, sa, sb, Masked{});
+    iter(j + 1, sK0, sK1, sV1, sV0, sb, sa, Masked{});
   }
   if (j < n_kv) {
-    iter(j, sK1, sK0, sV0, sV1);
-    ++j;
+    iter(j, sK1, sK0, sV0, sV1, sa, sb, Masked{});
+    last_pv(sb, sV1);          // last tile j is odd
+  } else {
+    last_pv(sa, sV0);          // last tile j-1 is even
   }
-  // epilogue: P V of the last tile (its V sits in slot (n_kv-1)&1)
-  {
-    u32x4 pb[NU];
-    probs(pb);
-    rescale();
-    pv(((n_kv - 1) & 1) ? sV1 : sV0, pb);
-  }
-  // (the V slot chosen at run time above is only read; nothing is in flight)
 
   // ---- epilogue: O = O^T / l, LSE = ln(sum exp) = (m + log2 l) ln 2
   const float l_tot = l_run + swap_half(l_run);

@@ -122,3 +122,20 @@ def test_fwd_on_side_stream(gpu):
         o, lse = binding.fwd(q, k, v, causal=True, scale=0.09)
     s.synchronize()
     assert torch.equal(o.float().cpu(), ref[0]) and torch.equal(lse.cpu(), ref[1])
+
+
+# Scores that climb tile after tile move every row's running maximum again and
+# again.  Per 64-key tile the rise in base-2 units is scale*align*ramp*log2(e):
+# ~14 makes the accumulated output rescale on every tile, ~4 keeps the old
+# reference with probabilities up to 2^4, and a falling ramp never moves it.
+# The oracle's max-subtracted softmax is exact in all three cases.
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("rise", [14.0, 4.0, -6.0])
+def test_fwd_running_max_moves(gpu, d, causal, rise):
+    N, align = 520, 4.0
+    scale = 1.0 / math.sqrt(d)
+    ramp = rise / (scale * align * math.log2(math.e))
+    x = workloads.ramp_inputs(1, 2, N, d, "bf16", seed=4242 + d, align=align, ramp=ramp)
+    o, lse = _gpu_fwd(gpu, x, causal, scale)
+    _check(x, o, lse, causal, scale, TOL["bf16"])

@@ -113,6 +113,27 @@ def attention_inputs(B: int, H: int, N: int, d: int, dtype: str = "bf16", *,
     return out
 
 
+def ramp_inputs(B: int, H: int, N: int, d: int, dtype: str = "bf16", *, seed: int,
+                align: float, ramp: float, noise: float = 0.1) -> dict:
+    """Q, K, V whose scores grow along the key axis.
+
+    Every query and key shares a component along one fixed unit direction e:
+    q_i = noise*z + align*e and k_j = noise*z + ramp*(j/64)*e, so the score of
+    key j rises by about scale*align*ramp per 64 keys (one key tile of the
+    kernels) and every row's maximum keeps moving to later keys.  ``ramp`` < 0
+    makes it fall instead.  V is plain N(0, 1).  CPU tensors, storage dtype.
+    """
+    tdt = _TORCH_DTYPES[dtype]
+    g = _gen(seed)
+    e = torch.randn(d, generator=g, dtype=torch.float32)
+    e = e / e.norm()
+    q = noise * torch.randn((B, H, N, d), generator=g, dtype=torch.float32) + align * e
+    pos = torch.arange(N, dtype=torch.float32).view(1, 1, N, 1) / 64.0
+    k = noise * torch.randn((B, H, N, d), generator=g, dtype=torch.float32) + ramp * pos * e
+    v = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    return {"q": q.to(tdt).contiguous(), "k": k.to(tdt).contiguous(), "v": v.to(tdt).contiguous()}
+
+
 def paged_inputs(num_seqs: int, H: int, d: int, block_size: int, min_len: int, max_len: int,
                  *, seed: int, dtype: str = "bf16", pad_value: float | None = None,
                  seq_lens: list | None = None, extra_blocks: int = 0) -> dict:
