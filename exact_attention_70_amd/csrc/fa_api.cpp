@@ -70,7 +70,8 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   (void)d;
   if (B <= 0 || H <= 0 || N <= 0) return 0;
-  return round_up((size_t)B * H * N * sizeof(float), 256);
+  // D_i and -LSE_i log2(e), fp32 [B, H, N] each
+  return round_up(2 * (size_t)B * H * N * sizeof(float), 256);
 }
 
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,

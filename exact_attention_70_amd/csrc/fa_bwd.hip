@@ -11,12 +11,14 @@
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Three kernels, all on the caller's stream, deterministic (no atomics):
-//   1. bwd_dot:  D_i = rowsum(dO o O) into the workspace.
+//   1. bwd_dot:  D_i = rowsum(dO o O) and -LSE_i log2(e) into the workspace.
 //   2. bwd_dkdv: workgroup = 128 keys (wave = 32 keys); loops over 64-row
 //      query tiles; recomputes S = Q K^T and dP = dO V^T with this wave's K
 //      and V rows held in registers, and accumulates dV^T += dO^T P and
 //      dK^T += Q^T dS on the matrix cores.  Q, dO, LSE and D tiles stream into
-//      LDS by buffer->LDS transfers; Q^T and dO^T come from transpose reads.
+//      LDS by buffer->LDS transfers through a four-slot ring, two tiles ahead;
+//      Q^T and dO^T come from transpose reads.  Iteration i overlaps the
+//      exponentials of tile i-1 with the S / dP matrix ops of tile i.
 //   3. bwd_dq:   workgroup = 128 queries (wave = 32); loops over 64-key K/V tiles;
 //      recomputes S^T = K Q^T and dP^T = V dO^T (each lane then holds one
 //      query's row, so LSE_i and D_i are per-lane scalars) and accumulates
@@ -24,6 +26,7 @@
 // Causal: tiles wholly above the diagonal are skipped; straddling tiles masked.
 #include "fa_device.h"
 #include "fa_internal.h"
+#include <type_traits>
 
 namespace fa {
 
@@ -35,7 +38,9 @@ constexpr int kThreads = 256;
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(const __bf16* __restrict__ O,
                                                            const __bf16* __restrict__ dO,
+                                                           const float* __restrict__ LSE,
                                                            float* __restrict__ Dvec,
+                                                           float* __restrict__ NL,
                                                            long long rows) {
   constexpr int LPR = D / 8;                      // lanes per row, 8 values each
   const long long row = (long long)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR;
@@ -51,7 +56,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(const __bf16* __restr
     acc = fmaf(bf16hi(a[e]), bf16hi(b[e]), acc);
   }
   acc = group_sum<LPR>(acc);
-  if (ok && c == 0) Dvec[row] = acc;
+  if (ok && c == 0) {
+    Dvec[row] = acc;
+    NL[row] = -LSE[row] * kLog2e;   // exp(scale s - LSE) = exp2(scale log2(e) s + NL)
+  }
 }
 
 // Direct buffer -> LDS copy of one dword per lane (lane i lands at lds + 4 i).
@@ -75,39 +83,43 @@ __device__ __forceinline__ bf16x8 tr_operand(const unsigned char* tile, int u, i
 
 // ---------------------------------------------------------------- dK, dV
 // Workgroup = 128 keys (wave = 32 keys, held in registers as B operands);
-// loops over 64-row query tiles streamed into LDS (Q, dO, LSE, D) by
-// buffer->LDS transfers, double-buffered.  Per tile and wave:
-//   S = Q K^T, dP = dO V^T (rows = queries, columns = this wave's keys),
-//   P = exp(scale S - LSE), dS = P o (dP - D),
-//   dV^T += dO^T P, dK^T += Q^T dS  (dO^T and Q^T from transpose reads).
+// loops over 64-row query tiles streamed into LDS (Q, dO, -LSE log2 e, D) by
+// buffer->LDS transfers through a four-slot ring, two tiles ahead.  Per tile
+// and wave, three stages:
+//   A: S = Q K^T, dP = dO V^T (rows = queries, columns = this wave's keys);
+//   B: P = exp2(scale log2(e) S - LSE log2(e)), dS = P o (dP - D), both to bf16;
+//   C: dV^T += dO^T P, dK^T += Q^T dS  (dO^T and Q^T from transpose reads).
+// Iteration i runs A of tile i with B of tile i-1 interleaved between its
+// matrix ops, then C of tile i-1, so the exponentials overlap matrix work.
 constexpr int kKvBN = 128;   // keys per workgroup
 constexpr int kKvBQ = 64;    // queries per inner tile
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dvec,
+    const __bf16* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ Dvec,
     float* __restrict__ dK, float* __restrict__ dV, int N, float scale, float scale_log2,
     int n_ktiles) {
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;
   constexpr int TILE = kKvBQ * D * 2;
-  __shared__ __attribute__((aligned(1024))) unsigned char sQ0[TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char sQ1[TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char sO0[TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char sO1[TILE];
-  __shared__ __attribute__((aligned(256))) float sL0[kKvBQ];
-  __shared__ __attribute__((aligned(256))) float sL1[kKvBQ];
-  __shared__ __attribute__((aligned(256))) float sD0[kKvBQ];
-  __shared__ __attribute__((aligned(256))) float sD1[kKvBQ];
+  constexpr int NU = kKvBQ / 16;           // 16-query k-steps of the dV / dK products
+  constexpr int NA = 2 * 2 * KSTEPS;       // matrix ops of stage A (2 sub-tiles x {S, dP})
+  constexpr int NC = 2 * NU * DT;          // matrix ops of stage C ({dV, dK})
+  constexpr int NE = 32;                   // score elements per lane per tile
+  constexpr int LEAD = 4;                  // operand reads in flight ahead of their matrix op
+  constexpr int VM_TILE = 2 * (TILE / 1024 / 4) + 2;   // transfers a wave issues per tile
+  __shared__ __attribute__((aligned(1024))) unsigned char sQ0[TILE], sQ1[TILE], sQ2[TILE], sQ3[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char sO0[TILE], sO1[TILE], sO2[TILE], sO3[TILE];
+  __shared__ __attribute__((aligned(256))) float sL0[kKvBQ], sL1[kKvBQ], sL2[kKvBQ], sL3[kKvBQ];
+  __shared__ __attribute__((aligned(256))) float sD0[kKvBQ], sD1[kKvBQ], sD2[kKvBQ], sD3[kKvBQ];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / n_ktiles;
   const int kb = (tile % n_ktiles) * kKvBN;       // low key tiles see the most queries
-  const int wave_k0 = kb + wave * 32;
-  const int my_k = wave_k0 + l32;                 // this lane's key (C-layout column)
+  const int my_k = kb + wave * 32 + l32;          // this lane's key (C-layout column)
 
   const size_t head_off = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
@@ -115,21 +127,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const auto rK = make_rsrc(K + head_off, head_bytes);
   const auto rV = make_rsrc(V + head_off, head_bytes);
   const auto rdO = make_rsrc(dO + head_off, head_bytes);
-  const auto rL = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
+  const auto rL = make_rsrc(NL + (size_t)bh * N, (uint32_t)N * 4);
   const auto rD = make_rsrc(Dvec + (size_t)bh * N, (uint32_t)N * 4);
   const auto rdK = make_rsrc(dK + head_off, (uint32_t)N * D * 4);
   const auto rdV = make_rsrc(dV + head_off, (uint32_t)N * D * 4);
 
   const int q_first = CAUSAL ? kb : 0;            // earlier queries see none of these keys
   const int n_q = (N - q_first + kKvBQ - 1) / kKvBQ;
-  auto load = [&](int i, unsigned char* sQ, unsigned char* sO, float* sL, float* sD) {
+  // Tiles past the end read as zeros (buffer range check); every wave copies
+  // the LSE and D rows too, so each wave issues VM_TILE transfers per tile.
+  auto load = [&](int i, unsigned char* sQ, unsigned char* sO, float* sL, float* sD)
+      __attribute__((always_inline)) {
     const int q0 = q_first + i * kKvBQ;
     dma_rows<D, kKvBQ, kThreads / 64>(rQ, sQ, q0, wave, lane);
     dma_rows<D, kKvBQ, kThreads / 64>(rdO, sO, q0, wave, lane);
-    if (wave == 0) dma4(rL, sL, (uint32_t)(q0 + lane) * 4);
-    if (wave == 1) dma4(rD, sD, (uint32_t)(q0 + lane) * 4);
+    dma4(rL, sL, (uint32_t)(q0 + lane) * 4);
+    dma4(rD, sD, (uint32_t)(q0 + lane) * 4);
   };
   load(0, sQ0, sO0, sL0, sD0);
+  load(1, sQ1, sO1, sL1, sD1);
+  load(2, sQ2, sO2, sL2, sD2);
 
   // this wave's 32 keys as B operands: B[k = d][n = key] = K[key][d]
   bf16x8 kf[KSTEPS], vf[KSTEPS];
@@ -144,64 +161,195 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     dk[t] = zero16();
     dv[t] = zero16();
   }
+  // per-lane LDS byte offsets: 16-byte row reads (per k-step) and transpose
+  // reads (per 32-column block); sub-tile / row-block / slot offsets are
+  // compile-time immediates on top.  Re-pinned every iteration.
+  uint32_t rofs[KSTEPS], tofs[DT][2];
+#pragma unroll
+  for (int k = 0; k < KSTEPS; ++k) rofs[k] = tile_off<D>(l32, 2 * k + half);
+  {
+    const int row = 4 * half + ((lane & 15) >> 2);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      const int col = t * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      tofs[t][0] = tile_off<D>(row, col >> 3) + (col & 7) * 2;
+      tofs[t][1] = tile_off<D>(row + 8, col >> 3) + (col & 7) * 2;
+    }
+  }
+  auto pin_offsets = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < KSTEPS; ++k) asm volatile("" : "+v"(rofs[k]));
+#pragma unroll
+    for (int t = 0; t < DT; ++t) asm volatile("" : "+v"(tofs[t][0]), "+v"(tofs[t][1]));
+  };
   barrier_all();
 
-  auto compute = [&](int i, const unsigned char* sQ, const unsigned char* sO, const float* sL,
-                     const float* sD) {
-    const int q0 = q_first + i * kKvBQ;
-    if (CAUSAL && q0 + kKvBQ - 1 < wave_k0) return;        // every query precedes every key
-    f32x16 s[2], dp[2];
+  // stage A operand idx: sub-tile, k-step, {Q -> S, dO -> dP}
+  auto a_operand = [&](const unsigned char* sQ, const unsigned char* sO, int idx)
+      __attribute__((always_inline)) {
+    const int sub = idx / (2 * KSTEPS), k = (idx / 2) % KSTEPS;
+    const unsigned char* base = (idx & 1) ? sO : sQ;
+    return as_u32x4(*(const bf16x8*)(base + rofs[k] + sub * 32 * D * 2));
+  };
+  auto a_op = [&](int idx, u32x4 a, f32x16 (&s)[2], f32x16 (&dp)[2]) __attribute__((always_inline)) {
+    const int sub = idx / (2 * KSTEPS), k = (idx / 2) % KSTEPS;
+    if (idx & 1) dp[sub] = mfma_bf16(as_bf16x8(a), vf[k], dp[sub]);
+    else s[sub] = mfma_bf16(as_bf16x8(a), kf[k], s[sub]);
+  };
+  // stage C operand idx: k-step u, column block t, {dO^T -> dV, Q^T -> dK}
+  auto c_operand = [&](const unsigned char* sQ, const unsigned char* sO, int idx)
+      __attribute__((always_inline)) {
+    const int u = idx / (2 * DT), t = (idx / 2) % DT;
+    const unsigned char* base = (idx & 1) ? sQ : sO;
+    const u32x2 lo = ds_read_tr16(base + tofs[t][0] + u * 16 * D * 2);
+    const u32x2 hi = ds_read_tr16(base + tofs[t][1] + u * 16 * D * 2);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  auto stage_c = [&](const unsigned char* sQ, const unsigned char* sO, const u32x4 (&pb)[NU],
+                     const u32x4 (&db)[NU]) __attribute__((always_inline)) {
+    u32x4 ring[LEAD];
+#pragma unroll
+    for (int x = 0; x < LEAD; ++x) ring[x] = c_operand(sQ, sO, x);
+#pragma unroll
+    for (int idx = 0; idx < NC; ++idx) {
+      const u32x4 a = ring[idx % LEAD];
+      if (idx + LEAD < NC) ring[idx % LEAD] = c_operand(sQ, sO, idx + LEAD);
+      const int u = idx / (2 * DT), t = (idx / 2) % DT;
+      if (idx & 1) dk[t] = mfma_bf16(as_bf16x8(a), as_bf16x8(db[u]), dk[t]);
+      else dv[t] = mfma_bf16(as_bf16x8(a), as_bf16x8(pb[u]), dv[t]);
+    }
+  };
+  // stage B for score element e of this lane (sub-tile e/16, C-layout register e%16)
+  struct BState {
+    f32x4 nl4, d4;
+  };
+  auto stage_b_elem = [&](int e, const f32x16 (&s)[2], const f32x16 (&dp)[2], const float* sL,
+                          const float* sD, int q0, BState& st, float (&pv)[2], float (&dsv)[2],
+                          u32x4 (&pb)[NU], u32x4 (&db)[NU], auto masked) __attribute__((always_inline)) {
+    const int sub = e / 16, i = e % 16, g = i / 4, x = i % 4;
+    const int r0 = sub * 32 + 8 * g + 4 * half;   // first of this lane's 4 query rows
+    if (x == 0) {
+      st.nl4 = *(const f32x4*)(sL + r0);
+      st.d4 = *(const f32x4*)(sD + r0);
+    }
+    float p = fast_exp2(fmaf(s[sub][i], scale_log2, st.nl4[x]));
+    if constexpr (decltype(masked)::value) {
+      const int q = q0 + r0 + x;
+      if ((CAUSAL && my_k > q) || q >= N) p = 0.f;
+    }
+    pv[x & 1] = p;
+    dsv[x & 1] = p * (dp[sub][i] - st.d4[x]);
+    if (x & 1) {
+      const int u = 2 * sub + (g >> 1), w = (g & 1) * 2 + (x >> 1);   // B-operand k-step and word
+      pb[u][w] = pack_bf16(pv[0], pv[1]);
+      db[u][w] = pack_bf16(dsv[0], dsv[1]);
+    }
+  };
+
+  // iteration i: A(tile i in slot c) with B(tile i-1 in slot p) interleaved,
+  // then C(tile i-1); tile i+2 streams into slot n.
+  auto iter = [&](int i, const unsigned char* sQc, const unsigned char* sOc, const unsigned char* sQp,
+                  const unsigned char* sOp, const float* sLp, const float* sDp, unsigned char* sQn,
+                  unsigned char* sOn, float* sLn, float* sDn, f32x16 (&so)[2], f32x16 (&dpo)[2],
+                  f32x16 (&sn)[2], f32x16 (&dpn)[2], auto masked) __attribute__((always_inline)) {
+    pin_offsets();
+    load(i + 2, sQn, sOn, sLn, sDn);
+    const int q0p = q_first + (i - 1) * kKvBQ;
+    u32x4 pb[NU], db[NU];
+    BState st;
+    float pv[2], dsv[2];
+    u32x4 ring[LEAD];
+#pragma unroll
+    for (int x = 0; x < LEAD; ++x) ring[x] = a_operand(sQc, sOc, x);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-      for (int k = 0; k < KSTEPS; ++k) {
-        const bf16x8 aq = *(const bf16x8*)(sQ + tile_off<D>(sub * 32 + l32, 2 * k + half));
-        const bf16x8 ao = *(const bf16x8*)(sO + tile_off<D>(sub * 32 + l32, 2 * k + half));
-        s[sub] = mfma_bf16(aq, kf[k], k == 0 ? zero16() : s[sub]);
-        dp[sub] = mfma_bf16(ao, vf[k], k == 0 ? zero16() : dp[sub]);
-      }
+      sn[sub] = zero16();
+      dpn[sub] = zero16();
     }
-    const bool need_mask = (CAUSAL && q0 < wave_k0 + 31) || (q0 + kKvBQ > N);
-    u32x4 pb[4], db[4];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+    for (int idx = 0; idx < NA; ++idx) {
+      const u32x4 a = ring[idx % LEAD];
+      if (idx + LEAD < NA) ring[idx % LEAD] = a_operand(sQc, sOc, idx + LEAD);
+      a_op(idx, a, sn, dpn);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r0 = sub * 32 + 8 * g + 4 * half;   // first of this lane's 4 query rows
-        const f32x4 lse4 = *(const f32x4*)(sL + r0);
-        const f32x4 d4 = *(const f32x4*)(sD + r0);
-        float pv[4], dsv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g + e;
-          float p = fast_exp2(fmaf(s[sub][i], scale_log2, -lse4[e] * kLog2e));
-          if (need_mask && ((CAUSAL && my_k > q0 + r0 + e) || q0 + r0 + e >= N)) p = 0.f;
-          pv[e] = p;
-          dsv[e] = p * (dp[sub][i] - d4[e]);
-        }
-        const int u = 2 * sub + (g >> 1), w = (g & 1) * 2;   // B-operand k-step and word
-        pb[u][w] = pack_bf16(pv[0], pv[1]);
-        pb[u][w + 1] = pack_bf16(pv[2], pv[3]);
-        db[u][w] = pack_bf16(dsv[0], dsv[1]);
-        db[u][w + 1] = pack_bf16(dsv[2], dsv[3]);
-      }
-    // dV^T += dO^T P ; dK^T += Q^T dS   (contraction over the 64 queries)
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        dv[t] = mfma_bf16(tr_operand<D>(sO, u, t, lane), as_bf16x8(pb[u]), dv[t]);
-        dk[t] = mfma_bf16(tr_operand<D>(sQ, u, t, lane), as_bf16x8(db[u]), dk[t]);
-      }
+      for (int e = idx * NE / NA; e < (idx + 1) * NE / NA; ++e)
+        stage_b_elem(e, so, dpo, sLp, sDp, q0p, st, pv, dsv, pb, db, masked);
+    }
+    stage_c(sQp, sOp, pb, db);
+    barrier_vm<VM_TILE>();       // tile i+1 has landed; tile i+2 may still stream
   };
-  for (int i = 0; i < n_q; i += 2) {
-    if (i + 1 < n_q) load(i + 1, sQ1, sO1, sL1, sD1);
-    compute(i, sQ0, sO0, sL0, sD0);
-    barrier_all();
-    if (i + 1 < n_q) {
-      if (i + 2 < n_q) load(i + 2, sQ0, sO0, sL0, sD0);
-      compute(i + 1, sQ1, sO1, sL1, sD1);
-      barrier_all();
+  // last tile: B then C
+  auto fin = [&](int i, const unsigned char* sQp, const unsigned char* sOp, const float* sLp,
+                 const float* sDp, f32x16 (&so)[2], f32x16 (&dpo)[2]) __attribute__((always_inline)) {
+    const int q0p = q_first + i * kKvBQ;
+    u32x4 pb[NU], db[NU];
+    BState st;
+    float pv[2], dsv[2];
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+      stage_b_elem(e, so, dpo, sLp, sDp, q0p, st, pv, dsv, pb, db, std::integral_constant<bool, true>{});
+    stage_c(sQp, sOp, pb, db);
+  };
+  using Yes = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
+  f32x16 sa[2], dpa[2], sb[2], dpb[2];   // S, dP of even / odd tiles
+  // slot r = tile index mod 4; S of even tiles in (sa, dpa), odd in (sb, dpb)
+  auto it0 = [&](int i, auto m) __attribute__((always_inline)) {   // i = 0 mod 4
+    iter(i, sQ0, sO0, sQ3, sO3, sL3, sD3, sQ2, sO2, sL2, sD2, sb, dpb, sa, dpa, m);
+  };
+  auto it1 = [&](int i, auto m) __attribute__((always_inline)) {   // i = 1 mod 4
+    iter(i, sQ1, sO1, sQ0, sO0, sL0, sD0, sQ3, sO3, sL3, sD3, sa, dpa, sb, dpb, m);
+  };
+  auto it2 = [&](int i, auto m) __attribute__((always_inline)) {   // i = 2 mod 4
+    iter(i, sQ2, sO2, sQ1, sO1, sL1, sD1, sQ0, sO0, sL0, sD0, sb, dpb, sa, dpa, m);
+  };
+  auto it3 = [&](int i, auto m) __attribute__((always_inline)) {   // i = 3 mod 4
+    iter(i, sQ3, sO3, sQ2, sO2, sL2, sD2, sQ1, sO1, sL1, sD1, sa, dpa, sb, dpb, m);
+  };
+
+  // prologue: A of tile 0
+  pin_offsets();
+  {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      sa[sub] = zero16();
+      dpa[sub] = zero16();
+    }
+#pragma unroll
+    for (int idx = 0; idx < NA; ++idx) a_op(idx, a_operand(sQ0, sO0, idx), sa, dpa);
+  }
+  if (n_q == 1) {
+    fin(0, sQ0, sO0, sL0, sD0, sa, dpa);
+  } else {
+    it1(1, Yes{});                 // B of tile 0 (causal diagonal) is masked
+    if (n_q == 2) {
+      fin(1, sQ1, sO1, sL1, sD1, sb, dpb);
+    } else {
+      it2(2, Yes{});               // B of tile 1 (causal diagonal) is masked
+      int i = 3;
+      for (; i + 3 < n_q; i += 4) {
+        it3(i, No{});
+        it0(i + 1, No{});
+        it1(i + 2, No{});
+        it2(i + 3, No{});
+      }
+      // the last tile (possibly ragged) is finished masked
+      if (i < n_q) {
+        it3(i, No{});
+        if (i + 1 < n_q) {
+          it0(i + 1, No{});
+          if (i + 2 < n_q) {
+            it1(i + 2, No{});
+            fin(i + 2, sQ1, sO1, sL1, sD1, sb, dpb);
+          } else {
+            fin(i + 1, sQ0, sO0, sL0, sD0, sa, dpa);
+          }
+        } else {
+          fin(i, sQ3, sO3, sL3, sD3, sb, dpb);
+        }
+      } else {
+        fin(i - 1, sQ2, sO2, sL2, sD2, sa, dpa);
+      }
     }
   }
 
@@ -276,7 +424,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     qf[s] = as_bf16x8(bload16(rQ, (uint32_t)(my_q * D + 16 * s + 8 * half) * 2));
     dof[s] = as_bf16x8(bload16(rdO, (uint32_t)(my_q * D + 16 * s + 8 * half) * 2));
   }
-  const float neg_lse2 = -bload4f(rL, (uint32_t)my_q * 4) * kLog2e;
+  const float neg_lse2 = bload4f(rL, (uint32_t)my_q * 4);   // -LSE log2(e)
   const float Di = bload4f(rD, (uint32_t)my_q * 4);
   f32x16 dq[DT];
 #pragma unroll
@@ -344,22 +492,23 @@ template <int D, bool CAUSAL>
 hipError_t launch(const BwdArgs& a) {
   const long long rows = (long long)a.B * a.H * a.N;
   constexpr int rows_per_block = kThreads / (D / 8);
+  float* NLvec = a.Dvec + rows;   // -LSE log2(e), after D in the workspace
   hipLaunchKernelGGL((bwd_dot_kernel<D>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
-                     dim3(kThreads), 0, a.stream, (const __bf16*)a.O, (const __bf16*)a.dO, a.Dvec,
-                     rows);
+                     dim3(kThreads), 0, a.stream, (const __bf16*)a.O, (const __bf16*)a.dO, a.LSE,
+                     a.Dvec, NLvec, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float sl2 = a.scale * kLog2e;
   const int n_kt = (a.N + kKvBN - 1) / kKvBN;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(a.B * a.H * n_kt), dim3(kThreads), 0,
                      a.stream, (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V,
-                     (const __bf16*)a.dO, a.LSE, a.Dvec, a.dK, a.dV, a.N, a.scale, sl2, n_kt);
+                     (const __bf16*)a.dO, NLvec, a.Dvec, a.dK, a.dV, a.N, a.scale, sl2, n_kt);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_qt = (a.N + kQBM - 1) / kQBM;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(a.B * a.H * n_qt), dim3(kThreads), 0,
                      a.stream, (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V,
-                     (const __bf16*)a.dO, a.LSE, a.Dvec, a.dQ, a.N, a.scale, sl2, n_qt);
+                     (const __bf16*)a.dO, NLvec, a.Dvec, a.dQ, a.N, a.scale, sl2, n_qt);
   return hipGetLastError();
 }
 

@@ -107,6 +107,15 @@ __device__ __forceinline__ void barrier_lds() {
 __device__ __forceinline__ void barrier_all() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+// Barrier after this wave's vector-memory operations older than its last N
+// have completed: with buffer->LDS transfers issued in order, a tile issued
+// N operations ago has landed (for every wave, once all pass the barrier)
+// while the newest transfers keep streaming.
+template <int N>
+__device__ __forceinline__ void barrier_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 // Map the hardware workgroup id to a logical tile id so that consecutive
 // logical tiles land on the same XCD: the dispatcher hands workgroups to the

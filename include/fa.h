@@ -90,8 +90,9 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
            int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
 
 /*
- * fa_bwd_workspace_size -- bytes of workspace fa_bwd needs for this shape
- * (the per-row D_i = sum_d dO_id O_id vector, fp32 [B,H,N], rounded up).
+ * fa_bwd_workspace_size -- bytes of workspace fa_bwd needs for this shape:
+ * two fp32 [B,H,N] row vectors, D_i = sum_d dO_id O_id and -LSE_i log2(e),
+ * rounded up to 256 bytes.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 

@@ -79,7 +79,7 @@ def test_fwd_validation(lib):
 
 def test_bwd_validation(lib):
     ws = lib.fa_bwd_workspace_size(2, 3, 100, 128)
-    assert ws >= 2 * 3 * 100 * 4 and ws % 256 == 0
+    assert ws >= 2 * (2 * 3 * 100 * 4) and ws % 256 == 0
     assert lib.fa_bwd_workspace_size(0, 3, 100, 128) == 0
 
     def bwd(dt=1, d=128, N=100, ws_ptr=P2, ws_bytes=ws, dq=P2, B=2, scale=0.1):
