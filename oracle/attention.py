@@ -40,6 +40,18 @@ What is computed, and where the pages state it
   included.  Token t of sequence s lives in physical block
   block_table[s, t // block_size], slot t % block_size.
 
+* Offset blocks and merging partial results (HPC notes, section "Long context
+  and sequence parallelism"; CS231N L11 notes, context-parallel part, ring
+  attention): a rank holds a block of queries and meets the key/value blocks
+  of the other ranks one at a time.  Rows carry global positions: query i of
+  the block sits at q_offset + i, key j at k_offset + j, and the causal rule
+  compares global positions.  Two partial results over disjoint key sets
+  combine by the same rescale rule as the online softmax: with LSE = m + ln l,
+  the weights are exp(LSE_a - M) and exp(LSE_b - M) for M = max(LSE_a, LSE_b).
+  A query that sees no key of a block gets O = 0 and LSE = -inf there (the
+  online softmax's starting state m = -inf, l = 0), which the merge treats as
+  contributing nothing.
+
 LSE is the natural log of the softmax denominator over the visible scaled
 scores: LSE_i = m_i + ln(l_i).
 
@@ -64,6 +76,7 @@ __all__ = [
     "online_softmax", "attention_forward_head", "attention_forward",
     "attention_backward_head", "attention_backward", "gather_tokens",
     "paged_decode", "grad_v", "grad_p", "row_dot", "grad_s", "grad_q", "grad_k",
+    "merge_partials",
 ]
 
 
@@ -82,12 +95,18 @@ def scores(q: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
     return scale * (q @ k.T)
 
 
-def visible(rows: np.ndarray, nk: int, causal: bool) -> np.ndarray:
-    """Boolean [len(rows), nk]: key j visible to query i (all keys, or j <= i if causal)."""
-    cols = np.arange(nk)
+def visible(rows: np.ndarray, nk: int, causal: bool, q_offset: int = 0,
+            k_offset: int = 0) -> np.ndarray:
+    """Boolean [len(rows), nk]: key j visible to query i.
+
+    All keys without the causal rule; with it, key j (global position
+    k_offset + j) is visible to query i (global position q_offset + i) iff
+    k_offset + j <= q_offset + i.
+    """
+    cols = np.arange(nk, dtype=np.int64) + int(k_offset)
     if not causal:
         return np.ones((len(rows), nk), dtype=bool)
-    return cols[None, :] <= np.asarray(rows)[:, None]
+    return cols[None, :] <= (np.asarray(rows, dtype=np.int64) + int(q_offset))[:, None]
 
 
 def safe_softmax(s: np.ndarray):
@@ -148,24 +167,32 @@ def _row_chunks(rows: np.ndarray, nk: int, budget_elems: int = 1 << 22):
         yield rows[i:i + step]
 
 
-def attention_forward_head(q, k, v, scale: float, causal: bool, rows=None):
+def attention_forward_head(q, k, v, scale: float, causal: bool, rows=None, q_offset: int = 0,
+                           k_offset: int = 0):
     """Exact attention for one (batch, head).
 
     q [Nq, d], k [Nk, d], v [Nk, dv] float64.  ``rows`` selects a subset of the
-    query rows (default: all).  Returns (O [len(rows), dv], LSE [len(rows)]).
-    Rows are processed in chunks to bound memory; each row is independent.
+    query rows (default: all).  ``q_offset`` / ``k_offset`` are the global
+    positions of the first query / key row (they matter only for the causal
+    rule).  Returns (O [len(rows), dv], LSE [len(rows)]); a row with no visible
+    key gets O = 0 and LSE = -inf.  Rows are processed in chunks to bound
+    memory; each row is independent.
     """
     nq, nk = q.shape[0], k.shape[0]
     rows = np.arange(nq) if rows is None else np.asarray(rows, dtype=np.int64)
-    o = np.empty((len(rows), v.shape[1]), dtype=np.float64)
-    lse = np.empty((len(rows),), dtype=np.float64)
+    o = np.zeros((len(rows), v.shape[1]), dtype=np.float64)
+    lse = np.full((len(rows),), -np.inf, dtype=np.float64)
     pos = 0
     for r in _row_chunks(rows, nk):
-        s = scores(q[r], k, scale)
-        s = np.where(visible(r, nk, causal), s, -np.inf)
-        p, m, l = safe_softmax(s)
-        o[pos:pos + len(r)] = attend(p, v)
-        lse[pos:pos + len(r)] = lse_of(m, l)
+        vis = visible(r, nk, causal, q_offset, k_offset)
+        some = vis.any(axis=1)                     # rows that see at least one key
+        if some.any():
+            rs = r[some]
+            s = np.where(vis[some], scores(q[rs], k, scale), -np.inf)
+            p, m, l = safe_softmax(s)
+            idx = pos + np.nonzero(some)[0]
+            o[idx] = attend(p, v)
+            lse[idx] = lse_of(m, l)
         pos += len(r)
     return o, lse
 
@@ -182,11 +209,12 @@ def _pool_map(fn, items, workers):
 
 
 def attention_forward(q, k, v, scale: float, causal: bool, heads=None, rows=None,
-                      workers: int | None = None):
-    """Exact attention over [B, H, N, d] inputs (torch tensors or arrays).
+                      workers: int | None = None, q_offset: int = 0, k_offset: int = 0):
+    """Exact attention over [B, H, Nq, d] queries and [B, H, Nk, d] keys/values.
 
     ``heads`` is an optional list of (b, h) pairs to compute (default all);
-    ``rows`` an optional list of query rows within each head.  Returns
+    ``rows`` an optional list of query rows within each head; ``q_offset`` /
+    ``k_offset`` the global positions of the first query / key row.  Returns
     {(b, h): (O, LSE)} with float64 arrays.
     """
     B, H = q.shape[0], q.shape[1]
@@ -195,8 +223,32 @@ def attention_forward(q, k, v, scale: float, causal: bool, heads=None, rows=None
     def one(bh):
         b, h = bh
         return attention_forward_head(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]),
-                                      scale, causal, rows)
+                                      scale, causal, rows, q_offset, k_offset)
     return dict(zip(heads, _pool_map(one, heads, workers)))
+
+
+def merge_partials(o_a, lse_a, o_b, lse_b):
+    """Combine two partial attention results over disjoint key sets.
+
+    o_* [..., dv] are normalised partial outputs and lse_* [...] their
+    log-sum-exps.  By the rescale rule: M = max(LSE_a, LSE_b), weights
+    w = exp(LSE - M), O = (w_a O_a + w_b O_b) / (w_a + w_b), LSE = M + ln(w_a + w_b).
+    A side with LSE = -inf has weight 0; if both are -inf the result is O = 0,
+    LSE = -inf.
+    """
+    o_a, o_b = np.asarray(o_a, dtype=np.float64), np.asarray(o_b, dtype=np.float64)
+    lse_a, lse_b = np.asarray(lse_a, dtype=np.float64), np.asarray(lse_b, dtype=np.float64)
+    M = np.maximum(lse_a, lse_b)
+    empty = M == -np.inf
+    Ms = np.where(empty, 0.0, M)
+    w_a = np.where(lse_a == -np.inf, 0.0, np.exp(lse_a - Ms))
+    w_b = np.where(lse_b == -np.inf, 0.0, np.exp(lse_b - Ms))
+    tot = w_a + w_b
+    safe = np.where(empty, 1.0, tot)
+    o = (w_a[..., None] * o_a + w_b[..., None] * o_b) / safe[..., None]
+    o = np.where(empty[..., None], 0.0, o)
+    lse = np.where(empty, -np.inf, Ms + np.log(safe))
+    return o, lse
 
 
 # --------------------------------------------------------------- backward steps

@@ -35,15 +35,23 @@ def softmax_decimal(s) -> list:
         return [e / tot for e in ex]
 
 
-def attention_decimal(q, k, v, scale, causal: bool):
-    """O (list of lists of Decimal) and LSE (list of Decimal) by the literal definition."""
+def attention_decimal(q, k, v, scale, causal: bool, q_offset: int = 0, k_offset: int = 0):
+    """O (list of lists of Decimal) and LSE (list of Decimal) by the literal definition.
+
+    With offsets, query i sits at global position q_offset + i and key j at
+    k_offset + j; a row that sees no key yields O = 0 and LSE = None.
+    """
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     with localcontext() as ctx:
         ctx.prec = PREC
         sc = _D(scale)
         O, L = [], []
         for i in range(q.shape[0]):
-            keys = [j for j in range(k.shape[0]) if (not causal or j <= i)]
+            keys = [j for j in range(k.shape[0]) if (not causal or k_offset + j <= q_offset + i)]
+            if not keys:
+                O.append([Decimal(0)] * v.shape[1])
+                L.append(None)
+                continue
             s = [sc * sum((_D(q[i, c]) * _D(k[j, c]) for c in range(q.shape[1])), Decimal(0))
                  for j in keys]
             ex = [x.exp() for x in s]

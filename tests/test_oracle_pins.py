@@ -250,6 +250,105 @@ def test_backward_invariants():
 
 # ------------------------------------------------------------------ paged decode
 
+# ---------------------------------------- offset blocks and merged partials
+
+# (Nq, Nk, d, q_offset, k_offset): rows ahead of, straddling and behind the
+# key block, including rows that see no key at all
+OFFSET_CASES = ((3, 4, 2, 0, 2), (4, 3, 3, 5, 0), (5, 5, 2, 0, 0), (3, 5, 2, 2, 0), (2, 3, 2, 0, 7),
+                (4, 2, 1, 1, 3))
+
+
+def check_offset_vs_decimal(seed=5):
+    """Offset causal attention against the 50-digit literal definition."""
+    rng = np.random.default_rng(seed)
+    for (nq, nk, d, qo, ko) in OFFSET_CASES:
+        q = rng.standard_normal((nq, d)) * 1.5
+        k = rng.standard_normal((nk, d)) * 1.5
+        v = rng.standard_normal((nk, d + 1))
+        scale = 1.0 / math.sqrt(d)
+        o, lse = A.attention_forward_head(q, k, v, scale, True, q_offset=qo, k_offset=ko)
+        Od, Ld = brute.attention_decimal(q, k, v, scale, True, q_offset=qo, k_offset=ko)
+        np.testing.assert_allclose(o, np.array(Od, dtype=float), rtol=0, atol=1e-13)
+        for got, want in zip(lse, Ld):
+            if want is None:
+                assert got == -np.inf
+            else:
+                assert abs(got - float(want)) <= 1e-13
+
+
+def check_offset_reductions(seed=6):
+    """Offsets that put every key at or before every query give plain
+    (non-causal) attention; equal offsets give the ordinary causal case."""
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((6, 3)) for _ in range(3))
+    o_nc, l_nc = A.attention_forward_head(q, k, v, 0.7, False)
+    o_far, l_far = A.attention_forward_head(q, k, v, 0.7, True, q_offset=105, k_offset=100)
+    np.testing.assert_array_equal(o_far, o_nc)
+    np.testing.assert_array_equal(l_far, l_nc)
+    o_c, l_c = A.attention_forward_head(q, k, v, 0.7, True)
+    o_eq, l_eq = A.attention_forward_head(q, k, v, 0.7, True, q_offset=9, k_offset=9)
+    np.testing.assert_array_equal(o_eq, o_c)
+    np.testing.assert_array_equal(l_eq, l_c)
+    # a key block entirely after every query: nothing visible
+    o_none, l_none = A.attention_forward_head(q, k, v, 0.7, True, q_offset=0, k_offset=6)
+    assert np.all(o_none == 0) and np.all(l_none == -np.inf)
+
+
+def check_merge(seed=7):
+    """Attention over a key set equals the merge of its parts (any split), the
+    empty partial is the identity, and the merge is symmetric and associative."""
+    rng = np.random.default_rng(seed)
+    nq, nk, d = 7, 11, 3
+    q = rng.standard_normal((nq, d)) * 2.0
+    k = rng.standard_normal((nk, d)) * 2.0
+    v = rng.standard_normal((nk, d))
+    for causal, qo in ((True, 0), (True, 4), (True, -3), (False, 0)):
+        full = A.attention_forward_head(q, k, v, 0.6, causal, q_offset=qo)
+        for cut in (1, 5, 10):
+            a = A.attention_forward_head(q, k[:cut], v[:cut], 0.6, causal, q_offset=qo, k_offset=0)
+            b = A.attention_forward_head(q, k[cut:], v[cut:], 0.6, causal, q_offset=qo, k_offset=cut)
+            o, l = A.merge_partials(a[0], a[1], b[0], b[1])
+            np.testing.assert_allclose(o, full[0], rtol=0, atol=1e-13)
+            fin = np.isfinite(full[1])
+            np.testing.assert_allclose(l[fin], full[1][fin], rtol=0, atol=1e-13)
+            assert np.all(l[~fin] == -np.inf) and np.all(o[~fin] == 0)
+            o2, l2 = A.merge_partials(b[0], b[1], a[0], a[1])
+            np.testing.assert_allclose(o2, o, rtol=0, atol=1e-15)
+            np.testing.assert_allclose(l2, l, rtol=0, atol=1e-15)
+        # three parts in either grouping
+        p1, p2, p3 = (A.attention_forward_head(q, k[s:e], v[s:e], 0.6, causal, q_offset=qo, k_offset=s)
+                      for s, e in ((0, 3), (3, 8), (8, nk)))
+        left = A.merge_partials(*A.merge_partials(p1[0], p1[1], p2[0], p2[1]), p3[0], p3[1])
+        right = A.merge_partials(p1[0], p1[1], *A.merge_partials(p2[0], p2[1], p3[0], p3[1]))
+        np.testing.assert_allclose(left[0], full[0], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(right[0], full[0], rtol=0, atol=1e-13)
+    x = A.attention_forward_head(q, k, v, 0.6, False)
+    empty = (np.zeros_like(x[0]), np.full_like(x[1], -np.inf))
+    o, l = A.merge_partials(x[0], x[1], *empty)
+    np.testing.assert_array_equal(o, x[0])
+    np.testing.assert_array_equal(l, x[1])
+    o, l = A.merge_partials(*empty, *empty)
+    assert np.all(o == 0) and np.all(l == -np.inf)
+
+
+def test_offset_attention_vs_decimal_brute_force():
+    check_offset_vs_decimal()
+
+
+def test_offset_attention_reductions():
+    check_offset_reductions()
+
+
+def test_merge_of_partials():
+    check_merge()
+
+
+def _all_offset_pins():
+    check_offset_vs_decimal()
+    check_offset_reductions()
+    check_merge()
+
+
 def _scatter_to_pool(Kc, Vc, lens, block_size, H, d, seed):
     """Build a paged pool from contiguous per-sequence K/V by an independent route."""
     rng = np.random.default_rng(seed)
@@ -357,16 +456,53 @@ FORWARD_MUTANTS = {
     "scale_squared": ("scores", lambda q, k, scale: scale * scale * (q @ k.T)),
     "transposed_scores": ("scores", lambda q, k, scale: scale * (k @ q.T) if q.shape == k.shape
                           else scale * (q @ k.T)[:, ::-1]),
-    "causal_strict": ("visible", lambda rows, nk, causal: (np.arange(nk)[None, :] < np.asarray(rows)[:, None])
+    "causal_strict": ("visible", lambda rows, nk, causal, qo=0, ko=0:
+                      (np.arange(nk)[None, :] + ko < np.asarray(rows)[:, None] + qo)
                       | (not causal) | (np.asarray(rows)[:, None] == 0) & (np.arange(nk)[None, :] == 0)),
-    "causal_reversed": ("visible", lambda rows, nk, causal: (np.arange(nk)[None, :] >= np.asarray(rows)[:, None])
-                        | (not causal)),
-    "causal_ignored": ("visible", lambda rows, nk, causal: np.ones((len(rows), nk), bool)),
+    "causal_reversed": ("visible", lambda rows, nk, causal, qo=0, ko=0:
+                        (np.arange(nk)[None, :] + ko >= np.asarray(rows)[:, None] + qo) | (not causal)),
+    "causal_ignored": ("visible", lambda rows, nk, causal, qo=0, ko=0: np.ones((len(rows), nk), bool)),
     "softmax_wrong_axis": ("safe_softmax", _bad_safe_softmax_axis),
     "softmax_no_max": ("safe_softmax", _bad_safe_softmax_nomax),
     "values_reversed": ("attend", lambda p, v: p @ v[::-1]),
     "lse_sign": ("lse_of", lambda m, l: m - np.log(l)),
     "lse_no_max": ("lse_of", lambda m, l: np.log(l)),
+}
+
+def _merge_plain_average(o_a, lse_a, o_b, lse_b):
+    return 0.5 * (np.asarray(o_a) + np.asarray(o_b)), np.maximum(lse_a, lse_b)
+
+
+def _merge_inverted_weights(o_a, lse_a, o_b, lse_b):
+    M = np.maximum(lse_a, lse_b)
+    w_a, w_b = np.exp(M - lse_a), np.exp(M - lse_b)
+    return (w_a[..., None] * o_a + w_b[..., None] * o_b) / (w_a + w_b)[..., None], M + np.log(w_a + w_b)
+
+
+def _merge_lse_of_max_only(o_a, lse_a, o_b, lse_b):
+    o, _ = _REAL_MERGE(o_a, lse_a, o_b, lse_b)
+    return o, np.maximum(lse_a, lse_b)
+
+
+def _merge_unnormalised(o_a, lse_a, o_b, lse_b):
+    M = np.maximum(lse_a, lse_b)
+    w_a, w_b = np.exp(lse_a - M), np.exp(lse_b - M)
+    return w_a[..., None] * o_a + w_b[..., None] * o_b, M + np.log(w_a + w_b)
+
+
+_REAL_MERGE = A.merge_partials
+
+OFFSET_MUTANTS = {
+    "offset_ignored": ("visible", lambda rows, nk, causal, qo=0, ko=0:
+                       (np.arange(nk)[None, :] <= np.asarray(rows)[:, None]) | (not causal)),
+    "offset_swapped": ("visible", lambda rows, nk, causal, qo=0, ko=0:
+                       (np.arange(nk)[None, :] + qo <= np.asarray(rows)[:, None] + ko) | (not causal)),
+    "offset_one_late": ("visible", lambda rows, nk, causal, qo=0, ko=0:
+                        (np.arange(nk)[None, :] + ko < np.asarray(rows)[:, None] + qo) | (not causal)),
+    "merge_plain_average": ("merge_partials", _merge_plain_average),
+    "merge_inverted_weights": ("merge_partials", _merge_inverted_weights),
+    "merge_lse_of_max_only": ("merge_partials", _merge_lse_of_max_only),
+    "merge_unnormalised": ("merge_partials", _merge_unnormalised),
 }
 
 BACKWARD_MUTANTS = {
@@ -406,6 +542,7 @@ DECODE_MUTANTS = {
 
 
 def test_pins_pass_on_unmodified_oracle(golden_dir):
+    _all_offset_pins()
     _all_forward_pins(golden_dir)
     _all_backward_pins()
     check_decode()
@@ -418,6 +555,15 @@ def test_forward_pins_catch_planted_mistake(mutant, monkeypatch, golden_dir):
     with pytest.raises((AssertionError, ValueError, FloatingPointError)):
         with np.errstate(all="ignore"):
             _all_forward_pins(golden_dir)
+
+
+@pytest.mark.parametrize("mutant", sorted(OFFSET_MUTANTS))
+def test_offset_pins_catch_planted_mistake(mutant, monkeypatch):
+    name, fn = OFFSET_MUTANTS[mutant]
+    monkeypatch.setattr(A, name, fn)
+    with pytest.raises((AssertionError, ValueError, FloatingPointError)):
+        with np.errstate(all="ignore"):
+            _all_offset_pins()
 
 
 @pytest.mark.parametrize("mutant", sorted(BACKWARD_MUTANTS))
