@@ -20,8 +20,8 @@ LIB_PATH = os.path.join(_PKG, "libfa.so")
 FA_DT_F32 = 0
 FA_DT_BF16 = 1
 
-EXPORTED = ("fa_status_string", "fa_version", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd",
-            "fa_paged_decode_workspace_size", "fa_paged_decode")
+EXPORTED = ("fa_status_string", "fa_version", "fa_fwd", "fa_fwd_offset", "fa_merge",
+            "fa_bwd_workspace_size", "fa_bwd", "fa_paged_decode_workspace_size", "fa_paged_decode")
 
 _lib = None
 
@@ -53,6 +53,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fa_version.restype = i
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lib.fa_fwd.restype = i
+    ll = ctypes.c_longlong
+    lib.fa_fwd_offset.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, ll, ll, f, i, i, vp]
+    lib.fa_fwd_offset.restype = i
+    lib.fa_merge.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.fa_merge.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd.argtypes = [vp] * 9 + [i, i, i, i, f, i, i, vp, sz, vp]
@@ -109,6 +114,42 @@ def fwd(q, k, v, *, causal: bool, scale: float | None = None, out=None, lse=None
     st = load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, N, d, scale,
                                int(bool(causal)), _dtype_code(q), _stream(q.device))
     _check(st, "fa_fwd")
+    return o, l
+
+
+def fwd_offset(q, k, v, *, q_offset: int, k_offset: int, causal: bool, scale: float | None = None,
+               out=None, lse=None):
+    """O, LSE of a query block [B, H, Nq, d] against a key/value block [B, H, Nk, d]
+    whose rows sit at global positions q_offset + i and k_offset + j."""
+    _need_cuda(q, k, v)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if (k.shape[:2] != q.shape[:2] or k.shape[3] != d or v.shape != k.shape
+            or k.dtype != q.dtype or v.dtype != q.dtype):
+        raise ValueError("q [B,H,Nq,d], k and v [B,H,Nk,d] must share B, H, d and dtype")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = load_library().fa_fwd_offset(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, Nq, Nk, d,
+                                      int(q_offset), int(k_offset), scale, int(bool(causal)),
+                                      _dtype_code(q), _stream(q.device))
+    _check(st, "fa_fwd_offset")
+    return o, l
+
+
+def merge(o_a, lse_a, o_b, lse_b, *, out=None, lse_out=None):
+    """Combine two partial results over disjoint key sets; ``out``/``lse_out`` may
+    be ``o_a``/``lse_a`` (or the b side) for in-place accumulation."""
+    _need_cuda(o_a, o_b, lse_a, lse_b)
+    B, H, N, d = o_a.shape
+    if o_b.shape != o_a.shape or o_b.dtype != o_a.dtype or lse_a.shape != (B, H, N) \
+            or lse_b.shape != (B, H, N):
+        raise ValueError("partials must share [B, H, N, d] / [B, H, N] shapes and dtype")
+    o = torch.empty_like(o_a) if out is None else out
+    l = torch.empty_like(lse_a) if lse_out is None else lse_out
+    st = load_library().fa_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o), _ptr(l),
+                                 B, H, N, d, _dtype_code(o_a), _stream(o_a.device))
+    _check(st, "fa_merge")
     return o, l
 
 

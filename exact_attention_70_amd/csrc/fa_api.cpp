@@ -29,6 +29,15 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Per-head byte sizes must fit the 32-bit range of a buffer resource.
 bool head_fits(long long N, long long d, long long elem) { return N * d * elem < (1LL << 31); }
 
+// Global positions handed to fa_fwd_offset (their difference must not overflow).
+constexpr long long kMaxOffset = 1LL << 60;
+
+// Two equal-length buffers overlap without being the same buffer.
+bool partial_overlap(const void* x, const void* y, size_t bytes) {
+  const auto a = reinterpret_cast<uintptr_t>(x), b = reinterpret_cast<uintptr_t>(y);
+  return a != b && a < b + bytes && b < a + bytes;
+}
+
 }  // namespace
 
 extern "C" {
@@ -42,7 +51,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: configuration not implemented";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointer not 16-byte aligned";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
-    case FA_ERR_INVALID: return "FA_ERR_INVALID: block_table or seq_lens contents invalid";
+    case FA_ERR_INVALID: return "FA_ERR_INVALID: invalid contents or overlapping buffers";
     case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error";
     default: return "unknown libfa status";
   }
@@ -50,21 +59,55 @@ const char* fa_status_string(int status) {
 
 int fa_version(void) { return 100; }
 
-int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N,
-           int d, float scale, int causal, int dtype, void* stream) {
+int fa_fwd_offset(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                  int Nq, int Nk, int d, long long q_offset, long long k_offset, float scale,
+                  int causal, int dtype, void* stream) {
   if (dtype != FA_DT_F32 && dtype != FA_DT_BF16) return FA_ERR_DTYPE;
-  if (B < 0 || H < 1 || N < 1 || N > kMaxN || d < 1) return FA_ERR_SHAPE;
+  if (B < 0 || H < 1 || Nq < 1 || Nq > kMaxN || Nk < 1 || Nk > kMaxN || d < 1) return FA_ERR_SHAPE;
+  if (q_offset < -kMaxOffset || q_offset > kMaxOffset || k_offset < -kMaxOffset ||
+      k_offset > kMaxOffset)
+    return FA_ERR_SHAPE;
   if (!std::isfinite(scale)) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if (!head_fits(N, d, dtype == FA_DT_F32 ? 4 : 2)) return FA_ERR_SHAPE;
-  if ((long long)B * H * ((N + 31) / 32) >= (1LL << 31)) return FA_ERR_SHAPE;
+  const int elem = dtype == FA_DT_F32 ? 4 : 2;
+  if (!head_fits(Nq, d, elem) || !head_fits(Nk, d, elem)) return FA_ERR_SHAPE;
+  if ((long long)B * H * ((Nq + 31) / 32) >= (1LL << 31)) return FA_ERR_SHAPE;
   if (B == 0) return FA_OK;
   if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
     return FA_ERR_ALIGN;
-  fa::FwdArgs a{Q, K, V, O, LSE, B, H, N, d, scale, causal != 0, dtype,
+  fa::FwdArgs a{Q, K, V, O, LSE, B, H, Nq, d, scale, causal != 0, dtype,
                 reinterpret_cast<hipStream_t>(stream)};
+  a.Nk = Nk;
+  a.delta = q_offset - k_offset;
   return hip_status(fa::launch_fwd(a));
+}
+
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N,
+           int d, float scale, int causal, int dtype, void* stream) {
+  return fa_fwd_offset(Q, K, V, O, LSE, B, H, N, N, d, 0, 0, scale, causal, dtype, stream);
+}
+
+int fa_merge(const void* O_a, const float* LSE_a, const void* O_b, const float* LSE_b, void* O,
+             float* LSE, int B, int H, int N, int d, int dtype, void* stream) {
+  if (dtype != FA_DT_F32 && dtype != FA_DT_BF16) return FA_ERR_DTYPE;
+  if (B < 0 || H < 1 || N < 1 || N > kMaxN || d < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (B == 0) return FA_OK;
+  if (!O_a || !LSE_a || !O_b || !LSE_b || !O || !LSE) return FA_ERR_NULL;
+  if (!aligned16(O_a) || !aligned16(O_b) || !aligned16(O) || !aligned16(LSE_a) ||
+      !aligned16(LSE_b) || !aligned16(LSE))
+    return FA_ERR_ALIGN;
+  const long long rows = (long long)B * H * N;
+  const size_t obytes = (size_t)rows * d * (dtype == FA_DT_F32 ? 4 : 2);
+  const size_t lbytes = (size_t)rows * sizeof(float);
+  // outputs may be exactly an input buffer (in-place accumulation), never a shifted overlap
+  if (partial_overlap(O, O_a, obytes) || partial_overlap(O, O_b, obytes) ||
+      partial_overlap(LSE, LSE_a, lbytes) || partial_overlap(LSE, LSE_b, lbytes))
+    return FA_ERR_INVALID;
+  fa::MergeArgs a{O_a, LSE_a, O_b, LSE_b, O, LSE, rows, d, dtype,
+                  reinterpret_cast<hipStream_t>(stream)};
+  return hip_status(fa::launch_merge(a));
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {

@@ -34,6 +34,8 @@
 //     separate tail of the loop.
 //   * workgroups are ordered heaviest-first within each head and mapped so
 //     that one head's query tiles share an XCD (and its L2).
+#include <algorithm>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 #include <type_traits>
@@ -54,8 +56,11 @@ constexpr float kSlack = 8.f;
 template <int D, bool CAUSAL, int BN, int OCC>
 __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int N, float scale_log2, int n_qtiles) {
-  // scale_log2 = scale * log2(e): scores are handled in base 2
+    __bf16* __restrict__ O, float* __restrict__ LSE, int N, int Nk, int delta, float scale_log2,
+    int n_qtiles) {
+  // scale_log2 = scale * log2(e): scores are handled in base 2.  N query rows
+  // and Nk key rows per head; with CAUSAL, key j is visible to row i iff
+  // j <= i + delta.
   constexpr int KSTEPS = D / 16;         // matrix k-steps over the head dim
   constexpr int DT = D / 32;             // 32-row tiles of O^T
   constexpr int TILE = BN * D * 2;       // bytes of one K or V tile
@@ -80,17 +85,30 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
   const int q0 = qt * kBM;
 
   const size_t head_off = (size_t)bh * (size_t)N * D;
+  const size_t khead_off = (size_t)bh * (size_t)Nk * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const uint32_t khead_bytes = (uint32_t)Nk * D * 2;
   const auto rQ = make_rsrc(Q + head_off, head_bytes);
-  const auto rK = make_rsrc(K + head_off, head_bytes);
-  const auto rV = make_rsrc(V + head_off, head_bytes);
+  const auto rK = make_rsrc(K + khead_off, khead_bytes);
+  const auto rV = make_rsrc(V + khead_off, khead_bytes);
   const auto rO = make_rsrc(O + head_off, head_bytes);
   const auto rL = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
 
-  const int kv_end = CAUSAL ? min(N, q0 + kBM) : N;
-  const int n_kv = (kv_end + BN - 1) / BN;
+  const int kv_end = CAUSAL ? min(Nk, q0 + kBM + delta) : Nk;
+  const int n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
   // tiles [0, n_full) need no masking for any row of this workgroup
-  const int n_full = min(CAUSAL ? q0 / BN : n_kv, N / BN);
+  const int n_full = min(CAUSAL ? max(0, q0 + delta + 1) / BN : n_kv, Nk / BN);
+  if (n_kv == 0) {
+    // no row of this tile sees any key: empty softmax, O = 0 and LSE = -inf
+    const int row = q0 + tid / 2;
+    if (tid < 2 * kBM) {
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+        bstore16(u32x4{0u, 0u, 0u, 0u}, rO, (uint32_t)(row * D + (tid & 1) * (D / 2) + 8 * c) * 2);
+      if ((tid & 1) == 0) bstore4f(kNegInf, rL, (uint32_t)row * 4);
+    }
+    return;
+  }
 
   // ---- this wave's query rows, straight from HBM into B-operand registers;
   //      K_0 and V_0 into ring slot 0
@@ -166,7 +184,7 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
   };
   // keys beyond this lane's row (causal) or beyond N become -inf
   auto mask = [&](f32x16 (&s)[NSUB], int kb) {
-    const int lim = min(CAUSAL ? my_q : N - 1, N - 1) - kb - 4 * half;
+    const int lim = min(CAUSAL ? my_q + delta : Nk - 1, Nk - 1) - kb - 4 * half;
 #pragma unroll
     for (int t = 0; t < NSUB; ++t)
 #pragma unroll
@@ -313,7 +331,8 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
 
   // ---- epilogue: O = O^T / l, LSE = ln(sum exp) = (m + log2 l) ln 2
   const float l_tot = l_run + swap_half(l_run);
-  const float inv = 1.f / l_tot;
+  // a row that saw no key (l = 0) gets O = 0 and LSE = -inf
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
   for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -324,7 +343,8 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
       w[1] = pack_bf16(o[t][4 * g + 2] * inv, o[t][4 * g + 3] * inv);
       bstore8(w, rO, (uint32_t)(my_q * D + d0) * 2);
     }
-  if (half == 0) bstore4f((m_run + fast_log2(l_tot)) * kLn2, rL, (uint32_t)my_q * 4);
+  if (half == 0)
+    bstore4f(l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf, rL, (uint32_t)my_q * 4);
 }
 
 // ---------------------------------------------------------------------------
@@ -339,8 +359,8 @@ constexpr int kF32BN = 32;
 template <int D>
 __global__ __launch_bounds__(64) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ LSE, int N, float scale_log2, int causal,
-    int n_qtiles) {
+    float* __restrict__ O, float* __restrict__ LSE, int N, int Nk, int delta, float scale_log2,
+    int causal, int n_qtiles) {
   constexpr int KSTEPS = D / 2;
   constexpr int DT = D / 32;
   constexpr int PAD = 1;                         // one-float row pad: conflict-free column reads
@@ -354,10 +374,12 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(
   const int bh = tile / n_qtiles;
   const int q0 = (tile % n_qtiles) * kF32BM;
   const size_t head_off = (size_t)bh * (size_t)N * D;
+  const size_t khead_off = (size_t)bh * (size_t)Nk * D;
   const uint32_t head_bytes = (uint32_t)N * D * 4;
+  const uint32_t khead_bytes = (uint32_t)Nk * D * 4;
   const auto rQ = make_rsrc(Q + head_off, head_bytes);
-  const auto rK = make_rsrc(K + head_off, head_bytes);
-  const auto rV = make_rsrc(V + head_off, head_bytes);
+  const auto rK = make_rsrc(K + khead_off, khead_bytes);
+  const auto rV = make_rsrc(V + khead_off, khead_bytes);
   const auto rO = make_rsrc(O + head_off, head_bytes);
   const auto rL = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
 
@@ -372,7 +394,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(
   for (int t = 0; t < DT; ++t) o[t] = zero16();
   float m_run = kNegInf, l_run = 0.f;
 
-  const int kv_end = causal ? min(N, q0 + kF32BM) : N;
+  const int kv_end = causal ? min(Nk, q0 + kF32BM + delta) : Nk;   // may be <= 0: no key
   for (int kb = 0; kb < kv_end; kb += kF32BN) {
     __syncthreads();
     for (int e = lane; e < kF32BN * D / 4; e += 64) {
@@ -396,7 +418,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(
     for (int i = 0; i < 16; ++i) {
       const int key = kb + 8 * (i >> 2) + 4 * half + (i & 3);
       float x = s[i] * scale_log2;
-      if ((causal && key > my_q) || key >= N) x = kNegInf;
+      if ((causal && key > my_q + delta) || key >= Nk) x = kNegInf;
       s[i] = x;
       mx = fmaxf(mx, x);
     }
@@ -428,7 +450,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(
   }
 
   const float l_tot = l_run + swap_half(l_run);
-  const float inv = 1.f / l_tot;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // no visible key: O = 0
 #pragma unroll
   for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -439,37 +461,129 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(
       for (int x = 0; x < 4; ++x) w[x] = as_u32(o[t][4 * g + x] * inv);
       bstore16(w, rO, (uint32_t)(my_q * D + d0) * 4);
     }
-  if (half == 0) bstore4f((m_run + fast_log2(l_tot)) * kLn2, rL, (uint32_t)my_q * 4);
+  if (half == 0)
+    bstore4f(l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf, rL, (uint32_t)my_q * 4);
+}
+
+// ---------------------------------------------------------------------------
+// Empty result for query rows that see no key at all: O = 0, LSE = -inf.
+template <typename T>
+__global__ __launch_bounds__(256) void fill_empty_kernel(T* __restrict__ O, float* __restrict__ LSE,
+                                                         long long rows, int d) {
+  const long long n = rows * d;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
+    O[i] = T(0.f);
+  for (long long r = (long long)blockIdx.x * 256 + threadIdx.x; r < rows; r += (long long)gridDim.x * 256)
+    LSE[r] = kNegInf;
+}
+
+// ---------------------------------------------------------------------------
+// Merge of two partial results over disjoint key sets (the rescale rule):
+// M = max(LSE_a, LSE_b), w = exp(LSE - M), O = (w_a O_a + w_b O_b) / (w_a + w_b),
+// LSE = M + ln(w_a + w_b); a side at LSE = -inf weighs nothing.  One thread
+// handles 16 bytes of a row; a row's threads sit in one wave, so the output
+// may be the same buffer as either input.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_kernel(const T* Oa, const float* La, const T* Ob,
+                                                    const float* Lb, T* O, float* L, long long rows) {
+  constexpr int EPT = 16 / sizeof(T);      // elements per thread
+  constexpr int TPR = D / EPT;             // threads per row (<= 32)
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = gid / TPR;
+  const int c = (int)(gid % TPR);
+  if (row >= rows) return;
+  const float la = La[row], lb = Lb[row];
+  const float M = fmaxf(la, lb);
+  const bool empty = M == kNegInf;
+  const float wa = empty ? 0.f : fast_exp2((la - M) * kLog2e);
+  const float wb = empty ? 0.f : fast_exp2((lb - M) * kLog2e);
+  const float tot = wa + wb;
+  const float inv = empty ? 0.f : 1.f / tot;
+  const float ca = wa * inv, cb = wb * inv;
+  const long long off = row * D + (long long)c * EPT;
+  const u32x4 a = *(const u32x4*)(Oa + off);
+  const u32x4 b = *(const u32x4*)(Ob + off);
+  u32x4 r;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      r[e] = pack_bf16(ca * bf16lo(a[e]) + cb * bf16lo(b[e]), ca * bf16hi(a[e]) + cb * bf16hi(b[e]));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = as_u32(ca * as_f32(a[e]) + cb * as_f32(b[e]));
+  }
+  *(u32x4*)(O + off) = r;
+  if (c == 0) L[row] = empty ? kNegInf : M + fast_log2(tot) * kLn2;
 }
 
 template <int D, bool CAUSAL, int BN = kBNDefault, int OCC = 2>
-hipError_t launch_bf16(const FwdArgs& a) {
+hipError_t launch_bf16(const FwdArgs& a, int Nk, int delta) {
   const int n_qtiles = (a.N + kBM - 1) / kBM;
   const int grid = a.B * a.H * n_qtiles;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, BN, OCC>), dim3(grid), dim3(kThreads), 0, a.stream,
                      (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (__bf16*)a.O,
-                     a.LSE, a.N, a.scale * kLog2e, n_qtiles);
+                     a.LSE, a.N, Nk, delta, a.scale * kLog2e, n_qtiles);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_f32(const FwdArgs& a) {
+hipError_t launch_f32(const FwdArgs& a, int Nk, int delta, bool causal) {
   const int n_qtiles = (a.N + kF32BM - 1) / kF32BM;
   const int grid = a.B * a.H * n_qtiles;
   hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3(grid), dim3(64), 0, a.stream,
                      (const float*)a.Q, (const float*)a.K, (const float*)a.V, (float*)a.O, a.LSE,
-                     a.N, a.scale * kLog2e, a.causal ? 1 : 0, n_qtiles);
+                     a.N, Nk, delta, a.scale * kLog2e, causal ? 1 : 0, n_qtiles);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs& a) {
-  if (a.dtype == 1) {
-    if (a.d == 64) return a.causal ? launch_bf16<64, true>(a) : launch_bf16<64, false>(a);
-    return a.causal ? launch_bf16<128, true>(a) : launch_bf16<128, false>(a);
+  const int Nk = a.Nk > 0 ? a.Nk : a.N;
+  bool causal = a.causal;
+  // every key at or before every query: the mask is void
+  if (causal && a.delta >= (long long)Nk - 1) causal = false;
+  if (causal && a.delta + a.N - 1 < 0) {
+    // no query sees any key
+    const long long rows = (long long)a.B * a.H * a.N;
+    const long long n = rows * a.d;
+    const int grid = (int)std::min<long long>((n + 255) / 256, 65536);
+    if (a.dtype == 1)
+      hipLaunchKernelGGL((fill_empty_kernel<__bf16>), dim3(grid), dim3(256), 0, a.stream,
+                         (__bf16*)a.O, a.LSE, rows, a.d);
+    else
+      hipLaunchKernelGGL((fill_empty_kernel<float>), dim3(grid), dim3(256), 0, a.stream,
+                         (float*)a.O, a.LSE, rows, a.d);
+    return hipGetLastError();
   }
-  return a.d == 64 ? launch_f32<64>(a) : launch_f32<128>(a);
+  const int delta = causal ? (int)a.delta : 0;   // |delta| < max(N, Nk) here
+  if (a.dtype == 1) {
+    if (a.d == 64) return causal ? launch_bf16<64, true>(a, Nk, delta) : launch_bf16<64, false>(a, Nk, delta);
+    return causal ? launch_bf16<128, true>(a, Nk, delta) : launch_bf16<128, false>(a, Nk, delta);
+  }
+  return a.d == 64 ? launch_f32<64>(a, Nk, delta, causal) : launch_f32<128>(a, Nk, delta, causal);
+}
+
+hipError_t launch_merge(const MergeArgs& a) {
+  const int tpr = a.d * (a.dtype == 1 ? 2 : 4) / 16;
+  const long long threads = a.rows * tpr;
+  const unsigned grid = (unsigned)((threads + 255) / 256);
+  if (a.dtype == 1) {
+    if (a.d == 64)
+      hipLaunchKernelGGL((merge_kernel<__bf16, 64>), dim3(grid), dim3(256), 0, a.stream,
+                         (const __bf16*)a.Oa, a.La, (const __bf16*)a.Ob, a.Lb, (__bf16*)a.O, a.L, a.rows);
+    else
+      hipLaunchKernelGGL((merge_kernel<__bf16, 128>), dim3(grid), dim3(256), 0, a.stream,
+                         (const __bf16*)a.Oa, a.La, (const __bf16*)a.Ob, a.Lb, (__bf16*)a.O, a.L, a.rows);
+  } else {
+    if (a.d == 64)
+      hipLaunchKernelGGL((merge_kernel<float, 64>), dim3(grid), dim3(256), 0, a.stream,
+                         (const float*)a.Oa, a.La, (const float*)a.Ob, a.Lb, (float*)a.O, a.L, a.rows);
+    else
+      hipLaunchKernelGGL((merge_kernel<float, 128>), dim3(grid), dim3(256), 0, a.stream,
+                         (const float*)a.Oa, a.La, (const float*)a.Ob, a.Lb, (float*)a.O, a.L, a.rows);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace fa

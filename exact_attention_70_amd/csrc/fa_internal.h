@@ -14,10 +14,25 @@ struct FwdArgs {
   const void* V;
   void* O;
   float* LSE;
-  int B, H, N, d;
+  int B, H, N, d;   // N: query rows per head
   float scale;
   bool causal;
-  int dtype;  // 0 = fp32, 1 = bf16
+  int dtype;        // 0 = fp32, 1 = bf16
+  hipStream_t stream;
+  int Nk = 0;       // key/value rows per head (0: same as N)
+  long long delta = 0;   // q_offset - k_offset: key j is visible to row i iff j <= i + delta
+};
+
+struct MergeArgs {
+  const void* Oa;
+  const float* La;
+  const void* Ob;
+  const float* Lb;
+  void* O;
+  float* L;
+  long long rows;   // B * H * N
+  int d;
+  int dtype;
   hipStream_t stream;
 };
 
@@ -55,6 +70,7 @@ struct DecodeArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_merge(const MergeArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 

@@ -49,7 +49,7 @@ typedef enum {
   FA_ERR_UNSUPPORTED = -4, /* valid but not implemented (head_dim, block_size, ...) */
   FA_ERR_ALIGN = -5,       /* a tensor pointer is not 16-byte aligned             */
   FA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than the query returns */
-  FA_ERR_INVALID = -7,     /* block_table / seq_lens contents invalid (FA_DEBUG=1) */
+  FA_ERR_INVALID = -7,     /* block_table / seq_lens invalid (FA_DEBUG=1), or overlapping buffers */
   FA_ERR_HIP = -8          /* the HIP runtime reported an error                   */
 } fa_status;
 
@@ -88,6 +88,50 @@ int fa_version(void);
  */
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
            int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_fwd_offset -- attention forward of one query block against one key/value
+ * block whose rows carry global positions: query row i of the block sits at
+ * q_offset + i and key row j at k_offset + j.  This is the per-step kernel of
+ * ring attention (HPC notes "07-16 afternoon", section "Long context and
+ * sequence parallelism"; CS231N L11 notes, context-parallel part): each rank
+ * keeps its query block and meets the key/value blocks of the ring one by
+ * one, combining the partial results with fa_merge.  It is also the
+ * bottom-right-aligned causal forward of a prefill chunk (q_offset = Nk - Nq,
+ * k_offset = 0).
+ *
+ *   Q        in   [B,H,Nq,d];  K, V in [B,H,Nk,d]; dtype `dtype`
+ *   O        out  [B,H,Nq,d], same dtype;  LSE out [B,H,Nq] fp32
+ *   Nq, Nk   1 .. 1<<20;  d 64 or 128
+ *   q_offset, k_offset  global positions, |offset| <= 2^60 (else FA_ERR_SHAPE)
+ *   causal   0 = every key visible; non-zero = key j visible to query i iff
+ *            k_offset + j <= q_offset + i
+ *
+ * A query row that sees no key of the block gets O = 0 and LSE = -inf (the
+ * online softmax's starting state), which fa_merge treats as weight 0.  With
+ * Nq == Nk and equal offsets this is fa_fwd; arithmetic as for fa_fwd.
+ */
+int fa_fwd_offset(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                  int B, int H, int Nq, int Nk, int d, long long q_offset, long long k_offset,
+                  float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_merge -- combine two partial attention results for the same queries
+ * over disjoint key sets, by the rescale rule of the online softmax (HPC
+ * notes "07-16 afternoon", section "Long context and sequence parallelism":
+ * rescale the old accumulators by exp(m_old - m_new) before adding a block):
+ *   M = max(LSE_a, LSE_b),  w = exp(LSE - M),
+ *   O = (w_a O_a + w_b O_b) / (w_a + w_b),  LSE = M + ln(w_a + w_b).
+ * A side with LSE = -inf weighs nothing; if both are -inf, O = 0, LSE = -inf.
+ *
+ *   O_a, O_b, O   [B,H,N,d] dtype `dtype` (bf16 results round to nearest even)
+ *   LSE_a, LSE_b, LSE  [B,H,N] fp32
+ *   O may be the same buffer as O_a or O_b, and LSE the same as LSE_a or
+ *   LSE_b (in-place accumulation); a partial overlap returns FA_ERR_INVALID.
+ *   d 64 or 128.  All pointers 16-byte aligned.
+ */
+int fa_merge(const void* O_a, const float* LSE_a, const void* O_b, const float* LSE_b,
+             void* O, float* LSE, int B, int H, int N, int d, int dtype, void* stream);
 
 /*
  * fa_bwd_workspace_size -- bytes of workspace fa_bwd needs for this shape:

@@ -35,8 +35,9 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_bwd", "fa_paged_decode", "fa_bwd_workspace_size",
-              "fa_paged_decode_workspace_size", "fa_status_string", "fa_version"):
+    for n in ("fa_fwd", "fa_fwd_offset", "fa_merge", "fa_bwd", "fa_paged_decode",
+              "fa_bwd_workspace_size", "fa_paged_decode_workspace_size", "fa_status_string",
+              "fa_version"):
         assert n in names
 
 
@@ -75,6 +76,44 @@ def test_fwd_validation(lib):
     assert fwd(lib, o=MIS) == ERR_ALIGN
     # B == 0 is a no-op (nothing is touched, so even NULL pointers are fine)
     assert fwd(lib, B=0, q=None, k=None, v=None, o=None, lse=None) == OK
+
+
+def fwd_off(lib, q=P, k=P, v=P, o=P2, lse=P2, B=1, H=1, Nq=64, Nk=96, d=64, qo=0, ko=0, scale=0.125,
+            causal=1, dt=1):
+    return lib.fa_fwd_offset(q, k, v, o, lse, B, H, Nq, Nk, d, qo, ko, scale, causal, dt, None)
+
+
+def test_fwd_offset_validation(lib):
+    assert fwd_off(lib, dt=3) == ERR_DTYPE
+    assert fwd_off(lib, Nq=0) == ERR_SHAPE
+    assert fwd_off(lib, Nk=0) == ERR_SHAPE
+    assert fwd_off(lib, Nk=(1 << 20) + 1) == ERR_SHAPE
+    assert fwd_off(lib, qo=(1 << 60) + 1) == ERR_SHAPE
+    assert fwd_off(lib, ko=-(1 << 60) - 1) == ERR_SHAPE
+    assert fwd_off(lib, scale=float("nan")) == ERR_SHAPE
+    assert fwd_off(lib, d=80) == ERR_UNSUP
+    assert fwd_off(lib, k=None) == ERR_NULL
+    assert fwd_off(lib, v=MIS) == ERR_ALIGN
+    # B == 0 is a no-op even with NULL pointers
+    assert fwd_off(lib, B=0, q=None, k=None, v=None, o=None, lse=None) == OK
+
+
+def merge(lib, oa=P, la=P, ob=P2, lb=P2, o=ctypes.c_void_p(0x40000), l=ctypes.c_void_p(0x80000),
+          B=1, H=2, N=64, d=64, dt=1):
+    return lib.fa_merge(oa, la, ob, lb, o, l, B, H, N, d, dt, None)
+
+
+def test_merge_validation(lib):
+    assert merge(lib, dt=9) == ERR_DTYPE
+    assert merge(lib, N=0) == ERR_SHAPE
+    assert merge(lib, H=0) == ERR_SHAPE
+    assert merge(lib, d=32) == ERR_UNSUP
+    assert merge(lib, ob=None) == ERR_NULL
+    assert merge(lib, lb=MIS) == ERR_ALIGN
+    # an output shifted into an input (not the same buffer) is refused
+    assert merge(lib, o=ctypes.c_void_p(0x10000 + 64)) == ERR_INVALID
+    assert merge(lib, l=ctypes.c_void_p(0x20000 + 16)) == ERR_INVALID
+    assert merge(lib, B=0, oa=None, la=None, ob=None, lb=None, o=None, l=None) == OK
 
 
 def test_bwd_validation(lib):
