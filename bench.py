@@ -6,6 +6,8 @@ benchmark shapes:
   * fa_fwd   causal bf16 B=8 H=12 N=1024 d=64
   * fa_fwd + fa_bwd causal bf16 B=4 H=16 N=2048 d=128
   * fa_paged_decode bf16 64 seqs x H=32 x d=128, lengths U[128,4096], 16-token blocks
+  * one ring-attention step at the long-context shape: fa_fwd_offset of the
+    8192 queries against the previous 8192-token block, then fa_merge
 Inputs are resident in HBM before timing starts.  Each call is bracketed by
 HIP events on the stream it runs on; `value` is the headline forward's
 algorithmic TFLOP/s (causal pairs only) over its average kernel time.
@@ -70,7 +72,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
                     help="comma list of parts to run: fwd_c3, fwd_c2, fwd_c4, bwd_c4, decode_c5, "
-                         "copy_calib (a 1 GiB device copy used to scale the HBM-traffic counters)")
+                         "ring_c3 (offset forward + merge of one ring step), copy_calib (a 1 GiB "
+                         "device copy used to scale the HBM-traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -100,6 +103,22 @@ def main():
         parts["fwd_c3"] = dict(fn=lambda: binding.fwd(q, k, v, causal=True, scale=c3.scale, out=o,
                                                        lse=lse),
                                flops=causal_flops(c3.B, c3.H, c3.N, c3.d))
+    if want("ring_c3"):
+        # one rank's non-diagonal ring step at the long-context shape: its 8192
+        # queries (global rows 8192..16383) against the previous 8192-token
+        # key/value block (every key visible), merged into the running result
+        xr = x if want("fwd_c3") else workloads.attention_inputs(c3.B, c3.H, c3.N, c3.d, "bf16",
+                                                                 seed=workloads.seed_for(3))
+        qr, kr, vr = (xr[n].to(dev) for n in "qkv")
+        po = torch.empty_like(qr)
+        pl = torch.empty(c3.B, c3.H, c3.N, device=dev)
+        acc_o, acc_l = binding.fwd(qr, kr, vr, causal=True, scale=c3.scale)   # diagonal block
+        parts["ring_c3_fwd"] = dict(fn=lambda: binding.fwd_offset(
+            qr, kr, vr, q_offset=c3.N, k_offset=0, causal=True, scale=c3.scale, out=po, lse=pl),
+            flops=4 * c3.B * c3.H * c3.N * c3.N * c3.d)
+        parts["ring_c3_merge"] = dict(fn=lambda: binding.merge(acc_o, acc_l, po, pl, out=acc_o,
+                                                                lse_out=acc_l),
+                                      bytes=3 * acc_o.numel() * 2 + 3 * acc_l.numel() * 4)
     if want("fwd_c2"):
         x2 = workloads.attention_inputs(c2.B, c2.H, c2.N, c2.d, "bf16", seed=workloads.seed_for(2),
                                         in_scale=c2.in_scale)
@@ -148,8 +167,8 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs ready: {list(parts)}")
 
-    order = [n for n in ("fwd_c3", "fwd_c2", "fwd_c4", "bwd_c4", "decode_c5", "copy_calib")
-             if n in parts]
+    order = [n for n in ("fwd_c3", "fwd_c2", "fwd_c4", "bwd_c4", "decode_c5", "ring_c3_fwd",
+                         "ring_c3_merge", "copy_calib") if n in parts]
     for _ in range(args.warmup):
         for n in order:
             parts[n]["fn"]()
@@ -192,19 +211,21 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline and "fwd_c3" in parts:
-        import numpy as np
         import oracle
         workers = min(os.cpu_count() or 1, 16)
-        heads = [(0, h) for h in range(0, 32, 2)]          # 16 of the 32 heads, every row
-        t0 = time.perf_counter()
-        oracle.attention_forward(x["q"], x["k"], x["v"], c3.scale, True, heads=heads,
-                                 workers=workers)
-        dt = time.perf_counter() - t0
-        fl = causal_flops(1, len(heads), c3.N, c3.d)
+        # whole passes of the fp64 oracle over the headline workload (all 32
+        # heads, every row) until at least 10 s of host work, at most 8 passes
+        passes, dt = 0, 0.0
+        while passes < 8 and (passes == 0 or dt < 10.0):
+            t0 = time.perf_counter()
+            oracle.attention_forward(x["q"], x["k"], x["v"], c3.scale, True, workers=workers)
+            dt += time.perf_counter() - t0
+            passes += 1
+        fl = passes * causal_flops(c3.B, c3.H, c3.N, c3.d)
         cpu = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": workers,
                "kind": "oracle",
-               "sample": f"fp64 oracle forward on 16 of 32 heads (all 8192 rows) of the causal "
-                         f"B=1 H=32 N=8192 d=128 workload; {dt:.1f} s wall"}
+               "sample": f"fp64 oracle forward over the whole causal B=1 H=32 N=8192 d=128 "
+                         f"workload, {passes} pass(es), {dt:.1f} s wall on {workers} threads"}
         log("cpu baseline", cpu)
 
     head = res.get("fwd_c3")
@@ -234,7 +255,8 @@ def main():
         "dtype": "bf16", "data": "synthetic (seeded N(0,1))",
         "config": {"workload": "causal bf16 attention forward B=1 H=32 N=8192 d=128 "
                                "(one step also runs fwd B=8 H=12 N=1024 d=64, fwd+bwd "
-                               "B=4 H=16 N=2048 d=128, paged decode 64x32x128)",
+                               "B=4 H=16 N=2048 d=128, paged decode 64x32x128, and one "
+                               "ring-attention step: offset fwd + merge at 32x8192x128)",
                    "global_batch": 1, "seq_len": 8192, "parallelism": "single-gpu"},
         "roofline": roof,
         "roofline_decode": roof_dec,
