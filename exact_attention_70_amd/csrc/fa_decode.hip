@@ -14,12 +14,16 @@
 // a block streams contiguous memory.
 //
 // Partial kernel: workgroup = (sequence, KV partition of 256 tokens, group of
-//   16 heads); wave = 4 heads; 16 lanes per head, each lane owning 8 of the
-//   128 head-dim values.  Per 16-token block: 16-byte loads of K and V rows
-//   through a buffer resource over that physical block (an out-of-range
-//   block id therefore reads zeros instead of faulting), q.k partial dot
-//   products reduced across the 16 lanes with DPP, one online-softmax update
-//   per block, and the P V accumulation.  Writes (m, l, unnormalised o).
+//   32 heads), so at H = 32 every 16-token block is read as one contiguous
+//   128 KiB stream; wave = 4 heads; 16 lanes per head, each lane owning 8 of
+//   the 128 head-dim values.  Per 16-token block: 16-byte loads of K and V
+//   rows through a buffer resource over that physical block (an out-of-range
+//   block id therefore reads zeros instead of faulting), the token stride in
+//   the wave-uniform offset; q.k partial dot products reduced across the 16
+//   lanes with DPP, one online-softmax update per block, and the P V
+//   accumulation.  K and V are separate load batches: the scores of block t
+//   run while V_t streams in, and K_{t+1} streams in while V_t is accumulated.
+//   Writes (m, l, unnormalised o).
 // Merge kernel: one wave per (sequence, head) combines its partitions.
 //   Throughput is bound by HBM: the flops per byte are ~1.
 #include "fa_device.h"
@@ -31,11 +35,11 @@ namespace {
 
 constexpr int kDecD = 128;
 constexpr int kDecBS = 16;
-constexpr int kDecThreads = 256;
+constexpr int kDecThreads = 512;
 constexpr int kHeadsPerWave = 4;
-constexpr int kHeadsPerGroup = 16;
+constexpr int kHeadsPerGroup = 32;   // heads per workgroup: whole 8 KiB token rows at H = 32
 
-__global__ __launch_bounds__(kDecThreads, 2) void decode_partial_kernel(
+__global__ __launch_bounds__(kDecThreads, 1) void decode_partial_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k_pool,
     const __bf16* __restrict__ v_pool, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int H, int max_blocks_per_seq, int num_blocks,
@@ -51,6 +55,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_partial_kernel(
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  if (hg * kHeadsPerGroup + wave * kHeadsPerWave >= H) return;   // no head of this wave exists
   const int head = hg * kHeadsPerGroup + wave * kHeadsPerWave + (lane >> 4);
   const int ch = lane & 15;                          // which 8 of the 128 d values
   const bool head_ok = head < H;
@@ -78,19 +83,28 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_partial_kernel(
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 
   const int32_t* table = block_table + (size_t)s * max_blocks_per_seq;
-  for (int t0 = t_begin; t0 < t_end; t0 += kDecBS) {
+  // K of a block and V of a block are separate load batches: the scores of
+  // block t run while V_t streams in, and K_{t+1} streams in while V_t is
+  // accumulated, so every compute phase has the next batch in flight.
+  auto block_rsrc = [&](int t0, __amdgpu_buffer_rsrc_t& rk, __amdgpu_buffer_rsrc_t& rv) {
     const int32_t phys = table[t0 / kDecBS];
     const bool phys_ok = (uint32_t)phys < (uint32_t)num_blocks;
     const size_t boff = (size_t)(phys_ok ? phys : 0) * kDecBS * H * kDecD;
-    const auto rk = make_rsrc(k_pool + boff, phys_ok ? blk_bytes : 0u);
-    const auto rv = make_rsrc(v_pool + boff, phys_ok ? blk_bytes : 0u);
-    u32x4 kr[kDecBS], vr[kDecBS];
+    rk = make_rsrc(k_pool + boff, phys_ok ? blk_bytes : 0u);
+    rv = make_rsrc(v_pool + boff, phys_ok ? blk_bytes : 0u);
+  };
+  u32x4 kr[kDecBS], vr[kDecBS];
+  __amdgpu_buffer_rsrc_t rk, rv;
+  block_rsrc(t_begin, rk, rv);
 #pragma unroll
-    for (int u = 0; u < kDecBS; ++u) kr[u] = bload16(rk, u * tok_stride + row_off);
+  for (int u = 0; u < kDecBS; ++u) kr[u] = bload16s(rk, row_off, u * tok_stride);
 #pragma unroll
-    for (int u = 0; u < kDecBS; ++u) vr[u] = bload16(rv, u * tok_stride + row_off);
-
-    const int n_valid = min(kDecBS, t_end - t0);    // tokens of this block inside the range
+  for (int u = 0; u < kDecBS; ++u) vr[u] = bload16s(rv, row_off, u * tok_stride);
+  for (int t0 = t_begin; t0 < t_end; t0 += kDecBS) {
+    const bool more = t0 + kDecBS < t_end;
+    __amdgpu_buffer_rsrc_t rk2 = rk, rv2 = rv;
+    if (more) block_rsrc(t0 + kDecBS, rk2, rv2);
+    const int n_valid = min(kDecBS, t_end - t0);
     float sc[kDecBS];
     float mx = kNegInf;
 #pragma unroll
@@ -106,7 +120,11 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_partial_kernel(
       sc[u] = x;
       mx = fmaxf(mx, x);
     }
-    const float m_new = fmaxf(m_run, mx);            // finite: token t0 is always valid
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < kDecBS; ++u) kr[u] = bload16s(rk2, row_off, u * tok_stride);
+    }
+    const float m_new = fmaxf(m_run, mx);
     const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
     float rs = 0.f;
@@ -116,7 +134,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_partial_kernel(
     for (int u = 0; u < kDecBS; ++u) {
       const float pu = fast_exp2(sc[u] - m_new);
       rs += pu;
-      if (u < n_valid) {                             // pad slots never enter the sum
+      if (u < n_valid) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           acc[2 * e] = fmaf(pu, bf16lo(vr[u][e]), acc[2 * e]);
@@ -125,8 +143,13 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_partial_kernel(
       }
     }
     l_run = l_run * alpha + rs;
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < kDecBS; ++u) vr[u] = bload16s(rv2, row_off, u * tok_stride);
+    }
+    rk = rk2;
+    rv = rv2;
   }
-
   if (!head_ok) return;
   const size_t entry = ((size_t)s * n_parts + p) * H + head;
   u32x4 w0, w1;
@@ -144,7 +167,21 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_partial_kernel(
 }
 
 // One wave per (sequence, head): rescale every partition's (m, l, o) to the
-// common maximum and sum.  Each lane owns 2 of the 128 output values.
+// common maximum and sum.  Lanes take the partitions' (m, l) in parallel for
+// the maximum and the weights; then each lane owns 2 of the 128 output values
+// and sums the partitions' contributions with the weights broadcast from the
+// lane that computed them.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ seq_lens, int num_seqs, int H, int part_tokens, int n_parts,
@@ -162,15 +199,28 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   const int np = min(n_parts, (len + part_tokens - 1) / part_tokens);
   const size_t base = (size_t)s * n_parts * H + head;
   float m_star = kNegInf;
-  for (int p = 0; p < np; ++p) m_star = fmaxf(m_star, part_ml[(base + (size_t)p * H) * 2]);
+  for (int p = lane; p < np; p += 64) m_star = fmaxf(m_star, part_ml[(base + (size_t)p * H) * 2]);
+  m_star = wave_max(m_star);
   float L = 0.f, a0 = 0.f, a1 = 0.f;
-  for (int p = 0; p < np; ++p) {
-    const size_t e = base + (size_t)p * H;
-    const float w = fast_exp2(part_ml[e * 2] - m_star);
-    L = fmaf(w, part_ml[e * 2 + 1], L);
-    a0 = fmaf(w, part_o[e * kDecD + 2 * lane], a0);
-    a1 = fmaf(w, part_o[e * kDecD + 2 * lane + 1], a1);
+  for (int p0 = 0; p0 < np; p0 += 64) {
+    // this lane's partition p0 + lane: weight and its share of the denominator
+    float w = 0.f;
+    if (p0 + lane < np) {
+      const size_t e = base + (size_t)(p0 + lane) * H;
+      w = fast_exp2(part_ml[e * 2] - m_star);
+      L = fmaf(w, part_ml[e * 2 + 1], L);
+    }
+    const int cnt = min(64, np - p0);
+#pragma unroll 4
+    for (int q = 0; q < cnt; ++q) {
+      const float wq = __shfl(w, q, 64);
+      const size_t e = base + (size_t)(p0 + q) * H;
+      const float2 v = *(const float2*)(part_o + e * kDecD + 2 * lane);
+      a0 = fmaf(wq, v.x, a0);
+      a1 = fmaf(wq, v.y, a1);
+    }
   }
+  L = wave_sum(L);
   const float inv = 1.f / L;
   *(uint32_t*)(o + ((size_t)s * H + head) * kDecD + 2 * lane) = pack_bf16(a0 * inv, a1 * inv);
   if (lane == 0) lse[(size_t)s * H + head] = (m_star + fast_log2(L)) * kLn2;
