@@ -13,6 +13,9 @@ What is computed, and where the pages state it
   raw scores are the q.k dot products (i.e. Q K^T), softmax turns each row into
   weights that sum to 1, and the output is the weight-sum of the value rows.
   Shapes [B, heads, S, S] for scores and [B, heads, S, head_dim] for outputs.
+  With grouped-query attention the cache holds fewer key/value heads than
+  there are query heads (HPC notes, "Prefill, Decode and inference
+  scheduling", KV-cache size); consecutive query heads share one.
   The scale factor on the scores is an argument (the pages never print one);
   the workloads use 1/sqrt(head_dim).
 * Safe softmax in three passes (CMU 10-423 L17-L18 notes, section "Prerequisite
@@ -76,7 +79,7 @@ __all__ = [
     "online_softmax", "attention_forward_head", "attention_forward",
     "attention_backward_head", "attention_backward", "gather_tokens",
     "paged_decode", "grad_v", "grad_p", "row_dot", "grad_s", "grad_q", "grad_k",
-    "merge_partials",
+    "merge_partials", "kv_head_of", "paged_append",
 ]
 
 
@@ -332,17 +335,26 @@ def gather_tokens(pool, table_row, length: int, block_size: int):
     return to_f64(np.asarray(pool)[phys, slot])
 
 
+def kv_head_of(h: int, H: int, kv_heads: int) -> int:
+    """Grouped-query attention: query head h reads key/value head h // (H / kv_heads)
+    (consecutive query heads share one cached head)."""
+    return h // (H // kv_heads)
+
+
 def paged_decode(q, k_pool, v_pool, block_table, seq_lens, block_size: int, scale: float,
                  seqs=None, workers: int | None = None):
     """Single-query attention of each sequence's new token over its cached tokens.
 
-    q [S, H, d]; pools [num_blocks, block_size, H, d]; block_table [S, max_blocks];
+    q [S, H, d]; pools [num_blocks, block_size, KVH, d] with H a multiple of
+    KVH (KVH = H is plain multi-head attention); block_table [S, max_blocks];
     seq_lens [S].  Returns (o [len(seqs), H, d], lse [len(seqs), H]) float64.
     """
     table = np.asarray(block_table.numpy() if hasattr(block_table, "numpy") else block_table)
     lens = np.asarray(seq_lens.numpy() if hasattr(seq_lens, "numpy") else seq_lens)
     seqs = list(range(table.shape[0])) if seqs is None else list(seqs)
     H = q.shape[1]
+    KVH = k_pool.shape[2]
+    assert H % KVH == 0
 
     def one(s):
         L = int(lens[s])
@@ -352,8 +364,56 @@ def paged_decode(q, k_pool, v_pool, block_table, seq_lens, block_size: int, scal
         o = np.empty((H, V.shape[2]))
         lse = np.empty((H,))
         for h in range(H):
-            oh, lh = attention_forward_head(qs[h:h + 1], K[:, h], V[:, h], scale, False)
+            g = kv_head_of(h, H, KVH)
+            oh, lh = attention_forward_head(qs[h:h + 1], K[:, g], V[:, g], scale, False)
             o[h], lse[h] = oh[0], lh[0]
         return o, lse
     res = _pool_map(one, seqs, workers)
     return np.stack([r[0] for r in res]), np.stack([r[1] for r in res])
+
+
+def paged_append(k_pool, v_pool, block_table, seq_lens, free_list, free_count: int, k_new, v_new,
+                 block_size: int):
+    """Append one new token's K/V to every sequence of a paged cache.
+
+    Blocks are taken only when needed (CMU notes, "Decoding: PagedAttention";
+    HPC notes, "Prefill, Decode and inference scheduling": the runtime keeps
+    each sequence's length and block mapping).  Sequences are visited in
+    order.  Sequence s writes its token at position t = seq_lens[s]: when t is
+    a multiple of block_size the sequence's blocks are full, so the block
+    on top of the free stack, free_list[free_count - 1], is popped into
+    block_table[s, t // block_size].  The token goes to slot t % block_size of
+    that block and seq_lens[s] becomes t + 1.  A sequence that is at its table's
+    capacity, or needs a block when the stack is empty, is left unchanged and
+    counted as failed.
+
+    Inputs are not modified.  Returns a dict with float64 pools, int64 table,
+    lens, the new free_count and n_failed.
+    """
+    kp = to_f64(k_pool).copy()
+    vp = to_f64(v_pool).copy()
+    table = np.array(block_table.numpy() if hasattr(block_table, "numpy") else block_table,
+                     dtype=np.int64)
+    lens = np.array(seq_lens.numpy() if hasattr(seq_lens, "numpy") else seq_lens, dtype=np.int64)
+    free = np.array(free_list.numpy() if hasattr(free_list, "numpy") else free_list, dtype=np.int64)
+    kn, vn = to_f64(k_new), to_f64(v_new)
+    top = int(free_count)
+    failed = 0
+    for s in range(table.shape[0]):
+        t = int(lens[s])
+        b, slot = t // block_size, t % block_size
+        if b >= table.shape[1]:
+            failed += 1
+            continue
+        if slot == 0:
+            if top == 0:
+                failed += 1
+                continue
+            top -= 1
+            table[s, b] = free[top]
+        phys = table[s, b]
+        kp[phys, slot] = kn[s]
+        vp[phys, slot] = vn[s]
+        lens[s] = t + 1
+    return {"k_pool": kp, "v_pool": vp, "block_table": table, "seq_lens": lens,
+            "free_count": top, "n_failed": failed}

@@ -420,6 +420,116 @@ def test_paged_decode_on_generated_pool_with_nan_pads():
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
 
 
+# ------------------------------------------- grouped-query decode and append
+
+def check_gqa_decode(seed=8):
+    """Query head h reads cached head h // (H / KVH): against the 50-digit
+    definition per head, and equal to multi-head decode over pools whose heads
+    are repeated group-wise."""
+    rng = np.random.default_rng(seed)
+    H, d, bs = 6, 4, 4
+    lens = [1, 5, 9]
+    for KVH in (1, 2, 3, 6):
+        g = H // KVH
+        Kc = [rng.standard_normal((L, KVH, d)) for L in lens]
+        Vc = [rng.standard_normal((L, KVH, d)) for L in lens]
+        q = rng.standard_normal((len(lens), H, d))
+        kp, vp, table = _scatter_to_pool(Kc, Vc, lens, bs, KVH, d, seed + KVH)
+        o, lse = A.paged_decode(q, kp, vp, table, np.array(lens), bs, 0.4)
+        for s_, L in enumerate(lens):
+            for h in range(H):
+                Od, Ld = brute.attention_decimal(q[s_, h][None], Kc[s_][:, h // g], Vc[s_][:, h // g],
+                                                 0.4, False)
+                np.testing.assert_allclose(o[s_, h], np.array(Od[0], dtype=float), atol=1e-13)
+                np.testing.assert_allclose(lse[s_, h], float(Ld[0]), atol=1e-13)
+        o_rep, lse_rep = A.paged_decode(q, np.repeat(kp, g, axis=2), np.repeat(vp, g, axis=2), table,
+                                        np.array(lens), bs, 0.4)
+        np.testing.assert_allclose(o_rep, o, atol=1e-15)
+        np.testing.assert_allclose(lse_rep, lse, atol=1e-15)
+
+
+def _paged_state(lens, bs, max_blocks, kvh, d, extra, seed):
+    """A paged cache holding ``lens`` tokens per sequence plus ``extra`` free
+    blocks, built by an independent scatter; returns contiguous copies too."""
+    rng = np.random.default_rng(seed)
+    Kc = [rng.standard_normal((L, kvh, d)) for L in lens]
+    Vc = [rng.standard_normal((L, kvh, d)) for L in lens]
+    used = sum(-(-L // bs) for L in lens)
+    total = used + extra
+    perm = rng.permutation(total)
+    kp = rng.standard_normal((total, bs, kvh, d))
+    vp = rng.standard_normal((total, bs, kvh, d))
+    table = -np.ones((len(lens), max_blocks), dtype=np.int64)
+    off = 0
+    for s_, L in enumerate(lens):
+        for t in range(L):
+            b, slot = divmod(t, bs)
+            if slot == 0:
+                table[s_, b] = perm[off]
+                off += 1
+            kp[table[s_, b], slot] = Kc[s_][t]
+            vp[table[s_, b], slot] = Vc[s_][t]
+    free = perm[off:].copy()
+    return kp, vp, table, free, Kc, Vc, rng
+
+
+def check_paged_append(seed=9):
+    """Appending tokens one step at a time: every sequence then holds exactly
+    its old tokens followed by the new ones (read back through the table),
+    blocks come off the top of the free stack in sequence order only at block
+    boundaries, no block is shared, and full tables or an empty stack leave a
+    sequence unchanged."""
+    bs, kvh, d, max_blocks = 4, 2, 3, 3
+    lens = [0, 3, 4, 7, 8, 11]
+    kp, vp, table, free, Kc, Vc, rng = _paged_state(lens, bs, max_blocks, kvh, d, 4, seed)
+    lens = np.array(lens)
+    top = len(free)
+    for step in range(3):
+        kn = rng.standard_normal((len(lens), kvh, d))
+        vn = rng.standard_normal((len(lens), kvh, d))
+        r = A.paged_append(kp, vp, table, lens, free, top, kn, vn, bs)
+        expect_fail = 0
+        pops = []
+        for s_ in range(len(lens)):
+            t = int(lens[s_])
+            if t >= bs * max_blocks or (t % bs == 0 and top - len(pops) == 0):
+                expect_fail += 1
+                assert r["seq_lens"][s_] == t
+                continue
+            if t % bs == 0:
+                pops.append(s_)
+            Kc[s_] = np.concatenate([Kc[s_], kn[s_][None]])
+            Vc[s_] = np.concatenate([Vc[s_], vn[s_][None]])
+            assert r["seq_lens"][s_] == t + 1
+        assert r["n_failed"] == expect_fail
+        assert r["free_count"] == top - len(pops)
+        for i, s_ in enumerate(pops):                 # stack order: top first
+            assert r["block_table"][s_, int(lens[s_]) // bs] == free[top - 1 - i]
+        kp, vp, table, lens, top = r["k_pool"], r["v_pool"], r["block_table"], r["seq_lens"], r["free_count"]
+        owned = []
+        for s_, L in enumerate(lens):
+            np.testing.assert_array_equal(A.gather_tokens(kp, table[s_], int(L), bs), Kc[s_])
+            np.testing.assert_array_equal(A.gather_tokens(vp, table[s_], int(L), bs), Vc[s_])
+            owned += list(table[s_, :-(-int(L) // bs)])
+        assert len(owned) == len(set(owned))
+        assert not set(owned) & set(free[:top].tolist())
+    assert expect_fail >= 1                            # the sequence at capacity
+
+
+def test_gqa_decode_pins():
+    check_gqa_decode()
+
+
+def test_paged_append_pins():
+    check_paged_append()
+
+
+def _all_paged_pins():
+    check_decode()
+    check_gqa_decode()
+    check_paged_append()
+
+
 # ---------------------------------------------------------- planted mistakes
 
 def _all_forward_pins(golden_dir):
@@ -534,6 +644,56 @@ def _gather_one_extra(pool, table_row, length, block_size):
                                   block_size)
 
 
+_REAL_APPEND = A.paged_append
+
+
+def _append_variant(kind):
+    """paged_append with one planted mistake."""
+    def f(k_pool, v_pool, block_table, seq_lens, free_list, free_count, k_new, v_new, block_size):
+        kp, vp = A.to_f64(k_pool).copy(), A.to_f64(v_pool).copy()
+        table = np.array(block_table, dtype=np.int64)
+        lens = np.array(seq_lens, dtype=np.int64)
+        free = np.array(free_list, dtype=np.int64)
+        kn, vn = A.to_f64(k_new), A.to_f64(v_new)
+        top, bottom, failed = int(free_count), 0, 0
+        for s_ in range(table.shape[0]):
+            t = int(lens[s_])
+            b, slot = t // block_size, t % block_size
+            if kind == "slot_next":
+                slot = (t + 1) % block_size
+            if b >= table.shape[1]:
+                failed += 1
+                continue
+            boundary = (t % block_size == 1) if kind == "alloc_one_late" else (t % block_size == 0)
+            if boundary:
+                if top - bottom == 0:
+                    failed += 1
+                    continue
+                if kind == "pop_bottom":
+                    table[s_, b] = free[bottom]
+                    bottom += 1
+                else:
+                    top -= 1
+                    table[s_, b] = free[top]
+            phys = table[s_, b]
+            kp[phys, slot] = kn[s_]
+            vp[phys, slot] = vn[s_]
+            if kind != "len_not_advanced":
+                lens[s_] = t + 1
+        return {"k_pool": kp, "v_pool": vp, "block_table": table, "seq_lens": lens,
+                "free_count": top - bottom, "n_failed": failed}
+    return f
+
+
+PAGED_MUTANTS = {
+    "gqa_modulo_heads": ("kv_head_of", lambda h, H, kvh: h % kvh),
+    "gqa_reversed_groups": ("kv_head_of", lambda h, H, kvh: kvh - 1 - h // (H // kvh)),
+    "append_pops_bottom": ("paged_append", _append_variant("pop_bottom")),
+    "append_alloc_one_late": ("paged_append", _append_variant("alloc_one_late")),
+    "append_slot_next": ("paged_append", _append_variant("slot_next")),
+    "append_len_not_advanced": ("paged_append", _append_variant("len_not_advanced")),
+}
+
 DECODE_MUTANTS = {
     "slot_off_by_one": ("gather_tokens", _gather_off_by_one),
     "logical_block_ids": ("gather_tokens", _gather_logical),
@@ -543,6 +703,7 @@ DECODE_MUTANTS = {
 
 def test_pins_pass_on_unmodified_oracle(golden_dir):
     _all_offset_pins()
+    _all_paged_pins()
     _all_forward_pins(golden_dir)
     _all_backward_pins()
     check_decode()
@@ -572,6 +733,15 @@ def test_backward_pins_catch_planted_mistake(mutant, monkeypatch):
     monkeypatch.setattr(A, name, fn)
     with pytest.raises((AssertionError, ValueError)):
         _all_backward_pins()
+
+
+@pytest.mark.parametrize("mutant", sorted(PAGED_MUTANTS))
+def test_paged_pins_catch_planted_mistake(mutant, monkeypatch):
+    name, fn = PAGED_MUTANTS[mutant]
+    monkeypatch.setattr(A, name, fn)
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        with np.errstate(all="ignore"):
+            _all_paged_pins()
 
 
 @pytest.mark.parametrize("mutant", sorted(DECODE_MUTANTS))

@@ -136,7 +136,8 @@ def ramp_inputs(B: int, H: int, N: int, d: int, dtype: str = "bf16", *, seed: in
 
 def paged_inputs(num_seqs: int, H: int, d: int, block_size: int, min_len: int, max_len: int,
                  *, seed: int, dtype: str = "bf16", pad_value: float | None = None,
-                 seq_lens: list | None = None, extra_blocks: int = 0) -> dict:
+                 seq_lens: list | None = None, extra_blocks: int = 0,
+                 kv_heads: int | None = None) -> dict:
     """Draw a paged KV pool with randomly permuted physical block placement.
 
     Draw order: seq_lens ~ U{min_len..max_len}; a permutation of the physical
@@ -145,7 +146,9 @@ def paged_inputs(num_seqs: int, H: int, d: int, block_size: int, min_len: int, m
     sequence's last block are -1.  ``pad_value`` (e.g. NaN) overwrites the
     token slots past each sequence's length inside its last block, which the
     decode must never read into its result.  ``extra_blocks`` adds unused
-    physical blocks to the pool.
+    physical blocks to the pool; they are returned as ``free_list`` (int32, the
+    rest of the permutation) with ``free_count`` entries.  ``kv_heads`` (default
+    H) is the number of key/value heads the pools hold; q always has H heads.
     """
     tdt = _TORCH_DTYPES[dtype]
     g = _gen(seed)
@@ -163,7 +166,8 @@ def paged_inputs(num_seqs: int, H: int, d: int, block_size: int, min_len: int, m
     for s, nb in enumerate(nblk):
         table[s, :nb] = perm[off:off + nb].to(torch.int32)
         off += nb
-    shape = (total, block_size, H, d)
+    kvh = H if kv_heads is None else int(kv_heads)
+    shape = (total, block_size, kvh, d)
     k_pool = _randn_chunked(shape, g, tdt)
     v_pool = _randn_chunked(shape, g, tdt)
     q = torch.randn((num_seqs, H, d), generator=g, dtype=torch.float32).to(tdt)
@@ -174,9 +178,11 @@ def paged_inputs(num_seqs: int, H: int, d: int, block_size: int, min_len: int, m
                 p = int(table[s, nblk[s] - 1])
                 k_pool[p, r:] = pad_value
                 v_pool[p, r:] = pad_value
+    free = perm[off:].to(torch.int32).contiguous()
     return {"q": q.contiguous(), "k_pool": k_pool, "v_pool": v_pool,
             "block_table": table.contiguous(), "seq_lens": lens.to(torch.int32).contiguous(),
-            "block_size": block_size, "num_blocks": total, "max_blocks_per_seq": max_blocks}
+            "block_size": block_size, "num_blocks": total, "max_blocks_per_seq": max_blocks,
+            "free_list": free, "free_count": int(free.numel()), "kv_heads": kvh}
 
 
 def _randn_chunked(shape, g, tdt, chunk_rows: int = 512) -> torch.Tensor:
