@@ -6,6 +6,8 @@ benchmark shapes:
   * fa_fwd   causal bf16 B=8 H=12 N=1024 d=64
   * fa_fwd + fa_bwd causal bf16 B=4 H=16 N=2048 d=128
   * fa_paged_decode bf16 64 seqs x H=32 x d=128, lengths U[128,4096], 16-token blocks
+  * the same decode with 8 cached key/value heads (grouped-query attention)
+    and one paged KV append of a token per sequence
   * one ring-attention step at the long-context shape: fa_fwd_offset of the
     8192 queries against the previous 8192-token block, then fa_merge
 Inputs are resident in HBM before timing starts.  Each call is bracketed by
@@ -72,6 +74,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
                     help="comma list of parts to run: fwd_c3, fwd_c2, fwd_c4, bwd_c4, decode_c5, "
+                         "decode_gqa_c5 (8 cached heads), append_c5 (paged KV append), "
                          "ring_c3 (offset forward + merge of one ring step), copy_calib (a 1 GiB "
                          "device copy used to scale the HBM-traffic counters)")
     args = ap.parse_args()
@@ -157,6 +160,36 @@ def main():
         parts["decode_c5"] = dict(fn=lambda: binding.paged_decode(
             pd["q"], pd["k_pool"], pd["v_pool"], pd["block_table"], pd["seq_lens"], block_size=16,
             scale=c5.scale, workspace=wsd, out=od, lse=lsed), bytes=kv_bytes, tokens=tokens)
+    if want("decode_gqa_c5") or want("append_c5"):
+        # the same sequences with 8 cached heads for the 32 query heads, and
+        # enough free blocks for every timed append step
+        pg = workloads.paged_inputs(c5.num_seqs, c5.H, c5.d, c5.block_size, c5.min_len,
+                                    c5.max_len, seed=workloads.seed_for(5), kv_heads=8,
+                                    extra_blocks=4 * c5.num_seqs)
+        pgd = {kk: (vv.to(dev) if isinstance(vv, torch.Tensor) else vv) for kk, vv in pg.items()}
+        tokens_g = int(pg["seq_lens"].long().sum())
+        if want("decode_gqa_c5"):
+            og = torch.empty_like(pgd["q"])
+            lseg = torch.empty(c5.num_seqs, c5.H, device=dev)
+            wsg = torch.empty(binding.paged_decode_workspace_size(c5.num_seqs, c5.H, c5.d,
+                                                                  pg["max_blocks_per_seq"], 16),
+                              dtype=torch.uint8, device=dev)
+            parts["decode_gqa_c5"] = dict(fn=lambda: binding.paged_decode(
+                pgd["q"], pgd["k_pool"], pgd["v_pool"], pgd["block_table"], pgd["seq_lens"],
+                block_size=16, scale=c5.scale, workspace=wsg, out=og, lse=lseg),
+                bytes=tokens_g * 8 * c5.d * 2 * 2, tokens=tokens_g)
+        if want("append_c5"):
+            ga = torch.Generator().manual_seed(workloads.seed_for(5) + 1)
+            kn = torch.randn((c5.num_seqs, 8, c5.d), generator=ga).to(torch.bfloat16).to(dev)
+            vn = torch.randn((c5.num_seqs, 8, c5.d), generator=ga).to(torch.bfloat16).to(dev)
+            fc = torch.tensor([pg["free_count"]], dtype=torch.int32, device=dev)
+            nf = torch.zeros(1, dtype=torch.int32, device=dev)
+            # lengths and the free stack advance on every call (state of a real decode loop)
+            lens_a = pgd["seq_lens"].clone()
+            table_a = pgd["block_table"].clone()
+            parts["append_c5"] = dict(fn=lambda: binding.paged_kv_append(
+                kn, vn, pgd["k_pool"], pgd["v_pool"], table_a, lens_a, pgd["free_list"], fc, nf,
+                block_size=16), bytes=2 * 2 * kn.numel() * 2)
     if "copy_calib" in only:
         # plain device copy of known size: the HBM-traffic counters of the kernels
         # are scaled by what the same counters read for this copy
@@ -167,8 +200,8 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs ready: {list(parts)}")
 
-    order = [n for n in ("fwd_c3", "fwd_c2", "fwd_c4", "bwd_c4", "decode_c5", "ring_c3_fwd",
-                         "ring_c3_merge", "copy_calib") if n in parts]
+    order = [n for n in ("fwd_c3", "fwd_c2", "fwd_c4", "bwd_c4", "decode_c5", "decode_gqa_c5",
+                         "append_c5", "ring_c3_fwd", "ring_c3_merge", "copy_calib") if n in parts]
     for _ in range(args.warmup):
         for n in order:
             parts[n]["fn"]()
@@ -255,7 +288,8 @@ def main():
         "dtype": "bf16", "data": "synthetic (seeded N(0,1))",
         "config": {"workload": "causal bf16 attention forward B=1 H=32 N=8192 d=128 "
                                "(one step also runs fwd B=8 H=12 N=1024 d=64, fwd+bwd "
-                               "B=4 H=16 N=2048 d=128, paged decode 64x32x128, and one "
+                               "B=4 H=16 N=2048 d=128, paged decode 64x32x128 with 32 and "
+                               "with 8 cached heads, a paged KV append, and one "
                                "ring-attention step: offset fwd + merge at 32x8192x128)",
                    "global_batch": 1, "seq_len": 8192, "parallelism": "single-gpu"},
         "roofline": roof,

@@ -21,7 +21,8 @@ FA_DT_F32 = 0
 FA_DT_BF16 = 1
 
 EXPORTED = ("fa_status_string", "fa_version", "fa_fwd", "fa_fwd_offset", "fa_merge",
-            "fa_bwd_workspace_size", "fa_bwd", "fa_paged_decode_workspace_size", "fa_paged_decode")
+            "fa_bwd_workspace_size", "fa_bwd", "fa_paged_decode_workspace_size", "fa_paged_decode",
+            "fa_paged_decode_gqa", "fa_paged_kv_append_workspace_size", "fa_paged_kv_append")
 
 _lib = None
 
@@ -66,6 +67,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fa_paged_decode_workspace_size.restype = sz
     lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, i, vp, sz, vp]
     lib.fa_paged_decode.restype = i
+    lib.fa_paged_decode_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, i, vp, sz,
+                                        vp]
+    lib.fa_paged_decode_gqa.restype = i
+    lib.fa_paged_kv_append_workspace_size.argtypes = [i]
+    lib.fa_paged_kv_append_workspace_size.restype = sz
+    lib.fa_paged_kv_append.argtypes = [vp] * 9 + [i] * 8 + [vp, sz, vp]
+    lib.fa_paged_kv_append.restype = i
     if path is None:
         _lib = lib
     return lib
@@ -185,10 +193,14 @@ def paged_decode_workspace_size(num_seqs, H, d, max_blocks_per_seq, block_size) 
 
 def paged_decode(q, k_pool, v_pool, block_table, seq_lens, *, block_size: int,
                  scale: float | None = None, workspace=None, out=None, lse=None):
-    """o [S, H, d] bf16 and lse [S, H] fp32 of one decode step over a paged KV pool."""
+    """o [S, H, d] bf16 and lse [S, H] fp32 of one decode step over a paged KV pool.
+
+    The pools are [num_blocks, block_size, KVH, d]; KVH < H (grouped-query
+    attention) calls fa_paged_decode_gqa, KVH == H fa_paged_decode.
+    """
     _need_cuda(q, k_pool, v_pool, block_table, seq_lens)
     S, H, d = q.shape
-    num_blocks = k_pool.shape[0]
+    num_blocks, KVH = k_pool.shape[0], k_pool.shape[2]
     mbps = block_table.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
@@ -196,9 +208,39 @@ def paged_decode(q, k_pool, v_pool, block_table, seq_lens, *, block_size: int,
     ws_bytes = paged_decode_workspace_size(S, H, d, mbps, block_size)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
-    st = load_library().fa_paged_decode(
-        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), block_size, S, H,
-        d, mbps, num_blocks, scale, _ptr(o), _ptr(l), _dtype_code(q), _ptr(workspace),
-        workspace.numel(), _stream(q.device))
-    _check(st, "fa_paged_decode")
+    lib = load_library()
+    if KVH == H:
+        st = lib.fa_paged_decode(
+            _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), block_size, S,
+            H, d, mbps, num_blocks, scale, _ptr(o), _ptr(l), _dtype_code(q), _ptr(workspace),
+            workspace.numel(), _stream(q.device))
+        _check(st, "fa_paged_decode")
+    else:
+        st = lib.fa_paged_decode_gqa(
+            _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), block_size, S,
+            H, KVH, d, mbps, num_blocks, scale, _ptr(o), _ptr(l), _dtype_code(q), _ptr(workspace),
+            workspace.numel(), _stream(q.device))
+        _check(st, "fa_paged_decode_gqa")
     return o, l
+
+
+def paged_kv_append(k_new, v_new, k_pool, v_pool, block_table, seq_lens, free_list, free_count,
+                    n_failed, *, block_size: int, workspace=None):
+    """Write one token's K/V per sequence into the paged pools (in place), taking
+    blocks from the free stack on demand.  ``free_count`` and ``n_failed`` are
+    one-element int32 device tensors; every argument is updated in place."""
+    _need_cuda(k_new, v_new, k_pool, v_pool, block_table, seq_lens, free_list, free_count,
+               n_failed)
+    S, KVH, d = k_new.shape
+    if v_new.shape != k_new.shape or k_pool.shape[2:] != (KVH, d) or v_pool.shape != k_pool.shape:
+        raise ValueError("k_new/v_new [S, KVH, d] must match pools [num_blocks, bs, KVH, d]")
+    lib = load_library()
+    ws_bytes = int(lib.fa_paged_kv_append_workspace_size(S))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=k_new.device)
+    st = lib.fa_paged_kv_append(
+        _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
+        _ptr(free_list), _ptr(free_count), _ptr(n_failed), S, KVH, d, block_size,
+        block_table.shape[1], k_pool.shape[0], free_list.numel(), _dtype_code(k_new),
+        _ptr(workspace), workspace.numel(), _stream(k_new.device))
+    _check(st, "fa_paged_kv_append")

@@ -19,7 +19,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 ARCH = os.environ.get("FA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_cache.hip"]
 # Per-source extra flags.  The attention kernels never test for NaN, so they
 # are built without NaN-preserving semantics; that lets max() compile to a
 # single v_max/v_max3 instead of canonicalize + max.

@@ -146,19 +146,20 @@ size_t fa_paged_decode_workspace_size(int num_seqs, int H, int d, int max_blocks
   return round_up((size_t)num_seqs * parts * H * (size_t)(d + 2) * sizeof(float), 256);
 }
 
-int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
-                    const int32_t* block_table, const int32_t* seq_lens, int block_size,
-                    int num_seqs, int H, int d, int max_blocks_per_seq, int num_blocks,
-                    float scale, void* o, float* lse, int dtype, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+int fa_paged_decode_gqa(const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* block_table, const int32_t* seq_lens, int block_size,
+                        int num_seqs, int H, int KVH, int d, int max_blocks_per_seq, int num_blocks,
+                        float scale, void* o, float* lse, int dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   if (dtype != FA_DT_F32 && dtype != FA_DT_BF16) return FA_ERR_DTYPE;
-  if (num_seqs < 0 || H < 1 || d < 1 || max_blocks_per_seq < 1 || num_blocks < 1 ||
+  if (num_seqs < 0 || H < 1 || KVH < 1 || d < 1 || max_blocks_per_seq < 1 || num_blocks < 1 ||
       block_size < 1)
     return FA_ERR_SHAPE;
+  if (H % KVH != 0) return FA_ERR_SHAPE;
   if (!std::isfinite(scale)) return FA_ERR_SHAPE;
   if (dtype != FA_DT_BF16 || block_size != 16 || d != 128 || (H % 4) != 0)
     return FA_ERR_UNSUPPORTED;
-  const long long block_bytes = (long long)block_size * H * d * 2;
+  const long long block_bytes = (long long)block_size * KVH * d * 2;
   if (block_bytes >= (1LL << 31)) return FA_ERR_SHAPE;
   if ((long long)max_blocks_per_seq * block_size > kMaxN) return FA_ERR_SHAPE;
   if (num_seqs == 0) return FA_OK;
@@ -195,7 +196,73 @@ int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
                    max_blocks_per_seq, num_blocks, scale, o, lse,
                    static_cast<float*>(workspace), fa::kDecodePartTokens,
                    fa::decode_n_parts(max_blocks_per_seq, block_size), st};
+  a.KVH = KVH;
   return hip_status(fa::launch_decode(a));
+}
+
+int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_table, const int32_t* seq_lens, int block_size,
+                    int num_seqs, int H, int d, int max_blocks_per_seq, int num_blocks,
+                    float scale, void* o, float* lse, int dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return fa_paged_decode_gqa(q, k_pool, v_pool, block_table, seq_lens, block_size, num_seqs, H, H,
+                             d, max_blocks_per_seq, num_blocks, scale, o, lse, dtype, workspace,
+                             workspace_bytes, stream);
+}
+
+size_t fa_paged_kv_append_workspace_size(int num_seqs) {
+  if (num_seqs <= 0) return 0;
+  return round_up((size_t)num_seqs * sizeof(int32_t), 256);   // the per-sequence slot map
+}
+
+int fa_paged_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                       int32_t* block_table, int32_t* seq_lens, const int32_t* free_list,
+                       int32_t* free_count, int32_t* n_failed, int num_seqs, int KVH, int d,
+                       int block_size, int max_blocks_per_seq, int num_blocks, int free_capacity,
+                       int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != FA_DT_F32 && dtype != FA_DT_BF16) return FA_ERR_DTYPE;
+  if (num_seqs < 0 || KVH < 1 || d < 1 || block_size < 1 || max_blocks_per_seq < 1 ||
+      num_blocks < 1 || free_capacity < 0)
+    return FA_ERR_SHAPE;
+  const long long row_bytes = (long long)KVH * d * (dtype == FA_DT_F32 ? 4 : 2);
+  if (row_bytes % 16 != 0 || row_bytes >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+  if ((long long)num_blocks * block_size >= (1LL << 31)) return FA_ERR_SHAPE;
+  if ((long long)max_blocks_per_seq * block_size > (1LL << 30)) return FA_ERR_SHAPE;
+  if (num_seqs == 0) return FA_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_table || !seq_lens || !free_count ||
+      !n_failed || (free_capacity > 0 && !free_list))
+    return FA_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !aligned16(workspace))
+    return FA_ERR_ALIGN;
+  const void* ints[] = {block_table, seq_lens, free_list, free_count, n_failed};
+  for (const void* p : ints)
+    if (reinterpret_cast<uintptr_t>(p) & 3u) return FA_ERR_ALIGN;
+  if (!workspace || workspace_bytes < fa_paged_kv_append_workspace_size(num_seqs))
+    return FA_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    // lengths within the table, stack height within the list, stack ids in the pool
+    std::vector<int32_t> lens(num_seqs), fl(free_capacity > 0 ? free_capacity : 0);
+    int32_t fc = 0;
+    if (hipMemcpyAsync(lens.data(), seq_lens, lens.size() * 4, hipMemcpyDeviceToHost, st) !=
+            hipSuccess ||
+        hipMemcpyAsync(&fc, free_count, 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+        (!fl.empty() && hipMemcpyAsync(fl.data(), free_list, fl.size() * 4,
+                                       hipMemcpyDeviceToHost, st) != hipSuccess) ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return FA_ERR_HIP;
+    for (int s = 0; s < num_seqs; ++s)
+      if (lens[s] < 0 || (long long)lens[s] > (long long)max_blocks_per_seq * block_size)
+        return FA_ERR_INVALID;
+    if (fc < 0 || fc > free_capacity) return FA_ERR_INVALID;
+    for (int i = 0; i < fc; ++i)
+      if (fl[i] < 0 || fl[i] >= num_blocks) return FA_ERR_INVALID;
+  }
+  fa::AppendArgs a{k_new, v_new, k_pool, v_pool, block_table, seq_lens, free_list, free_count,
+                   n_failed, static_cast<int32_t*>(workspace), num_seqs, block_size,
+                   max_blocks_per_seq, num_blocks, free_capacity, (int)row_bytes, st};
+  return hip_status(fa::launch_append(a));
 }
 
 }  // extern "C"

@@ -9,9 +9,13 @@
 // over KV partitions is merged with the rescaling rule of the online softmax
 // (HPC notes, section "Long context and sequence parallelism").
 //
-// Pool layout [num_blocks, block_size = 16, H, d = 128]: one physical block is
-// a contiguous 16 * H * 256-byte chunk, so a workgroup that reads all heads of
-// a block streams contiguous memory.
+// Pool layout [num_blocks, block_size = 16, KVH, d = 128]: one physical block
+// is a contiguous 16 * KVH * 256-byte chunk, so a workgroup that reads all
+// heads of a block streams contiguous memory.  With grouped-query attention
+// (KVH < H; HPC notes, "Prefill, Decode and inference scheduling", KV-cache
+// size) consecutive query heads share one cached head: their lanes load the
+// same bytes, which the vector L1 merges, so HBM traffic per token falls by
+// H / KVH.
 //
 // Partial kernel: workgroup = (sequence, KV partition of 256 tokens, group of
 //   32 heads), so at H = 32 every 16-token block is read as one contiguous
@@ -42,9 +46,11 @@ constexpr int kHeadsPerGroup = 32;   // heads per workgroup: whole 8 KiB token r
 __global__ __launch_bounds__(kDecThreads, 1) void decode_partial_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k_pool,
     const __bf16* __restrict__ v_pool, const int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ seq_lens, int H, int max_blocks_per_seq, int num_blocks,
+    const int32_t* __restrict__ seq_lens, int H, int KVH, int max_blocks_per_seq, int num_blocks,
     float scale_log2, float* __restrict__ part_o, float* __restrict__ part_ml, int part_tokens,
     int n_parts) {
+  // H query heads; the pools hold KVH key/value heads and query head h reads
+  // cached head h / (H / KVH)
   const int p = blockIdx.x;
   const int hg = blockIdx.y;
   const int s = blockIdx.z;
@@ -60,16 +66,17 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_partial_kernel(
   const int ch = lane & 15;                          // which 8 of the 128 d values
   const bool head_ok = head < H;
   const int hh = head_ok ? head : 0;
+  const int kvh = hh / (H / KVH);                   // the cached head this query head reads
 
-  const uint32_t blk_bytes = (uint32_t)kDecBS * H * kDecD * 2;
-  const uint32_t row_off = (uint32_t)(hh * kDecD + ch * 8) * 2;    // within one token row
-  const uint32_t tok_stride = (uint32_t)H * kDecD * 2;
+  const uint32_t blk_bytes = (uint32_t)kDecBS * KVH * kDecD * 2;
+  const uint32_t row_off = (uint32_t)(kvh * kDecD + ch * 8) * 2;   // within one token row
+  const uint32_t tok_stride = (uint32_t)KVH * kDecD * 2;
 
   // this lane's 8 query values, fp32
   float qv[8];
   {
     const auto rq = make_rsrc(q + (size_t)s * H * kDecD, (uint32_t)H * kDecD * 2);
-    const u32x4 w = bload16(rq, row_off);
+    const u32x4 w = bload16(rq, (uint32_t)(hh * kDecD + ch * 8) * 2);   // this query head
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       qv[2 * e] = bf16lo(w[e]);
@@ -89,7 +96,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_partial_kernel(
   auto block_rsrc = [&](int t0, __amdgpu_buffer_rsrc_t& rk, __amdgpu_buffer_rsrc_t& rv) {
     const int32_t phys = table[t0 / kDecBS];
     const bool phys_ok = (uint32_t)phys < (uint32_t)num_blocks;
-    const size_t boff = (size_t)(phys_ok ? phys : 0) * kDecBS * H * kDecD;
+    const size_t boff = (size_t)(phys_ok ? phys : 0) * kDecBS * KVH * kDecD;
     rk = make_rsrc(k_pool + boff, phys_ok ? blk_bytes : 0u);
     rv = make_rsrc(v_pool + boff, phys_ok ? blk_bytes : 0u);
   };
@@ -235,7 +242,8 @@ hipError_t launch_decode(const DecodeArgs& a) {
   dim3 grid(a.n_parts, (a.H + kHeadsPerGroup - 1) / kHeadsPerGroup, a.num_seqs);
   hipLaunchKernelGGL(decode_partial_kernel, grid, dim3(kDecThreads), 0, a.stream,
                      (const __bf16*)a.q, (const __bf16*)a.k_pool, (const __bf16*)a.v_pool,
-                     a.block_table, a.seq_lens, a.H, a.max_blocks_per_seq, a.num_blocks,
+                     a.block_table, a.seq_lens, a.H, a.KVH > 0 ? a.KVH : a.H,
+                     a.max_blocks_per_seq, a.num_blocks,
                      a.scale * kLog2e, part_o, part_ml, a.part_tokens, a.n_parts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -67,12 +67,30 @@ struct DecodeArgs {
   int part_tokens;  // tokens per KV partition
   int n_parts;      // partitions per sequence (max)
   hipStream_t stream;
+  int KVH = 0;      // key/value heads in the pools (0: same as H)
+};
+
+struct AppendArgs {
+  const void* k_new;      // [num_seqs, KVH, d]
+  const void* v_new;
+  void* k_pool;           // [num_blocks, block_size, KVH, d]
+  void* v_pool;
+  int32_t* block_table;   // [num_seqs, max_blocks_per_seq]
+  int32_t* seq_lens;      // [num_seqs]
+  const int32_t* free_list;
+  int32_t* free_count;    // device scalar, updated
+  int32_t* n_failed;      // device scalar, written
+  int32_t* slot_map;      // workspace [num_seqs]: pool slot written, or -1
+  int num_seqs, block_size, max_blocks_per_seq, num_blocks, free_capacity;
+  int row_bytes;          // bytes of one token's K (or V) row: KVH * d * element size
+  hipStream_t stream;
 };
 
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_merge(const MergeArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_append(const AppendArgs& a);
 
 // Decode partitioning shared by the workspace query and the launcher.
 #ifndef FA_DECODE_PART_TOKENS

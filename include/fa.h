@@ -210,6 +210,74 @@ int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
                     float scale, void* o, float* lse, int dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fa_paged_decode_gqa -- fa_paged_decode with grouped-query attention: the
+ * pools hold KVH key/value heads, fewer than the H query heads, and query
+ * head h reads cached head h / (H / KVH) (consecutive query heads share one
+ * cached head; HPC notes, section "Prefill, Decode and inference scheduling":
+ * with grouped-query attention kv_heads < query heads and the KV cache shrinks
+ * accordingly).  One cached byte then serves H / KVH query heads.
+ *
+ *   k_pool/v_pool in  [num_blocks, block_size, KVH, d] bf16
+ *   KVH          >= 1 and divides H (else FA_ERR_SHAPE)
+ * Every other argument, the workspace size (fa_paged_decode_workspace_size
+ * with the query head count H) and the error behaviour are those of
+ * fa_paged_decode, which is this call with KVH = H.
+ */
+int fa_paged_decode_gqa(const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* block_table, const int32_t* seq_lens, int block_size,
+                        int num_seqs, int H, int KVH, int d, int max_blocks_per_seq,
+                        int num_blocks, float scale, void* o, float* lse, int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_paged_kv_append_workspace_size -- bytes of workspace fa_paged_kv_append
+ * needs: one int32 pool-slot index per sequence, rounded up to 256 bytes.
+ */
+size_t fa_paged_kv_append_workspace_size(int num_seqs);
+
+/*
+ * fa_paged_kv_append -- write one new token's K and V for every sequence into
+ * a paged KV cache, taking blocks on demand from a stack of free blocks.
+ *
+ * Blocks are allocated only when needed (CMU 10-423 L17-L18 notes, section
+ * "Decoding: PagedAttention"); the runtime keeps each sequence's length and
+ * block mapping (HPC notes, section "Prefill, Decode and inference
+ * scheduling").  Sequence s writes its token at position t = seq_lens[s]:
+ *   - when t is a multiple of block_size (its blocks are full), it takes the
+ *     block on top of the free stack, free_list[*free_count - 1], and stores
+ *     it in block_table[s, t / block_size]; sequences take blocks in sequence
+ *     order, so the stack is popped as if they were served one by one;
+ *   - the token's K and V rows go to slot t % block_size of the sequence's
+ *     block table[s, t / block_size], and seq_lens[s] becomes t + 1.
+ * A sequence whose table is full (t >= max_blocks_per_seq * block_size), that
+ * needs a block when the stack is empty, or whose block id is outside the
+ * pool is left unchanged (nothing written) and counted in *n_failed.
+ *
+ *   k_new, v_new   in     [num_seqs, KVH, d], dtype `dtype` (bf16 or fp32)
+ *   k_pool, v_pool in/out [num_blocks, block_size, KVH, d], same dtype
+ *   block_table    in/out [num_seqs, max_blocks_per_seq] int32
+ *   seq_lens       in/out [num_seqs] int32
+ *   free_list      in     [free_capacity] int32 physical ids; entries
+ *                         [0, *free_count) are the stack, top last
+ *   free_count     in/out device int32 scalar: stack height, reduced by the
+ *                         blocks taken
+ *   n_failed       out    device int32 scalar
+ *   KVH * d * element size must be a multiple of 16 bytes (else
+ *   FA_ERR_UNSUPPORTED); num_blocks * block_size < 2^31.
+ *   workspace      >= fa_paged_kv_append_workspace_size(num_seqs) bytes.
+ * num_seqs == 0 is a no-op that writes nothing.  All device pointers are the
+ * caller's; tensor pointers 16-byte aligned, int32 pointers 4-byte aligned.
+ * With FA_DEBUG=1 the lengths, the stack height and the stack's ids are
+ * checked on the host first (FA_ERR_INVALID, nothing launched).  Calls are
+ * ordered on `stream`; two calls that share a pool must not overlap.
+ */
+int fa_paged_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                       int32_t* block_table, int32_t* seq_lens, const int32_t* free_list,
+                       int32_t* free_count, int32_t* n_failed, int num_seqs, int KVH, int d,
+                       int block_size, int max_blocks_per_seq, int num_blocks, int free_capacity,
+                       int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

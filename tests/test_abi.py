@@ -36,6 +36,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("fa_fwd", "fa_fwd_offset", "fa_merge", "fa_bwd", "fa_paged_decode",
+              "fa_paged_decode_gqa", "fa_paged_kv_append", "fa_paged_kv_append_workspace_size",
               "fa_bwd_workspace_size", "fa_paged_decode_workspace_size", "fa_status_string",
               "fa_version"):
         assert n in names
@@ -167,3 +168,41 @@ def test_python_binding_refuses_host_tensors():
     x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         libfa.fwd(x, x, x, causal=True)
+
+
+def gqa(lib, H=32, KVH=8, d=128, bs=16, dt=1, S=4, q=P):
+    ws = lib.fa_paged_decode_workspace_size(S, H, d, 8, bs)
+    return lib.fa_paged_decode_gqa(q, P, P, P, P, bs, S, H, KVH, d, 8, 100, 0.1, P2, P2, dt, P2, ws,
+                                   None)
+
+
+def test_paged_decode_gqa_validation(lib):
+    assert gqa(lib, KVH=0) == ERR_SHAPE
+    assert gqa(lib, KVH=5) == ERR_SHAPE          # must divide H
+    assert gqa(lib, KVH=64) == ERR_SHAPE
+    assert gqa(lib, d=64) == ERR_UNSUP
+    assert gqa(lib, q=None) == ERR_NULL
+    assert gqa(lib, S=0, q=None) == OK
+
+
+def append(lib, S=4, KVH=8, d=128, bs=16, mbps=8, nb=100, cap=10, dt=1, kn=P, ws=P2, wsb=None,
+           fl=P, fc=P):
+    wsb = lib.fa_paged_kv_append_workspace_size(S) if wsb is None else wsb
+    return lib.fa_paged_kv_append(kn, P, P, P, P, P, fl, fc, P, S, KVH, d, bs, mbps, nb, cap, dt,
+                                  ws, wsb, None)
+
+
+def test_paged_kv_append_validation(lib):
+    assert lib.fa_paged_kv_append_workspace_size(10) == 256
+    assert lib.fa_paged_kv_append_workspace_size(0) == 0
+    assert append(lib, dt=4) == ERR_DTYPE
+    assert append(lib, KVH=0) == ERR_SHAPE
+    assert append(lib, cap=-1) == ERR_SHAPE
+    assert append(lib, nb=1 << 28) == ERR_SHAPE          # slots past 2^31
+    assert append(lib, KVH=1, d=4) == ERR_UNSUP          # 8-byte rows
+    assert append(lib, kn=None) == ERR_NULL
+    assert append(lib, fl=None) == ERR_NULL              # a stack with capacity needs a list
+    assert append(lib, kn=MIS) == ERR_ALIGN
+    assert append(lib, fc=ctypes.c_void_p(0x10002)) == ERR_ALIGN
+    assert append(lib, wsb=16) == ERR_WS
+    assert append(lib, S=0, kn=None) == OK
