@@ -3,6 +3,7 @@
 One step = one pass of the whole hot path over synthetic inputs of the
 benchmark shapes:
   * fa_fwd   causal bf16 B=1 H=32 N=8192 d=128   (the headline: TFLOP/s, % MFMA peak)
+  * the same forward with fp16 inputs
   * fa_fwd   causal bf16 B=8 H=12 N=1024 d=64
   * fa_fwd + fa_bwd causal bf16 B=4 H=16 N=2048 d=128
   * fa_paged_decode bf16 64 seqs x H=32 x d=128, lengths U[128,4096], 16-token blocks
@@ -73,7 +74,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
-                    help="comma list of parts to run: fwd_c3, fwd_c2, fwd_c4, bwd_c4, decode_c5, "
+                    help="comma list of parts to run: fwd_c3, fwd_c3_f16, fwd_c2, fwd_c4, bwd_c4, "
+                         "decode_c5, "
                          "decode_gqa_c5 (8 cached heads), append_c5 (paged KV append), "
                          "ring_c3 (offset forward + merge of one ring step), copy_calib (a 1 GiB "
                          "device copy used to scale the HBM-traffic counters)")
@@ -106,6 +108,15 @@ def main():
         parts["fwd_c3"] = dict(fn=lambda: binding.fwd(q, k, v, causal=True, scale=c3.scale, out=o,
                                                        lse=lse),
                                flops=causal_flops(c3.B, c3.H, c3.N, c3.d))
+    if want("fwd_c3_f16"):
+        # the headline forward with fp16 inputs (same draws, cast to fp16)
+        xh = workloads.attention_inputs(c3.B, c3.H, c3.N, c3.d, "f16", seed=workloads.seed_for(3))
+        qh, kh, vh = (xh[n].to(dev) for n in "qkv")
+        oh = torch.empty_like(qh)
+        lseh = torch.empty(c3.B, c3.H, c3.N, device=dev)
+        parts["fwd_c3_f16"] = dict(fn=lambda: binding.fwd(qh, kh, vh, causal=True, scale=c3.scale,
+                                                           out=oh, lse=lseh),
+                                   flops=causal_flops(c3.B, c3.H, c3.N, c3.d))
     if want("ring_c3"):
         # one rank's non-diagonal ring step at the long-context shape: its 8192
         # queries (global rows 8192..16383) against the previous 8192-token
@@ -200,7 +211,8 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs ready: {list(parts)}")
 
-    order = [n for n in ("fwd_c3", "fwd_c2", "fwd_c4", "bwd_c4", "decode_c5", "decode_gqa_c5",
+    order = [n for n in ("fwd_c3", "fwd_c3_f16", "fwd_c2", "fwd_c4", "bwd_c4", "decode_c5",
+                         "decode_gqa_c5",
                          "append_c5", "ring_c3_fwd", "ring_c3_merge", "copy_calib") if n in parts]
     for _ in range(args.warmup):
         for n in order:

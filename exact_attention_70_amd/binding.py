@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libfa.so")
 
 FA_DT_F32 = 0
 FA_DT_BF16 = 1
+FA_DT_F16 = 2
 
 EXPORTED = ("fa_status_string", "fa_version", "fa_fwd", "fa_fwd_offset", "fa_merge",
             "fa_bwd_workspace_size", "fa_bwd", "fa_paged_decode_workspace_size", "fa_paged_decode",
@@ -99,9 +100,11 @@ def _stream(device) -> ctypes.c_void_p:
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return FA_DT_BF16
+    if t.dtype == torch.float16:
+        return FA_DT_F16
     if t.dtype == torch.float32:
         return FA_DT_F32
-    raise TypeError(f"libfa supports bf16 and fp32 tensors, got {t.dtype}")
+    raise TypeError(f"libfa supports bf16, fp16 and fp32 tensors, got {t.dtype}")
 
 
 def _need_cuda(*ts):

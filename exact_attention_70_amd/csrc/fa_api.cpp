@@ -62,7 +62,7 @@ int fa_version(void) { return 100; }
 int fa_fwd_offset(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
                   int Nq, int Nk, int d, long long q_offset, long long k_offset, float scale,
                   int causal, int dtype, void* stream) {
-  if (dtype != FA_DT_F32 && dtype != FA_DT_BF16) return FA_ERR_DTYPE;
+  if (dtype != FA_DT_F32 && dtype != FA_DT_BF16 && dtype != FA_DT_F16) return FA_ERR_DTYPE;
   if (B < 0 || H < 1 || Nq < 1 || Nq > kMaxN || Nk < 1 || Nk > kMaxN || d < 1) return FA_ERR_SHAPE;
   if (q_offset < -kMaxOffset || q_offset > kMaxOffset || k_offset < -kMaxOffset ||
       k_offset > kMaxOffset)
@@ -90,7 +90,7 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int
 
 int fa_merge(const void* O_a, const float* LSE_a, const void* O_b, const float* LSE_b, void* O,
              float* LSE, int B, int H, int N, int d, int dtype, void* stream) {
-  if (dtype != FA_DT_F32 && dtype != FA_DT_BF16) return FA_ERR_DTYPE;
+  if (dtype != FA_DT_F32 && dtype != FA_DT_BF16 && dtype != FA_DT_F16) return FA_ERR_DTYPE;
   if (B < 0 || H < 1 || N < 1 || N > kMaxN || d < 1) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (B == 0) return FA_OK;
@@ -99,7 +99,7 @@ int fa_merge(const void* O_a, const float* LSE_a, const void* O_b, const float* 
       !aligned16(LSE_b) || !aligned16(LSE))
     return FA_ERR_ALIGN;
   const long long rows = (long long)B * H * N;
-  const size_t obytes = (size_t)rows * d * (dtype == FA_DT_F32 ? 4 : 2);
+  const size_t obytes = (size_t)rows * d * (dtype == FA_DT_F32 ? 4 : 2);   // bf16 / fp16: 2
   const size_t lbytes = (size_t)rows * sizeof(float);
   // outputs may be exactly an input buffer (in-place accumulation), never a shifted overlap
   if (partial_overlap(O, O_a, obytes) || partial_overlap(O, O_b, obytes) ||
@@ -121,10 +121,10 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
            const float* LSE, float* dQ, float* dK, float* dV, int B, int H, int N, int d,
            float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
            void* stream) {
-  if (dtype != FA_DT_F32 && dtype != FA_DT_BF16) return FA_ERR_DTYPE;
+  if (dtype != FA_DT_F32 && dtype != FA_DT_BF16 && dtype != FA_DT_F16) return FA_ERR_DTYPE;
   if (B < 0 || H < 1 || N < 1 || N > kMaxN || d < 1) return FA_ERR_SHAPE;
   if (!std::isfinite(scale)) return FA_ERR_SHAPE;
-  if (dtype != FA_DT_BF16) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_DT_F32) return FA_ERR_UNSUPPORTED;   // 16-bit inputs only
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (!head_fits(N, d, 4)) return FA_ERR_SHAPE;
   if (B == 0) return FA_OK;
@@ -135,6 +135,7 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
     if (!aligned16(p)) return FA_ERR_ALIGN;
   fa::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, static_cast<float*>(workspace),
                 B, H, N, d, scale, causal != 0, reinterpret_cast<hipStream_t>(stream)};
+  a.dtype = dtype;
   return hip_status(fa::launch_bwd(a));
 }
 
@@ -151,13 +152,13 @@ int fa_paged_decode_gqa(const void* q, const void* k_pool, const void* v_pool,
                         int num_seqs, int H, int KVH, int d, int max_blocks_per_seq, int num_blocks,
                         float scale, void* o, float* lse, int dtype, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  if (dtype != FA_DT_F32 && dtype != FA_DT_BF16) return FA_ERR_DTYPE;
+  if (dtype != FA_DT_F32 && dtype != FA_DT_BF16 && dtype != FA_DT_F16) return FA_ERR_DTYPE;
   if (num_seqs < 0 || H < 1 || KVH < 1 || d < 1 || max_blocks_per_seq < 1 || num_blocks < 1 ||
       block_size < 1)
     return FA_ERR_SHAPE;
   if (H % KVH != 0) return FA_ERR_SHAPE;
   if (!std::isfinite(scale)) return FA_ERR_SHAPE;
-  if (dtype != FA_DT_BF16 || block_size != 16 || d != 128 || (H % 4) != 0)
+  if (dtype == FA_DT_F32 || block_size != 16 || d != 128 || (H % 4) != 0)
     return FA_ERR_UNSUPPORTED;
   const long long block_bytes = (long long)block_size * KVH * d * 2;
   if (block_bytes >= (1LL << 31)) return FA_ERR_SHAPE;
@@ -197,6 +198,7 @@ int fa_paged_decode_gqa(const void* q, const void* k_pool, const void* v_pool,
                    static_cast<float*>(workspace), fa::kDecodePartTokens,
                    fa::decode_n_parts(max_blocks_per_seq, block_size), st};
   a.KVH = KVH;
+  a.dtype = dtype;
   return hip_status(fa::launch_decode(a));
 }
 
@@ -220,7 +222,7 @@ int fa_paged_kv_append(const void* k_new, const void* v_new, void* k_pool, void*
                        int32_t* free_count, int32_t* n_failed, int num_seqs, int KVH, int d,
                        int block_size, int max_blocks_per_seq, int num_blocks, int free_capacity,
                        int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  if (dtype != FA_DT_F32 && dtype != FA_DT_BF16) return FA_ERR_DTYPE;
+  if (dtype != FA_DT_F32 && dtype != FA_DT_BF16 && dtype != FA_DT_F16) return FA_ERR_DTYPE;
   if (num_seqs < 0 || KVH < 1 || d < 1 || block_size < 1 || max_blocks_per_seq < 1 ||
       num_blocks < 1 || free_capacity < 0)
     return FA_ERR_SHAPE;

@@ -35,9 +35,9 @@ namespace {
 constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------- D = rowsum(dO o O)
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_dot_kernel(const __bf16* __restrict__ O,
-                                                           const __bf16* __restrict__ dO,
+template <class E, int D>
+__global__ __launch_bounds__(kThreads) void bwd_dot_kernel(const typename E::elem* __restrict__ O,
+                                                           const typename E::elem* __restrict__ dO,
                                                            const float* __restrict__ LSE,
                                                            float* __restrict__ Dvec,
                                                            float* __restrict__ NL,
@@ -52,8 +52,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(const __bf16* __restr
   float acc = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    acc = fmaf(bf16lo(a[e]), bf16lo(b[e]), acc);
-    acc = fmaf(bf16hi(a[e]), bf16hi(b[e]), acc);
+    acc = fmaf(E::lo(a[e]), E::lo(b[e]), acc);
+    acc = fmaf(E::hi(a[e]), E::hi(b[e]), acc);
   }
   acc = group_sum<LPR>(acc);
   if (ok && c == 0) {
@@ -72,13 +72,13 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* lds, uint32
 // The row order matches the C-layout of a 32 x 32 score tile, so the result
 // pairs slot-for-slot with a C-layout tile fed back as the B operand.
 template <int D>
-__device__ __forceinline__ bf16x8 tr_operand(const unsigned char* tile, int u, int t, int lane) {
+__device__ __forceinline__ u32x4 tr_operand(const unsigned char* tile, int u, int t, int lane) {
   const int half = lane >> 5;
   const int row = 16 * u + 4 * half + ((lane & 15) >> 2);
   const int col = t * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const u32x2 lo = ds_read_tr16(tile + tile_off<D>(row, col >> 3) + (col & 7) * 2);
   const u32x2 hi = ds_read_tr16(tile + tile_off<D>(row + 8, col >> 3) + (col & 7) * 2);
-  return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -94,10 +94,11 @@ __device__ __forceinline__ bf16x8 tr_operand(const unsigned char* tile, int u, i
 constexpr int kKvBN = 128;   // keys per workgroup
 constexpr int kKvBQ = 64;    // queries per inner tile
 
-template <int D, bool CAUSAL>
+template <class E, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ dO, const float* __restrict__ NL, const float* __restrict__ Dvec,
+    const typename E::elem* __restrict__ Q, const typename E::elem* __restrict__ K,
+    const typename E::elem* __restrict__ V, const typename E::elem* __restrict__ dO,
+    const float* __restrict__ NL, const float* __restrict__ Dvec,
     float* __restrict__ dK, float* __restrict__ dV, int N, float scale, float scale_log2,
     int n_ktiles) {
   constexpr int KSTEPS = D / 16;
@@ -149,11 +150,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   load(2, sQ2, sO2, sL2, sD2);
 
   // this wave's 32 keys as B operands: B[k = d][n = key] = K[key][d]
-  bf16x8 kf[KSTEPS], vf[KSTEPS];
+  u32x4 kf[KSTEPS], vf[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
-    kf[s] = as_bf16x8(bload16(rK, (uint32_t)(my_k * D + 16 * s + 8 * half) * 2));
-    vf[s] = as_bf16x8(bload16(rV, (uint32_t)(my_k * D + 16 * s + 8 * half) * 2));
+    kf[s] = bload16(rK, (uint32_t)(my_k * D + 16 * s + 8 * half) * 2);
+    vf[s] = bload16(rV, (uint32_t)(my_k * D + 16 * s + 8 * half) * 2);
   }
   f32x16 dk[DT], dv[DT];
 #pragma unroll
@@ -189,12 +190,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       __attribute__((always_inline)) {
     const int sub = idx / (2 * KSTEPS), k = (idx / 2) % KSTEPS;
     const unsigned char* base = (idx & 1) ? sO : sQ;
-    return as_u32x4(*(const bf16x8*)(base + rofs[k] + sub * 32 * D * 2));
+    return *(const u32x4*)(base + rofs[k] + sub * 32 * D * 2);
   };
   auto a_op = [&](int idx, u32x4 a, f32x16 (&s)[2], f32x16 (&dp)[2]) __attribute__((always_inline)) {
     const int sub = idx / (2 * KSTEPS), k = (idx / 2) % KSTEPS;
-    if (idx & 1) dp[sub] = mfma_bf16(as_bf16x8(a), vf[k], dp[sub]);
-    else s[sub] = mfma_bf16(as_bf16x8(a), kf[k], s[sub]);
+    if (idx & 1) dp[sub] = E::mfma(a, vf[k], dp[sub]);
+    else s[sub] = E::mfma(a, kf[k], s[sub]);
   };
   // stage C operand idx: k-step u, column block t, {dO^T -> dV, Q^T -> dK}
   auto c_operand = [&](const unsigned char* sQ, const unsigned char* sO, int idx)
@@ -215,8 +216,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       const u32x4 a = ring[idx % LEAD];
       if (idx + LEAD < NC) ring[idx % LEAD] = c_operand(sQ, sO, idx + LEAD);
       const int u = idx / (2 * DT), t = (idx / 2) % DT;
-      if (idx & 1) dk[t] = mfma_bf16(as_bf16x8(a), as_bf16x8(db[u]), dk[t]);
-      else dv[t] = mfma_bf16(as_bf16x8(a), as_bf16x8(pb[u]), dv[t]);
+      if (idx & 1) dk[t] = E::mfma(a, db[u], dk[t]);
+      else dv[t] = E::mfma(a, pb[u], dv[t]);
     }
   };
   // stage B for score element e of this lane (sub-tile e/16, C-layout register e%16)
@@ -241,8 +242,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     dsv[x & 1] = p * (dp[sub][i] - st.d4[x]);
     if (x & 1) {
       const int u = 2 * sub + (g >> 1), w = (g & 1) * 2 + (x >> 1);   // B-operand k-step and word
-      pb[u][w] = pack_bf16(pv[0], pv[1]);
-      db[u][w] = pack_bf16(dsv[0], dsv[1]);
+      pb[u][w] = E::pack(pv[0], pv[1]);
+      db[u][w] = E::pack(dsv[0], dsv[1]);
     }
   };
 
@@ -379,10 +380,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 constexpr int kQBM = 128;   // queries per workgroup
 constexpr int kQBN = 64;    // keys per tile
 
-template <int D, bool CAUSAL>
+template <class E, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dvec,
+    const typename E::elem* __restrict__ Q, const typename E::elem* __restrict__ K,
+    const typename E::elem* __restrict__ V, const typename E::elem* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Dvec,
     float* __restrict__ dQ, int N, float scale, float scale_log2, int n_qtiles) {
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;
@@ -418,11 +420,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     dma_rows<D, kQBN, kThreads / 64>(rV, sV, j * kQBN, wave, lane);
   };
   load(0, sK0, sV0);
-  bf16x8 qf[KSTEPS], dof[KSTEPS];
+  u32x4 qf[KSTEPS], dof[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
-    qf[s] = as_bf16x8(bload16(rQ, (uint32_t)(my_q * D + 16 * s + 8 * half) * 2));
-    dof[s] = as_bf16x8(bload16(rdO, (uint32_t)(my_q * D + 16 * s + 8 * half) * 2));
+    qf[s] = bload16(rQ, (uint32_t)(my_q * D + 16 * s + 8 * half) * 2);
+    dof[s] = bload16(rdO, (uint32_t)(my_q * D + 16 * s + 8 * half) * 2);
   }
   const float neg_lse2 = bload4f(rL, (uint32_t)my_q * 4);   // -LSE log2(e)
   const float Di = bload4f(rD, (uint32_t)my_q * 4);
@@ -439,10 +441,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int k = 0; k < KSTEPS; ++k) {
-        const bf16x8 ak = *(const bf16x8*)(sK + tile_off<D>(t * 32 + l32, 2 * k + half));
-        const bf16x8 av = *(const bf16x8*)(sV + tile_off<D>(t * 32 + l32, 2 * k + half));
-        s[t] = mfma_bf16(ak, qf[k], k == 0 ? zero16() : s[t]);
-        dp[t] = mfma_bf16(av, dof[k], k == 0 ? zero16() : dp[t]);
+        const u32x4 ak = *(const u32x4*)(sK + tile_off<D>(t * 32 + l32, 2 * k + half));
+        const u32x4 av = *(const u32x4*)(sV + tile_off<D>(t * 32 + l32, 2 * k + half));
+        s[t] = E::mfma(ak, qf[k], k == 0 ? zero16() : s[t]);
+        dp[t] = E::mfma(av, dof[k], k == 0 ? zero16() : dp[t]);
       }
     const bool need_mask = (CAUSAL && kb + kQBN - 1 > q0 + wave * 32) || (kb + kQBN > N);
     const int lim = min(CAUSAL ? my_q : N - 1, N - 1) - kb - 4 * half;
@@ -457,13 +459,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
           if (t * 32 + 8 * (i >> 2) + (i & 3) > lim) p0 = 0.f;
           if (t * 32 + 8 * ((i + 1) >> 2) + ((i + 1) & 3) > lim) p1 = 0.f;
         }
-        db[2 * t + (i >> 3)][(i & 7) >> 1] = pack_bf16(p0 * (dp[t][i] - Di), p1 * (dp[t][i + 1] - Di));
+        db[2 * t + (i >> 3)][(i & 7) >> 1] = E::pack(p0 * (dp[t][i] - Di), p1 * (dp[t][i + 1] - Di));
       }
     // dQ^T += K^T dS^T  (contraction over the 64 keys)
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int t = 0; t < DT; ++t) dq[t] = mfma_bf16(tr_operand<D>(sK, u, t, lane), as_bf16x8(db[u]), dq[t]);
+      for (int t = 0; t < DT; ++t) dq[t] = E::mfma(tr_operand<D>(sK, u, t, lane), db[u], dq[t]);
   };
   for (int j = 0; j < n_kv; j += 2) {
     if (j + 1 < n_kv) load(j + 1, sK1, sV1);
@@ -488,35 +490,39 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     }
 }
 
-template <int D, bool CAUSAL>
+template <class E, int D, bool CAUSAL>
 hipError_t launch(const BwdArgs& a) {
+  using T = typename E::elem;
   const long long rows = (long long)a.B * a.H * a.N;
   constexpr int rows_per_block = kThreads / (D / 8);
   float* NLvec = a.Dvec + rows;   // -LSE log2(e), after D in the workspace
-  hipLaunchKernelGGL((bwd_dot_kernel<D>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
-                     dim3(kThreads), 0, a.stream, (const __bf16*)a.O, (const __bf16*)a.dO, a.LSE,
+  hipLaunchKernelGGL((bwd_dot_kernel<E, D>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
+                     dim3(kThreads), 0, a.stream, (const T*)a.O, (const T*)a.dO, a.LSE,
                      a.Dvec, NLvec, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float sl2 = a.scale * kLog2e;
   const int n_kt = (a.N + kKvBN - 1) / kKvBN;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(a.B * a.H * n_kt), dim3(kThreads), 0,
-                     a.stream, (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V,
-                     (const __bf16*)a.dO, NLvec, a.Dvec, a.dK, a.dV, a.N, a.scale, sl2, n_kt);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL>), dim3(a.B * a.H * n_kt), dim3(kThreads), 0,
+                     a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V, (const T*)a.dO, NLvec, a.Dvec, a.dK, a.dV, a.N, a.scale, sl2, n_kt);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_qt = (a.N + kQBM - 1) / kQBM;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(a.B * a.H * n_qt), dim3(kThreads), 0,
-                     a.stream, (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V,
-                     (const __bf16*)a.dO, NLvec, a.Dvec, a.dQ, a.N, a.scale, sl2, n_qt);
+  hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL>), dim3(a.B * a.H * n_qt), dim3(kThreads), 0,
+                     a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V, (const T*)a.dO, NLvec, a.Dvec, a.dQ, a.N, a.scale, sl2, n_qt);
   return hipGetLastError();
+}
+
+template <class E>
+hipError_t launch_e(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? launch<E, 64, true>(a) : launch<E, 64, false>(a);
+  return a.causal ? launch<E, 128, true>(a) : launch<E, 128, false>(a);
 }
 
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? launch<64, true>(a) : launch<64, false>(a);
-  return a.causal ? launch<128, true>(a) : launch<128, false>(a);
+  return a.dtype == 2 ? launch_e<F16>(a) : launch_e<Bf16>(a);
 }
 
 }  // namespace fa

@@ -43,9 +43,10 @@ constexpr int kDecThreads = 512;
 constexpr int kHeadsPerWave = 4;
 constexpr int kHeadsPerGroup = 32;   // heads per workgroup: whole 8 KiB token rows at H = 32
 
+template <class E>
 __global__ __launch_bounds__(kDecThreads, 1) void decode_partial_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k_pool,
-    const __bf16* __restrict__ v_pool, const int32_t* __restrict__ block_table,
+    const typename E::elem* __restrict__ q, const typename E::elem* __restrict__ k_pool,
+    const typename E::elem* __restrict__ v_pool, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int H, int KVH, int max_blocks_per_seq, int num_blocks,
     float scale_log2, float* __restrict__ part_o, float* __restrict__ part_ml, int part_tokens,
     int n_parts) {
@@ -79,8 +80,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_partial_kernel(
     const u32x4 w = bload16(rq, (uint32_t)(hh * kDecD + ch * 8) * 2);   // this query head
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      qv[2 * e] = bf16lo(w[e]);
-      qv[2 * e + 1] = bf16hi(w[e]);
+      qv[2 * e] = E::lo(w[e]);
+      qv[2 * e + 1] = E::hi(w[e]);
     }
   }
 
@@ -119,8 +120,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_partial_kernel(
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        part = fmaf(qv[2 * e], bf16lo(kr[u][e]), part);
-        part = fmaf(qv[2 * e + 1], bf16hi(kr[u][e]), part);
+        part = fmaf(qv[2 * e], E::lo(kr[u][e]), part);
+        part = fmaf(qv[2 * e + 1], E::hi(kr[u][e]), part);
       }
       float x = group_sum<16>(part) * scale_log2;
       if (u >= n_valid) x = kNegInf;
@@ -144,8 +145,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_partial_kernel(
       if (u < n_valid) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[2 * e] = fmaf(pu, bf16lo(vr[u][e]), acc[2 * e]);
-          acc[2 * e + 1] = fmaf(pu, bf16hi(vr[u][e]), acc[2 * e + 1]);
+          acc[2 * e] = fmaf(pu, E::lo(vr[u][e]), acc[2 * e]);
+          acc[2 * e + 1] = fmaf(pu, E::hi(vr[u][e]), acc[2 * e + 1]);
         }
       }
     }
@@ -189,10 +190,11 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+template <class E>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ seq_lens, int num_seqs, int H, int part_tokens, int n_parts,
-    __bf16* __restrict__ o, float* __restrict__ lse) {
+    typename E::elem* __restrict__ o, float* __restrict__ lse) {
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (gw >= num_seqs * H) return;
   const int lane = threadIdx.x & 63;
@@ -229,29 +231,34 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   }
   L = wave_sum(L);
   const float inv = 1.f / L;
-  *(uint32_t*)(o + ((size_t)s * H + head) * kDecD + 2 * lane) = pack_bf16(a0 * inv, a1 * inv);
+  *(uint32_t*)(o + ((size_t)s * H + head) * kDecD + 2 * lane) = E::pack(a0 * inv, a1 * inv);
   if (lane == 0) lse[(size_t)s * H + head] = (m_star + fast_log2(L)) * kLn2;
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a) {
+template <class E>
+hipError_t launch_decode_e(const DecodeArgs& a) {
+  using T = typename E::elem;
   const size_t n_entries = (size_t)a.num_seqs * a.n_parts * a.H;
   float* part_o = a.part;
   float* part_ml = a.part + n_entries * kDecD;
   dim3 grid(a.n_parts, (a.H + kHeadsPerGroup - 1) / kHeadsPerGroup, a.num_seqs);
-  hipLaunchKernelGGL(decode_partial_kernel, grid, dim3(kDecThreads), 0, a.stream,
-                     (const __bf16*)a.q, (const __bf16*)a.k_pool, (const __bf16*)a.v_pool,
-                     a.block_table, a.seq_lens, a.H, a.KVH > 0 ? a.KVH : a.H,
-                     a.max_blocks_per_seq, a.num_blocks,
+  hipLaunchKernelGGL((decode_partial_kernel<E>), grid, dim3(kDecThreads), 0, a.stream,
+                     (const T*)a.q, (const T*)a.k_pool, (const T*)a.v_pool, a.block_table,
+                     a.seq_lens, a.H, a.KVH > 0 ? a.KVH : a.H, a.max_blocks_per_seq, a.num_blocks,
                      a.scale * kLog2e, part_o, part_ml, a.part_tokens, a.n_parts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int waves = a.num_seqs * a.H;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3((waves + 3) / 4), dim3(256), 0, a.stream, part_o,
-                     part_ml, a.seq_lens, a.num_seqs, a.H, a.part_tokens, a.n_parts,
-                     (__bf16*)a.o, a.lse);
+  hipLaunchKernelGGL((decode_merge_kernel<E>), dim3((waves + 3) / 4), dim3(256), 0, a.stream,
+                     part_o, part_ml, a.seq_lens, a.num_seqs, a.H, a.part_tokens, a.n_parts, (T*)a.o,
+                     a.lse);
   return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a) {
+  return a.dtype == 2 ? launch_decode_e<F16>(a) : launch_decode_e<Bf16>(a);
 }
 
 }  // namespace fa

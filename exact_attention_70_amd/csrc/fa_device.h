@@ -92,6 +92,55 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 __device__ __forceinline__ float bf16lo(uint32_t u) { return as_f32(u << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t u) { return as_f32(u & 0xffff0000u); }
 
+// 16-bit input formats.  Operands travel as raw 16-byte register patterns
+// (u32x4, eight values); the format decides the matrix instruction, the
+// rounding of fp32 results back to 16 bits (round to nearest even), the
+// widening of a packed pair, and a two-element dot product.
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
+
+struct Bf16 {
+  using elem = __bf16;
+  static constexpr int code = 1;
+  __device__ static __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ uint32_t pack(float lo, float hi) { return pack_bf16(lo, hi); }
+  __device__ static __forceinline__ float lo(uint32_t u) { return bf16lo(u); }
+  __device__ static __forceinline__ float hi(uint32_t u) { return bf16hi(u); }
+  // lo(a) * lo(b) + hi(a) * hi(b) + c, fp32 accumulation
+  __device__ static __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+  }
+  static constexpr uint32_t kOnes = 0x3f803f80u;   // the pair (1, 1)
+};
+
+struct F16 {
+  using elem = _Float16;
+  static constexpr int code = 2;
+  __device__ static __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ uint32_t pack(float lo, float hi) {
+    f16x2 h = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, h);
+  }
+  __device__ static __forceinline__ float lo(uint32_t u) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu));
+  }
+  __device__ static __forceinline__ float hi(uint32_t u) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+  }
+  __device__ static __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c,
+                                  false);
+  }
+  static constexpr uint32_t kOnes = 0x3c003c00u;
+};
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -53,10 +53,10 @@ constexpr int kVLead = 2;        // V operand read pairs in flight ahead of thei
 // it by more than this (base-2 exponent): probabilities stay <= 2^kSlack.
 constexpr float kSlack = 8.f;
 
-template <int D, bool CAUSAL, int BN, int OCC>
+template <class E, int D, bool CAUSAL, int BN, int OCC>
 __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int N, int Nk, int delta, float scale_log2,
+    const typename E::elem* __restrict__ Q, const typename E::elem* __restrict__ K,
+    const typename E::elem* __restrict__ V, typename E::elem* __restrict__ O, float* __restrict__ LSE, int N, int Nk, int delta, float scale_log2,
     int n_qtiles) {
   // scale_log2 = scale * log2(e): scores are handled in base 2.  N query rows
   // and Nk key rows per head; with CAUSAL, key j is visible to row i iff
@@ -115,16 +115,16 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
   dma_rows<D, BN, kThreads / 64>(rK, sK0, 0, wave, lane);
   dma_rows<D, BN, kThreads / 64>(rV, sV0, 0, wave, lane);
   const int my_q_row = q0 + wave * 32 + l32;
-  bf16x8 qf[KSTEPS];
+  u32x4 qf[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s)
-    qf[s] = as_bf16x8(bload16(rQ, (uint32_t)(my_q_row * D + 16 * s + 8 * half) * 2));
+    qf[s] = bload16(rQ, (uint32_t)(my_q_row * D + 16 * s + 8 * half) * 2);
   // The softmax takes its maximum over raw scores and folds the scale into one
   // multiply-add, which needs a positive multiplier: for a negative scale,
   // negate Q once (exact in bf16) and use |scale|.
   if (scale_log2 < 0.f) {
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(as_u32x4(qf[s]) ^ 0x80008000u);
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = qf[s] ^ 0x80008000u;
     scale_log2 = -scale_log2;
   }
   barrier_all();                                    // K_0, V_0 landed
@@ -140,8 +140,6 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
   float m_run = kNegInf;   // running max of scale*log2(e)*score (through the last reduced tile)
   float l_run = 0.f;       // this lane's share of the running denominator
   float alpha = 1.f;       // exp2(m_old - m_new) of the last reduced tile
-  const float one = 1.0f;
-  const bf16x2 ones = {(__bf16)one, (__bf16)one};
   constexpr int NQ = NSUB * KSTEPS;     // matrix ops of S = K Q^T per tile
   constexpr int NP = DT * NU;           // matrix ops of O^T += V^T P^T per tile
   constexpr int KLEAD = kKLead;
@@ -173,7 +171,7 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
   };
   auto k_operand = [&](const unsigned char* sK, int idx) {
     const int t = idx / KSTEPS, k = idx % KSTEPS;
-    return *(const bf16x8*)(sK + kofs[k] + t * 32 * D * 2);
+    return *(const u32x4*)(sK + kofs[k] + t * 32 * D * 2);
   };
   auto v_operand = [&](const unsigned char* sV, int idx) {
     const int t = idx / NU, u = idx % NU;
@@ -220,7 +218,7 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     for (int t = 0; t < NSUB; ++t) sa[t] = zero16();
 #pragma unroll
     for (int idx = 0; idx < NQ; ++idx)
-      sa[idx / KSTEPS] = mfma_bf16(k_operand(sK0, idx), qf[idx % KSTEPS], sa[idx / KSTEPS]);
+      sa[idx / KSTEPS] = E::mfma(k_operand(sK0, idx), qf[idx % KSTEPS], sa[idx / KSTEPS]);
     if (0 >= n_full) mask(sa, 0);
     float mx = kNegInf;
 #pragma unroll
@@ -245,24 +243,24 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
     u32x4 pb[NU];
     float rs = 0.f;
-    bf16x8 ka[KLEAD];
+    u32x4 ka[KLEAD];
 #pragma unroll
     for (int x = 0; x < KLEAD; ++x) ka[x] = k_operand(kcur, x);
 #pragma unroll
     for (int t = 0; t < NSUB; ++t) sn[t] = zero16();
 #pragma unroll
     for (int idx = 0; idx < NQ; ++idx) {
-      const bf16x8 a = ka[idx % KLEAD];
+      const u32x4 a = ka[idx % KLEAD];
       if (idx + KLEAD < NQ) ka[idx % KLEAD] = k_operand(kcur, idx + KLEAD);
-      sn[idx / KSTEPS] = mfma_bf16(a, qf[idx % KSTEPS], sn[idx / KSTEPS]);
+      sn[idx / KSTEPS] = E::mfma(a, qf[idx % KSTEPS], sn[idx / KSTEPS]);
 #pragma unroll
       for (int e = 0; e < PPER; e += 2) {
         const int flat = idx * PPER + e;
         const int t = flat / 16, i = flat % 16;
         const float p0 = fast_exp2(fmaf(so[t][i], scale_log2, neg_m));
         const float p1 = fast_exp2(fmaf(so[t][i + 1], scale_log2, neg_m));
-        const uint32_t pk = pack_bf16(p0, p1);
-        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, rs, false);
+        const uint32_t pk = E::pack(p0, p1);
+        rs = E::dot2(pk, E::kOnes, rs);
         pb[2 * t + (i >> 3)][(i & 7) >> 1] = pk;
       }
     }
@@ -276,7 +274,7 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     for (int idx = 0; idx < NP; ++idx) {
       const u32x4 a = va[idx % VLEAD];
       if (idx + VLEAD < NP) va[idx % VLEAD] = v_operand(vprev, idx + VLEAD);
-      o[idx / NU] = mfma_bf16(as_bf16x8(a), as_bf16x8(pb[idx % NU]), o[idx / NU]);
+      o[idx / NU] = E::mfma(a, pb[idx % NU], o[idx / NU]);
 #pragma unroll
       for (int e = 0; e < RPER; e += 2) {
         const int flat = idx * RPER + e;
@@ -306,14 +304,14 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
       for (int i = 0; i < 16; i += 2) {
         const float p0 = fast_exp2(fmaf(sl[t][i], scale_log2, neg_m));
         const float p1 = fast_exp2(fmaf(sl[t][i + 1], scale_log2, neg_m));
-        const uint32_t pk = pack_bf16(p0, p1);
-        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, rs, false);
+        const uint32_t pk = E::pack(p0, p1);
+        rs = E::dot2(pk, E::kOnes, rs);
         pb[2 * t + (i >> 3)][(i & 7) >> 1] = pk;
       }
     l_run = fmaf(l_run, alpha, rs);
 #pragma unroll
     for (int idx = 0; idx < NP; ++idx)
-      o[idx / NU] = mfma_bf16(as_bf16x8(v_operand(vl, idx)), as_bf16x8(pb[idx % NU]), o[idx / NU]);
+      o[idx / NU] = E::mfma(v_operand(vl, idx), pb[idx % NU], o[idx / NU]);
   };
   // The rest (at most one unmasked tile plus the tiles that straddle the
   // diagonal or the ragged end) runs with the mask on.  j is odd here, so
@@ -339,8 +337,8 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     for (int g = 0; g < 4; ++g) {
       const int d0 = t * 32 + 8 * g + 4 * half;
       u32x2 w;
-      w[0] = pack_bf16(o[t][4 * g] * inv, o[t][4 * g + 1] * inv);
-      w[1] = pack_bf16(o[t][4 * g + 2] * inv, o[t][4 * g + 3] * inv);
+      w[0] = E::pack(o[t][4 * g] * inv, o[t][4 * g + 1] * inv);
+      w[1] = E::pack(o[t][4 * g + 2] * inv, o[t][4 * g + 3] * inv);
       bstore8(w, rO, (uint32_t)(my_q * D + d0) * 2);
     }
   if (half == 0)
@@ -483,6 +481,11 @@ __global__ __launch_bounds__(256) void fill_empty_kernel(T* __restrict__ O, floa
 // LSE = M + ln(w_a + w_b); a side at LSE = -inf weighs nothing.  One thread
 // handles 16 bytes of a row; a row's threads sit in one wave, so the output
 // may be the same buffer as either input.
+template <typename T>
+struct Traits16 { using type = Bf16; };
+template <>
+struct Traits16<_Float16> { using type = F16; };
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const T* Oa, const float* La, const T* Ob,
                                                     const float* Lb, T* O, float* L, long long rows) {
@@ -507,7 +510,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const T* Oa, const float* La
   if constexpr (sizeof(T) == 2) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      r[e] = pack_bf16(ca * bf16lo(a[e]) + cb * bf16lo(b[e]), ca * bf16hi(a[e]) + cb * bf16hi(b[e]));
+    {
+      using E = typename Traits16<T>::type;
+      r[e] = E::pack(ca * E::lo(a[e]) + cb * E::lo(b[e]), ca * E::hi(a[e]) + cb * E::hi(b[e]));
+    }
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e) r[e] = as_u32(ca * as_f32(a[e]) + cb * as_f32(b[e]));
@@ -516,14 +522,22 @@ __global__ __launch_bounds__(256) void merge_kernel(const T* Oa, const float* La
   if (c == 0) L[row] = empty ? kNegInf : M + fast_log2(tot) * kLn2;
 }
 
-template <int D, bool CAUSAL, int BN = kBNDefault, int OCC = 2>
+template <class E, int D, bool CAUSAL, int BN = kBNDefault, int OCC = 2>
 hipError_t launch_bf16(const FwdArgs& a, int Nk, int delta) {
+  using T = typename E::elem;
   const int n_qtiles = (a.N + kBM - 1) / kBM;
   const int grid = a.B * a.H * n_qtiles;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, BN, OCC>), dim3(grid), dim3(kThreads), 0, a.stream,
-                     (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (__bf16*)a.O,
-                     a.LSE, a.N, Nk, delta, a.scale * kLog2e, n_qtiles);
+  hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, BN, OCC>), dim3(grid), dim3(kThreads), 0,
+                     a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V, (T*)a.O, a.LSE, a.N, Nk,
+                     delta, a.scale * kLog2e, n_qtiles);
   return hipGetLastError();
+}
+
+template <class E>
+hipError_t launch_16(const FwdArgs& a, int Nk, int delta, bool causal) {
+  if (a.d == 64)
+    return causal ? launch_bf16<E, 64, true>(a, Nk, delta) : launch_bf16<E, 64, false>(a, Nk, delta);
+  return causal ? launch_bf16<E, 128, true>(a, Nk, delta) : launch_bf16<E, 128, false>(a, Nk, delta);
 }
 
 template <int D>
@@ -551,21 +565,22 @@ hipError_t launch_fwd(const FwdArgs& a) {
     if (a.dtype == 1)
       hipLaunchKernelGGL((fill_empty_kernel<__bf16>), dim3(grid), dim3(256), 0, a.stream,
                          (__bf16*)a.O, a.LSE, rows, a.d);
+    else if (a.dtype == 2)
+      hipLaunchKernelGGL((fill_empty_kernel<_Float16>), dim3(grid), dim3(256), 0, a.stream,
+                         (_Float16*)a.O, a.LSE, rows, a.d);
     else
       hipLaunchKernelGGL((fill_empty_kernel<float>), dim3(grid), dim3(256), 0, a.stream,
                          (float*)a.O, a.LSE, rows, a.d);
     return hipGetLastError();
   }
   const int delta = causal ? (int)a.delta : 0;   // |delta| < max(N, Nk) here
-  if (a.dtype == 1) {
-    if (a.d == 64) return causal ? launch_bf16<64, true>(a, Nk, delta) : launch_bf16<64, false>(a, Nk, delta);
-    return causal ? launch_bf16<128, true>(a, Nk, delta) : launch_bf16<128, false>(a, Nk, delta);
-  }
+  if (a.dtype == 1) return launch_16<Bf16>(a, Nk, delta, causal);
+  if (a.dtype == 2) return launch_16<F16>(a, Nk, delta, causal);
   return a.d == 64 ? launch_f32<64>(a, Nk, delta, causal) : launch_f32<128>(a, Nk, delta, causal);
 }
 
 hipError_t launch_merge(const MergeArgs& a) {
-  const int tpr = a.d * (a.dtype == 1 ? 2 : 4) / 16;
+  const int tpr = a.d * (a.dtype != 0 ? 2 : 4) / 16;
   const long long threads = a.rows * tpr;
   const unsigned grid = (unsigned)((threads + 255) / 256);
   if (a.dtype == 1) {
@@ -575,6 +590,15 @@ hipError_t launch_merge(const MergeArgs& a) {
     else
       hipLaunchKernelGGL((merge_kernel<__bf16, 128>), dim3(grid), dim3(256), 0, a.stream,
                          (const __bf16*)a.Oa, a.La, (const __bf16*)a.Ob, a.Lb, (__bf16*)a.O, a.L, a.rows);
+  } else if (a.dtype == 2) {
+    if (a.d == 64)
+      hipLaunchKernelGGL((merge_kernel<_Float16, 64>), dim3(grid), dim3(256), 0, a.stream,
+                         (const _Float16*)a.Oa, a.La, (const _Float16*)a.Ob, a.Lb, (_Float16*)a.O,
+                         a.L, a.rows);
+    else
+      hipLaunchKernelGGL((merge_kernel<_Float16, 128>), dim3(grid), dim3(256), 0, a.stream,
+                         (const _Float16*)a.Oa, a.La, (const _Float16*)a.Ob, a.Lb, (_Float16*)a.O,
+                         a.L, a.rows);
   } else {
     if (a.d == 64)
       hipLaunchKernelGGL((merge_kernel<float, 64>), dim3(grid), dim3(256), 0, a.stream,

@@ -51,6 +51,7 @@ struct BwdArgs {
   float scale;
   bool causal;
   hipStream_t stream;
+  int dtype = 1;   // 1 = bf16, 2 = fp16 inputs
 };
 
 struct DecodeArgs {
@@ -68,6 +69,7 @@ struct DecodeArgs {
   int n_parts;      // partitions per sequence (max)
   hipStream_t stream;
   int KVH = 0;      // key/value heads in the pools (0: same as H)
+  int dtype = 1;    // 1 = bf16, 2 = fp16
 };
 
 struct AppendArgs {

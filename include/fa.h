@@ -53,7 +53,11 @@ typedef enum {
   FA_ERR_HIP = -8          /* the HIP runtime reported an error                   */
 } fa_status;
 
-typedef enum { FA_DT_F32 = 0, FA_DT_BF16 = 1 } fa_dtype;
+/* Element formats.  FA_DT_F16 is IEEE half: the explainer's mixed-precision
+ * example is fp16 inputs with 32-bit matrix accumulation (dcwnkz.com
+ * explainer, mixed-precision technique), and its softmax appendix shows why
+ * the maximum must be subtracted first (e^12 already overflows fp16). */
+typedef enum { FA_DT_F32 = 0, FA_DT_BF16 = 1, FA_DT_F16 = 2 } fa_dtype;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fa_status_string(int status);
@@ -74,17 +78,18 @@ int fa_version(void);
  * softmax" and "FlashAttention itself").  The N x N matrix never reaches
  * memory.
  *
- *   Q, K, V  in   [B,H,N,d], dtype `dtype` (FA_DT_BF16 or FA_DT_F32)
- *   O        out  [B,H,N,d], same dtype as the inputs (bf16: round-to-nearest-even)
+ *   Q, K, V  in   [B,H,N,d], dtype `dtype` (FA_DT_BF16, FA_DT_F16 or FA_DT_F32)
+ *   O        out  [B,H,N,d], same dtype as the inputs (16-bit: round-to-nearest-even)
  *   LSE      out  [B,H,N] fp32, natural-log log-sum-exp of the visible scaled scores
  *   B, H, N  >= 0, >= 1, >= 1 (B == 0 is a no-op); N <= 1<<20
  *   d        64 or 128 (else FA_ERR_UNSUPPORTED)
  *   scale    finite; multiplies the raw scores (1/sqrt(d) in the usual setting)
  *   causal   0 = every key visible; non-zero = key j visible to query i iff j <= i
  *
- * bf16 inputs are multiplied on the matrix cores with fp32 accumulation; the
- * softmax weights are rounded to bf16 before the P V product.  fp32 inputs are
- * multiplied with fp32 matrix instructions throughout.
+ * 16-bit inputs (bf16, fp16) are multiplied on the matrix cores with fp32
+ * accumulation; the softmax weights are rounded to the input format before
+ * the P V product.  fp32 inputs are multiplied with fp32 matrix instructions
+ * throughout.
  */
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
            int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
@@ -124,7 +129,7 @@ int fa_fwd_offset(const void* Q, const void* K, const void* V, void* O, float* L
  *   O = (w_a O_a + w_b O_b) / (w_a + w_b),  LSE = M + ln(w_a + w_b).
  * A side with LSE = -inf weighs nothing; if both are -inf, O = 0, LSE = -inf.
  *
- *   O_a, O_b, O   [B,H,N,d] dtype `dtype` (bf16 results round to nearest even)
+ *   O_a, O_b, O   [B,H,N,d] dtype `dtype` (16-bit results round to nearest even)
  *   LSE_a, LSE_b, LSE  [B,H,N] fp32
  *   O may be the same buffer as O_a or O_b, and LSE the same as LSE_a or
  *   LSE_b (in-place accumulation); a partial overlap returns FA_ERR_INVALID.
@@ -152,10 +157,10 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  *   dV = P^T dO;  dP = dO V^T;  D_i = sum_d dO_id O_id;  dS = P o (dP - D);
  *   dQ = scale dS K;  dK = scale dS^T Q.
  *
- *   Q, K, V, O, dO  in   [B,H,N,d] bf16 (O is the forward's output)
+ *   Q, K, V, O, dO  in   [B,H,N,d] bf16 or fp16, per `dtype` (O is the forward's output)
  *   LSE             in   [B,H,N] fp32 from fa_fwd with the same scale/causal
  *   dQ, dK, dV      out  [B,H,N,d] fp32 (fully overwritten)
- *   d               64 or 128; dtype must be FA_DT_BF16
+ *   d               64 or 128; dtype FA_DT_BF16 or FA_DT_F16 (16-bit inputs)
  *   workspace       device buffer of >= fa_bwd_workspace_size() bytes, 16-B aligned
  * The result is deterministic (no atomics).
  */
@@ -187,12 +192,12 @@ size_t fa_paged_decode_workspace_size(int num_seqs, int H, int d, int max_blocks
  * the rescaling rule of the online softmax (HPC notes, section "Long context
  * and sequence parallelism").
  *
- *   q            in   [num_seqs, H, d] bf16
- *   k_pool/v_pool in  [num_blocks, block_size, H, d] bf16
+ *   q            in   [num_seqs, H, d] bf16 or fp16, per `dtype`
+ *   k_pool/v_pool in  [num_blocks, block_size, H, d], same dtype
  *   block_table  in   [num_seqs, max_blocks_per_seq] int32 physical block ids;
  *                     entries past a sequence's last block are never read
  *   seq_lens     in   [num_seqs] int32, 1 <= seq_lens[s] <= max_blocks_per_seq*block_size
- *   o            out  [num_seqs, H, d] bf16
+ *   o            out  [num_seqs, H, d], same dtype
  *   lse          out  [num_seqs, H] fp32 (natural log)
  *   block_size   16 (else FA_ERR_UNSUPPORTED); d 128 (else FA_ERR_UNSUPPORTED)
  *   H            a multiple of 4
@@ -218,7 +223,7 @@ int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
  * with grouped-query attention kv_heads < query heads and the KV cache shrinks
  * accordingly).  One cached byte then serves H / KVH query heads.
  *
- *   k_pool/v_pool in  [num_blocks, block_size, KVH, d] bf16
+ *   k_pool/v_pool in  [num_blocks, block_size, KVH, d], dtype `dtype`
  *   KVH          >= 1 and divides H (else FA_ERR_SHAPE)
  * Every other argument, the workspace size (fa_paged_decode_workspace_size
  * with the query head count H) and the error behaviour are those of
@@ -254,7 +259,7 @@ size_t fa_paged_kv_append_workspace_size(int num_seqs);
  * needs a block when the stack is empty, or whose block id is outside the
  * pool is left unchanged (nothing written) and counted in *n_failed.
  *
- *   k_new, v_new   in     [num_seqs, KVH, d], dtype `dtype` (bf16 or fp32)
+ *   k_new, v_new   in     [num_seqs, KVH, d], dtype `dtype` (bf16, fp16 or fp32)
  *   k_pool, v_pool in/out [num_blocks, block_size, KVH, d], same dtype
  *   block_table    in/out [num_seqs, max_blocks_per_seq] int32
  *   seq_lens       in/out [num_seqs] int32

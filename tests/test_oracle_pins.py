@@ -201,6 +201,14 @@ def test_forward_batched_matches_per_head():
         np.testing.assert_array_equal(lse, l2)
 
 
+def test_f16_inputs_converted_exactly():
+    x = workloads.attention_inputs(1, 1, 4, 8, "f16", seed=9, in_scale=300.0)
+    f = A.to_f64(x["q"])
+    assert x["q"].dtype == torch.float16
+    assert np.array_equal(f, x["q"].float().double().numpy())
+    assert np.abs(f).max() > 256            # values beyond bf16's 8-bit mantissa steps survive
+
+
 def test_bf16_inputs_converted_exactly():
     x = workloads.attention_inputs(1, 1, 4, 8, "bf16", seed=9)
     f = A.to_f64(x["q"])

@@ -1,0 +1,115 @@
+"""GPU parity of the fp16 input path (forward, offset forward + merge,
+backward, paged decode) against the fp64 oracle on the same seeded inputs.
+
+Tolerance for fp16 inputs, derived from the arithmetic: the products are exact
+in fp32 and accumulate in fp32; the error comes from rounding the weights P to
+fp16 (relative 2^-11) before P V and rounding O to fp16 (relative 2^-11).
+With |V| <= 5 (N(0,1) draws at these sizes) a weighted average then errs by at
+most about 2 * 2^-11 * 5 ~ 5e-3 in O and 2^-11 in LSE; the bound used is 1e-2.
+Gradients use the bf16 bound 5e-2.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from conftest import max_abs
+from exact_attention_70_amd import binding
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+TOL_GRAD = 5e-2
+
+
+def _fwd_check(gpu, x, causal, scale, qo=None, ko=None):
+    q, k, v = (x[n].to(gpu) for n in "qkv")
+    if qo is None:
+        o, lse = binding.fwd(q, k, v, causal=causal, scale=scale)
+        ref = oracle.attention_forward(x["q"], x["k"], x["v"], scale, causal)
+    else:
+        o, lse = binding.fwd_offset(q, k, v, q_offset=qo, k_offset=ko, causal=causal, scale=scale)
+        ref = oracle.attention_forward(x["q"], x["k"], x["v"], scale, causal, q_offset=qo,
+                                       k_offset=ko)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float16
+    o, lse = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    for (b, h), (ro, rl) in ref.items():
+        fin = np.isfinite(rl)
+        assert np.all(np.isfinite(o[b, h]))
+        assert np.all(lse[b, h][~fin] == -np.inf)
+        assert max_abs(o[b, h], ro) <= TOL
+        assert max_abs(lse[b, h][fin], rl[fin]) <= TOL
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 65, 129, 300])
+def test_fwd_f16(gpu, d, causal, N):
+    x = workloads.attention_inputs(2, 3, N, d, "f16", seed=6000 + N + d + causal)
+    _fwd_check(gpu, x, causal, 1.0 / math.sqrt(d))
+
+
+def test_fwd_f16_scores_beyond_fp16_exp_range(gpu):
+    """Scores well past 12 natural units: e^12 alone is beyond fp16's 65504
+    (the explainer's softmax appendix), so only the max-subtracted softmax can
+    give a finite result."""
+    x = workloads.attention_inputs(1, 2, 200, 128, "f16", seed=6100, in_scale=2.5)
+    q = x["q"].double()
+    k = x["k"].double()
+    assert (q @ k.transpose(-1, -2)).abs().max().item() / math.sqrt(128) > 12
+    _fwd_check(gpu, x, True, 1.0 / math.sqrt(128))
+
+
+def test_fwd_offset_and_merge_f16(gpu):
+    """A two-block ring step in fp16 equals the one-shot causal forward."""
+    n, d = 256, 128
+    x = workloads.attention_inputs(1, 2, 2 * n, d, "f16", seed=6200)
+    q, k, v = (x[t].to(gpu) for t in "qkv")
+    qr = q[:, :, n:].contiguous()
+    a = binding.fwd_offset(qr, k[:, :, :n].contiguous(), v[:, :, :n].contiguous(), q_offset=n,
+                           k_offset=0, causal=True)
+    b = binding.fwd_offset(qr, k[:, :, n:].contiguous(), v[:, :, n:].contiguous(), q_offset=n,
+                           k_offset=n, causal=True)
+    o, l = binding.merge(a[0], a[1], b[0], b[1])
+    torch.cuda.synchronize()
+    ref = oracle.attention_forward(x["q"], x["k"], x["v"], 1.0 / math.sqrt(d), True,
+                                   rows=np.arange(n, 2 * n))
+    for (bb, h), (ro, rl) in ref.items():
+        assert max_abs(o[bb, h].double().cpu().numpy(), ro) <= TOL
+        assert max_abs(l[bb, h].double().cpu().numpy(), rl) <= TOL
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_f16(gpu, d, causal):
+    B, H, N = 1, 2, 200
+    scale = 1.0 / math.sqrt(d)
+    x = workloads.attention_inputs(B, H, N, d, "f16", seed=6300 + d + causal, with_do=True)
+    q, k, v, do = (x[n].to(gpu) for n in ("q", "k", "v", "do"))
+    o, lse = binding.fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = binding.bwd(q, k, v, o, do, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward(x["q"], x["k"], x["v"], x["do"], scale, causal)
+    for (b, h), r in ref.items():
+        assert max_abs(dq[b, h].double().cpu().numpy(), r["dq"]) <= TOL_GRAD
+        assert max_abs(dk[b, h].double().cpu().numpy(), r["dk"]) <= TOL_GRAD
+        assert max_abs(dv[b, h].double().cpu().numpy(), r["dv"]) <= TOL_GRAD
+
+
+@pytest.mark.parametrize("kvh", [32, 8])
+def test_paged_decode_f16(gpu, kvh):
+    p = workloads.paged_inputs(10, 32, 128, 16, 1, 700, seed=6400 + kvh, dtype="f16", kv_heads=kvh,
+                               pad_value=float("nan"))
+    pd = {k: (v.to(gpu) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+    o, lse = binding.paged_decode(pd["q"], pd["k_pool"], pd["v_pool"], pd["block_table"],
+                                  pd["seq_lens"], block_size=16, scale=128 ** -0.5)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float16
+    ro, rl = oracle.paged_decode(p["q"], p["k_pool"], p["v_pool"], p["block_table"], p["seq_lens"],
+                                 16, 128 ** -0.5)
+    assert max_abs(o.double().cpu().numpy(), ro) <= TOL
+    assert max_abs(lse.double().cpu().numpy(), rl) <= TOL

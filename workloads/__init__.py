@@ -29,7 +29,7 @@ __all__ = [
     "seed_for",
 ]
 
-_TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+_TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 @dataclass(frozen=True)
