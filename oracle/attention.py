@@ -79,7 +79,7 @@ __all__ = [
     "online_softmax", "attention_forward_head", "attention_forward",
     "attention_backward_head", "attention_backward", "gather_tokens",
     "paged_decode", "grad_v", "grad_p", "row_dot", "grad_s", "grad_q", "grad_k",
-    "merge_partials", "kv_head_of", "paged_append",
+    "merge_partials", "kv_head_of", "paged_append", "paged_prefill",
 ]
 
 
@@ -417,3 +417,44 @@ def paged_append(k_pool, v_pool, block_table, seq_lens, free_list, free_count: i
         lens[s] = t + 1
     return {"k_pool": kp, "v_pool": vp, "block_table": table, "seq_lens": lens,
             "free_count": top, "n_failed": failed}
+
+
+def paged_prefill(q, q_start, k_pool, v_pool, block_table, seq_lens, block_size: int, scale: float,
+                  causal: bool = True, seqs=None, workers: int | None = None):
+    """Prefill of a chunk of new queries per sequence over a paged KV cache.
+
+    Sequence s holds seq_lens[s] cached tokens (its chunk's own K/V included)
+    through its block table; its chunk has q_start[s+1] - q_start[s] queries,
+    packed as rows of q [total_q, H, d], and they are the sequence's last
+    tokens: query r of the chunk sits at position seq_lens[s] - n_s + r, so the
+    causal rule is the offset one with q_offset = seq_lens[s] - n_s, k_offset 0
+    (HPC notes, "Prefill, Decode and inference scheduling": prefill builds the
+    cache for a whole prompt at once).  Query head h reads cached head
+    kv_head_of(h, H, KVH).  Returns (o [total_q, H, d], lse [total_q, H]) for
+    the rows of ``seqs`` (default all), float64.
+    """
+    table = np.asarray(block_table.numpy() if hasattr(block_table, "numpy") else block_table)
+    lens = np.asarray(seq_lens.numpy() if hasattr(seq_lens, "numpy") else seq_lens)
+    starts = np.asarray(q_start.numpy() if hasattr(q_start, "numpy") else q_start)
+    seqs = list(range(table.shape[0])) if seqs is None else list(seqs)
+    H, d = q.shape[1], q.shape[2]
+    KVH = k_pool.shape[2]
+    qf = to_f64(q)
+    o = np.zeros((qf.shape[0], H, v_pool.shape[3]))
+    lse = np.full((qf.shape[0], H), -np.inf)
+
+    def one(s):
+        L = int(lens[s])
+        a, b = int(starts[s]), int(starts[s + 1])
+        K = gather_tokens(k_pool, table[s], L, block_size)
+        V = gather_tokens(v_pool, table[s], L, block_size)
+        res = []
+        for h in range(H):
+            g = kv_head_of(h, H, KVH)
+            res.append(attention_forward_head(qf[a:b, h], K[:, g], V[:, g], scale, causal,
+                                              q_offset=L - (b - a), k_offset=0))
+        return a, b, res
+    for a, b, res in _pool_map(one, seqs, workers):
+        for h, (oh, lh) in enumerate(res):
+            o[a:b, h], lse[a:b, h] = oh, lh
+    return o, lse

@@ -524,6 +524,43 @@ def check_paged_append(seed=9):
     assert expect_fail >= 1                            # the sequence at capacity
 
 
+def check_paged_prefill(seed=10):
+    """A prefill chunk over a paged cache equals: the offset forward over the
+    same tokens laid out contiguously (built by an independent scatter), plain
+    causal attention when the chunk is the whole sequence, the paged decode
+    when the chunk is one token, and the 50-digit definition."""
+    rng = np.random.default_rng(seed)
+    H, KVH, d, bs = 4, 2, 3, 4
+    lens = [1, 5, 9, 12]
+    chunks = [1, 3, 9, 4]                    # the last 'chunk' tokens of each sequence are queries
+    Kc = [rng.standard_normal((L, KVH, d)) for L in lens]
+    Vc = [rng.standard_normal((L, KVH, d)) for L in lens]
+    kp, vp, table = _scatter_to_pool(Kc, Vc, lens, bs, KVH, d, seed)
+    starts = np.concatenate([[0], np.cumsum(chunks)])
+    q = rng.standard_normal((starts[-1], H, d))
+    o, lse = A.paged_prefill(q, starts, kp, vp, table, np.array(lens), bs, 0.45)
+    for s_, (L, n) in enumerate(zip(lens, chunks)):
+        a, b = starts[s_], starts[s_ + 1]
+        for h in range(H):
+            g = h // (H // KVH)
+            # the 50-digit definition with the chunk at the end of the sequence
+            Od, Ld = brute.attention_decimal(q[a:b, h], Kc[s_][:, g], Vc[s_][:, g], 0.45, True,
+                                             q_offset=L - n, k_offset=0)
+            np.testing.assert_allclose(o[a:b, h], np.array(Od, dtype=float), atol=1e-13)
+            np.testing.assert_allclose(lse[a:b, h], np.array(Ld, dtype=float), atol=1e-13)
+            if n == L:      # the whole sequence: ordinary causal attention
+                of, lf = A.attention_forward_head(q[a:b, h], Kc[s_][:, g], Vc[s_][:, g], 0.45, True)
+                np.testing.assert_allclose(o[a:b, h], of, atol=1e-14)
+        if n == 1:          # one new token: the paged decode
+            od, ld = A.paged_decode(q[a:b], kp, vp, table[s_:s_ + 1], np.array([L]), bs, 0.45)
+            np.testing.assert_allclose(o[a:b], od, atol=1e-14)
+            np.testing.assert_allclose(lse[a:b], ld, atol=1e-14)
+
+
+def test_paged_prefill_pins():
+    check_paged_prefill()
+
+
 def test_gqa_decode_pins():
     check_gqa_decode()
 
@@ -536,6 +573,7 @@ def _all_paged_pins():
     check_decode()
     check_gqa_decode()
     check_paged_append()
+    check_paged_prefill()
 
 
 # ---------------------------------------------------------- planted mistakes
@@ -693,7 +731,38 @@ def _append_variant(kind):
     return f
 
 
+def _prefill_top_aligned(q, q_start, k_pool, v_pool, block_table, seq_lens, block_size, scale,
+                         causal=True, seqs=None, workers=None):
+    """paged_prefill with the chunk's queries placed at positions 0.. (top-left
+    alignment) instead of at the end of the sequence."""
+    lens = np.asarray(seq_lens)
+    starts = np.asarray(q_start)
+    n = starts[1:] - starts[:-1]
+    return _REAL_PREFILL(q, q_start, k_pool, v_pool, block_table, n, block_size, scale, causal,
+                         seqs, workers) if np.all(n == lens) else _prefill_shift(
+        q, starts, k_pool, v_pool, block_table, lens, block_size, scale)
+
+
+def _prefill_shift(q, starts, k_pool, v_pool, block_table, lens, block_size, scale):
+    H = q.shape[1]
+    KVH = k_pool.shape[2]
+    o = np.zeros((q.shape[0], H, v_pool.shape[3]))
+    lse = np.full((q.shape[0], H), -np.inf)
+    for s_ in range(len(lens)):
+        a, b = int(starts[s_]), int(starts[s_ + 1])
+        K = A.gather_tokens(k_pool, block_table[s_], int(lens[s_]), block_size)
+        V = A.gather_tokens(v_pool, block_table[s_], int(lens[s_]), block_size)
+        for h in range(H):
+            g = A.kv_head_of(h, H, KVH)
+            o[a:b, h], lse[a:b, h] = A.attention_forward_head(A.to_f64(q)[a:b, h], K[:, g], V[:, g],
+                                                              scale, True)
+    return o, lse
+
+
+_REAL_PREFILL = A.paged_prefill
+
 PAGED_MUTANTS = {
+    "prefill_top_left_aligned": ("paged_prefill", _prefill_top_aligned),
     "gqa_modulo_heads": ("kv_head_of", lambda h, H, kvh: h % kvh),
     "gqa_reversed_groups": ("kv_head_of", lambda h, H, kvh: kvh - 1 - h // (H // kvh)),
     "append_pops_bottom": ("paged_append", _append_variant("pop_bottom")),
