@@ -9,6 +9,7 @@ benchmark shapes:
   * fa_paged_decode bf16 64 seqs x H=32 x d=128, lengths U[128,4096], 16-token blocks
   * the same decode with 8 cached key/value heads (grouped-query attention)
     and one paged KV append of a token per sequence
+  * chunked prefill over a paged cache: 8 sequences x 1024 new tokens
   * one ring-attention step at the long-context shape: fa_fwd_offset of the
     8192 queries against the previous 8192-token block, then fa_merge
 Inputs are resident in HBM before timing starts.  Each call is bracketed by
@@ -77,6 +78,7 @@ def main():
                     help="comma list of parts to run: fwd_c3, fwd_c3_f16, fwd_c2, fwd_c4, bwd_c4, "
                          "decode_c5, "
                          "decode_gqa_c5 (8 cached heads), append_c5 (paged KV append), "
+                         "prefill_gqa (chunked prefill over a paged cache), "
                          "ring_c3 (offset forward + merge of one ring step), copy_calib (a 1 GiB "
                          "device copy used to scale the HBM-traffic counters)")
     args = ap.parse_args()
@@ -201,6 +203,22 @@ def main():
             parts["append_c5"] = dict(fn=lambda: binding.paged_kv_append(
                 kn, vn, pgd["k_pool"], pgd["v_pool"], table_a, lens_a, pgd["free_list"], fc, nf,
                 block_size=16), bytes=2 * 2 * kn.numel() * 2)
+    if want("prefill_gqa"):
+        # chunked prefill: 8 sequences, a 1024-token chunk each at the end of
+        # 1500..4000 cached tokens, 32 query heads on 8 cached heads
+        lens_p = [1500, 2048, 2500, 3000, 3333, 3700, 4000, 1024]
+        pp = workloads.paged_inputs(len(lens_p), c5.H, c5.d, 16, 1, max(lens_p),
+                                    seed=workloads.seed_for(5) + 2, seq_lens=lens_p, kv_heads=8)
+        qp = workloads.prefill_queries([1024] * len(lens_p), c5.H, c5.d, seed=workloads.seed_for(5) + 3)
+        ppd = {kk: (vv.to(dev) if isinstance(vv, torch.Tensor) else vv) for kk, vv in pp.items()}
+        qpd, qsd = qp["q"].to(dev), qp["q_start"].to(dev)
+        op = torch.empty_like(qpd)
+        lsep = torch.empty(qpd.shape[0], c5.H, device=dev)
+        pairs = sum(sum(L - 1024 + r + 1 for r in range(1024)) for L in lens_p)
+        parts["prefill_gqa"] = dict(fn=lambda: binding.paged_prefill(
+            qpd, qsd, ppd["k_pool"], ppd["v_pool"], ppd["block_table"], ppd["seq_lens"],
+            block_size=16, max_q_len=1024, scale=c5.scale, out=op, lse=lsep),
+            flops=4 * c5.H * c5.d * pairs)
     if "copy_calib" in only:
         # plain device copy of known size: the HBM-traffic counters of the kernels
         # are scaled by what the same counters read for this copy
@@ -213,7 +231,8 @@ def main():
 
     order = [n for n in ("fwd_c3", "fwd_c3_f16", "fwd_c2", "fwd_c4", "bwd_c4", "decode_c5",
                          "decode_gqa_c5",
-                         "append_c5", "ring_c3_fwd", "ring_c3_merge", "copy_calib") if n in parts]
+                         "append_c5", "prefill_gqa", "ring_c3_fwd", "ring_c3_merge", "copy_calib")
+             if n in parts]
     for _ in range(args.warmup):
         for n in order:
             parts[n]["fn"]()

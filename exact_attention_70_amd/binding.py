@@ -23,7 +23,8 @@ FA_DT_F16 = 2
 
 EXPORTED = ("fa_status_string", "fa_version", "fa_fwd", "fa_fwd_offset", "fa_merge",
             "fa_bwd_workspace_size", "fa_bwd", "fa_paged_decode_workspace_size", "fa_paged_decode",
-            "fa_paged_decode_gqa", "fa_paged_kv_append_workspace_size", "fa_paged_kv_append")
+            "fa_paged_decode_gqa", "fa_paged_kv_append_workspace_size", "fa_paged_kv_append",
+            "fa_paged_prefill")
 
 _lib = None
 
@@ -75,6 +76,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fa_paged_kv_append_workspace_size.restype = sz
     lib.fa_paged_kv_append.argtypes = [vp] * 9 + [i] * 8 + [vp, sz, vp]
     lib.fa_paged_kv_append.restype = i
+    lib.fa_paged_prefill.argtypes = [vp] * 6 + [i] * 8 + [f, i, vp, vp, i, vp]
+    lib.fa_paged_prefill.restype = i
     if path is None:
         _lib = lib
     return lib
@@ -247,3 +250,22 @@ def paged_kv_append(k_new, v_new, k_pool, v_pool, block_table, seq_lens, free_li
         block_table.shape[1], k_pool.shape[0], free_list.numel(), _dtype_code(k_new),
         _ptr(workspace), workspace.numel(), _stream(k_new.device))
     _check(st, "fa_paged_kv_append")
+
+
+def paged_prefill(q, q_start, k_pool, v_pool, block_table, seq_lens, *, block_size: int,
+                  max_q_len: int, causal: bool = True, scale: float | None = None, out=None,
+                  lse=None):
+    """o [total_q, H, d] and lse [total_q, H] of chunked prefill over a paged cache."""
+    _need_cuda(q, q_start, k_pool, v_pool, block_table, seq_lens)
+    T, H, d = q.shape
+    S = seq_lens.numel()
+    KVH = k_pool.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((T, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = load_library().fa_paged_prefill(
+        _ptr(q), _ptr(q_start), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), S, H,
+        KVH, d, block_size, block_table.shape[1], k_pool.shape[0], int(max_q_len), scale,
+        int(bool(causal)), _ptr(o), _ptr(l), _dtype_code(q), _stream(q.device))
+    _check(st, "fa_paged_prefill")
+    return o, l

@@ -212,6 +212,66 @@ int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
                              workspace_bytes, stream);
 }
 
+int fa_paged_prefill(const void* q, const int32_t* q_start, const void* k_pool, const void* v_pool,
+                     const int32_t* block_table, const int32_t* seq_lens, int num_seqs, int H,
+                     int KVH, int d, int block_size, int max_blocks_per_seq, int num_blocks,
+                     int max_q_len, float scale, int causal, void* o, float* lse, int dtype,
+                     void* stream) {
+  if (dtype != FA_DT_F32 && dtype != FA_DT_BF16 && dtype != FA_DT_F16) return FA_ERR_DTYPE;
+  if (num_seqs < 0 || H < 1 || KVH < 1 || d < 1 || block_size < 1 || max_blocks_per_seq < 1 ||
+      num_blocks < 1 || max_q_len < 1 || max_q_len > kMaxN)
+    return FA_ERR_SHAPE;
+  if (H % KVH != 0 || !std::isfinite(scale)) return FA_ERR_SHAPE;
+  if (dtype == FA_DT_F32 || block_size != 16 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
+  if ((long long)max_q_len * H * d * 2 >= (1LL << 31)) return FA_ERR_SHAPE;
+  if ((long long)max_blocks_per_seq * block_size > kMaxN) return FA_ERR_SHAPE;
+  if ((long long)block_size * KVH * d * 2 >= (1LL << 31)) return FA_ERR_SHAPE;
+  if ((long long)num_seqs * H * ((max_q_len + 127) / 128) >= (1LL << 31)) return FA_ERR_SHAPE;
+  if (num_seqs == 0) return FA_OK;
+  if (!q || !q_start || !k_pool || !v_pool || !block_table || !seq_lens || !o || !lse)
+    return FA_ERR_NULL;
+  const void* ptrs[] = {q, k_pool, v_pool, o};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  const void* ints[] = {q_start, block_table, seq_lens, lse};
+  for (const void* p : ints)
+    if (reinterpret_cast<uintptr_t>(p) & 3u) return FA_ERR_ALIGN;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    // chunk offsets ascend with chunks <= max_q_len, each chunk fits inside its
+    // sequence's cached tokens, and every block the sequence uses is in the pool
+    std::vector<int32_t> starts(num_seqs + 1), lens(num_seqs),
+        tbl((size_t)num_seqs * max_blocks_per_seq);
+    if (hipMemcpyAsync(starts.data(), q_start, starts.size() * 4, hipMemcpyDeviceToHost, st) !=
+            hipSuccess ||
+        hipMemcpyAsync(lens.data(), seq_lens, lens.size() * 4, hipMemcpyDeviceToHost, st) !=
+            hipSuccess ||
+        hipMemcpyAsync(tbl.data(), block_table, tbl.size() * 4, hipMemcpyDeviceToHost, st) !=
+            hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return FA_ERR_HIP;
+    if (starts[0] != 0) return FA_ERR_INVALID;
+    for (int s = 0; s < num_seqs; ++s) {
+      const int n = starts[s + 1] - starts[s], L = lens[s];
+      if (n < 0 || n > max_q_len || L < n || (long long)L > (long long)max_blocks_per_seq * block_size)
+        return FA_ERR_INVALID;
+      for (int b = 0; b < (L + block_size - 1) / block_size; ++b) {
+        const int32_t p = tbl[(size_t)s * max_blocks_per_seq + b];
+        if (p < 0 || p >= num_blocks) return FA_ERR_INVALID;
+      }
+    }
+  }
+  fa::FwdArgs a{q, k_pool, v_pool, o, lse, num_seqs, H, max_q_len, d, scale, causal != 0, dtype, st};
+  a.paged = true;
+  a.table = block_table;
+  a.q_start = q_start;
+  a.seq_lens = seq_lens;
+  a.KVH = KVH;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  return hip_status(fa::launch_fwd(a));
+}
+
 size_t fa_paged_kv_append_workspace_size(int num_seqs) {
   if (num_seqs <= 0) return 0;
   return round_up((size_t)num_seqs * sizeof(int32_t), 256);   // the per-sequence slot map

@@ -53,14 +53,58 @@ constexpr int kVLead = 2;        // V operand read pairs in flight ahead of thei
 // it by more than this (base-2 exponent): probabilities stay <= 2^kSlack.
 constexpr float kSlack = 8.f;
 
-template <class E, int D, bool CAUSAL, int BN, int OCC>
+// Paged K/V source of a prefill: sequence s's queries are rows
+// [q_start[s], q_start[s+1]) of the packed Q/O/LSE, its seq_lens[s] cached
+// tokens (the chunk's own included) live in 16-token blocks of the pools
+// [num_blocks, 16, KVH, D] named by block_table[s, :].
+struct PagedKV {
+  const int32_t* table;
+  const int32_t* q_start;
+  const int32_t* seq_lens;
+  int H, KVH, max_blocks, num_blocks;
+};
+
+// Copy key rows [row0, row0 + ROWS) of one cached head of a paged sequence
+// into a swizzled LDS tile.  Every transfer instruction covers RPI rows of a
+// single 16-token block (RPI divides 16, row0 is a multiple of ROWS), so it
+// gets a buffer resource over that physical block, sized to stop at the
+// sequence's last valid token: slots past the length, bad block ids and rows
+// past the table all read as zeros.
+template <int D, int ROWS, int NWAVES, typename T>
+__device__ __forceinline__ void dma_rows_paged(const T* pool, const int32_t* table_row, int n_tok,
+                                               int max_blocks, int num_blocks, int kvh, int KVH,
+                                               unsigned char* lds, int row0, int wave, int lane) {
+  constexpr int DCH = D / 8;
+  constexpr int RPI = 64 / DCH;
+  constexpr int NI = ROWS / RPI;
+  static_assert(16 % RPI == 0 && NI % NWAVES == 0, "instruction rows must stay inside a block");
+  const uint32_t row_bytes = (uint32_t)KVH * D * 2;
+#pragma unroll
+  for (int ii = 0; ii < NI / NWAVES; ++ii) {
+    const int ins = ii * NWAVES + wave;
+    const int j0 = row0 + ins * RPI;                // first key of this instruction
+    const int b = j0 >> 4;
+    const int phys = b < max_blocks ? table_row[b] : -1;
+    const int valid = min(16, n_tok - (b << 4));    // tokens of this block inside the sequence
+    const bool ok = (unsigned)phys < (unsigned)num_blocks && valid > 0;
+    const auto r = make_rsrc(pool + (size_t)(ok ? phys : 0) * 16 * KVH * D,
+                             ok ? (uint32_t)valid * row_bytes : 0u);
+    const int rr = ins * RPI + lane / DCH;          // LDS row written by this lane
+    const int c = (lane % DCH) ^ tile_swz<D>(rr);
+    const int slot = (row0 + rr) & 15;
+    dma16(r, lds + ins * 1024, (uint32_t)((slot * KVH + kvh) * D + c * 8) * 2);
+  }
+}
+
+template <class E, int D, bool CAUSAL, int BN, int OCC, bool PAGED = false>
 __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     const typename E::elem* __restrict__ Q, const typename E::elem* __restrict__ K,
-    const typename E::elem* __restrict__ V, typename E::elem* __restrict__ O, float* __restrict__ LSE, int N, int Nk, int delta, float scale_log2,
-    int n_qtiles) {
+    const typename E::elem* __restrict__ V, typename E::elem* __restrict__ O,
+    float* __restrict__ LSE, int N, int Nk, int delta, float scale_log2, int n_qtiles, PagedKV pg) {
   // scale_log2 = scale * log2(e): scores are handled in base 2.  N query rows
   // and Nk key rows per head; with CAUSAL, key j is visible to row i iff
-  // j <= i + delta.
+  // j <= i + delta.  PAGED: one (sequence, head) per bh; N, Nk and delta are
+  // that sequence's chunk length, cached length and cached length - chunk.
   constexpr int KSTEPS = D / 16;         // matrix k-steps over the head dim
   constexpr int DT = D / 32;             // 32-row tiles of O^T
   constexpr int TILE = BN * D * 2;       // bytes of one K or V tile
@@ -75,7 +119,7 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
@@ -84,15 +128,54 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
   const int qt = CAUSAL ? (n_qtiles - 1 - tile % n_qtiles) : (tile % n_qtiles);
   const int q0 = qt * kBM;
 
-  const size_t head_off = (size_t)bh * (size_t)N * D;
+  // row strides of Q/O (elements) and LSE: one head's rows are contiguous, or
+  // interleaved with the other heads in the packed layout of a prefill
+  const int qstride = PAGED ? pg.H * D : D;
+  const int lstride = PAGED ? pg.H : 1;
+  size_t head_off, lse_off;
+  uint32_t head_bytes, lse_bytes;
+  const int32_t* table_row = nullptr;
+  int kvh = 0;
+  if constexpr (PAGED) {
+    const int seq = bh / pg.H, h = bh % pg.H;
+    const int qs = pg.q_start[seq];
+    N = pg.q_start[seq + 1] - qs;
+    Nk = pg.seq_lens[seq];
+    delta = Nk - N;                                 // the chunk is the sequence's last tokens
+    if (q0 >= N) return;                            // query tile past this sequence's chunk
+    head_off = ((size_t)qs * pg.H + h) * D;
+    head_bytes = (uint32_t)(((size_t)(N - 1) * pg.H + 1) * D * 2);
+    lse_off = (size_t)qs * pg.H + h;
+    lse_bytes = (uint32_t)(((size_t)(N - 1) * pg.H + 1) * 4);
+    table_row = pg.table + (size_t)seq * pg.max_blocks;
+    kvh = h / (pg.H / pg.KVH);
+  } else {
+    head_off = (size_t)bh * (size_t)N * D;
+    head_bytes = (uint32_t)N * D * 2;
+    lse_off = (size_t)bh * N;
+    lse_bytes = (uint32_t)N * 4;
+  }
   const size_t khead_off = (size_t)bh * (size_t)Nk * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
   const uint32_t khead_bytes = (uint32_t)Nk * D * 2;
   const auto rQ = make_rsrc(Q + head_off, head_bytes);
-  const auto rK = make_rsrc(K + khead_off, khead_bytes);
-  const auto rV = make_rsrc(V + khead_off, khead_bytes);
+  const auto rK = make_rsrc(K + (PAGED ? 0 : khead_off), PAGED ? 0u : khead_bytes);
+  const auto rV = make_rsrc(V + (PAGED ? 0 : khead_off), PAGED ? 0u : khead_bytes);
   const auto rO = make_rsrc(O + head_off, head_bytes);
-  const auto rL = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
+  const auto rL = make_rsrc(LSE + lse_off, lse_bytes);
+  auto dma_k = [&](unsigned char* dst, int row0) __attribute__((always_inline)) {
+    if constexpr (PAGED)
+      dma_rows_paged<D, BN, kThreads / 64>(K, table_row, Nk, pg.max_blocks, pg.num_blocks, kvh,
+                                           pg.KVH, dst, row0, wave, lane);
+    else
+      dma_rows<D, BN, kThreads / 64>(rK, dst, row0, wave, lane);
+  };
+  auto dma_v = [&](unsigned char* dst, int row0) __attribute__((always_inline)) {
+    if constexpr (PAGED)
+      dma_rows_paged<D, BN, kThreads / 64>(V, table_row, Nk, pg.max_blocks, pg.num_blocks, kvh,
+                                           pg.KVH, dst, row0, wave, lane);
+    else
+      dma_rows<D, BN, kThreads / 64>(rV, dst, row0, wave, lane);
+  };
 
   const int kv_end = CAUSAL ? min(Nk, q0 + kBM + delta) : Nk;
   const int n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
@@ -104,21 +187,22 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     if (tid < 2 * kBM) {
 #pragma unroll
       for (int c = 0; c < D / 16; ++c)
-        bstore16(u32x4{0u, 0u, 0u, 0u}, rO, (uint32_t)(row * D + (tid & 1) * (D / 2) + 8 * c) * 2);
-      if ((tid & 1) == 0) bstore4f(kNegInf, rL, (uint32_t)row * 4);
+        bstore16(u32x4{0u, 0u, 0u, 0u}, rO,
+                 (uint32_t)(row * qstride + (tid & 1) * (D / 2) + 8 * c) * 2);
+      if ((tid & 1) == 0) bstore4f(kNegInf, rL, (uint32_t)row * lstride * 4);
     }
     return;
   }
 
   // ---- this wave's query rows, straight from HBM into B-operand registers;
   //      K_0 and V_0 into ring slot 0
-  dma_rows<D, BN, kThreads / 64>(rK, sK0, 0, wave, lane);
-  dma_rows<D, BN, kThreads / 64>(rV, sV0, 0, wave, lane);
+  dma_k(sK0, 0);
+  dma_v(sV0, 0);
   const int my_q_row = q0 + wave * 32 + l32;
   u32x4 qf[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s)
-    qf[s] = bload16(rQ, (uint32_t)(my_q_row * D + 16 * s + 8 * half) * 2);
+    qf[s] = bload16(rQ, (uint32_t)(my_q_row * qstride + 16 * s + 8 * half) * 2);
   // The softmax takes its maximum over raw scores and folds the scale into one
   // multiply-add, which needs a positive multiplier: for a negative scale,
   // negate Q once (exact in bf16) and use |scale|.
@@ -212,7 +296,7 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
 
   // prologue: S_0, its max; K_1 streams meanwhile
   f32x16 sa[NSUB], sb[NSUB];
-  if (n_kv > 1) dma_rows<D, BN, kThreads / 64>(rK, sK1, BN, wave, lane);
+  if (n_kv > 1) dma_k(sK1, BN);
   {
 #pragma unroll
     for (int t = 0; t < NSUB; ++t) sa[t] = zero16();
@@ -238,8 +322,8 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
                   const unsigned char* vprev, unsigned char* vcur, f32x16 (&so)[NSUB],
                   f32x16 (&sn)[NSUB], auto masked) {
     pin_offsets();
-    if (j + 1 < n_kv) dma_rows<D, BN, kThreads / 64>(rK, knxt, (j + 1) * BN, wave, lane);
-    dma_rows<D, BN, kThreads / 64>(rV, vcur, j * BN, wave, lane);
+    if (j + 1 < n_kv) dma_k(knxt, (j + 1) * BN);
+    dma_v(vcur, j * BN);
     const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
     u32x4 pb[NU];
     float rs = 0.f;
@@ -339,10 +423,11 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
       u32x2 w;
       w[0] = E::pack(o[t][4 * g] * inv, o[t][4 * g + 1] * inv);
       w[1] = E::pack(o[t][4 * g + 2] * inv, o[t][4 * g + 3] * inv);
-      bstore8(w, rO, (uint32_t)(my_q * D + d0) * 2);
+      bstore8(w, rO, (uint32_t)(my_q * qstride + d0) * 2);
     }
   if (half == 0)
-    bstore4f(l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf, rL, (uint32_t)my_q * 4);
+    bstore4f(l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf, rL,
+             (uint32_t)my_q * lstride * 4);
 }
 
 // ---------------------------------------------------------------------------
@@ -529,8 +614,26 @@ hipError_t launch_bf16(const FwdArgs& a, int Nk, int delta) {
   const int grid = a.B * a.H * n_qtiles;
   hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, BN, OCC>), dim3(grid), dim3(kThreads), 0,
                      a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V, (T*)a.O, a.LSE, a.N, Nk,
-                     delta, a.scale * kLog2e, n_qtiles);
+                     delta, a.scale * kLog2e, n_qtiles, PagedKV{});
   return hipGetLastError();
+}
+
+template <class E, int D, bool CAUSAL>
+hipError_t launch_paged(const FwdArgs& a) {
+  using T = typename E::elem;
+  const int n_qtiles = (a.N + kBM - 1) / kBM;          // a.N: the longest chunk
+  const int grid = a.B * a.H * n_qtiles;                // a.B: the number of sequences
+  const PagedKV pg{a.table, a.q_start, a.seq_lens, a.H, a.KVH, a.max_blocks, a.num_blocks};
+  hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, kBNDefault, 2, true>), dim3(grid),
+                     dim3(kThreads), 0, a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V,
+                     (T*)a.O, a.LSE, 0, 0, 0, a.scale * kLog2e, n_qtiles, pg);
+  return hipGetLastError();
+}
+
+template <class E>
+hipError_t launch_paged_e(const FwdArgs& a) {
+  if (a.d == 64) return a.causal ? launch_paged<E, 64, true>(a) : launch_paged<E, 64, false>(a);
+  return a.causal ? launch_paged<E, 128, true>(a) : launch_paged<E, 128, false>(a);
 }
 
 template <class E>
@@ -553,6 +656,7 @@ hipError_t launch_f32(const FwdArgs& a, int Nk, int delta, bool causal) {
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs& a) {
+  if (a.paged) return a.dtype == 2 ? launch_paged_e<F16>(a) : launch_paged_e<Bf16>(a);
   const int Nk = a.Nk > 0 ? a.Nk : a.N;
   bool causal = a.causal;
   // every key at or before every query: the mask is void

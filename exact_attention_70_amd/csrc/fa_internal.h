@@ -21,6 +21,14 @@ struct FwdArgs {
   hipStream_t stream;
   int Nk = 0;       // key/value rows per head (0: same as N)
   long long delta = 0;   // q_offset - k_offset: key j is visible to row i iff j <= i + delta
+  // paged prefill: K/V are pools read through a block table, Q/O/LSE are
+  // packed [total_q, H, ...] with per-sequence start offsets; B is the number
+  // of sequences and N the longest chunk
+  bool paged = false;
+  const int32_t* table = nullptr;
+  const int32_t* q_start = nullptr;
+  const int32_t* seq_lens = nullptr;
+  int KVH = 0, max_blocks = 0, num_blocks = 0;
 };
 
 struct MergeArgs {

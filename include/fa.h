@@ -236,6 +236,39 @@ int fa_paged_decode_gqa(const void* q, const void* k_pool, const void* v_pool,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_paged_prefill -- the forward of a chunk of new queries per sequence over
+ * a paged KV cache (chunked prefill).  Prefill processes a prompt's tokens
+ * together and builds the cache (HPC notes, section "Prefill, Decode and
+ * inference scheduling"); the cache is read through the block table, block by
+ * block (CMU 10-423 L17-L18 notes, section "Decoding: PagedAttention").
+ *
+ * Sequence s has seq_lens[s] cached tokens, the chunk's own K/V included
+ * (append them first, e.g. with fa_paged_kv_append); its chunk is the last
+ * n_s = q_start[s+1] - q_start[s] tokens, so with `causal` query r of the
+ * chunk sees keys j <= seq_lens[s] - n_s + r (bottom-right alignment: the
+ * offset rule of fa_fwd_offset with q_offset = seq_lens[s] - n_s).  Query
+ * head h reads cached head h / (H / KVH).
+ *
+ *   q            in   [total_q, H, d] packed rows of all chunks, dtype bf16/fp16
+ *   q_start      in   [num_seqs + 1] int32, q_start[0] = 0, ascending
+ *   k_pool/v_pool in  [num_blocks, 16, KVH, d], same dtype
+ *   block_table  in   [num_seqs, max_blocks_per_seq] int32
+ *   seq_lens     in   [num_seqs] int32, n_s <= seq_lens[s] <= max_blocks_per_seq*16
+ *   max_q_len    >= every n_s (sizes the launch), <= 1<<20
+ *   o            out  [total_q, H, d], same dtype;  lse out [total_q, H] fp32
+ *   block_size 16, d 64 or 128, KVH divides H (else FA_ERR_UNSUPPORTED / FA_ERR_SHAPE)
+ * Cached slots past a sequence's length and out-of-range block ids read as
+ * zeros.  With FA_DEBUG=1 the offsets, lengths and used table entries are
+ * checked on the host first (FA_ERR_INVALID, nothing launched).  Arithmetic
+ * as for fa_fwd.
+ */
+int fa_paged_prefill(const void* q, const int32_t* q_start, const void* k_pool, const void* v_pool,
+                     const int32_t* block_table, const int32_t* seq_lens, int num_seqs, int H,
+                     int KVH, int d, int block_size, int max_blocks_per_seq, int num_blocks,
+                     int max_q_len, float scale, int causal, void* o, float* lse, int dtype,
+                     void* stream);
+
+/*
  * fa_paged_kv_append_workspace_size -- bytes of workspace fa_paged_kv_append
  * needs: one int32 pool-slot index per sequence, rounded up to 256 bytes.
  */

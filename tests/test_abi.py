@@ -37,6 +37,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("fa_fwd", "fa_fwd_offset", "fa_merge", "fa_bwd", "fa_paged_decode",
               "fa_paged_decode_gqa", "fa_paged_kv_append", "fa_paged_kv_append_workspace_size",
+              "fa_paged_prefill",
               "fa_bwd_workspace_size", "fa_paged_decode_workspace_size", "fa_status_string",
               "fa_version"):
         assert n in names
@@ -206,3 +207,20 @@ def test_paged_kv_append_validation(lib):
     assert append(lib, fc=ctypes.c_void_p(0x10002)) == ERR_ALIGN
     assert append(lib, wsb=16) == ERR_WS
     assert append(lib, S=0, kn=None) == OK
+
+
+def prefill(lib, S=3, H=8, KVH=2, d=128, bs=16, mq=64, dt=1, q=P, causal=1):
+    return lib.fa_paged_prefill(q, P, P, P, P, P, S, H, KVH, d, bs, 8, 100, mq, 0.1, causal, P2, P2,
+                                dt, None)
+
+
+def test_paged_prefill_validation(lib):
+    assert prefill(lib, dt=9) == ERR_DTYPE
+    assert prefill(lib, mq=0) == ERR_SHAPE
+    assert prefill(lib, KVH=3) == ERR_SHAPE
+    assert prefill(lib, dt=0) == ERR_UNSUP
+    assert prefill(lib, bs=32) == ERR_UNSUP
+    assert prefill(lib, d=96) == ERR_UNSUP
+    assert prefill(lib, q=None) == ERR_NULL
+    assert prefill(lib, q=MIS) == ERR_ALIGN
+    assert prefill(lib, S=0, q=None) == OK

@@ -185,6 +185,18 @@ def paged_inputs(num_seqs: int, H: int, d: int, block_size: int, min_len: int, m
             "free_list": free, "free_count": int(free.numel()), "kv_heads": kvh}
 
 
+def prefill_queries(chunks: list, H: int, d: int, dtype: str = "bf16", *, seed: int) -> dict:
+    """Packed query rows of a chunked prefill: q [sum(chunks), H, d] drawn
+    N(0, 1) in one go, and q_start [len(chunks) + 1] int32 (prefix sums of the
+    chunk lengths).  CPU tensors, storage dtype."""
+    g = _gen(seed)
+    starts = [0]
+    for n in chunks:
+        starts.append(starts[-1] + int(n))
+    q = torch.randn((starts[-1], H, d), generator=g, dtype=torch.float32).to(_TORCH_DTYPES[dtype])
+    return {"q": q.contiguous(), "q_start": torch.tensor(starts, dtype=torch.int32)}
+
+
 def _randn_chunked(shape, g, tdt, chunk_rows: int = 512) -> torch.Tensor:
     """N(0,1) draws of ``shape`` filled along dim 0 in chunks (bounded fp32 temporaries)."""
     out = torch.empty(shape, dtype=tdt)
