@@ -64,27 +64,35 @@ struct PagedKV {
   int H, KVH, max_blocks, num_blocks;
 };
 
+// Physical ids of the four 16-token blocks one 64-key tile spans (-1: past
+// the sequence's table row).
+struct TileIds {
+  int b[4];
+};
+
 // Copy key rows [row0, row0 + ROWS) of one cached head of a paged sequence
-// into a swizzled LDS tile.  Every transfer instruction covers RPI rows of a
-// single 16-token block (RPI divides 16, row0 is a multiple of ROWS), so it
-// gets a buffer resource over that physical block, sized to stop at the
-// sequence's last valid token: slots past the length, bad block ids and rows
-// past the table all read as zeros.
+// into a swizzled LDS tile.  The tile's four block ids arrive in `ids`
+// (read from the table ahead of time).  Every transfer
+// instruction covers RPI rows of a single block (RPI divides 16, row0 is a
+// multiple of ROWS), so it gets a buffer resource over that physical block,
+// sized to stop at the sequence's last valid token: slots past the length,
+// bad block ids and rows past the table all read as zeros.
 template <int D, int ROWS, int NWAVES, typename T>
-__device__ __forceinline__ void dma_rows_paged(const T* pool, const int32_t* table_row, int n_tok,
-                                               int max_blocks, int num_blocks, int kvh, int KVH,
-                                               unsigned char* lds, int row0, int wave, int lane) {
+__device__ __forceinline__ void dma_rows_paged(const T* pool, TileIds ids, int n_tok, int num_blocks,
+                                               int kvh, int KVH, unsigned char* lds, int row0,
+                                               int wave, int lane) {
   constexpr int DCH = D / 8;
   constexpr int RPI = 64 / DCH;
   constexpr int NI = ROWS / RPI;
   static_assert(16 % RPI == 0 && NI % NWAVES == 0, "instruction rows must stay inside a block");
+  static_assert(ROWS == 64, "a tile spans four blocks");
   const uint32_t row_bytes = (uint32_t)KVH * D * 2;
 #pragma unroll
   for (int ii = 0; ii < NI / NWAVES; ++ii) {
     const int ins = ii * NWAVES + wave;
-    const int j0 = row0 + ins * RPI;                // first key of this instruction
-    const int b = j0 >> 4;
-    const int phys = b < max_blocks ? table_row[b] : -1;
+    const int bi = (ins * RPI) >> 4;                // block of this instruction within the tile
+    const int b = (row0 >> 4) + bi;
+    const int phys = bi == 0 ? ids.b[0] : bi == 1 ? ids.b[1] : bi == 2 ? ids.b[2] : ids.b[3];
     const int valid = min(16, n_tok - (b << 4));    // tokens of this block inside the sequence
     const bool ok = (unsigned)phys < (unsigned)num_blocks && valid > 0;
     const auto r = make_rsrc(pool + (size_t)(ok ? phys : 0) * 16 * KVH * D,
@@ -162,17 +170,42 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
   const auto rV = make_rsrc(V + (PAGED ? 0 : khead_off), PAGED ? 0u : khead_bytes);
   const auto rO = make_rsrc(O + head_off, head_bytes);
   const auto rL = make_rsrc(LSE + lse_off, lse_bytes);
+  // Paged: a tile's block ids are read from the table one iteration before
+  // the transfers that use them (ids_v: tile j, ids_k: tile j+1, ids_f: tile
+  // j+2, read during iteration j), so no transfer waits on a table read.  The
+  // read index is clamped into the row (max_blocks >= 1) and entries past it
+  // become -1, which the transfer turns into zeros.
+  auto tile_ids = [&](int t) __attribute__((always_inline)) {
+    TileIds r{{-1, -1, -1, -1}};
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int b = 4 * t + q;
+        const int v = table_row[min(b, pg.max_blocks - 1)];
+        r.b[q] = b < pg.max_blocks ? v : -1;
+      }
+    }
+    return r;
+  };
+  TileIds ids_v = tile_ids(0), ids_k = tile_ids(1), ids_f = ids_k;
+  // after a barrier (which has waited for the reads): the ids move to scalar
+  // registers, leaving only the ids in flight in vector registers
+  auto rotate_ids = [&]() __attribute__((always_inline)) {
+    ids_v = ids_k;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ids_k.b[q] = __builtin_amdgcn_readfirstlane(ids_f.b[q]);
+  };
   auto dma_k = [&](unsigned char* dst, int row0) __attribute__((always_inline)) {
     if constexpr (PAGED)
-      dma_rows_paged<D, BN, kThreads / 64>(K, table_row, Nk, pg.max_blocks, pg.num_blocks, kvh,
+      dma_rows_paged<D, BN, kThreads / 64>(K, row0 == 0 ? ids_v : ids_k, Nk, pg.num_blocks, kvh,
                                            pg.KVH, dst, row0, wave, lane);
     else
       dma_rows<D, BN, kThreads / 64>(rK, dst, row0, wave, lane);
   };
   auto dma_v = [&](unsigned char* dst, int row0) __attribute__((always_inline)) {
     if constexpr (PAGED)
-      dma_rows_paged<D, BN, kThreads / 64>(V, table_row, Nk, pg.max_blocks, pg.num_blocks, kvh,
-                                           pg.KVH, dst, row0, wave, lane);
+      dma_rows_paged<D, BN, kThreads / 64>(V, ids_v, Nk, pg.num_blocks, kvh, pg.KVH, dst, row0,
+                                           wave, lane);
     else
       dma_rows<D, BN, kThreads / 64>(rV, dst, row0, wave, lane);
   };
@@ -296,6 +329,7 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
 
   // prologue: S_0, its max; K_1 streams meanwhile
   f32x16 sa[NSUB], sb[NSUB];
+  if constexpr (PAGED) ids_f = tile_ids(2);
   if (n_kv > 1) dma_k(sK1, BN);
   {
 #pragma unroll
@@ -312,6 +346,7 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     update_max(mx);   // O is still zero: no rescale needed
   }
   __syncthreads();
+  if constexpr (PAGED) rotate_ids();
 
   // Iteration j: S_j = K_j Q^T on the matrix cores interleaved with the
   // probabilities P_{j-1} (exponentials), then O^T += V_{j-1}^T P_{j-1}^T
@@ -322,6 +357,7 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
                   const unsigned char* vprev, unsigned char* vcur, f32x16 (&so)[NSUB],
                   f32x16 (&sn)[NSUB], auto masked) {
     pin_offsets();
+    if constexpr (PAGED) ids_f = tile_ids(j + 2);
     if (j + 1 < n_kv) dma_k(knxt, (j + 1) * BN);
     dma_v(vcur, j * BN);
     const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
@@ -367,6 +403,7 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     }
     if (update_max(mx)) rescale();
     __syncthreads();
+    if constexpr (PAGED) rotate_ids();
   };
   using Plain = std::integral_constant<bool, false>;
   using Masked = std::integral_constant<bool, true>;
