@@ -28,6 +28,15 @@
 //   accumulation.  K and V are separate load batches: the scores of block t
 //   run while V_t streams in, and K_{t+1} streams in while V_t is accumulated.
 //   Writes (m, l, unnormalised o).
+// Grouped-query partial kernel (G = H / KVH in {2, 4, 8}): a wave serves one
+//   cached head and the G query heads that read it, so each cached row is
+//   loaded once.  Lane = (token phase tq = lane / 16, 8 of the 128 d values);
+//   the four quarter-waves take interleaved tokens (4i + tq), so one 16-byte
+//   load instruction brings 4 token rows.  Each lane scores its rows against
+//   all G queries (packed two-element dot products, reduced across the 16
+//   lanes with DPP).  The running max is shared by the quarters; their
+//   denominators and outputs stay separate until the partition ends, when
+//   two cross-quarter exchanges combine them.
 // Merge kernel: one wave per (sequence, head) combines its partitions.
 //   Throughput is bound by HBM: the flops per byte are ~1.
 #include "fa_device.h"
@@ -174,6 +183,179 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_partial_kernel(
   }
 }
 
+constexpr int kGqaWaves = 4;   // cached heads per workgroup
+
+template <class E, int G>
+__global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_partial_kernel(
+    const typename E::elem* __restrict__ q, const typename E::elem* __restrict__ k_pool,
+    const typename E::elem* __restrict__ v_pool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, int H, int KVH, int max_blocks_per_seq, int num_blocks,
+    float scale_log2, float* __restrict__ part_o, float* __restrict__ part_ml, int part_tokens,
+    int n_parts) {
+  constexpr int NI = G <= 4 ? 8 : 4;     // token rows per lane per step
+  constexpr int STEP = 4 * NI;           // tokens per step: whole blocks
+  constexpr int NB = STEP / kDecBS;      // blocks per step
+  static_assert(STEP % kDecBS == 0, "a step is whole blocks");
+  const int p = blockIdx.x;
+  const int s = blockIdx.z;
+  const int len = min(seq_lens[s], max_blocks_per_seq * kDecBS);
+  const int t_begin = p * part_tokens;              // a multiple of STEP (host-checked)
+  if (t_begin >= len) return;                       // partition past this sequence's end
+  const int t_end = min(len, t_begin + part_tokens);
+
+  const int lane = threadIdx.x & 63;
+  const int kvh = __builtin_amdgcn_readfirstlane(blockIdx.y * kGqaWaves + (threadIdx.x >> 6));
+  if (kvh >= KVH) return;                           // no cached head for this wave
+  const int tq = lane >> 4;                         // token phase within 4 consecutive tokens
+  const int ch = lane & 15;                         // which 8 of the 128 d values
+
+  const uint32_t blk_bytes = (uint32_t)kDecBS * KVH * kDecD * 2;
+  const uint32_t tok_stride = (uint32_t)KVH * kDecD * 2;
+  // row (4i + tq) of a step: block i / 4, slot 4 (i % 4) + tq
+  const uint32_t lane_off = tq * tok_stride + (uint32_t)(kvh * kDecD + ch * 8) * 2;
+
+  // the G query heads' 8 values of this lane, packed pairs
+  u32x4 qv[G];
+  {
+    const auto rq = make_rsrc(q + (size_t)s * H * kDecD, (uint32_t)H * kDecD * 2);
+#pragma unroll
+    for (int j = 0; j < G; ++j) qv[j] = bload16(rq, (uint32_t)((kvh * G + j) * kDecD + ch * 8) * 2);
+  }
+
+  float m_run[G], l_run[G], acc[G][8];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m_run[j] = kNegInf;
+    l_run[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+  }
+
+  const int32_t* table = block_table + (size_t)s * max_blocks_per_seq;
+  // resources over the NB blocks of the step starting at t0; a block past the
+  // partition (or an out-of-range id) gets an empty resource and reads zeros
+  auto step_rsrc = [&](int t0, __amdgpu_buffer_rsrc_t (&rk)[NB], __amdgpu_buffer_rsrc_t (&rv)[NB])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int tb = t0 + b * kDecBS;
+      const int32_t phys = tb < t_end ? table[tb / kDecBS] : -1;
+      const bool ok = (uint32_t)phys < (uint32_t)num_blocks;
+      const size_t boff = (size_t)(ok ? phys : 0) * kDecBS * KVH * kDecD;
+      rk[b] = make_rsrc(k_pool + boff, ok ? blk_bytes : 0u);
+      rv[b] = make_rsrc(v_pool + boff, ok ? blk_bytes : 0u);
+    }
+  };
+  auto load_rows = [&](const __amdgpu_buffer_rsrc_t (&r)[NB], u32x4 (&dst)[NI])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dst[i] = bload16s(r[i / 4], lane_off, (i % 4) * 4 * tok_stride);
+  };
+
+  // One step over tokens [t0, t0 + STEP): K of the next step streams in while
+  // the softmax runs, V of the next step while this step's V is accumulated.
+  // MASKED: some rows lie past t_end; they are excluded by selects, so pad
+  // slots (which may hold NaN) never reach the sums.
+  u32x4 kr[NI], vr[NI];
+  __amdgpu_buffer_rsrc_t rk[NB], rv[NB];
+  step_rsrc(t_begin, rk, rv);
+  load_rows(rk, kr);
+  load_rows(rv, vr);
+  auto step = [&](int t0, auto masked) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
+    const bool more = t0 + STEP < t_end;
+    __amdgpu_buffer_rsrc_t rk2[NB], rv2[NB];
+    if (more) step_rsrc(t0 + STEP, rk2, rv2);
+    float sc[NI][G];
+    float mx[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) mx[j] = kNegInf;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const bool valid = !MASKED || t0 + 4 * i + tq < t_end;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part = E::dot2(qv[j][e], kr[i][e], part);
+        float x = group_sum<16>(part) * scale_log2;
+        if constexpr (MASKED) x = valid ? x : kNegInf;
+        sc[i][j] = x;
+        mx[j] = fmaxf(mx[j], x);
+      }
+    }
+    if (more) load_rows(rk2, kr);
+    float alpha[G], m_new[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float m = fmaxf(mx[j], __shfl_xor(mx[j], 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));          // the step's max over all four quarters
+      m_new[j] = fmaxf(m_run[j], m);
+      alpha[j] = fast_exp2(m_run[j] - m_new[j]);
+      m_run[j] = m_new[j];
+      l_run[j] *= alpha[j];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[j][e] *= alpha[j];
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const bool valid = !MASKED || t0 + 4 * i + tq < t_end;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = E::lo(vr[i][e]);
+        v[2 * e + 1] = E::hi(vr[i][e]);
+      }
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const float pij = fast_exp2(sc[i][j] - m_new[j]);   // 0 for a masked row
+        l_run[j] += pij;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float a2 = fmaf(pij, v[e], acc[j][e]);
+          acc[j][e] = MASKED ? (valid ? a2 : acc[j][e]) : a2;
+        }
+      }
+    }
+    if (more) load_rows(rv2, vr);
+  };
+  using Plain = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+  int t0 = t_begin;
+  for (; t0 + STEP <= t_end; t0 += STEP) step(t0, Plain{});
+  if (t0 < t_end) step(t0, Masked{});
+
+  // combine the four quarters' denominators and outputs
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    l_run[j] += __shfl_xor(l_run[j], 16, 64);
+    l_run[j] += __shfl_xor(l_run[j], 32, 64);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[j][e] += __shfl_xor(acc[j][e], 16, 64);
+      acc[j][e] += __shfl_xor(acc[j][e], 32, 64);
+    }
+  }
+  // quarter j % 4 writes query head kvh * G + j
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    if (tq != j % 4) continue;
+    const size_t entry = ((size_t)s * n_parts + p) * H + kvh * G + j;
+    u32x4 w0, w1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w0[e] = as_u32(acc[j][e]);
+      w1[e] = as_u32(acc[j][4 + e]);
+    }
+    *(u32x4*)(part_o + entry * kDecD + ch * 8) = w0;
+    *(u32x4*)(part_o + entry * kDecD + ch * 8 + 4) = w1;
+    if (ch == 0) {
+      part_ml[entry * 2] = m_run[j];
+      part_ml[entry * 2 + 1] = l_run[j];
+    }
+  }
+}
+
 // One wave per (sequence, head): rescale every partition's (m, l, o) to the
 // common maximum and sum.  Lanes take the partitions' (m, l) in parallel for
 // the maximum and the weights; then each lane owns 2 of the 128 output values
@@ -243,11 +425,25 @@ hipError_t launch_decode_e(const DecodeArgs& a) {
   const size_t n_entries = (size_t)a.num_seqs * a.n_parts * a.H;
   float* part_o = a.part;
   float* part_ml = a.part + n_entries * kDecD;
-  dim3 grid(a.n_parts, (a.H + kHeadsPerGroup - 1) / kHeadsPerGroup, a.num_seqs);
-  hipLaunchKernelGGL((decode_partial_kernel<E>), grid, dim3(kDecThreads), 0, a.stream,
-                     (const T*)a.q, (const T*)a.k_pool, (const T*)a.v_pool, a.block_table,
-                     a.seq_lens, a.H, a.KVH > 0 ? a.KVH : a.H, a.max_blocks_per_seq, a.num_blocks,
-                     a.scale * kLog2e, part_o, part_ml, a.part_tokens, a.n_parts);
+  const int KVH = a.KVH > 0 ? a.KVH : a.H;
+  const int g = a.H / KVH;
+  // grouped heads with a group size the grouped kernel is built for (its step,
+  // at most 32 tokens, divides the 256-token partition)
+  if ((g == 2 || g == 4 || g == 8) && a.part_tokens % 32 == 0) {
+    dim3 grid(a.n_parts, (KVH + kGqaWaves - 1) / kGqaWaves, a.num_seqs);
+    auto kern = g == 2 ? decode_gqa_partial_kernel<E, 2>
+              : g == 4 ? decode_gqa_partial_kernel<E, 4> : decode_gqa_partial_kernel<E, 8>;
+    hipLaunchKernelGGL(kern, grid, dim3(kGqaWaves * 64), 0, a.stream, (const T*)a.q,
+                       (const T*)a.k_pool, (const T*)a.v_pool, a.block_table, a.seq_lens, a.H, KVH,
+                       a.max_blocks_per_seq, a.num_blocks, a.scale * kLog2e, part_o, part_ml,
+                       a.part_tokens, a.n_parts);
+  } else {
+    dim3 grid(a.n_parts, (a.H + kHeadsPerGroup - 1) / kHeadsPerGroup, a.num_seqs);
+    hipLaunchKernelGGL((decode_partial_kernel<E>), grid, dim3(kDecThreads), 0, a.stream,
+                       (const T*)a.q, (const T*)a.k_pool, (const T*)a.v_pool, a.block_table,
+                       a.seq_lens, a.H, KVH, a.max_blocks_per_seq, a.num_blocks,
+                       a.scale * kLog2e, part_o, part_ml, a.part_tokens, a.n_parts);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int waves = a.num_seqs * a.H;

@@ -39,6 +39,25 @@ def test_gqa_decode_matches_oracle(gpu, kvh):
     assert max_abs(lse.double().cpu().numpy(), rl) <= TOL
 
 
+@pytest.mark.parametrize("H,kvh", [(8, 2), (24, 6), (16, 2), (12, 3), (12, 6)])
+def test_gqa_decode_head_counts_and_step_edges(gpu, H, kvh):
+    """Cached-head counts that leave waves of a workgroup idle (6 = 4 + 2),
+    group sizes 4, 8, 2, and lengths at the edges of a 32-token step and a
+    256-token partition; pad slots hold NaN."""
+    d, bs = 128, 16
+    lens = [1, 15, 16, 31, 32, 33, 63, 64, 255, 256, 257, 512, 600]
+    p = workloads.paged_inputs(len(lens), H, d, bs, 1, max(lens), seed=5200 + H + kvh,
+                               seq_lens=lens, kv_heads=kvh, pad_value=float("nan"))
+    pd = _to_dev(p, gpu)
+    o, lse = binding.paged_decode(pd["q"], pd["k_pool"], pd["v_pool"], pd["block_table"],
+                                  pd["seq_lens"], block_size=bs, scale=d ** -0.5)
+    torch.cuda.synchronize()
+    ro, rl = oracle.paged_decode(p["q"], p["k_pool"], p["v_pool"], p["block_table"], p["seq_lens"],
+                                 bs, d ** -0.5)
+    assert max_abs(o.double().cpu().numpy(), ro) <= TOL
+    assert max_abs(lse.double().cpu().numpy(), rl) <= TOL
+
+
 def test_gqa_decode_at_benchmark_shape(gpu):
     """The decode workload's sequences and lengths with 8 cached heads for the
     32 query heads, every sequence against the oracle."""
