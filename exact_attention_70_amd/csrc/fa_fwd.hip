@@ -104,6 +104,15 @@ __device__ __forceinline__ void dma_rows_paged(const T* pool, TileIds ids, int n
   }
 }
 
+// True when every probability pair g (key block g / 4), issued in slot
+// g * pslots / npair, precedes the first P V op that reads its block (slot
+// nq + (g / 4) * dt).
+constexpr bool probs_before_use(int npair, int pslots, int nq, int dt) {
+  for (int g = 0; g < npair; ++g)
+    if (g * pslots / npair >= nq + (g / 4) * dt) return false;
+  return true;
+}
+
 template <class E, int D, bool CAUSAL, int BN, int OCC, bool PAGED = false>
 __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     const typename E::elem* __restrict__ Q, const typename E::elem* __restrict__ K,
@@ -261,10 +270,19 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
   constexpr int NP = DT * NU;           // matrix ops of O^T += V^T P^T per tile
   constexpr int KLEAD = kKLead;
   constexpr int VLEAD = kVLead;
-  static_assert(2 * NSUB * 16 / NQ >= 1 && (NSUB * 16) % NQ == 0, "probs split");
-  constexpr int PPER = NSUB * 16 / NQ;  // probabilities per S matrix op
-  static_assert((NSUB * 16) % NP == 0, "reduce split");
-  constexpr int RPER = NSUB * 16 / NP;  // scores per P V matrix op in the row max
+  // Issue schedule of one iteration's vector work over its NQ + NP matrix-op
+  // slots (S ops first, then P V ops ordered key block by key block).  The
+  // probabilities of the previous tile come in NPAIR pairs, key block kb
+  // being pairs [4kb, 4kb + 4); they are spread evenly over the first PSLOTS
+  // slots, so block kb is done before the first P V op that reads it (slot
+  // NQ + kb * DT).  The row max of the new tile takes pairs of scores in the
+  // P V slots, after the last S op.
+  constexpr int NPAIR = NSUB * 8;
+  constexpr int PSLOTS = NQ + NP - DT;
+  static_assert(NPAIR == 4 * NU, "four probability pairs per key block");
+  static_assert(NPAIR % NP == 0, "row-max pairs per P V op");
+  static_assert(probs_before_use(NPAIR, PSLOTS, NQ, DT), "a key block's probabilities come late");
+  constexpr int MPER = NPAIR / NP;      // row-max pairs per P V op
 
   // Per-lane byte offsets of the operand reads inside a tile.  The swizzle
   // makes them differ per k-step (K) and per column block (V); sub-tile,
@@ -368,39 +386,47 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     for (int x = 0; x < KLEAD; ++x) ka[x] = k_operand(kcur, x);
 #pragma unroll
     for (int t = 0; t < NSUB; ++t) sn[t] = zero16();
+    // probability pair g of the previous tile (scores so), in the slot the
+    // schedule gives it
+    auto probs = [&](const int slot) __attribute__((always_inline)) {
 #pragma unroll
-    for (int idx = 0; idx < NQ; ++idx) {
-      const u32x4 a = ka[idx % KLEAD];
-      if (idx + KLEAD < NQ) ka[idx % KLEAD] = k_operand(kcur, idx + KLEAD);
-      sn[idx / KSTEPS] = E::mfma(a, qf[idx % KSTEPS], sn[idx / KSTEPS]);
-#pragma unroll
-      for (int e = 0; e < PPER; e += 2) {
-        const int flat = idx * PPER + e;
-        const int t = flat / 16, i = flat % 16;
+      for (int g = 0; g < NPAIR; ++g) {
+        if (g * PSLOTS / NPAIR != slot) continue;
+        const int t = g / 8, i = 2 * (g % 8);
         const float p0 = fast_exp2(fmaf(so[t][i], scale_log2, neg_m));
         const float p1 = fast_exp2(fmaf(so[t][i + 1], scale_log2, neg_m));
         const uint32_t pk = E::pack(p0, p1);
         rs = E::dot2(pk, E::kOnes, rs);
         pb[2 * t + (i >> 3)][(i & 7) >> 1] = pk;
       }
+    };
+#pragma unroll
+    for (int idx = 0; idx < NQ; ++idx) {
+      const u32x4 a = ka[idx % KLEAD];
+      if (idx + KLEAD < NQ) ka[idx % KLEAD] = k_operand(kcur, idx + KLEAD);
+      sn[idx / KSTEPS] = E::mfma(a, qf[idx % KSTEPS], sn[idx / KSTEPS]);
+      probs(idx);
     }
-    l_run = fmaf(l_run, alpha, rs);
     if constexpr (decltype(masked)::value) mask(sn, j * BN);
+    // P V op ip reads key block ip / DT and writes output column block ip % DT
+    auto vidx = [](int ip) { return (ip % DT) * NU + ip / DT; };
     u32x4 va[VLEAD];
 #pragma unroll
-    for (int x = 0; x < VLEAD; ++x) va[x] = v_operand(vprev, x);
+    for (int x = 0; x < VLEAD; ++x) va[x] = v_operand(vprev, vidx(x));
     float mx = kNegInf;
 #pragma unroll
-    for (int idx = 0; idx < NP; ++idx) {
-      const u32x4 a = va[idx % VLEAD];
-      if (idx + VLEAD < NP) va[idx % VLEAD] = v_operand(vprev, idx + VLEAD);
-      o[idx / NU] = E::mfma(a, pb[idx % NU], o[idx / NU]);
+    for (int ip = 0; ip < NP; ++ip) {
+      const u32x4 a = va[ip % VLEAD];
+      if (ip + VLEAD < NP) va[ip % VLEAD] = v_operand(vprev, vidx(ip + VLEAD));
+      o[ip % DT] = E::mfma(a, pb[ip / DT], o[ip % DT]);
+      probs(NQ + ip);
 #pragma unroll
-      for (int e = 0; e < RPER; e += 2) {
-        const int flat = idx * RPER + e;
+      for (int e = 0; e < MPER; ++e) {
+        const int flat = 2 * (ip * MPER + e);
         mx = fmaxf(mx, fmaxf(sn[flat / 16][flat % 16], sn[flat / 16][flat % 16 + 1]));
       }
     }
+    l_run = fmaf(l_run, alpha, rs);
     if (update_max(mx)) rescale();
     __syncthreads();
     if constexpr (PAGED) rotate_ids();
