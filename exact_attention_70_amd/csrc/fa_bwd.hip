@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const typename E::elem* __restrict__ V, const typename E::elem* __restrict__ dO,
     const float* __restrict__ NL, const float* __restrict__ Dvec,
     float* __restrict__ dK, float* __restrict__ dV, int N, float scale, float scale_log2,
-    int n_ktiles) {
+    int n_ktiles, int hgroup) {
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;
   constexpr int TILE = kKvBQ * D * 2;
@@ -117,7 +117,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = hgroup > 0 ? xcd_grouped(blockIdx.x, n_ktiles, hgroup)
+                             : xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / n_ktiles;
   const int kb = (tile % n_ktiles) * kKvBN;       // low key tiles see the most queries
   const int my_k = kb + wave * 32 + l32;          // this lane's key (C-layout column)
@@ -385,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const typename E::elem* __restrict__ Q, const typename E::elem* __restrict__ K,
     const typename E::elem* __restrict__ V, const typename E::elem* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dvec,
-    float* __restrict__ dQ, int N, float scale, float scale_log2, int n_qtiles) {
+    float* __restrict__ dQ, int N, float scale, float scale_log2, int n_qtiles, int hgroup) {
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;
   constexpr int TILE = kQBN * D * 2;
@@ -396,7 +397,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = hgroup > 0 ? xcd_grouped(blockIdx.x, n_qtiles, hgroup)
+                             : xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / n_qtiles;
   const int qt = CAUSAL ? (n_qtiles - 1 - tile % n_qtiles) : (tile % n_qtiles);
   const int q0 = qt * kQBM;
@@ -503,13 +505,16 @@ hipError_t launch(const BwdArgs& a) {
   if (e != hipSuccess) return e;
   const float sl2 = a.scale * kLog2e;
   const int n_kt = (a.N + kKvBN - 1) / kKvBN;
+  // causal tiles differ in length: interleave heads so long tiles start first
+  // (each tile streams two [N, d] operands of its head)
+  const int hg = CAUSAL ? xcd_group((long long)a.B * a.H, (long long)a.N * D * 4) : 0;
   hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL>), dim3(a.B * a.H * n_kt), dim3(kThreads), 0,
-                     a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V, (const T*)a.dO, NLvec, a.Dvec, a.dK, a.dV, a.N, a.scale, sl2, n_kt);
+                     a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V, (const T*)a.dO, NLvec, a.Dvec, a.dK, a.dV, a.N, a.scale, sl2, n_kt, hg);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_qt = (a.N + kQBM - 1) / kQBM;
   hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL>), dim3(a.B * a.H * n_qt), dim3(kThreads), 0,
-                     a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V, (const T*)a.dO, NLvec, a.Dvec, a.dQ, a.N, a.scale, sl2, n_qt);
+                     a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V, (const T*)a.dO, NLvec, a.Dvec, a.dQ, a.N, a.scale, sl2, n_qt, hg);
   return hipGetLastError();
 }
 

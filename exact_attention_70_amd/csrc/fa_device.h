@@ -180,6 +180,20 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
+// Map hardware workgroup id b to a logical tile head * n_ranks + rank, for a
+// grid of heads * n_ranks workgroups with heads a multiple of 8 and rank 0 the
+// longest tile of a head.  Head h runs on XCD h % 8, so its tiles share that
+// XCD's L2.  Each XCD takes its heads in groups of g (g divides heads / 8) and
+// walks a group rank by rank, so the long tiles of every head in the group
+// start before the short ones of any of them.  Bijective under those
+// conditions, which the host checks before passing g > 0.
+__device__ __forceinline__ int xcd_grouped(int b, int n_ranks, int g) {
+  const int xcd = b & 7, slot = b >> 3;
+  const int grp = slot / (g * n_ranks), s = slot % (g * n_ranks);
+  const int u = grp * g + s % g;                 // the XCD's u-th head: xcd + 8u
+  return (xcd + 8 * u) * n_ranks + s / g;
+}
+
 // --------------------------------------------------------------------------
 // LDS tile layouts.  gfx950's LDS serves 256 bytes per clock as 64 banks of 4
 // bytes.  Rows are stored unpadded and 16-byte chunks are XOR-swizzled so that

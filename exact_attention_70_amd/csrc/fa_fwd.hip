@@ -117,11 +117,13 @@ template <class E, int D, bool CAUSAL, int BN, int OCC, bool PAGED = false>
 __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     const typename E::elem* __restrict__ Q, const typename E::elem* __restrict__ K,
     const typename E::elem* __restrict__ V, typename E::elem* __restrict__ O,
-    float* __restrict__ LSE, int N, int Nk, int delta, float scale_log2, int n_qtiles, PagedKV pg) {
+    float* __restrict__ LSE, int N, int Nk, int delta, float scale_log2, int n_qtiles, PagedKV pg,
+    int hgroup) {
   // scale_log2 = scale * log2(e): scores are handled in base 2.  N query rows
   // and Nk key rows per head; with CAUSAL, key j is visible to row i iff
   // j <= i + delta.  PAGED: one (sequence, head) per bh; N, Nk and delta are
   // that sequence's chunk length, cached length and cached length - chunk.
+  // hgroup > 0: workgroups map to tiles by xcd_grouped with that group size.
   constexpr int KSTEPS = D / 16;         // matrix k-steps over the head dim
   constexpr int DT = D / 32;             // 32-row tiles of O^T
   constexpr int TILE = BN * D * 2;       // bytes of one K or V tile
@@ -140,7 +142,8 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = hgroup > 0 ? xcd_grouped(blockIdx.x, n_qtiles, hgroup)
+                             : xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / n_qtiles;
   const int qt = CAUSAL ? (n_qtiles - 1 - tile % n_qtiles) : (tile % n_qtiles);
   const int q0 = qt * kBM;
@@ -675,9 +678,11 @@ hipError_t launch_bf16(const FwdArgs& a, int Nk, int delta) {
   using T = typename E::elem;
   const int n_qtiles = (a.N + kBM - 1) / kBM;
   const int grid = a.B * a.H * n_qtiles;
+  // causal tiles differ in length: interleave heads so long tiles start first
+  const int hg = CAUSAL ? xcd_group((long long)a.B * a.H, (long long)Nk * D * 4) : 0;
   hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, BN, OCC>), dim3(grid), dim3(kThreads), 0,
                      a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V, (T*)a.O, a.LSE, a.N, Nk,
-                     delta, a.scale * kLog2e, n_qtiles, PagedKV{});
+                     delta, a.scale * kLog2e, n_qtiles, PagedKV{}, hg);
   return hipGetLastError();
 }
 
@@ -687,9 +692,11 @@ hipError_t launch_paged(const FwdArgs& a) {
   const int n_qtiles = (a.N + kBM - 1) / kBM;          // a.N: the longest chunk
   const int grid = a.B * a.H * n_qtiles;                // a.B: the number of sequences
   const PagedKV pg{a.table, a.q_start, a.seq_lens, a.H, a.KVH, a.max_blocks, a.num_blocks};
+  const int hg =
+      CAUSAL ? xcd_group((long long)a.B * a.H, (long long)a.max_blocks * 16 * D * 4) : 0;
   hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, kBNDefault, 2, true>), dim3(grid),
                      dim3(kThreads), 0, a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V,
-                     (T*)a.O, a.LSE, 0, 0, 0, a.scale * kLog2e, n_qtiles, pg);
+                     (T*)a.O, a.LSE, 0, 0, 0, a.scale * kLog2e, n_qtiles, pg, hg);
   return hipGetLastError();
 }
 

@@ -102,6 +102,19 @@ hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_append(const AppendArgs& a);
 
+// Heads per group for xcd_grouped over a grid of `heads` heads whose tiles
+// each stream bytes_per_head of operands: the largest divisor g of heads / 8
+// whose g heads' operands fit in one XCD's 4 MiB L2 (at least 1).  0 when
+// heads is not a positive multiple of 8: the plain XCD blocking is used then.
+inline int xcd_group(long long heads, long long bytes_per_head) {
+  if (heads <= 0 || heads % 8 != 0) return 0;
+  const long long hpx = heads / 8;
+  int g = 1;
+  for (long long c = 2; c <= hpx; ++c)
+    if (hpx % c == 0 && c * bytes_per_head <= (4ll << 20)) g = (int)c;
+  return g;
+}
+
 // Decode partitioning shared by the workspace query and the launcher.
 #ifndef FA_DECODE_PART_TOKENS
 #define FA_DECODE_PART_TOKENS 256
