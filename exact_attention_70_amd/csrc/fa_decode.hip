@@ -34,7 +34,8 @@
 //   the four quarter-waves take interleaved tokens (4i + tq), so one 16-byte
 //   load instruction brings 4 token rows.  Each lane scores its rows against
 //   all G queries (packed two-element dot products, reduced across the 16
-//   lanes with DPP).  The running max is shared by the quarters; their
+//   lanes with DPP); the weights of two rows, rounded to the element type,
+//   meet the V values of those rows in one two-element dot product per d.  The running max is shared by the quarters; their
 //   denominators and outputs stay separate until the partition ends, when
 //   two cross-quarter exchanges combine them.
 // Merge kernel: one wave per (sequence, head) combines its partitions.
@@ -196,6 +197,7 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_partial_kernel(
   constexpr int STEP = 4 * NI;           // tokens per step: whole blocks
   constexpr int NB = STEP / kDecBS;      // blocks per step
   static_assert(STEP % kDecBS == 0, "a step is whole blocks");
+  static_assert(NI % 2 == 0, "rows are weighted in pairs");
   const int p = blockIdx.x;
   const int s = blockIdx.z;
   const int len = min(seq_lens[s], max_blocks_per_seq * kDecBS);
@@ -297,24 +299,32 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_partial_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[j][e] *= alpha[j];
     }
+    // rows of masked tokens become zeros (pad slots may hold NaN, and a zero
+    // weight times NaN is NaN)
+    if constexpr (MASKED) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const bool valid = !MASKED || t0 + 4 * i + tq < t_end;
-      float v[8];
+      for (int i = 0; i < NI; ++i)
+        if (t0 + 4 * i + tq >= t_end) vr[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+    // Two rows at a time: the pair's weights, rounded to the element type
+    // (as the forward rounds P), weight the pair of V values of each d
+    // through one two-element dot product; the denominator sums the same
+    // rounded weights.
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[2 * e] = E::lo(vr[i][e]);
-        v[2 * e + 1] = E::hi(vr[i][e]);
+    for (int i = 0; i < NI; i += 2) {
+      uint32_t vp[8];   // (row i, row i + 1) values of each of the lane's 8 d
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        vp[2 * w] = __builtin_amdgcn_perm(vr[i + 1][w], vr[i][w], 0x05040100u);
+        vp[2 * w + 1] = __builtin_amdgcn_perm(vr[i + 1][w], vr[i][w], 0x07060302u);
       }
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        const float pij = fast_exp2(sc[i][j] - m_new[j]);   // 0 for a masked row
-        l_run[j] += pij;
+        const uint32_t pk = E::pack(fast_exp2(sc[i][j] - m_new[j]),    // 0 for a masked row
+                                    fast_exp2(sc[i + 1][j] - m_new[j]));
+        l_run[j] = E::dot2(pk, E::kOnes, l_run[j]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float a2 = fmaf(pij, v[e], acc[j][e]);
-          acc[j][e] = MASKED ? (valid ? a2 : acc[j][e]) : a2;
-        }
+        for (int e = 0; e < 8; ++e) acc[j][e] = E::dot2(pk, vp[e], acc[j][e]);
       }
     }
     if (more) load_rows(rv2, vr);
