@@ -116,15 +116,49 @@ def _need_cuda(*ts):
             raise ValueError("libfa expects contiguous device tensors")
 
 
+def _want(t, shape, dtype, device, name):
+    """The kernels index every tensor by the shapes they are told, so a tensor
+    of another shape, type or device would be read or written out of bounds:
+    refuse it here, before any pointer reaches the library."""
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device:
+        raise ValueError(f"{name} must be {tuple(shape)} {dtype} on {device}, got "
+                         f"{tuple(t.shape)} {t.dtype} on {t.device}")
+    return t
+
+
+def _workspace(ws, nbytes, device):
+    if ws is None:
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    _need_cuda(ws)
+    if ws.device != device:
+        raise ValueError(f"workspace must be on {device}")
+    return ws
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _check_pool(k_pool, v_pool, like, block_size, KVH, d):
+    if k_pool.dim() != 4 or k_pool.shape[1] != block_size or k_pool.shape[2:] != (KVH, d):
+        raise ValueError(f"k_pool must be [num_blocks, {block_size}, {KVH}, {d}], got "
+                         f"{tuple(k_pool.shape)}")
+    _want(k_pool, tuple(k_pool.shape), like.dtype, like.device, "k_pool")
+    _want(v_pool, tuple(k_pool.shape), like.dtype, like.device, "v_pool")
+
+
 def fwd(q, k, v, *, causal: bool, scale: float | None = None, out=None, lse=None):
-    """O, LSE = attention(q, k, v) for [B, H, N, d] device tensors (bf16 or fp32)."""
+    """O, LSE = attention(q, k, v) for [B, H, N, d] device tensors (bf16, fp16 or fp32)."""
     _need_cuda(q, k, v)
     B, H, N, d = q.shape
     if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share shape [B, H, N, d] and dtype")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = torch.empty_like(q) if out is None else _want(out, q.shape, q.dtype, q.device, "out")
+    l = (torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None
+         else _want(lse, (B, H, N), torch.float32, q.device, "lse"))
     st = load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, N, d, scale,
                                int(bool(causal)), _dtype_code(q), _stream(q.device))
     _check(st, "fa_fwd")
@@ -142,8 +176,9 @@ def fwd_offset(q, k, v, *, q_offset: int, k_offset: int, causal: bool, scale: fl
             or k.dtype != q.dtype or v.dtype != q.dtype):
         raise ValueError("q [B,H,Nq,d], k and v [B,H,Nk,d] must share B, H, d and dtype")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = torch.empty_like(q) if out is None else _want(out, q.shape, q.dtype, q.device, "out")
+    l = (torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None
+         else _want(lse, (B, H, Nq), torch.float32, q.device, "lse"))
     st = load_library().fa_fwd_offset(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, Nq, Nk, d,
                                       int(q_offset), int(k_offset), scale, int(bool(causal)),
                                       _dtype_code(q), _stream(q.device))
@@ -159,8 +194,11 @@ def merge(o_a, lse_a, o_b, lse_b, *, out=None, lse_out=None):
     if o_b.shape != o_a.shape or o_b.dtype != o_a.dtype or lse_a.shape != (B, H, N) \
             or lse_b.shape != (B, H, N):
         raise ValueError("partials must share [B, H, N, d] / [B, H, N] shapes and dtype")
-    o = torch.empty_like(o_a) if out is None else out
-    l = torch.empty_like(lse_a) if lse_out is None else lse_out
+    if lse_a.dtype != torch.float32 or lse_b.dtype != torch.float32:
+        raise ValueError("lse_a and lse_b must be float32")
+    o = torch.empty_like(o_a) if out is None else _want(out, o_a.shape, o_a.dtype, o_a.device, "out")
+    l = (torch.empty_like(lse_a) if lse_out is None
+         else _want(lse_out, (B, H, N), torch.float32, o_a.device, "lse_out"))
     st = load_library().fa_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o), _ptr(l),
                                  B, H, N, d, _dtype_code(o_a), _stream(o_a.device))
     _check(st, "fa_merge")
@@ -176,17 +214,19 @@ def bwd(q, k, v, o, do, lse, *, causal: bool, scale: float | None = None, worksp
     """dQ, dK, dV (fp32) of attention given the forward's O and LSE and dO."""
     _need_cuda(q, k, v, o, do, lse)
     B, H, N, d = q.shape
+    for t, name in ((k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _want(t, q.shape, q.dtype, q.device, name)
+    _want(lse, (B, H, N), torch.float32, q.device, "lse")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if grads is None:
         grads = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
                       for _ in range(3))
-    dq, dk, dv = grads
-    ws_bytes = bwd_workspace_size(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = (_want(g, (B, H, N, d), torch.float32, q.device, n)
+                  for g, n in zip(grads, ("dq", "dk", "dv")))
+    workspace = _workspace(workspace, bwd_workspace_size(B, H, N, d), q.device)
     st = load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                                _ptr(dk), _ptr(dv), B, H, N, d, scale, int(bool(causal)),
-                               _dtype_code(q), _ptr(workspace), workspace.numel(),
+                               _dtype_code(q), _ptr(workspace), _nbytes(workspace),
                                _stream(q.device))
     _check(st, "fa_bwd")
     return dq, dk, dv
@@ -208,24 +248,27 @@ def paged_decode(q, k_pool, v_pool, block_table, seq_lens, *, block_size: int,
     S, H, d = q.shape
     num_blocks, KVH = k_pool.shape[0], k_pool.shape[2]
     mbps = block_table.shape[1]
+    _check_pool(k_pool, v_pool, q, block_size, KVH, d)
+    _want(block_table, (S, mbps), torch.int32, q.device, "block_table")
+    _want(seq_lens, (S,), torch.int32, q.device, "seq_lens")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((S, H), dtype=torch.float32, device=q.device) if lse is None else lse
-    ws_bytes = paged_decode_workspace_size(S, H, d, mbps, block_size)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else _want(out, q.shape, q.dtype, q.device, "out")
+    l = (torch.empty((S, H), dtype=torch.float32, device=q.device) if lse is None
+         else _want(lse, (S, H), torch.float32, q.device, "lse"))
+    workspace = _workspace(workspace, paged_decode_workspace_size(S, H, d, mbps, block_size),
+                           q.device)
     lib = load_library()
     if KVH == H:
         st = lib.fa_paged_decode(
             _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), block_size, S,
             H, d, mbps, num_blocks, scale, _ptr(o), _ptr(l), _dtype_code(q), _ptr(workspace),
-            workspace.numel(), _stream(q.device))
+            _nbytes(workspace), _stream(q.device))
         _check(st, "fa_paged_decode")
     else:
         st = lib.fa_paged_decode_gqa(
             _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), block_size, S,
             H, KVH, d, mbps, num_blocks, scale, _ptr(o), _ptr(l), _dtype_code(q), _ptr(workspace),
-            workspace.numel(), _stream(q.device))
+            _nbytes(workspace), _stream(q.device))
         _check(st, "fa_paged_decode_gqa")
     return o, l
 
@@ -238,17 +281,23 @@ def paged_kv_append(k_new, v_new, k_pool, v_pool, block_table, seq_lens, free_li
     _need_cuda(k_new, v_new, k_pool, v_pool, block_table, seq_lens, free_list, free_count,
                n_failed)
     S, KVH, d = k_new.shape
-    if v_new.shape != k_new.shape or k_pool.shape[2:] != (KVH, d) or v_pool.shape != k_pool.shape:
-        raise ValueError("k_new/v_new [S, KVH, d] must match pools [num_blocks, bs, KVH, d]")
+    dev = k_new.device
+    _want(v_new, k_new.shape, k_new.dtype, dev, "v_new")
+    _check_pool(k_pool, v_pool, k_new, block_size, KVH, d)
+    if block_table.dim() != 2 or block_table.shape[0] != S:
+        raise ValueError("block_table must be [S, max_blocks_per_seq]")
+    _want(block_table, tuple(block_table.shape), torch.int32, dev, "block_table")
+    _want(seq_lens, (S,), torch.int32, dev, "seq_lens")
+    _want(free_list, (free_list.numel(),), torch.int32, dev, "free_list")
+    _want(free_count, (1,), torch.int32, dev, "free_count")
+    _want(n_failed, (1,), torch.int32, dev, "n_failed")
     lib = load_library()
-    ws_bytes = int(lib.fa_paged_kv_append_workspace_size(S))
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=k_new.device)
+    workspace = _workspace(workspace, int(lib.fa_paged_kv_append_workspace_size(S)), dev)
     st = lib.fa_paged_kv_append(
         _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
         _ptr(free_list), _ptr(free_count), _ptr(n_failed), S, KVH, d, block_size,
         block_table.shape[1], k_pool.shape[0], free_list.numel(), _dtype_code(k_new),
-        _ptr(workspace), workspace.numel(), _stream(k_new.device))
+        _ptr(workspace), _nbytes(workspace), _stream(k_new.device))
     _check(st, "fa_paged_kv_append")
 
 
@@ -260,9 +309,16 @@ def paged_prefill(q, q_start, k_pool, v_pool, block_table, seq_lens, *, block_si
     T, H, d = q.shape
     S = seq_lens.numel()
     KVH = k_pool.shape[2]
+    _check_pool(k_pool, v_pool, q, block_size, KVH, d)
+    _want(q_start, (S + 1,), torch.int32, q.device, "q_start")
+    _want(seq_lens, (S,), torch.int32, q.device, "seq_lens")
+    if block_table.dim() != 2 or block_table.shape[0] != S:
+        raise ValueError("block_table must be [S, max_blocks_per_seq]")
+    _want(block_table, tuple(block_table.shape), torch.int32, q.device, "block_table")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((T, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = torch.empty_like(q) if out is None else _want(out, q.shape, q.dtype, q.device, "out")
+    l = (torch.empty((T, H), dtype=torch.float32, device=q.device) if lse is None
+         else _want(lse, (T, H), torch.float32, q.device, "lse"))
     st = load_library().fa_paged_prefill(
         _ptr(q), _ptr(q_start), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), S, H,
         KVH, d, block_size, block_table.shape[1], k_pool.shape[0], int(max_q_len), scale,

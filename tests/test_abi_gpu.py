@@ -46,3 +46,46 @@ def test_bwd_workspace_too_small_raises(gpu):
     with pytest.raises(binding.LibfaError) as ei:
         binding.bwd(x, x, x, x, x, lse, causal=True, workspace=ws)
     assert ei.value.status == -6
+
+
+def test_binding_refuses_mismatched_tensors(gpu):
+    """Plain pointers cross the C ABI, so the binding refuses tensors whose
+    shape, type or device differ from what the call implies; nothing runs."""
+    q = torch.zeros(1, 2, 64, 64, device=gpu, dtype=torch.bfloat16)
+    o_short = torch.full((1, 2, 32, 64), 5.0, device=gpu).to(torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.fwd(q, q, q, causal=True, out=o_short)
+    with pytest.raises(ValueError):
+        binding.fwd(q, q, q, causal=True, lse=torch.zeros(1, 2, 64, device=gpu, dtype=torch.bfloat16))
+    lse = torch.zeros(1, 2, 64, device=gpu)
+    with pytest.raises(ValueError):
+        binding.bwd(q, q, q, q, q[:, :1].contiguous(), lse, causal=True)
+    with pytest.raises(ValueError):
+        binding.bwd(q, q, q, q, q, lse, causal=True,
+                    grads=tuple(torch.empty(1, 2, 64, 64, device=gpu, dtype=torch.bfloat16)
+                                for _ in range(3)))
+    qd = torch.zeros(2, 4, 128, device=gpu, dtype=torch.bfloat16)
+    pool = torch.zeros(3, 16, 4, 128, device=gpu, dtype=torch.bfloat16)
+    lens = torch.tensor([5, 7], device=gpu, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        binding.paged_decode(qd, pool, pool, torch.zeros(2, 1, device=gpu, dtype=torch.int64), lens,
+                             block_size=16)
+    with pytest.raises(ValueError):
+        binding.paged_decode(qd, pool.float(), pool.float(),
+                             torch.zeros(2, 1, device=gpu, dtype=torch.int32), lens, block_size=16)
+    torch.cuda.synchronize()
+    assert bool((o_short.float() == 5.0).all())
+
+
+def test_workspace_size_counts_bytes(gpu):
+    """A workspace of another element type is sized by its bytes."""
+    g = torch.Generator(device=gpu).manual_seed(3)
+    q, k, v, do = (torch.randn(1, 2, 128, 64, device=gpu, generator=g).to(torch.bfloat16)
+                   for _ in range(4))
+    o, lse = binding.fwd(q, k, v, causal=True)
+    ref = binding.bwd(q, k, v, o, do, lse, causal=True)
+    ws = torch.empty(binding.bwd_workspace_size(1, 2, 128, 64) // 4, device=gpu)   # float32
+    got = binding.bwd(q, k, v, o, do, lse, causal=True, workspace=ws)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
