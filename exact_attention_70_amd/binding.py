@@ -76,7 +76,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fa_paged_kv_append_workspace_size.restype = sz
     lib.fa_paged_kv_append.argtypes = [vp] * 9 + [i] * 8 + [vp, sz, vp]
     lib.fa_paged_kv_append.restype = i
-    lib.fa_paged_prefill.argtypes = [vp] * 6 + [i] * 8 + [f, i, vp, vp, i, vp]
+    lib.fa_paged_prefill.argtypes = [vp] * 6 + [i] * 9 + [f, i, vp, vp, i, vp]
     lib.fa_paged_prefill.restype = i
     if path is None:
         _lib = lib
@@ -320,8 +320,8 @@ def paged_prefill(q, q_start, k_pool, v_pool, block_table, seq_lens, *, block_si
     l = (torch.empty((T, H), dtype=torch.float32, device=q.device) if lse is None
          else _want(lse, (T, H), torch.float32, q.device, "lse"))
     st = load_library().fa_paged_prefill(
-        _ptr(q), _ptr(q_start), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), S, H,
-        KVH, d, block_size, block_table.shape[1], k_pool.shape[0], int(max_q_len), scale,
+        _ptr(q), _ptr(q_start), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), S, T,
+        H, KVH, d, block_size, block_table.shape[1], k_pool.shape[0], int(max_q_len), scale,
         int(bool(causal)), _ptr(o), _ptr(l), _dtype_code(q), _stream(q.device))
     _check(st, "fa_paged_prefill")
     return o, l

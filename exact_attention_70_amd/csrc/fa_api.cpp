@@ -213,21 +213,24 @@ int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
 }
 
 int fa_paged_prefill(const void* q, const int32_t* q_start, const void* k_pool, const void* v_pool,
-                     const int32_t* block_table, const int32_t* seq_lens, int num_seqs, int H,
-                     int KVH, int d, int block_size, int max_blocks_per_seq, int num_blocks,
-                     int max_q_len, float scale, int causal, void* o, float* lse, int dtype,
-                     void* stream) {
+                     const int32_t* block_table, const int32_t* seq_lens, int num_seqs,
+                     int total_q, int H, int KVH, int d, int block_size, int max_blocks_per_seq,
+                     int num_blocks, int max_q_len, float scale, int causal, void* o, float* lse,
+                     int dtype, void* stream) {
   if (dtype != FA_DT_F32 && dtype != FA_DT_BF16 && dtype != FA_DT_F16) return FA_ERR_DTYPE;
-  if (num_seqs < 0 || H < 1 || KVH < 1 || d < 1 || block_size < 1 || max_blocks_per_seq < 1 ||
-      num_blocks < 1 || max_q_len < 1 || max_q_len > kMaxN)
+  if (num_seqs < 0 || total_q < 0 || H < 1 || KVH < 1 || d < 1 || block_size < 1 ||
+      max_blocks_per_seq < 1 || num_blocks < 1 || max_q_len < 1 || max_q_len > kMaxN)
     return FA_ERR_SHAPE;
+  // the packed tensors are addressed through 32-bit buffer offsets (plus the
+  // rows a last query tile reads past the end)
+  if (((long long)total_q + 128) * H * d * 2 >= (1LL << 31)) return FA_ERR_SHAPE;
   if (H % KVH != 0 || !std::isfinite(scale)) return FA_ERR_SHAPE;
   if (dtype == FA_DT_F32 || block_size != 16 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
   if ((long long)max_q_len * H * d * 2 >= (1LL << 31)) return FA_ERR_SHAPE;
   if ((long long)max_blocks_per_seq * block_size > kMaxN) return FA_ERR_SHAPE;
   if ((long long)block_size * KVH * d * 2 >= (1LL << 31)) return FA_ERR_SHAPE;
   if ((long long)num_seqs * H * ((max_q_len + 127) / 128) >= (1LL << 31)) return FA_ERR_SHAPE;
-  if (num_seqs == 0) return FA_OK;
+  if (num_seqs == 0 || total_q == 0) return FA_OK;
   if (!q || !q_start || !k_pool || !v_pool || !block_table || !seq_lens || !o || !lse)
     return FA_ERR_NULL;
   const void* ptrs[] = {q, k_pool, v_pool, o};
@@ -250,7 +253,7 @@ int fa_paged_prefill(const void* q, const int32_t* q_start, const void* k_pool, 
             hipSuccess ||
         hipStreamSynchronize(st) != hipSuccess)
       return FA_ERR_HIP;
-    if (starts[0] != 0) return FA_ERR_INVALID;
+    if (starts[0] != 0 || starts[num_seqs] > total_q) return FA_ERR_INVALID;
     for (int s = 0; s < num_seqs; ++s) {
       const int n = starts[s + 1] - starts[s], L = lens[s];
       if (n < 0 || n > max_q_len || L < n || (long long)L > (long long)max_blocks_per_seq * block_size)
@@ -269,6 +272,7 @@ int fa_paged_prefill(const void* q, const int32_t* q_start, const void* k_pool, 
   a.KVH = KVH;
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = num_blocks;
+  a.total_q = total_q;
   return hip_status(fa::launch_fwd(a));
 }
 

@@ -62,6 +62,7 @@ struct PagedKV {
   const int32_t* q_start;
   const int32_t* seq_lens;
   int H, KVH, max_blocks, num_blocks;
+  int total_q;   // rows of the packed Q/O/LSE
 };
 
 // Physical ids of the four 16-token blocks one 64-key tile spans (-1: past
@@ -154,6 +155,7 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
   const int lstride = PAGED ? pg.H : 1;
   size_t head_off, lse_off;
   uint32_t head_bytes, lse_bytes;
+  int qrow0 = 0;                                    // packed row of the chunk's first query
   const int32_t* table_row = nullptr;
   int kvh = 0;
   if constexpr (PAGED) {
@@ -162,11 +164,17 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     N = pg.q_start[seq + 1] - qs;
     Nk = pg.seq_lens[seq];
     delta = Nk - N;                                 // the chunk is the sequence's last tokens
-    if (q0 >= N) return;                            // query tile past this sequence's chunk
-    head_off = ((size_t)qs * pg.H + h) * D;
-    head_bytes = (uint32_t)(((size_t)(N - 1) * pg.H + 1) * D * 2);
-    lse_off = (size_t)qs * pg.H + h;
-    lse_bytes = (uint32_t)(((size_t)(N - 1) * pg.H + 1) * 4);
+    // a chunk outside the packed rows (malformed offsets) is skipped; so is a
+    // query tile past the chunk
+    if (qs < 0 || q0 >= N || qs > pg.total_q - N) return;
+    qrow0 = qs;
+    // resources over the whole packed tensors, from this head's column on:
+    // nothing outside them is touched whatever the offsets say; rows past the
+    // chunk (the next sequence's) are never stored
+    head_off = (size_t)h * D;
+    head_bytes = (uint32_t)(((size_t)pg.total_q * pg.H - h) * D * 2);
+    lse_off = (size_t)h;
+    lse_bytes = (uint32_t)(((size_t)pg.total_q * pg.H - h) * 4);
     table_row = pg.table + (size_t)seq * pg.max_blocks;
     kvh = h / (pg.H / pg.KVH);
   } else {
@@ -229,12 +237,12 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
   if (n_kv == 0) {
     // no row of this tile sees any key: empty softmax, O = 0 and LSE = -inf
     const int row = q0 + tid / 2;
-    if (tid < 2 * kBM) {
+    if (tid < 2 * kBM && (!PAGED || row < N)) {
+      const uint32_t prow = (uint32_t)(qrow0 + row);
 #pragma unroll
       for (int c = 0; c < D / 16; ++c)
-        bstore16(u32x4{0u, 0u, 0u, 0u}, rO,
-                 (uint32_t)(row * qstride + (tid & 1) * (D / 2) + 8 * c) * 2);
-      if ((tid & 1) == 0) bstore4f(kNegInf, rL, (uint32_t)row * lstride * 4);
+        bstore16(u32x4{0u, 0u, 0u, 0u}, rO, (prow * qstride + (tid & 1) * (D / 2) + 8 * c) * 2);
+      if ((tid & 1) == 0) bstore4f(kNegInf, rL, prow * lstride * 4);
     }
     return;
   }
@@ -247,7 +255,7 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
   u32x4 qf[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s)
-    qf[s] = bload16(rQ, (uint32_t)(my_q_row * qstride + 16 * s + 8 * half) * 2);
+    qf[s] = bload16(rQ, ((uint32_t)(qrow0 + my_q_row) * qstride + 16 * s + 8 * half) * 2);
   // The softmax takes its maximum over raw scores and folds the scale into one
   // multiply-add, which needs a positive multiplier: for a negative scale,
   // negate Q once (exact in bf16) and use |scale|.
@@ -489,11 +497,11 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
       u32x2 w;
       w[0] = E::pack(o[t][4 * g] * inv, o[t][4 * g + 1] * inv);
       w[1] = E::pack(o[t][4 * g + 2] * inv, o[t][4 * g + 3] * inv);
-      bstore8(w, rO, (uint32_t)(my_q * qstride + d0) * 2);
+      if (!PAGED || my_q < N) bstore8(w, rO, ((uint32_t)(qrow0 + my_q) * qstride + d0) * 2);
     }
-  if (half == 0)
+  if (half == 0 && (!PAGED || my_q < N))
     bstore4f(l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf, rL,
-             (uint32_t)my_q * lstride * 4);
+             (uint32_t)(qrow0 + my_q) * lstride * 4);
 }
 
 // ---------------------------------------------------------------------------
@@ -691,7 +699,8 @@ hipError_t launch_paged(const FwdArgs& a) {
   using T = typename E::elem;
   const int n_qtiles = (a.N + kBM - 1) / kBM;          // a.N: the longest chunk
   const int grid = a.B * a.H * n_qtiles;                // a.B: the number of sequences
-  const PagedKV pg{a.table, a.q_start, a.seq_lens, a.H, a.KVH, a.max_blocks, a.num_blocks};
+  const PagedKV pg{a.table,      a.q_start,    a.seq_lens,  a.H,
+                   a.KVH,        a.max_blocks, a.num_blocks, a.total_q};
   const int hg =
       CAUSAL ? xcd_group((long long)a.B * a.H, (long long)a.max_blocks * 16 * D * 4) : 0;
   hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, kBNDefault, 2, true>), dim3(grid),

@@ -29,6 +29,7 @@ struct FwdArgs {
   const int32_t* q_start = nullptr;
   const int32_t* seq_lens = nullptr;
   int KVH = 0, max_blocks = 0, num_blocks = 0;
+  int total_q = 0;   // rows of the packed Q/O/LSE
 };
 
 struct MergeArgs {

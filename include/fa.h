@@ -250,7 +250,11 @@ int fa_paged_decode_gqa(const void* q, const void* k_pool, const void* v_pool,
  * head h reads cached head h / (H / KVH).
  *
  *   q            in   [total_q, H, d] packed rows of all chunks, dtype bf16/fp16
- *   q_start      in   [num_seqs + 1] int32, q_start[0] = 0, ascending
+ *   q_start      in   [num_seqs + 1] int32, q_start[0] = 0, ascending, <= total_q;
+ *                     a chunk not inside [0, total_q) is skipped (its rows are
+ *                     not written), so malformed offsets never reach memory
+ *                     outside q, o and lse
+ *   total_q      rows of q, o and lse; (total_q + 128) * H * d * 2 < 2^31
  *   k_pool/v_pool in  [num_blocks, 16, KVH, d], same dtype
  *   block_table  in   [num_seqs, max_blocks_per_seq] int32
  *   seq_lens     in   [num_seqs] int32, n_s <= seq_lens[s] <= max_blocks_per_seq*16
@@ -263,10 +267,10 @@ int fa_paged_decode_gqa(const void* q, const void* k_pool, const void* v_pool,
  * as for fa_fwd.
  */
 int fa_paged_prefill(const void* q, const int32_t* q_start, const void* k_pool, const void* v_pool,
-                     const int32_t* block_table, const int32_t* seq_lens, int num_seqs, int H,
-                     int KVH, int d, int block_size, int max_blocks_per_seq, int num_blocks,
-                     int max_q_len, float scale, int causal, void* o, float* lse, int dtype,
-                     void* stream);
+                     const int32_t* block_table, const int32_t* seq_lens, int num_seqs,
+                     int total_q, int H, int KVH, int d, int block_size, int max_blocks_per_seq,
+                     int num_blocks, int max_q_len, float scale, int causal, void* o, float* lse,
+                     int dtype, void* stream);
 
 /*
  * fa_paged_kv_append_workspace_size -- bytes of workspace fa_paged_kv_append

@@ -209,9 +209,9 @@ def test_paged_kv_append_validation(lib):
     assert append(lib, S=0, kn=None) == OK
 
 
-def prefill(lib, S=3, H=8, KVH=2, d=128, bs=16, mq=64, dt=1, q=P, causal=1):
-    return lib.fa_paged_prefill(q, P, P, P, P, P, S, H, KVH, d, bs, 8, 100, mq, 0.1, causal, P2, P2,
-                                dt, None)
+def prefill(lib, S=3, T=96, H=8, KVH=2, d=128, bs=16, mq=64, dt=1, q=P, causal=1):
+    return lib.fa_paged_prefill(q, P, P, P, P, P, S, T, H, KVH, d, bs, 8, 100, mq, 0.1, causal, P2,
+                                P2, dt, None)
 
 
 def test_paged_prefill_validation(lib):
@@ -224,3 +224,6 @@ def test_paged_prefill_validation(lib):
     assert prefill(lib, q=None) == ERR_NULL
     assert prefill(lib, q=MIS) == ERR_ALIGN
     assert prefill(lib, S=0, q=None) == OK
+    assert prefill(lib, T=-1) == ERR_SHAPE
+    assert prefill(lib, T=1 << 20, H=32) == ERR_SHAPE    # packed rows past 32-bit offsets
+    assert prefill(lib, T=0, q=None) == OK

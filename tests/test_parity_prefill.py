@@ -75,3 +75,27 @@ def test_paged_prefill_debug_validation(gpu, monkeypatch):
         binding.paged_prefill(qq["q"].to(gpu), qq["q_start"].to(gpu), pd["k_pool"], pd["v_pool"],
                               pd["block_table"], pd["seq_lens"], block_size=16, max_q_len=11)
     assert e.value.status == -7
+
+
+def test_paged_prefill_chunks_outside_the_packed_rows_are_skipped(gpu):
+    """Offsets are trusted like a page table, but a chunk that does not lie
+    inside [0, total_q) is skipped rather than read or written out of bounds:
+    here the second chunk claims 195 rows from row 5 and the third starts past
+    the end.  The first chunk is still computed; the other rows keep what the
+    output held."""
+    lens = [20, 30, 40]
+    p = workloads.paged_inputs(3, 4, 128, 16, 1, 40, seed=7400, seq_lens=lens, kv_heads=2)
+    qq = workloads.prefill_queries([5, 7], 4, 128, seed=7401)          # 12 packed rows
+    q_start = torch.tensor([0, 5, 200, 12], dtype=torch.int32)
+    pd = {k: (v.to(gpu) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+    out = torch.full((12, 4, 128), 3.0, device=gpu).to(torch.bfloat16)
+    lse = torch.full((12, 4), 3.0, device=gpu)
+    binding.paged_prefill(qq["q"].to(gpu), q_start.to(gpu), pd["k_pool"], pd["v_pool"],
+                          pd["block_table"], pd["seq_lens"], block_size=16, max_q_len=8,
+                          scale=128 ** -0.5, out=out, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.paged_prefill(qq["q"][:5], torch.tensor([0, 5]), p["k_pool"], p["v_pool"],
+                                  p["block_table"][:1], p["seq_lens"][:1], 16, 128 ** -0.5, True)
+    assert max_abs(out[:5].double().cpu().numpy(), ro) <= TOL["bf16"]
+    assert max_abs(lse[:5].double().cpu().numpy(), rl) <= TOL["bf16"]
+    assert bool((out[5:].float() == 3.0).all()) and bool((lse[5:] == 3.0).all())
