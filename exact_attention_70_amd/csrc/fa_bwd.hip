@@ -186,15 +186,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   };
   barrier_all();
 
-  // stage A operand idx: sub-tile, k-step, {Q -> S, dO -> dP}
+  // stage A operand idx: k-step idx / 4, sub-tile (idx / 2) % 2, {Q -> S, dO -> dP}:
+  // four independent accumulator chains in turn, so that with one wave per
+  // SIMD a matrix op rarely waits for the result of the one before it
   auto a_operand = [&](const unsigned char* sQ, const unsigned char* sO, int idx)
       __attribute__((always_inline)) {
-    const int sub = idx / (2 * KSTEPS), k = (idx / 2) % KSTEPS;
+    const int sub = (idx >> 1) & 1, k = idx >> 2;
     const unsigned char* base = (idx & 1) ? sO : sQ;
     return *(const u32x4*)(base + rofs[k] + sub * 32 * D * 2);
   };
   auto a_op = [&](int idx, u32x4 a, f32x16 (&s)[2], f32x16 (&dp)[2]) __attribute__((always_inline)) {
-    const int sub = idx / (2 * KSTEPS), k = (idx / 2) % KSTEPS;
+    const int sub = (idx >> 1) & 1, k = idx >> 2;
     if (idx & 1) dp[sub] = E::mfma(a, vf[k], dp[sub]);
     else s[sub] = E::mfma(a, kf[k], s[sub]);
   };
