@@ -37,6 +37,21 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak (published)
 
+# benchmark parts, named by what they run and their shapes
+P_APPEND = "append_s64kv8d128"
+P_BWD4 = "bwd_causal_b4h16n2048d128"
+P_COPY = "copy_calib"
+P_DEC = "decode_s64h32d128"
+P_DEC_GQA = "decode_gqa_s64h32kv8d128"
+P_FWD = "fwd_causal_b1h32n8192d128"
+P_FWD16 = "fwd_causal_f16_b1h32n8192d128"
+P_FWD4 = "fwd_causal_b4h16n2048d128"
+P_FWD_GPT2 = "fwd_causal_b8h12n1024d64"
+P_PREFILL = "prefill_gqa_s8x1024h32kv8d128"
+P_RING = "ring_h32n8192d128"
+P_RING_FWD = "ring_fwd_h32n8192d128"
+P_RING_MERGE = "ring_merge_h32n8192d128"
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -75,16 +90,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
-                    help="comma list of parts to run: fwd_c3, fwd_c3_f16, fwd_c2, fwd_c4, bwd_c4, "
-                         "decode_c5, "
-                         "decode_gqa_c5 (8 cached heads), append_c5 (paged KV append), "
-                         "prefill_gqa (chunked prefill over a paged cache), "
-                         "ring_c3 (offset forward + merge of one ring step), copy_calib (a 1 GiB "
-                         "device copy used to scale the HBM-traffic counters)")
+                    help="comma list of parts to run: fwd_causal_b1h32n8192d128, "
+                         "fwd_causal_f16_b1h32n8192d128, fwd_causal_b8h12n1024d64, "
+                         "fwd_causal_b4h16n2048d128, bwd_causal_b4h16n2048d128, "
+                         "decode_s64h32d128, decode_gqa_s64h32kv8d128 (8 cached heads), "
+                         "append_s64kv8d128 (paged KV append), prefill_gqa_s8x1024h32kv8d128 "
+                         "(chunked prefill over a paged cache), ring_h32n8192d128 (offset "
+                         "forward + merge of one ring step), copy_calib (a 1 GiB device copy "
+                         "used to scale the HBM-traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(the kernels run on a single MI355X; see DESIGN.md for how the path would shard)",
+              "(the kernels run on a single MI355X; no multi-GPU path is built)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -100,138 +117,142 @@ def main():
         return not only or name in only
 
     # ------------------------------------------------------------ inputs (untimed)
-    c3, c2, c4, c5 = (workloads.CONFIGS[i] for i in (3, 2, 4, 5))
+    longctx, gpt2 = workloads.LONG_CONTEXT, workloads.GPT2_SHAPE
+    fwdbwd, dec = workloads.FWD_BWD, workloads.DECODE
     parts = {}
-    if want("fwd_c3"):
-        x = workloads.attention_inputs(c3.B, c3.H, c3.N, c3.d, "bf16", seed=workloads.seed_for(3))
+    if want(P_FWD):
+        x = workloads.attention_inputs(longctx.B, longctx.H, longctx.N, longctx.d, "bf16",
+                                       seed=longctx.seed)
         q, k, v = (x[n].to(dev) for n in "qkv")
         o = torch.empty_like(q)
-        lse = torch.empty(c3.B, c3.H, c3.N, device=dev)
-        parts["fwd_c3"] = dict(fn=lambda: binding.fwd(q, k, v, causal=True, scale=c3.scale, out=o,
-                                                       lse=lse),
-                               flops=causal_flops(c3.B, c3.H, c3.N, c3.d))
-    if want("fwd_c3_f16"):
+        lse = torch.empty(longctx.B, longctx.H, longctx.N, device=dev)
+        parts[P_FWD] = dict(fn=lambda: binding.fwd(q, k, v, causal=True, scale=longctx.scale,
+                                                   out=o, lse=lse),
+                            flops=causal_flops(longctx.B, longctx.H, longctx.N, longctx.d))
+    if want(P_FWD16):
         # the headline forward with fp16 inputs (same draws, cast to fp16)
-        xh = workloads.attention_inputs(c3.B, c3.H, c3.N, c3.d, "f16", seed=workloads.seed_for(3))
+        xh = workloads.attention_inputs(longctx.B, longctx.H, longctx.N, longctx.d, "f16",
+                                        seed=longctx.seed)
         qh, kh, vh = (xh[n].to(dev) for n in "qkv")
         oh = torch.empty_like(qh)
-        lseh = torch.empty(c3.B, c3.H, c3.N, device=dev)
-        parts["fwd_c3_f16"] = dict(fn=lambda: binding.fwd(qh, kh, vh, causal=True, scale=c3.scale,
-                                                           out=oh, lse=lseh),
-                                   flops=causal_flops(c3.B, c3.H, c3.N, c3.d))
-    if want("ring_c3"):
+        lseh = torch.empty(longctx.B, longctx.H, longctx.N, device=dev)
+        parts[P_FWD16] = dict(fn=lambda: binding.fwd(qh, kh, vh, causal=True, scale=longctx.scale,
+                                                     out=oh, lse=lseh),
+                              flops=causal_flops(longctx.B, longctx.H, longctx.N, longctx.d))
+    if want(P_RING):
         # one rank's non-diagonal ring step at the long-context shape: its 8192
         # queries (global rows 8192..16383) against the previous 8192-token
         # key/value block (every key visible), merged into the running result
-        xr = x if want("fwd_c3") else workloads.attention_inputs(c3.B, c3.H, c3.N, c3.d, "bf16",
-                                                                 seed=workloads.seed_for(3))
+        xr = x if want(P_FWD) else workloads.attention_inputs(
+            longctx.B, longctx.H, longctx.N, longctx.d, "bf16", seed=longctx.seed)
         qr, kr, vr = (xr[n].to(dev) for n in "qkv")
         po = torch.empty_like(qr)
-        pl = torch.empty(c3.B, c3.H, c3.N, device=dev)
-        acc_o, acc_l = binding.fwd(qr, kr, vr, causal=True, scale=c3.scale)   # diagonal block
-        parts["ring_c3_fwd"] = dict(fn=lambda: binding.fwd_offset(
-            qr, kr, vr, q_offset=c3.N, k_offset=0, causal=True, scale=c3.scale, out=po, lse=pl),
-            flops=4 * c3.B * c3.H * c3.N * c3.N * c3.d)
-        parts["ring_c3_merge"] = dict(fn=lambda: binding.merge(acc_o, acc_l, po, pl, out=acc_o,
-                                                                lse_out=acc_l),
-                                      bytes=3 * acc_o.numel() * 2 + 3 * acc_l.numel() * 4)
-    if want("fwd_c2"):
-        x2 = workloads.attention_inputs(c2.B, c2.H, c2.N, c2.d, "bf16", seed=workloads.seed_for(2),
-                                        in_scale=c2.in_scale)
+        pl = torch.empty(longctx.B, longctx.H, longctx.N, device=dev)
+        acc_o, acc_l = binding.fwd(qr, kr, vr, causal=True, scale=longctx.scale)   # diagonal block
+        parts[P_RING_FWD] = dict(fn=lambda: binding.fwd_offset(
+            qr, kr, vr, q_offset=longctx.N, k_offset=0, causal=True, scale=longctx.scale, out=po,
+            lse=pl),
+            flops=4 * longctx.B * longctx.H * longctx.N * longctx.N * longctx.d)
+        parts[P_RING_MERGE] = dict(fn=lambda: binding.merge(acc_o, acc_l, po, pl, out=acc_o,
+                                                            lse_out=acc_l),
+                                   bytes=3 * acc_o.numel() * 2 + 3 * acc_l.numel() * 4)
+    if want(P_FWD_GPT2):
+        x2 = workloads.attention_inputs(gpt2.B, gpt2.H, gpt2.N, gpt2.d, "bf16", seed=gpt2.seed,
+                                        in_scale=gpt2.in_scale)
         q2, k2, v2 = (x2[n].to(dev) for n in "qkv")
         o2 = torch.empty_like(q2)
-        lse2 = torch.empty(c2.B, c2.H, c2.N, device=dev)
-        parts["fwd_c2"] = dict(fn=lambda: binding.fwd(q2, k2, v2, causal=True, scale=c2.scale,
-                                                       out=o2, lse=lse2),
-                               flops=causal_flops(c2.B, c2.H, c2.N, c2.d))
-    if want("fwd_c4") or want("bwd_c4"):
-        x4 = workloads.attention_inputs(c4.B, c4.H, c4.N, c4.d, "bf16", seed=workloads.seed_for(4),
-                                        with_do=True)
+        lse2 = torch.empty(gpt2.B, gpt2.H, gpt2.N, device=dev)
+        parts[P_FWD_GPT2] = dict(fn=lambda: binding.fwd(q2, k2, v2, causal=True, scale=gpt2.scale,
+                                                        out=o2, lse=lse2),
+                                 flops=causal_flops(gpt2.B, gpt2.H, gpt2.N, gpt2.d))
+    if want(P_FWD4) or want(P_BWD4):
+        x4 = workloads.attention_inputs(fwdbwd.B, fwdbwd.H, fwdbwd.N, fwdbwd.d, "bf16",
+                                        seed=fwdbwd.seed, with_do=True)
         q4, k4, v4, do4 = (x4[n].to(dev) for n in ("q", "k", "v", "do"))
         o4 = torch.empty_like(q4)
-        lse4 = torch.empty(c4.B, c4.H, c4.N, device=dev)
+        lse4 = torch.empty(fwdbwd.B, fwdbwd.H, fwdbwd.N, device=dev)
         grads = tuple(torch.empty(q4.shape, dtype=torch.float32, device=dev) for _ in range(3))
-        ws4 = torch.empty(binding.bwd_workspace_size(c4.B, c4.H, c4.N, c4.d), dtype=torch.uint8,
-                          device=dev)
-        f4 = causal_flops(c4.B, c4.H, c4.N, c4.d)
-        parts["fwd_c4"] = dict(fn=lambda: binding.fwd(q4, k4, v4, causal=True, scale=c4.scale,
-                                                       out=o4, lse=lse4), flops=f4)
-        parts["bwd_c4"] = dict(fn=lambda: binding.bwd(q4, k4, v4, o4, do4, lse4, causal=True,
-                                                       scale=c4.scale, workspace=ws4, grads=grads),
-                               flops=int(2.5 * f4), flops_2x=2 * f4)
-    if want("decode_c5"):
-        p = workloads.paged_inputs(c5.num_seqs, c5.H, c5.d, c5.block_size, c5.min_len, c5.max_len,
-                                   seed=workloads.seed_for(5))
+        ws4 = torch.empty(binding.bwd_workspace_size(fwdbwd.B, fwdbwd.H, fwdbwd.N, fwdbwd.d),
+                          dtype=torch.uint8, device=dev)
+        f4 = causal_flops(fwdbwd.B, fwdbwd.H, fwdbwd.N, fwdbwd.d)
+        parts[P_FWD4] = dict(fn=lambda: binding.fwd(q4, k4, v4, causal=True, scale=fwdbwd.scale,
+                                                    out=o4, lse=lse4), flops=f4)
+        parts[P_BWD4] = dict(fn=lambda: binding.bwd(q4, k4, v4, o4, do4, lse4, causal=True,
+                                                    scale=fwdbwd.scale, workspace=ws4,
+                                                    grads=grads),
+                             flops=int(2.5 * f4), flops_2x=2 * f4)
+    if want(P_DEC):
+        p = workloads.paged_inputs(dec.num_seqs, dec.H, dec.d, dec.block_size, dec.min_len,
+                                   dec.max_len, seed=dec.seed)
         pd = {kk: (vv.to(dev) if isinstance(vv, torch.Tensor) else vv) for kk, vv in p.items()}
         od = torch.empty_like(pd["q"])
-        lsed = torch.empty(c5.num_seqs, c5.H, device=dev)
-        wsd = torch.empty(binding.paged_decode_workspace_size(c5.num_seqs, c5.H, c5.d,
+        lsed = torch.empty(dec.num_seqs, dec.H, device=dev)
+        wsd = torch.empty(binding.paged_decode_workspace_size(dec.num_seqs, dec.H, dec.d,
                                                               p["max_blocks_per_seq"], 16),
                           dtype=torch.uint8, device=dev)
         tokens = int(p["seq_lens"].long().sum())
-        kv_bytes = tokens * c5.H * c5.d * 2 * 2
-        parts["decode_c5"] = dict(fn=lambda: binding.paged_decode(
+        kv_bytes = tokens * dec.H * dec.d * 2 * 2
+        parts[P_DEC] = dict(fn=lambda: binding.paged_decode(
             pd["q"], pd["k_pool"], pd["v_pool"], pd["block_table"], pd["seq_lens"], block_size=16,
-            scale=c5.scale, workspace=wsd, out=od, lse=lsed), bytes=kv_bytes, tokens=tokens)
-    if want("decode_gqa_c5") or want("append_c5"):
+            scale=dec.scale, workspace=wsd, out=od, lse=lsed), bytes=kv_bytes, tokens=tokens)
+    if want(P_DEC_GQA) or want(P_APPEND):
         # the same sequences with 8 cached heads for the 32 query heads, and
         # enough free blocks for every timed append step
-        pg = workloads.paged_inputs(c5.num_seqs, c5.H, c5.d, c5.block_size, c5.min_len,
-                                    c5.max_len, seed=workloads.seed_for(5), kv_heads=8,
-                                    extra_blocks=4 * c5.num_seqs)
+        pg = workloads.paged_inputs(dec.num_seqs, dec.H, dec.d, dec.block_size, dec.min_len,
+                                    dec.max_len, seed=dec.seed, kv_heads=8,
+                                    extra_blocks=4 * dec.num_seqs)
         pgd = {kk: (vv.to(dev) if isinstance(vv, torch.Tensor) else vv) for kk, vv in pg.items()}
         tokens_g = int(pg["seq_lens"].long().sum())
-        if want("decode_gqa_c5"):
+        if want(P_DEC_GQA):
             og = torch.empty_like(pgd["q"])
-            lseg = torch.empty(c5.num_seqs, c5.H, device=dev)
-            wsg = torch.empty(binding.paged_decode_workspace_size(c5.num_seqs, c5.H, c5.d,
+            lseg = torch.empty(dec.num_seqs, dec.H, device=dev)
+            wsg = torch.empty(binding.paged_decode_workspace_size(dec.num_seqs, dec.H, dec.d,
                                                                   pg["max_blocks_per_seq"], 16),
                               dtype=torch.uint8, device=dev)
-            parts["decode_gqa_c5"] = dict(fn=lambda: binding.paged_decode(
+            parts[P_DEC_GQA] = dict(fn=lambda: binding.paged_decode(
                 pgd["q"], pgd["k_pool"], pgd["v_pool"], pgd["block_table"], pgd["seq_lens"],
-                block_size=16, scale=c5.scale, workspace=wsg, out=og, lse=lseg),
-                bytes=tokens_g * 8 * c5.d * 2 * 2, tokens=tokens_g)
-        if want("append_c5"):
-            ga = torch.Generator().manual_seed(workloads.seed_for(5) + 1)
-            kn = torch.randn((c5.num_seqs, 8, c5.d), generator=ga).to(torch.bfloat16).to(dev)
-            vn = torch.randn((c5.num_seqs, 8, c5.d), generator=ga).to(torch.bfloat16).to(dev)
+                block_size=16, scale=dec.scale, workspace=wsg, out=og, lse=lseg),
+                bytes=tokens_g * 8 * dec.d * 2 * 2, tokens=tokens_g)
+        if want(P_APPEND):
+            ga = torch.Generator().manual_seed(dec.seed + 1)
+            kn = torch.randn((dec.num_seqs, 8, dec.d), generator=ga).to(torch.bfloat16).to(dev)
+            vn = torch.randn((dec.num_seqs, 8, dec.d), generator=ga).to(torch.bfloat16).to(dev)
             fc = torch.tensor([pg["free_count"]], dtype=torch.int32, device=dev)
             nf = torch.zeros(1, dtype=torch.int32, device=dev)
             # lengths and the free stack advance on every call (state of a real decode loop)
             lens_a = pgd["seq_lens"].clone()
             table_a = pgd["block_table"].clone()
-            parts["append_c5"] = dict(fn=lambda: binding.paged_kv_append(
+            parts[P_APPEND] = dict(fn=lambda: binding.paged_kv_append(
                 kn, vn, pgd["k_pool"], pgd["v_pool"], table_a, lens_a, pgd["free_list"], fc, nf,
                 block_size=16), bytes=2 * 2 * kn.numel() * 2)
-    if want("prefill_gqa"):
+    if want(P_PREFILL):
         # chunked prefill: 8 sequences, a 1024-token chunk each at the end of
         # 1500..4000 cached tokens, 32 query heads on 8 cached heads
         lens_p = [1500, 2048, 2500, 3000, 3333, 3700, 4000, 1024]
-        pp = workloads.paged_inputs(len(lens_p), c5.H, c5.d, 16, 1, max(lens_p),
-                                    seed=workloads.seed_for(5) + 2, seq_lens=lens_p, kv_heads=8)
-        qp = workloads.prefill_queries([1024] * len(lens_p), c5.H, c5.d, seed=workloads.seed_for(5) + 3)
+        pp = workloads.paged_inputs(len(lens_p), dec.H, dec.d, 16, 1, max(lens_p),
+                                    seed=dec.seed + 2, seq_lens=lens_p, kv_heads=8)
+        qp = workloads.prefill_queries([1024] * len(lens_p), dec.H, dec.d, seed=dec.seed + 3)
         ppd = {kk: (vv.to(dev) if isinstance(vv, torch.Tensor) else vv) for kk, vv in pp.items()}
         qpd, qsd = qp["q"].to(dev), qp["q_start"].to(dev)
         op = torch.empty_like(qpd)
-        lsep = torch.empty(qpd.shape[0], c5.H, device=dev)
+        lsep = torch.empty(qpd.shape[0], dec.H, device=dev)
         pairs = sum(sum(L - 1024 + r + 1 for r in range(1024)) for L in lens_p)
-        parts["prefill_gqa"] = dict(fn=lambda: binding.paged_prefill(
+        parts[P_PREFILL] = dict(fn=lambda: binding.paged_prefill(
             qpd, qsd, ppd["k_pool"], ppd["v_pool"], ppd["block_table"], ppd["seq_lens"],
-            block_size=16, max_q_len=1024, scale=c5.scale, out=op, lse=lsep),
-            flops=4 * c5.H * c5.d * pairs)
-    if "copy_calib" in only:
+            block_size=16, max_q_len=1024, scale=dec.scale, out=op, lse=lsep),
+            flops=4 * dec.H * dec.d * pairs)
+    if P_COPY in only:
         # plain device copy of known size: the HBM-traffic counters of the kernels
         # are scaled by what the same counters read for this copy
         src = torch.empty(256 << 20, dtype=torch.float32, device=dev)      # 1 GiB
         src.fill_(1.0)
         dst = torch.empty_like(src)
-        parts["copy_calib"] = dict(fn=lambda: dst.copy_(src), bytes=2 * src.numel() * 4)
+        parts[P_COPY] = dict(fn=lambda: dst.copy_(src), bytes=2 * src.numel() * 4)
     torch.cuda.synchronize()
     log(f"inputs ready: {list(parts)}")
 
-    order = [n for n in ("fwd_c3", "fwd_c3_f16", "fwd_c2", "fwd_c4", "bwd_c4", "decode_c5",
-                         "decode_gqa_c5",
-                         "append_c5", "prefill_gqa", "ring_c3_fwd", "ring_c3_merge", "copy_calib")
+    order = [n for n in (P_FWD, P_FWD16, P_FWD_GPT2, P_FWD4, P_BWD4, P_DEC, P_DEC_GQA, P_APPEND,
+                         P_PREFILL, P_RING_FWD, P_RING_MERGE, P_COPY)
              if n in parts]
     for _ in range(args.warmup):
         for n in order:
@@ -274,7 +295,7 @@ def main():
         log(n, r)
 
     cpu = None
-    if not args.no_cpu_baseline and "fwd_c3" in parts:
+    if not args.no_cpu_baseline and P_FWD in parts:
         import oracle
         workers = min(os.cpu_count() or 1, 16)
         # whole passes of the fp64 oracle over the headline workload (all 32
@@ -282,35 +303,34 @@ def main():
         passes, dt = 0, 0.0
         while passes < 8 and (passes == 0 or dt < 10.0):
             t0 = time.perf_counter()
-            oracle.attention_forward(x["q"], x["k"], x["v"], c3.scale, True, workers=workers)
+            oracle.attention_forward(x["q"], x["k"], x["v"], longctx.scale, True, workers=workers)
             dt += time.perf_counter() - t0
             passes += 1
-        fl = passes * causal_flops(c3.B, c3.H, c3.N, c3.d)
+        fl = passes * causal_flops(longctx.B, longctx.H, longctx.N, longctx.d)
         cpu = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": workers,
                "kind": "oracle",
                "sample": f"fp64 oracle forward over the whole causal B=1 H=32 N=8192 d=128 "
                          f"workload, {passes} pass(es), {dt:.1f} s wall on {workers} threads"}
         log("cpu baseline", cpu)
 
-    head = res.get("fwd_c3")
+    head = res.get(P_FWD)
     src = source_hash("fa_fwd.hip", "fa_device.h")
     roof = None
     if head is not None:
-        traffic = load_traffic("fwd_c3", src)
+        traffic = load_traffic(P_FWD, src)
         roof = {"bound": "mfma", "achieved": head["tflops"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": head["frac_mfma_peak"], "traffic": traffic,
                 "kernel": "fwd_bf16_kernel<128,causal>", "source_hash": src}
-    dec = res.get("decode_c5")
+    dec_res = res.get(P_DEC)
     roof_dec = None
-    if dec is not None:
-        roof_dec = {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": dec["frac_hbm_peak"],
-                    "traffic": load_traffic("decode_c5",
+    if dec_res is not None:
+        roof_dec = {"bound": "hbm", "achieved": dec_res["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": dec_res["frac_hbm_peak"],
+                    "traffic": load_traffic(P_DEC,
                                             source_hash("fa_decode.hip", "fa_device.h")),
                     "kernel": "decode_partial_kernel + decode_merge_kernel"}
     out = {
-        "metric": "fwd attention TFLOP/s (causal bf16, % of MFMA dense bf16 peak); "
-                  "paged-decode GB/s in parts.decode_c5",
+        "metric": "fwd attention TFLOP/s & %MFMA peak; paged-decode GB/s & %HBM peak",
         "value": head["tflops"] if head else None,
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -52,9 +52,9 @@ def test_bwd_small_shapes(gpu, d, causal, N):
     _check(x, g, causal, scale, heads=None)
 
 
-def test_bwd_config4_sampled_heads(gpu):
-    c = workloads.CONFIGS[4]
-    x = workloads.attention_inputs(c.B, c.H, c.N, c.d, c.dtype, seed=workloads.seed_for(4),
+def test_bwd_b4h16n2048d128_sampled_heads(gpu):
+    c = workloads.FWD_BWD
+    x = workloads.attention_inputs(c.B, c.H, c.N, c.d, c.dtype, seed=workloads.FWD_BWD.seed,
                                    with_do=True)
     g = _run(gpu, x, c.causal, c.scale)
     _check(x, g, c.causal, c.scale, heads=[(0, 0), (1, 9), (2, 4), (3, 15)])

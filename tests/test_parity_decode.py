@@ -39,21 +39,21 @@ def _check(p, o, lse, scale, seqs=None):
 
 
 @pytest.fixture(scope="module")
-def config5():
-    c = workloads.CONFIGS[5]
+def decode_workload():
+    c = workloads.DECODE
     p = workloads.paged_inputs(c.num_seqs, c.H, c.d, c.block_size, c.min_len, c.max_len,
-                               seed=workloads.seed_for(5))
+                               seed=workloads.DECODE.seed)
     return c, p
 
 
-def test_decode_config5_all_sequences(gpu, config5):
-    c, p = config5
+def test_decode_s64h32d128_all_sequences(gpu, decode_workload):
+    c, p = decode_workload
     o, lse = _run(gpu, p, c.scale)
     _check(p, o, lse, c.scale)
 
 
-def test_decode_repermuted_pool_is_bitwise_identical(gpu, config5):
-    c, p = config5
+def test_decode_repermuted_pool_is_bitwise_identical(gpu, decode_workload):
+    c, p = decode_workload
     o, lse = _run(gpu, p, c.scale)
     g = torch.Generator().manual_seed(5)
     perm = torch.randperm(p["num_blocks"], generator=g)

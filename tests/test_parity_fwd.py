@@ -58,32 +58,32 @@ def test_fwd_small_shapes(gpu, dtype, d, causal, N):
     _check(x, o, lse, causal, scale, TOL[dtype])
 
 
-def test_fwd_config1_fp32_noncausal(gpu):
-    c = workloads.CONFIGS[1]
-    x = workloads.attention_inputs(c.B, c.H, c.N, c.d, c.dtype, seed=workloads.seed_for(1))
+def test_fwd_fp32_b1h2n256d64_noncausal(gpu):
+    c = workloads.FP32_SMALL
+    x = workloads.attention_inputs(c.B, c.H, c.N, c.d, c.dtype, seed=workloads.FP32_SMALL.seed)
     o, lse = _gpu_fwd(gpu, x, c.causal, c.scale)
     _check(x, o, lse, c.causal, c.scale, TOL["f32"])
 
 
-def test_fwd_config2_gpt2_small_causal(gpu):
-    c = workloads.CONFIGS[2]
-    x = workloads.attention_inputs(c.B, c.H, c.N, c.d, c.dtype, seed=workloads.seed_for(2),
+def test_fwd_gpt2_shape_b8h12n1024d64_causal(gpu):
+    c = workloads.GPT2_SHAPE
+    x = workloads.attention_inputs(c.B, c.H, c.N, c.d, c.dtype, seed=workloads.GPT2_SHAPE.seed,
                                    in_scale=c.in_scale)
     o, lse = _gpu_fwd(gpu, x, c.causal, c.scale)
     _check(x, o, lse, c.causal, c.scale, TOL["bf16"])
 
 
-def test_fwd_config2_unscaled_inputs_stress(gpu):
+def test_fwd_gpt2_shape_unscaled_inputs_stress(gpu):
     """Same shape without the 1/sqrt(d) input scaling: peakier softmax rows."""
-    c = workloads.CONFIGS[2]
-    x = workloads.attention_inputs(c.B, c.H, c.N, c.d, c.dtype, seed=workloads.seed_for(2) + 50)
+    c = workloads.GPT2_SHAPE
+    x = workloads.attention_inputs(c.B, c.H, c.N, c.d, c.dtype, seed=workloads.GPT2_SHAPE.seed + 50)
     o, lse = _gpu_fwd(gpu, x, c.causal, c.scale)
     _check(x, o, lse, c.causal, c.scale, TOL["bf16"], heads=[(b, h) for b in (0, 7) for h in range(12)])
 
 
-def test_fwd_config3_long_context_sampled(gpu):
-    c = workloads.CONFIGS[3]
-    x = workloads.attention_inputs(c.B, c.H, c.N, c.d, c.dtype, seed=workloads.seed_for(3))
+def test_fwd_long_context_b1h32n8192d128_sampled(gpu):
+    c = workloads.LONG_CONTEXT
+    x = workloads.attention_inputs(c.B, c.H, c.N, c.d, c.dtype, seed=workloads.LONG_CONTEXT.seed)
     o, lse = _gpu_fwd(gpu, x, c.causal, c.scale)
     # three whole heads
     _check(x, o, lse, c.causal, c.scale, TOL["bf16"], heads=[(0, 0), (0, 17), (0, 31)])

@@ -61,9 +61,9 @@ def test_gqa_decode_head_counts_and_step_edges(gpu, H, kvh):
 def test_gqa_decode_at_benchmark_shape(gpu):
     """The decode workload's sequences and lengths with 8 cached heads for the
     32 query heads, every sequence against the oracle."""
-    c5 = workloads.CONFIGS[5]
+    c5 = workloads.DECODE
     p = workloads.paged_inputs(c5.num_seqs, c5.H, c5.d, c5.block_size, c5.min_len, c5.max_len,
-                               seed=workloads.seed_for(5) + 7, kv_heads=8)
+                               seed=workloads.DECODE.seed + 7, kv_heads=8)
     pd = _to_dev(p, gpu)
     o, lse = binding.paged_decode(pd["q"], pd["k_pool"], pd["v_pool"], pd["block_table"],
                                   pd["seq_lens"], block_size=c5.block_size, scale=c5.scale)

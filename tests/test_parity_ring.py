@@ -161,8 +161,8 @@ def test_ring_step_long_context_block(gpu):
     """One rank's non-diagonal step at the long-context shape: 32 heads x 8192
     queries against the 8192-token key/value block just before them (every key
     visible).  Sampled heads and rows against the oracle."""
-    c = workloads.CONFIGS[3]
-    x = workloads.attention_inputs(c.B, c.H, c.N, c.d, c.dtype, seed=workloads.seed_for(3) + 1)
+    c = workloads.LONG_CONTEXT
+    x = workloads.attention_inputs(c.B, c.H, c.N, c.d, c.dtype, seed=workloads.LONG_CONTEXT.seed + 1)
     rows = np.r_[0:3, 4095:4097, 8189:8192]
     _check_offset(gpu, x, c.N, 0, True, c.scale, TOL["bf16"], heads=[(0, 0), (0, 17), (0, 31)],
                   rows=rows)

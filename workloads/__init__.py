@@ -25,8 +25,8 @@ from dataclasses import dataclass
 import torch
 
 __all__ = [
-    "AttnConfig", "DecodeConfig", "CONFIGS", "attention_inputs", "paged_inputs",
-    "seed_for",
+    "AttnConfig", "DecodeConfig", "FP32_SMALL", "GPT2_SHAPE", "LONG_CONTEXT", "FWD_BWD", "DECODE",
+    "WORKLOADS", "attention_inputs", "paged_inputs", "prefill_queries",
 ]
 
 _TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
@@ -43,6 +43,7 @@ class AttnConfig:
     causal: bool
     in_scale: float = 1.0  # multiplies the N(0,1) draws before the cast
     grads: bool = False    # also draw dO
+    seed: int = 0          # seed of the workload's draws
 
     @property
     def scale(self) -> float:
@@ -59,6 +60,7 @@ class DecodeConfig:
     min_len: int
     max_len: int
     dtype: str = "bf16"
+    seed: int = 0          # seed of the workload's draws
 
     @property
     def scale(self) -> float:
@@ -69,22 +71,20 @@ class DecodeConfig:
         return -(-self.max_len // self.block_size)
 
 
-# The five workloads of the benchmark.  Config 1 is the small fp32 case the
-# oracle finishes in well under a second; 2-4 are forward/backward shapes;
-# 5 is single-token decode over a paged cache.
-CONFIGS = {
-    1: AttnConfig("noncausal_f32_b1_h2_n256_d64", 1, 2, 256, 64, "f32", False),
-    2: AttnConfig("causal_bf16_b8_h12_n1024_d64", 8, 12, 1024, 64, "bf16", True,
-                  in_scale=1.0 / 8.0),
-    3: AttnConfig("causal_bf16_b1_h32_n8192_d128", 1, 32, 8192, 128, "bf16", True),
-    4: AttnConfig("causal_fwdbwd_bf16_b4_h16_n2048_d128", 4, 16, 2048, 128, "bf16", True,
-                  grads=True),
-    5: DecodeConfig("paged_decode_bf16_s64_h32_d128_bs16", 64, 32, 128, 16, 128, 4096),
-}
-
-
-def seed_for(cfg_id: int) -> int:
-    return 70000 + int(cfg_id)
+# The benchmark's workloads, each named by what it is.  FP32_SMALL is the
+# small fp32 case the oracle finishes in well under a second; GPT2_SHAPE,
+# LONG_CONTEXT and FWD_BWD are forward/backward shapes; DECODE is single-token
+# decode over a paged cache.  Each carries the seed its inputs are drawn from.
+FP32_SMALL = AttnConfig("noncausal_f32_b1_h2_n256_d64", 1, 2, 256, 64, "f32", False, seed=70001)
+GPT2_SHAPE = AttnConfig("causal_bf16_b8_h12_n1024_d64", 8, 12, 1024, 64, "bf16", True,
+                        in_scale=1.0 / 8.0, seed=70002)
+LONG_CONTEXT = AttnConfig("causal_bf16_b1_h32_n8192_d128", 1, 32, 8192, 128, "bf16", True,
+                          seed=70003)
+FWD_BWD = AttnConfig("causal_fwdbwd_bf16_b4_h16_n2048_d128", 4, 16, 2048, 128, "bf16", True,
+                     grads=True, seed=70004)
+DECODE = DecodeConfig("paged_decode_bf16_s64_h32_d128_bs16", 64, 32, 128, 16, 128, 4096,
+                      seed=70005)
+WORKLOADS = {w.name: w for w in (FP32_SMALL, GPT2_SHAPE, LONG_CONTEXT, FWD_BWD, DECODE)}
 
 
 def _gen(seed: int) -> torch.Generator:
