@@ -2,8 +2,9 @@
 
 Tolerances (max-abs): O <= 2e-2 for bf16 inputs, <= 1e-5 for fp32 inputs; the
 same bound is used for LSE.  Sizes span several tiles with ragged tails; the
-full-size workloads are checked on every head (configs 1, 2) or on sampled
-heads and rows (config 3, the benchmarked launch).
+full-size workloads are checked on every head (the small fp32 and GPT-2-shaped
+ones) or on sampled heads and rows (the benchmarked long-context launch, and
+the longest sequence the library accepts).
 """
 import math
 
@@ -92,6 +93,19 @@ def test_fwd_long_context_b1h32n8192d128_sampled(gpu):
     rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 4095, 4096, 8190, 8191],
                                      rng.integers(0, c.N, 54)]))
     _check(x, o, lse, c.causal, c.scale, TOL["bf16"], rows=rows)
+
+
+def test_fwd_maximum_length_sampled(gpu):
+    """The longest sequence the library accepts (N = 2^20, one head, d = 128),
+    where the 32-bit buffer offsets reach 256 MiB per head: rows at tile edges,
+    the middle, the last rows and random rows against the oracle."""
+    N = 1 << 20
+    x = workloads.attention_inputs(1, 1, N, 128, "bf16", seed=71000)
+    o, lse = _gpu_fwd(gpu, x, True, 128 ** -0.5)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, N // 2, N - 129, N - 128, N - 2, N - 1],
+                                     rng.integers(0, N, 7)]))
+    _check(x, o, lse, True, 128 ** -0.5, TOL["bf16"], rows=rows)
 
 
 def test_fwd_deterministic(gpu):

@@ -58,6 +58,21 @@ def test_gqa_decode_head_counts_and_step_edges(gpu, H, kvh):
     assert max_abs(lse.double().cpu().numpy(), rl) <= TOL
 
 
+def test_gqa_decode_maximum_length(gpu):
+    """One sequence of 2^20 cached tokens, the longest a table may describe
+    (65536 blocks of 16), 4 query heads on one cached head; pad slots NaN."""
+    L = 1 << 20
+    p = workloads.paged_inputs(1, 4, 128, 16, L, L, seed=5300, kv_heads=1, pad_value=float("nan"))
+    pd = _to_dev(p, gpu)
+    o, lse = binding.paged_decode(pd["q"], pd["k_pool"], pd["v_pool"], pd["block_table"],
+                                  pd["seq_lens"], block_size=16, scale=128 ** -0.5)
+    torch.cuda.synchronize()
+    ro, rl = oracle.paged_decode(p["q"], p["k_pool"], p["v_pool"], p["block_table"], p["seq_lens"],
+                                 16, 128 ** -0.5)
+    assert max_abs(o.double().cpu().numpy(), ro) <= TOL
+    assert max_abs(lse.double().cpu().numpy(), rl) <= TOL
+
+
 def test_gqa_decode_at_benchmark_shape(gpu):
     """The decode workload's sequences and lengths with 8 cached heads for the
     32 query heads, every sequence against the oracle."""
