@@ -15,8 +15,8 @@
  * Errors: status codes only; no C++ exception crosses this boundary.  Shapes,
  * dtypes, null pointers, alignment and workspace size are validated BEFORE
  * anything is launched, so a call that fails validation writes nothing.  A
- * launch failure reported by the HIP runtime maps to FA_ERR_HIP.  B == 0 or
- * num_seqs == 0 is a no-op that returns FA_OK.
+ * launch failure reported by the HIP runtime maps to FA_ERR_HIP.  B == 0,
+ * num_seqs == 0 or (prefill) total_q == 0 is a no-op that returns FA_OK.
  *
  * Layouts (row-major, contiguous): Q, K, V, O, dO and the fp32 gradients are
  * [B, H, N, d]; LSE is [B, H, N] fp32.  This is the [batch, heads, seq,
