@@ -114,7 +114,7 @@ constexpr bool probs_before_use(int npair, int pslots, int nq, int dt) {
   return true;
 }
 
-template <class E, int D, bool CAUSAL, int BN, int OCC, bool PAGED = false>
+template <class E, int D, bool CAUSAL, int BN, int OCC, bool PAGED = false, bool PAIRED = false>
 __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     const typename E::elem* __restrict__ Q, const typename E::elem* __restrict__ K,
     const typename E::elem* __restrict__ V, typename E::elem* __restrict__ O,
@@ -125,6 +125,10 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
   // j <= i + delta.  PAGED: one (sequence, head) per bh; N, Nk and delta are
   // that sequence's chunk length, cached length and cached length - chunk.
   // hgroup > 0: workgroups map to tiles by xcd_grouped with that group size.
+  // PAIRED (causal only): the workgroup runs rank r and rank n_qtiles - 1 - r
+  // of one head one after the other, so every workgroup has the same work and
+  // pays the per-tile start-up once per two tiles.  The host pairs only when
+  // the paired grid still fills the chip.
   constexpr int KSTEPS = D / 16;         // matrix k-steps over the head dim
   constexpr int DT = D / 32;             // 32-row tiles of O^T
   constexpr int TILE = BN * D * 2;       // bytes of one K or V tile
@@ -137,371 +141,391 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) unsigned char sV0[TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char sV1[TILE];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
-  const int l32 = lane & 31;
-  const int half = lane >> 5;
+  static_assert(!PAIRED || (CAUSAL && !PAGED), "pairing is for the contiguous causal forward");
 
-  const int tile = hgroup > 0 ? xcd_grouped(blockIdx.x, n_qtiles, hgroup)
+  int tile0, tile1 = 0, npass = 1;
+  if constexpr (PAIRED) {
+    const int n_ranks = (n_qtiles + 1) / 2;
+    const int t = hgroup > 0 ? xcd_grouped(blockIdx.x, n_ranks, hgroup)
                              : xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = tile / n_qtiles;
-  const int qt = CAUSAL ? (n_qtiles - 1 - tile % n_qtiles) : (tile % n_qtiles);
-  const int q0 = qt * kBM;
-
-  // row strides of Q/O (elements) and LSE: one head's rows are contiguous, or
-  // interleaved with the other heads in the packed layout of a prefill
-  const int qstride = PAGED ? pg.H * D : D;
-  const int lstride = PAGED ? pg.H : 1;
-  size_t head_off, lse_off;
-  uint32_t head_bytes, lse_bytes;
-  int qrow0 = 0;                                    // packed row of the chunk's first query
-  const int32_t* table_row = nullptr;
-  int kvh = 0;
-  if constexpr (PAGED) {
-    const int seq = bh / pg.H, h = bh % pg.H;
-    const int qs = pg.q_start[seq];
-    N = pg.q_start[seq + 1] - qs;
-    Nk = pg.seq_lens[seq];
-    delta = Nk - N;                                 // the chunk is the sequence's last tokens
-    // a chunk outside the packed rows (malformed offsets) is skipped; so is a
-    // query tile past the chunk
-    if (qs < 0 || q0 >= N || qs > pg.total_q - N) return;
-    qrow0 = qs;
-    // resources over the whole packed tensors, from this head's column on:
-    // nothing outside them is touched whatever the offsets say; rows past the
-    // chunk (the next sequence's) are never stored
-    head_off = (size_t)h * D;
-    head_bytes = (uint32_t)(((size_t)pg.total_q * pg.H - h) * D * 2);
-    lse_off = (size_t)h;
-    lse_bytes = (uint32_t)(((size_t)pg.total_q * pg.H - h) * 4);
-    table_row = pg.table + (size_t)seq * pg.max_blocks;
-    kvh = h / (pg.H / pg.KVH);
+    const int r = t % n_ranks, base = t / n_ranks * n_qtiles;
+    tile0 = base + r;
+    tile1 = base + n_qtiles - 1 - r;
+    npass = tile1 != tile0 ? 2 : 1;
   } else {
-    head_off = (size_t)bh * (size_t)N * D;
-    head_bytes = (uint32_t)N * D * 2;
-    lse_off = (size_t)bh * N;
-    lse_bytes = (uint32_t)N * 4;
+    tile0 = hgroup > 0 ? xcd_grouped(blockIdx.x, n_qtiles, hgroup)
+                       : xcd_remap(blockIdx.x, gridDim.x);
   }
-  const size_t khead_off = (size_t)bh * (size_t)Nk * D;
-  const uint32_t khead_bytes = (uint32_t)Nk * D * 2;
-  const auto rQ = make_rsrc(Q + head_off, head_bytes);
-  const auto rK = make_rsrc(K + (PAGED ? 0 : khead_off), PAGED ? 0u : khead_bytes);
-  const auto rV = make_rsrc(V + (PAGED ? 0 : khead_off), PAGED ? 0u : khead_bytes);
-  const auto rO = make_rsrc(O + head_off, head_bytes);
-  const auto rL = make_rsrc(LSE + lse_off, lse_bytes);
-  // Paged: a tile's block ids are read from the table one iteration before
-  // the transfers that use them (ids_v: tile j, ids_k: tile j+1, ids_f: tile
-  // j+2, read during iteration j), so no transfer waits on a table read.  The
-  // read index is clamped into the row (max_blocks >= 1) and entries past it
-  // become -1, which the transfer turns into zeros.
-  auto tile_ids = [&](int t) __attribute__((always_inline)) {
-    TileIds r{{-1, -1, -1, -1}};
+  for (int pass = 0; pass < npass; ++pass) {
+    if (pass) __syncthreads();                      // the first tile's LDS reads are done
+    const int tile = pass ? tile1 : tile0;
+    int tid = threadIdx.x;
+    // paired: hide the thread index from loop-invariant code motion, so that
+    // addresses derived from it are formed in each pass instead of being held
+    // in registers across both
+    if constexpr (PAIRED) asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
+    const int l32 = lane & 31;
+    const int half = lane >> 5;
+    const int bh = tile / n_qtiles;
+    const int qt = CAUSAL ? (n_qtiles - 1 - tile % n_qtiles) : (tile % n_qtiles);
+    const int q0 = qt * kBM;
+
+    // row strides of Q/O (elements) and LSE: one head's rows are contiguous, or
+    // interleaved with the other heads in the packed layout of a prefill
+    const int qstride = PAGED ? pg.H * D : D;
+    const int lstride = PAGED ? pg.H : 1;
+    size_t head_off, lse_off;
+    uint32_t head_bytes, lse_bytes;
+    int qrow0 = 0;                                    // packed row of the chunk's first query
+    const int32_t* table_row = nullptr;
+    int kvh = 0;
     if constexpr (PAGED) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int b = 4 * t + q;
-        const int v = table_row[min(b, pg.max_blocks - 1)];
-        r.b[q] = b < pg.max_blocks ? v : -1;
-      }
+      const int seq = bh / pg.H, h = bh % pg.H;
+      const int qs = pg.q_start[seq];
+      N = pg.q_start[seq + 1] - qs;
+      Nk = pg.seq_lens[seq];
+      delta = Nk - N;                                 // the chunk is the sequence's last tokens
+      // a chunk outside the packed rows (malformed offsets) is skipped; so is a
+      // query tile past the chunk
+      if (qs < 0 || q0 >= N || qs > pg.total_q - N) return;
+      qrow0 = qs;
+      // resources over the whole packed tensors, from this head's column on:
+      // nothing outside them is touched whatever the offsets say; rows past the
+      // chunk (the next sequence's) are never stored
+      head_off = (size_t)h * D;
+      head_bytes = (uint32_t)(((size_t)pg.total_q * pg.H - h) * D * 2);
+      lse_off = (size_t)h;
+      lse_bytes = (uint32_t)(((size_t)pg.total_q * pg.H - h) * 4);
+      table_row = pg.table + (size_t)seq * pg.max_blocks;
+      kvh = h / (pg.H / pg.KVH);
+    } else {
+      head_off = (size_t)bh * (size_t)N * D;
+      head_bytes = (uint32_t)N * D * 2;
+      lse_off = (size_t)bh * N;
+      lse_bytes = (uint32_t)N * 4;
     }
-    return r;
-  };
-  TileIds ids_v = tile_ids(0), ids_k = tile_ids(1), ids_f = ids_k;
-  // after a barrier (which has waited for the reads): the ids move to scalar
-  // registers, leaving only the ids in flight in vector registers
-  auto rotate_ids = [&]() __attribute__((always_inline)) {
-    ids_v = ids_k;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) ids_k.b[q] = __builtin_amdgcn_readfirstlane(ids_f.b[q]);
-  };
-  auto dma_k = [&](unsigned char* dst, int row0) __attribute__((always_inline)) {
-    if constexpr (PAGED)
-      dma_rows_paged<D, BN, kThreads / 64>(K, row0 == 0 ? ids_v : ids_k, Nk, pg.num_blocks, kvh,
-                                           pg.KVH, dst, row0, wave, lane);
-    else
-      dma_rows<D, BN, kThreads / 64>(rK, dst, row0, wave, lane);
-  };
-  auto dma_v = [&](unsigned char* dst, int row0) __attribute__((always_inline)) {
-    if constexpr (PAGED)
-      dma_rows_paged<D, BN, kThreads / 64>(V, ids_v, Nk, pg.num_blocks, kvh, pg.KVH, dst, row0,
-                                           wave, lane);
-    else
-      dma_rows<D, BN, kThreads / 64>(rV, dst, row0, wave, lane);
-  };
-
-  const int kv_end = CAUSAL ? min(Nk, q0 + kBM + delta) : Nk;
-  const int n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
-  // tiles [0, n_full) need no masking for any row of this workgroup
-  const int n_full = min(CAUSAL ? max(0, q0 + delta + 1) / BN : n_kv, Nk / BN);
-  if (n_kv == 0) {
-    // no row of this tile sees any key: empty softmax, O = 0 and LSE = -inf
-    const int row = q0 + tid / 2;
-    if (tid < 2 * kBM && (!PAGED || row < N)) {
-      const uint32_t prow = (uint32_t)(qrow0 + row);
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c)
-        bstore16(u32x4{0u, 0u, 0u, 0u}, rO, (prow * qstride + (tid & 1) * (D / 2) + 8 * c) * 2);
-      if ((tid & 1) == 0) bstore4f(kNegInf, rL, prow * lstride * 4);
-    }
-    return;
-  }
-
-  // ---- this wave's query rows, straight from HBM into B-operand registers;
-  //      K_0 and V_0 into ring slot 0
-  dma_k(sK0, 0);
-  dma_v(sV0, 0);
-  const int my_q_row = q0 + wave * 32 + l32;
-  u32x4 qf[KSTEPS];
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s)
-    qf[s] = bload16(rQ, ((uint32_t)(qrow0 + my_q_row) * qstride + 16 * s + 8 * half) * 2);
-  // The softmax takes its maximum over raw scores and folds the scale into one
-  // multiply-add, which needs a positive multiplier: for a negative scale,
-  // negate Q once (exact in bf16) and use |scale|.
-  if (scale_log2 < 0.f) {
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = qf[s] ^ 0x80008000u;
-    scale_log2 = -scale_log2;
-  }
-  barrier_all();                                    // K_0, V_0 landed
-
-  const int my_q = q0 + wave * 32 + l32;            // this lane's query row
-  // transpose-read geometry of the V^T operand (see tile_off / ds_read_tr16)
-  const int tr_row = 4 * half + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-  f32x16 o[DT];
-#pragma unroll
-  for (int t = 0; t < DT; ++t) o[t] = zero16();
-  float m_run = kNegInf;   // running max of scale*log2(e)*score (through the last reduced tile)
-  float l_run = 0.f;       // this lane's share of the running denominator
-  float alpha = 1.f;       // exp2(m_old - m_new) of the last reduced tile
-  constexpr int NQ = NSUB * KSTEPS;     // matrix ops of S = K Q^T per tile
-  constexpr int NP = DT * NU;           // matrix ops of O^T += V^T P^T per tile
-  constexpr int KLEAD = kKLead;
-  constexpr int VLEAD = kVLead;
-  // Issue schedule of one iteration's vector work over its NQ + NP matrix-op
-  // slots (S ops first, then P V ops ordered key block by key block).  The
-  // probabilities of the previous tile come in NPAIR pairs, key block kb
-  // being pairs [4kb, 4kb + 4); they are spread evenly over the first PSLOTS
-  // slots, so block kb is done before the first P V op that reads it (slot
-  // NQ + kb * DT).  The row max of the new tile takes pairs of scores in the
-  // P V slots, after the last S op.
-  constexpr int NPAIR = NSUB * 8;
-  constexpr int PSLOTS = NQ + NP - DT;
-  static_assert(NPAIR == 4 * NU, "four probability pairs per key block");
-  static_assert(NPAIR % NP == 0, "row-max pairs per P V op");
-  static_assert(probs_before_use(NPAIR, PSLOTS, NQ, DT), "a key block's probabilities come late");
-  constexpr int MPER = NPAIR / NP;      // row-max pairs per P V op
-
-  // Per-lane byte offsets of the operand reads inside a tile.  The swizzle
-  // makes them differ per k-step (K) and per column block (V); sub-tile,
-  // row-block and ring-slot offsets are compile-time constants added on top,
-  // which the LDS instructions take as immediates.  The offsets are re-pinned
-  // every iteration so they stay the only live copies.
-  uint32_t kofs[KSTEPS], vofs[DT][2];
-#pragma unroll
-  for (int k = 0; k < KSTEPS; ++k) kofs[k] = tile_off<D>(l32, 2 * k + half);
-#pragma unroll
-  for (int t = 0; t < DT; ++t) {
-    const int col = t * 32 + tr_col;
-    vofs[t][0] = tile_off<D>(tr_row, col >> 3) + (col & 7) * 2;
-    vofs[t][1] = tile_off<D>(tr_row + 8, col >> 3) + (col & 7) * 2;
-  }
-  auto pin_offsets = [&]() {
-#pragma unroll
-    for (int k = 0; k < KSTEPS; ++k) asm volatile("" : "+v"(kofs[k]));
-#pragma unroll
-    for (int t = 0; t < DT; ++t) asm volatile("" : "+v"(vofs[t][0]), "+v"(vofs[t][1]));
-  };
-  auto k_operand = [&](const unsigned char* sK, int idx) {
-    const int t = idx / KSTEPS, k = idx % KSTEPS;
-    return *(const u32x4*)(sK + kofs[k] + t * 32 * D * 2);
-  };
-  auto v_operand = [&](const unsigned char* sV, int idx) {
-    const int t = idx / NU, u = idx % NU;
-    const u32x2 lo = ds_read_tr16(sV + vofs[t][0] + u * 16 * D * 2);
-    const u32x2 hi = ds_read_tr16(sV + vofs[t][1] + u * 16 * D * 2);
-    const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-    return a;
-  };
-  // keys beyond this lane's row (causal) or beyond N become -inf
-  auto mask = [&](f32x16 (&s)[NSUB], int kb) {
-    const int lim = min(CAUSAL ? my_q + delta : Nk - 1, Nk - 1) - kb - 4 * half;
-#pragma unroll
-    for (int t = 0; t < NSUB; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (t * 32 + 8 * (i >> 2) + (i & 3) > lim) s[t][i] = kNegInf;
-  };
-  // Reference maximum from a tile's raw row max.  The reference moves only
-  // when the tile's maximum exceeds it by more than kSlack (base 2), so the
-  // probabilities stay <= 2^kSlack and the accumulated output is rescaled
-  // rarely; numerator and denominator share the reference, so their ratio
-  // and the log-sum-exp are unchanged.  Returns whether any row moved.
-  auto update_max = [&](float mx) {
-    mx = fmaxf(mx, swap_half(mx));
-    const float cand = mx * scale_log2;
-    const bool up = cand > m_run + kSlack;            // always true while m_run = -inf
-    const float m_new = up ? cand : m_run;
-    alpha = up ? fast_exp2(m_run - m_new) : 1.f;     // exp2(-inf) = 0 on the first tile
-    m_run = m_new;
-    return __builtin_amdgcn_ballot_w64(up) != 0;
-  };
-  auto rescale = [&]() {
-#pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
-  };
-
-  // prologue: S_0, its max; K_1 streams meanwhile
-  f32x16 sa[NSUB], sb[NSUB];
-  if constexpr (PAGED) ids_f = tile_ids(2);
-  if (n_kv > 1) dma_k(sK1, BN);
-  {
-#pragma unroll
-    for (int t = 0; t < NSUB; ++t) sa[t] = zero16();
-#pragma unroll
-    for (int idx = 0; idx < NQ; ++idx)
-      sa[idx / KSTEPS] = E::mfma(k_operand(sK0, idx), qf[idx % KSTEPS], sa[idx / KSTEPS]);
-    if (0 >= n_full) mask(sa, 0);
-    float mx = kNegInf;
-#pragma unroll
-    for (int t = 0; t < NSUB; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sa[t][i], sa[t][i + 1]));
-    update_max(mx);   // O is still zero: no rescale needed
-  }
-  __syncthreads();
-  if constexpr (PAGED) rotate_ids();
-
-  // Iteration j: S_j = K_j Q^T on the matrix cores interleaved with the
-  // probabilities P_{j-1} (exponentials), then O^T += V_{j-1}^T P_{j-1}^T
-  // interleaved with the row max of S_j; O is rescaled (rarely) at the end so
-  // the next P V product adds onto the right base.  K_j is in slot j&1,
-  // V_{j-1} in slot (j-1)&1; K_{j+1} and V_j stream into the other slots.
-  auto iter = [&](const int j, const unsigned char* kcur, unsigned char* knxt,
-                  const unsigned char* vprev, unsigned char* vcur, f32x16 (&so)[NSUB],
-                  f32x16 (&sn)[NSUB], auto masked) {
-    pin_offsets();
-    if constexpr (PAGED) ids_f = tile_ids(j + 2);
-    if (j + 1 < n_kv) dma_k(knxt, (j + 1) * BN);
-    dma_v(vcur, j * BN);
-    const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
-    u32x4 pb[NU];
-    float rs = 0.f;
-    u32x4 ka[KLEAD];
-#pragma unroll
-    for (int x = 0; x < KLEAD; ++x) ka[x] = k_operand(kcur, x);
-#pragma unroll
-    for (int t = 0; t < NSUB; ++t) sn[t] = zero16();
-    // probability pair g of the previous tile (scores so), in the slot the
-    // schedule gives it
-    auto probs = [&](const int slot) __attribute__((always_inline)) {
-#pragma unroll
-      for (int g = 0; g < NPAIR; ++g) {
-        if (g * PSLOTS / NPAIR != slot) continue;
-        const int t = g / 8, i = 2 * (g % 8);
-        const float p0 = fast_exp2(fmaf(so[t][i], scale_log2, neg_m));
-        const float p1 = fast_exp2(fmaf(so[t][i + 1], scale_log2, neg_m));
-        const uint32_t pk = E::pack(p0, p1);
-        rs = E::dot2(pk, E::kOnes, rs);
-        pb[2 * t + (i >> 3)][(i & 7) >> 1] = pk;
+    const size_t khead_off = (size_t)bh * (size_t)Nk * D;
+    const uint32_t khead_bytes = (uint32_t)Nk * D * 2;
+    const auto rQ = make_rsrc(Q + head_off, head_bytes);
+    const auto rK = make_rsrc(K + (PAGED ? 0 : khead_off), PAGED ? 0u : khead_bytes);
+    const auto rV = make_rsrc(V + (PAGED ? 0 : khead_off), PAGED ? 0u : khead_bytes);
+    const auto rO = make_rsrc(O + head_off, head_bytes);
+    const auto rL = make_rsrc(LSE + lse_off, lse_bytes);
+    // Paged: a tile's block ids are read from the table one iteration before
+    // the transfers that use them (ids_v: tile j, ids_k: tile j+1, ids_f: tile
+    // j+2, read during iteration j), so no transfer waits on a table read.  The
+    // read index is clamped into the row (max_blocks >= 1) and entries past it
+    // become -1, which the transfer turns into zeros.
+    auto tile_ids = [&](int t) __attribute__((always_inline)) {
+      TileIds r{{-1, -1, -1, -1}};
+      if constexpr (PAGED) {
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int b = 4 * t + q;
+          const int v = table_row[min(b, pg.max_blocks - 1)];
+          r.b[q] = b < pg.max_blocks ? v : -1;
+        }
       }
+      return r;
     };
-#pragma unroll
-    for (int idx = 0; idx < NQ; ++idx) {
-      const u32x4 a = ka[idx % KLEAD];
-      if (idx + KLEAD < NQ) ka[idx % KLEAD] = k_operand(kcur, idx + KLEAD);
-      sn[idx / KSTEPS] = E::mfma(a, qf[idx % KSTEPS], sn[idx / KSTEPS]);
-      probs(idx);
-    }
-    if constexpr (decltype(masked)::value) mask(sn, j * BN);
-    // P V op ip reads key block ip / DT and writes output column block ip % DT
-    auto vidx = [](int ip) { return (ip % DT) * NU + ip / DT; };
-    u32x4 va[VLEAD];
-#pragma unroll
-    for (int x = 0; x < VLEAD; ++x) va[x] = v_operand(vprev, vidx(x));
-    float mx = kNegInf;
-#pragma unroll
-    for (int ip = 0; ip < NP; ++ip) {
-      const u32x4 a = va[ip % VLEAD];
-      if (ip + VLEAD < NP) va[ip % VLEAD] = v_operand(vprev, vidx(ip + VLEAD));
-      o[ip % DT] = E::mfma(a, pb[ip / DT], o[ip % DT]);
-      probs(NQ + ip);
-#pragma unroll
-      for (int e = 0; e < MPER; ++e) {
-        const int flat = 2 * (ip * MPER + e);
-        mx = fmaxf(mx, fmaxf(sn[flat / 16][flat % 16], sn[flat / 16][flat % 16 + 1]));
+    TileIds ids_v = tile_ids(0), ids_k = tile_ids(1), ids_f = ids_k;
+    // after a barrier (which has waited for the reads): the ids move to scalar
+    // registers, leaving only the ids in flight in vector registers
+    auto rotate_ids = [&]() __attribute__((always_inline)) {
+      ids_v = ids_k;
+  #pragma unroll
+      for (int q = 0; q < 4; ++q) ids_k.b[q] = __builtin_amdgcn_readfirstlane(ids_f.b[q]);
+    };
+    auto dma_k = [&](unsigned char* dst, int row0) __attribute__((always_inline)) {
+      if constexpr (PAGED)
+        dma_rows_paged<D, BN, kThreads / 64>(K, row0 == 0 ? ids_v : ids_k, Nk, pg.num_blocks, kvh,
+                                             pg.KVH, dst, row0, wave, lane);
+      else
+        dma_rows<D, BN, kThreads / 64>(rK, dst, row0, wave, lane);
+    };
+    auto dma_v = [&](unsigned char* dst, int row0) __attribute__((always_inline)) {
+      if constexpr (PAGED)
+        dma_rows_paged<D, BN, kThreads / 64>(V, ids_v, Nk, pg.num_blocks, kvh, pg.KVH, dst, row0,
+                                             wave, lane);
+      else
+        dma_rows<D, BN, kThreads / 64>(rV, dst, row0, wave, lane);
+    };
+
+    const int kv_end = CAUSAL ? min(Nk, q0 + kBM + delta) : Nk;
+    const int n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+    // tiles [0, n_full) need no masking for any row of this workgroup
+    const int n_full = min(CAUSAL ? max(0, q0 + delta + 1) / BN : n_kv, Nk / BN);
+    if (n_kv == 0) {
+      // no row of this tile sees any key: empty softmax, O = 0 and LSE = -inf
+      const int row = q0 + tid / 2;
+      if (tid < 2 * kBM && (!PAGED || row < N)) {
+        const uint32_t prow = (uint32_t)(qrow0 + row);
+  #pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+          bstore16(u32x4{0u, 0u, 0u, 0u}, rO, (prow * qstride + (tid & 1) * (D / 2) + 8 * c) * 2);
+        if ((tid & 1) == 0) bstore4f(kNegInf, rL, prow * lstride * 4);
       }
+      continue;
     }
-    l_run = fmaf(l_run, alpha, rs);
-    if (update_max(mx)) rescale();
+
+    // ---- this wave's query rows, straight from HBM into B-operand registers;
+    //      K_0 and V_0 into ring slot 0
+    dma_k(sK0, 0);
+    dma_v(sV0, 0);
+    const int my_q_row = q0 + wave * 32 + l32;
+    u32x4 qf[KSTEPS];
+  #pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+      qf[s] = bload16(rQ, ((uint32_t)(qrow0 + my_q_row) * qstride + 16 * s + 8 * half) * 2);
+    // The softmax takes its maximum over raw scores and folds the scale into one
+    // multiply-add, which needs a positive multiplier: for a negative scale,
+    // negate Q once (exact in bf16) and use |scale|.
+    if (scale_log2 < 0.f) {
+  #pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) qf[s] = qf[s] ^ 0x80008000u;
+      scale_log2 = -scale_log2;
+    }
+    barrier_all();                                    // K_0, V_0 landed
+
+    const int my_q = q0 + wave * 32 + l32;            // this lane's query row
+    // transpose-read geometry of the V^T operand (see tile_off / ds_read_tr16)
+    const int tr_row = 4 * half + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+    f32x16 o[DT];
+  #pragma unroll
+    for (int t = 0; t < DT; ++t) o[t] = zero16();
+    float m_run = kNegInf;   // running max of scale*log2(e)*score (through the last reduced tile)
+    float l_run = 0.f;       // this lane's share of the running denominator
+    float alpha = 1.f;       // exp2(m_old - m_new) of the last reduced tile
+    constexpr int NQ = NSUB * KSTEPS;     // matrix ops of S = K Q^T per tile
+    constexpr int NP = DT * NU;           // matrix ops of O^T += V^T P^T per tile
+    constexpr int KLEAD = kKLead;
+    constexpr int VLEAD = kVLead;
+    // Issue schedule of one iteration's vector work over its NQ + NP matrix-op
+    // slots (S ops first, then P V ops ordered key block by key block).  The
+    // probabilities of the previous tile come in NPAIR pairs, key block kb
+    // being pairs [4kb, 4kb + 4); they are spread evenly over the first PSLOTS
+    // slots, so block kb is done before the first P V op that reads it (slot
+    // NQ + kb * DT).  The row max of the new tile takes pairs of scores in the
+    // P V slots, after the last S op.
+    constexpr int NPAIR = NSUB * 8;
+    constexpr int PSLOTS = NQ + NP - DT;
+    static_assert(NPAIR == 4 * NU, "four probability pairs per key block");
+    static_assert(NPAIR % NP == 0, "row-max pairs per P V op");
+    static_assert(probs_before_use(NPAIR, PSLOTS, NQ, DT), "a key block's probabilities come late");
+    constexpr int MPER = NPAIR / NP;      // row-max pairs per P V op
+
+    // Per-lane byte offsets of the operand reads inside a tile.  The swizzle
+    // makes them differ per k-step (K) and per column block (V); sub-tile,
+    // row-block and ring-slot offsets are compile-time constants added on top,
+    // which the LDS instructions take as immediates.  The offsets are re-pinned
+    // every iteration so they stay the only live copies.
+    uint32_t kofs[KSTEPS], vofs[DT][2];
+  #pragma unroll
+    for (int k = 0; k < KSTEPS; ++k) kofs[k] = tile_off<D>(l32, 2 * k + half);
+  #pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      const int col = t * 32 + tr_col;
+      vofs[t][0] = tile_off<D>(tr_row, col >> 3) + (col & 7) * 2;
+      vofs[t][1] = tile_off<D>(tr_row + 8, col >> 3) + (col & 7) * 2;
+    }
+    auto pin_offsets = [&]() {
+  #pragma unroll
+      for (int k = 0; k < KSTEPS; ++k) asm volatile("" : "+v"(kofs[k]));
+  #pragma unroll
+      for (int t = 0; t < DT; ++t) asm volatile("" : "+v"(vofs[t][0]), "+v"(vofs[t][1]));
+    };
+    auto k_operand = [&](const unsigned char* sK, int idx) {
+      const int t = idx / KSTEPS, k = idx % KSTEPS;
+      return *(const u32x4*)(sK + kofs[k] + t * 32 * D * 2);
+    };
+    auto v_operand = [&](const unsigned char* sV, int idx) {
+      const int t = idx / NU, u = idx % NU;
+      const u32x2 lo = ds_read_tr16(sV + vofs[t][0] + u * 16 * D * 2);
+      const u32x2 hi = ds_read_tr16(sV + vofs[t][1] + u * 16 * D * 2);
+      const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+      return a;
+    };
+    // keys beyond this lane's row (causal) or beyond N become -inf
+    auto mask = [&](f32x16 (&s)[NSUB], int kb) {
+      const int lim = min(CAUSAL ? my_q + delta : Nk - 1, Nk - 1) - kb - 4 * half;
+  #pragma unroll
+      for (int t = 0; t < NSUB; ++t)
+  #pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (t * 32 + 8 * (i >> 2) + (i & 3) > lim) s[t][i] = kNegInf;
+    };
+    // Reference maximum from a tile's raw row max.  The reference moves only
+    // when the tile's maximum exceeds it by more than kSlack (base 2), so the
+    // probabilities stay <= 2^kSlack and the accumulated output is rescaled
+    // rarely; numerator and denominator share the reference, so their ratio
+    // and the log-sum-exp are unchanged.  Returns whether any row moved.
+    auto update_max = [&](float mx) {
+      mx = fmaxf(mx, swap_half(mx));
+      const float cand = mx * scale_log2;
+      const bool up = cand > m_run + kSlack;            // always true while m_run = -inf
+      const float m_new = up ? cand : m_run;
+      alpha = up ? fast_exp2(m_run - m_new) : 1.f;     // exp2(-inf) = 0 on the first tile
+      m_run = m_new;
+      return __builtin_amdgcn_ballot_w64(up) != 0;
+    };
+    auto rescale = [&]() {
+  #pragma unroll
+      for (int t = 0; t < DT; ++t)
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+    };
+
+    // prologue: S_0, its max; K_1 streams meanwhile
+    f32x16 sa[NSUB], sb[NSUB];
+    if constexpr (PAGED) ids_f = tile_ids(2);
+    if (n_kv > 1) dma_k(sK1, BN);
+    {
+  #pragma unroll
+      for (int t = 0; t < NSUB; ++t) sa[t] = zero16();
+  #pragma unroll
+      for (int idx = 0; idx < NQ; ++idx)
+        sa[idx / KSTEPS] = E::mfma(k_operand(sK0, idx), qf[idx % KSTEPS], sa[idx / KSTEPS]);
+      if (0 >= n_full) mask(sa, 0);
+      float mx = kNegInf;
+  #pragma unroll
+      for (int t = 0; t < NSUB; ++t)
+  #pragma unroll
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sa[t][i], sa[t][i + 1]));
+      update_max(mx);   // O is still zero: no rescale needed
+    }
     __syncthreads();
     if constexpr (PAGED) rotate_ids();
-  };
-  using Plain = std::integral_constant<bool, false>;
-  using Masked = std::integral_constant<bool, true>;
-  int j = 1;
-  const int n_plain = max(1, min(n_full, n_kv));   // iterations [1, n_plain) need no mask
-  for (; j + 1 < n_plain; j += 2) {
-    iter(j, sK1, sK0, sV0, sV1, sa, sb, Plain{});
-    iter(j + 1, sK0, sK1, sV1, sV0, sb, sa, Plain{});
-  }
-  // epilogue: P V of the last tile (its V sits in slot (n_kv-1)&1, its
-  // scores in sa when n_kv-1 is even, else sb)
-  auto last_pv = [&](const f32x16 (&sl)[NSUB], const unsigned char* vl) {
-    const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
-    u32x4 pb[NU];
-    float rs = 0.f;
-#pragma unroll
-    for (int t = 0; t < NSUB; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const float p0 = fast_exp2(fmaf(sl[t][i], scale_log2, neg_m));
-        const float p1 = fast_exp2(fmaf(sl[t][i + 1], scale_log2, neg_m));
-        const uint32_t pk = E::pack(p0, p1);
-        rs = E::dot2(pk, E::kOnes, rs);
-        pb[2 * t + (i >> 3)][(i & 7) >> 1] = pk;
-      }
-    l_run = fmaf(l_run, alpha, rs);
-#pragma unroll
-    for (int idx = 0; idx < NP; ++idx)
-      o[idx / NU] = E::mfma(v_operand(vl, idx), pb[idx % NU], o[idx / NU]);
-  };
-  // The rest (at most one unmasked tile plus the tiles that straddle the
-  // diagonal or the ragged end) runs with the mask on.  j is odd here, so
-  // pairs keep the ring slots and score arrays static.
-  for (; j + 1 < n_kv; j += 2) {
-    iter(j, sK1, sK0, sV0, sV1, sa, sb, Masked{});
-    iter(j + 1, sK0, sK1, sV1, sV0, sb, sa, Masked{});
-  }
-  if (j < n_kv) {
-    iter(j, sK1, sK0, sV0, sV1, sa, sb, Masked{});
-    last_pv(sb, sV1);          // last tile j is odd
-  } else {
-    last_pv(sa, sV0);          // last tile j-1 is even
-  }
 
-  // ---- epilogue: O = O^T / l, LSE = ln(sum exp) = (m + log2 l) ln 2
-  const float l_tot = l_run + swap_half(l_run);
-  // a row that saw no key (l = 0) gets O = 0 and LSE = -inf
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-#pragma unroll
-  for (int t = 0; t < DT; ++t)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = t * 32 + 8 * g + 4 * half;
-      u32x2 w;
-      w[0] = E::pack(o[t][4 * g] * inv, o[t][4 * g + 1] * inv);
-      w[1] = E::pack(o[t][4 * g + 2] * inv, o[t][4 * g + 3] * inv);
-      if (!PAGED || my_q < N) bstore8(w, rO, ((uint32_t)(qrow0 + my_q) * qstride + d0) * 2);
+    // Iteration j: S_j = K_j Q^T on the matrix cores interleaved with the
+    // probabilities P_{j-1} (exponentials), then O^T += V_{j-1}^T P_{j-1}^T
+    // interleaved with the row max of S_j; O is rescaled (rarely) at the end so
+    // the next P V product adds onto the right base.  K_j is in slot j&1,
+    // V_{j-1} in slot (j-1)&1; K_{j+1} and V_j stream into the other slots.
+    auto iter = [&](const int j, const unsigned char* kcur, unsigned char* knxt,
+                    const unsigned char* vprev, unsigned char* vcur, f32x16 (&so)[NSUB],
+                    f32x16 (&sn)[NSUB], auto masked) {
+      pin_offsets();
+      if constexpr (PAGED) ids_f = tile_ids(j + 2);
+      if (j + 1 < n_kv) dma_k(knxt, (j + 1) * BN);
+      dma_v(vcur, j * BN);
+      const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
+      u32x4 pb[NU];
+      float rs = 0.f;
+      u32x4 ka[KLEAD];
+  #pragma unroll
+      for (int x = 0; x < KLEAD; ++x) ka[x] = k_operand(kcur, x);
+  #pragma unroll
+      for (int t = 0; t < NSUB; ++t) sn[t] = zero16();
+      // probability pair g of the previous tile (scores so), in the slot the
+      // schedule gives it
+      auto probs = [&](const int slot) __attribute__((always_inline)) {
+  #pragma unroll
+        for (int g = 0; g < NPAIR; ++g) {
+          if (g * PSLOTS / NPAIR != slot) continue;
+          const int t = g / 8, i = 2 * (g % 8);
+          const float p0 = fast_exp2(fmaf(so[t][i], scale_log2, neg_m));
+          const float p1 = fast_exp2(fmaf(so[t][i + 1], scale_log2, neg_m));
+          const uint32_t pk = E::pack(p0, p1);
+          rs = E::dot2(pk, E::kOnes, rs);
+          pb[2 * t + (i >> 3)][(i & 7) >> 1] = pk;
+        }
+      };
+  #pragma unroll
+      for (int idx = 0; idx < NQ; ++idx) {
+        const u32x4 a = ka[idx % KLEAD];
+        if (idx + KLEAD < NQ) ka[idx % KLEAD] = k_operand(kcur, idx + KLEAD);
+        sn[idx / KSTEPS] = E::mfma(a, qf[idx % KSTEPS], sn[idx / KSTEPS]);
+        probs(idx);
+      }
+      if constexpr (decltype(masked)::value) mask(sn, j * BN);
+      // P V op ip reads key block ip / DT and writes output column block ip % DT
+      auto vidx = [](int ip) { return (ip % DT) * NU + ip / DT; };
+      u32x4 va[VLEAD];
+  #pragma unroll
+      for (int x = 0; x < VLEAD; ++x) va[x] = v_operand(vprev, vidx(x));
+      float mx = kNegInf;
+  #pragma unroll
+      for (int ip = 0; ip < NP; ++ip) {
+        const u32x4 a = va[ip % VLEAD];
+        if (ip + VLEAD < NP) va[ip % VLEAD] = v_operand(vprev, vidx(ip + VLEAD));
+        o[ip % DT] = E::mfma(a, pb[ip / DT], o[ip % DT]);
+        probs(NQ + ip);
+  #pragma unroll
+        for (int e = 0; e < MPER; ++e) {
+          const int flat = 2 * (ip * MPER + e);
+          mx = fmaxf(mx, fmaxf(sn[flat / 16][flat % 16], sn[flat / 16][flat % 16 + 1]));
+        }
+      }
+      l_run = fmaf(l_run, alpha, rs);
+      if (update_max(mx)) rescale();
+      __syncthreads();
+      if constexpr (PAGED) rotate_ids();
+    };
+    using Plain = std::integral_constant<bool, false>;
+    using Masked = std::integral_constant<bool, true>;
+    int j = 1;
+    const int n_plain = max(1, min(n_full, n_kv));   // iterations [1, n_plain) need no mask
+    for (; j + 1 < n_plain; j += 2) {
+      iter(j, sK1, sK0, sV0, sV1, sa, sb, Plain{});
+      iter(j + 1, sK0, sK1, sV1, sV0, sb, sa, Plain{});
     }
-  if (half == 0 && (!PAGED || my_q < N))
-    bstore4f(l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf, rL,
-             (uint32_t)(qrow0 + my_q) * lstride * 4);
+    // epilogue: P V of the last tile (its V sits in slot (n_kv-1)&1, its
+    // scores in sa when n_kv-1 is even, else sb)
+    auto last_pv = [&](const f32x16 (&sl)[NSUB], const unsigned char* vl) {
+      const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
+      u32x4 pb[NU];
+      float rs = 0.f;
+  #pragma unroll
+      for (int t = 0; t < NSUB; ++t)
+  #pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const float p0 = fast_exp2(fmaf(sl[t][i], scale_log2, neg_m));
+          const float p1 = fast_exp2(fmaf(sl[t][i + 1], scale_log2, neg_m));
+          const uint32_t pk = E::pack(p0, p1);
+          rs = E::dot2(pk, E::kOnes, rs);
+          pb[2 * t + (i >> 3)][(i & 7) >> 1] = pk;
+        }
+      l_run = fmaf(l_run, alpha, rs);
+  #pragma unroll
+      for (int idx = 0; idx < NP; ++idx)
+        o[idx / NU] = E::mfma(v_operand(vl, idx), pb[idx % NU], o[idx / NU]);
+    };
+    // The rest (at most one unmasked tile plus the tiles that straddle the
+    // diagonal or the ragged end) runs with the mask on.  j is odd here, so
+    // pairs keep the ring slots and score arrays static.
+    for (; j + 1 < n_kv; j += 2) {
+      iter(j, sK1, sK0, sV0, sV1, sa, sb, Masked{});
+      iter(j + 1, sK0, sK1, sV1, sV0, sb, sa, Masked{});
+    }
+    if (j < n_kv) {
+      iter(j, sK1, sK0, sV0, sV1, sa, sb, Masked{});
+      last_pv(sb, sV1);          // last tile j is odd
+    } else {
+      last_pv(sa, sV0);          // last tile j-1 is even
+    }
+
+    // ---- epilogue: O = O^T / l, LSE = ln(sum exp) = (m + log2 l) ln 2
+    const float l_tot = l_run + swap_half(l_run);
+    // a row that saw no key (l = 0) gets O = 0 and LSE = -inf
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  #pragma unroll
+    for (int t = 0; t < DT; ++t)
+  #pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = t * 32 + 8 * g + 4 * half;
+        u32x2 w;
+        w[0] = E::pack(o[t][4 * g] * inv, o[t][4 * g + 1] * inv);
+        w[1] = E::pack(o[t][4 * g + 2] * inv, o[t][4 * g + 3] * inv);
+        if (!PAGED || my_q < N) bstore8(w, rO, ((uint32_t)(qrow0 + my_q) * qstride + d0) * 2);
+      }
+    if (half == 0 && (!PAGED || my_q < N))
+      bstore4f(l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf, rL,
+               (uint32_t)(qrow0 + my_q) * lstride * 4);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -685,12 +709,22 @@ template <class E, int D, bool CAUSAL, int BN = kBNDefault, int OCC = 2>
 hipError_t launch_bf16(const FwdArgs& a, int Nk, int delta) {
   using T = typename E::elem;
   const int n_qtiles = (a.N + kBM - 1) / kBM;
-  const int grid = a.B * a.H * n_qtiles;
   // causal tiles differ in length: interleave heads so long tiles start first
   const int hg = CAUSAL ? xcd_group((long long)a.B * a.H, (long long)Nk * D * 4) : 0;
-  hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, BN, OCC>), dim3(grid), dim3(kThreads), 0,
-                     a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V, (T*)a.O, a.LSE, a.N, Nk,
-                     delta, a.scale * kLog2e, n_qtiles, PagedKV{}, hg);
+  if constexpr (CAUSAL) {
+    // pair long and short tiles when the paired grid keeps four workgroups
+    // per compute unit
+    const long long pairs = (long long)a.B * a.H * ((n_qtiles + 1) / 2);
+    if (pairs >= 4 * 256) {
+      hipLaunchKernelGGL((fwd_bf16_kernel<E, D, true, BN, OCC, false, true>), dim3((int)pairs),
+                         dim3(kThreads), 0, a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V,
+                         (T*)a.O, a.LSE, a.N, Nk, delta, a.scale * kLog2e, n_qtiles, PagedKV{}, hg);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, BN, OCC>), dim3(a.B * a.H * n_qtiles),
+                     dim3(kThreads), 0, a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V,
+                     (T*)a.O, a.LSE, a.N, Nk, delta, a.scale * kLog2e, n_qtiles, PagedKV{}, hg);
   return hipGetLastError();
 }
 
