@@ -44,9 +44,7 @@ namespace fa {
 
 namespace {
 
-constexpr int kBM = 128;   // query rows per workgroup
 constexpr int kBNDefault = 64;   // keys per K/V tile
-constexpr int kThreads = 256;
 constexpr int kKLead = 3;        // K operand reads in flight ahead of their matrix op
 constexpr int kVLead = 2;        // V operand read pairs in flight ahead of their matrix op
 // The running reference maximum moves only when a tile's row maximum exceeds
@@ -114,8 +112,9 @@ constexpr bool probs_before_use(int npair, int pslots, int nq, int dt) {
   return true;
 }
 
-template <class E, int D, bool CAUSAL, int BN, int OCC, bool PAGED = false, bool PAIRED = false>
-__global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
+template <class E, int D, bool CAUSAL, int BN, int OCC, bool PAGED = false, bool PAIRED = false,
+          int NW = 4>
+__global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const typename E::elem* __restrict__ Q, const typename E::elem* __restrict__ K,
     const typename E::elem* __restrict__ V, typename E::elem* __restrict__ O,
     float* __restrict__ LSE, int N, int Nk, int delta, float scale_log2, int n_qtiles, PagedKV pg,
@@ -128,7 +127,9 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
   // PAIRED (causal only): the workgroup runs rank r and rank n_qtiles - 1 - r
   // of one head one after the other, so every workgroup has the same work and
   // pays the per-tile start-up once per two tiles.  The host pairs only when
-  // the paired grid still fills the chip.
+  // the paired grid still fills the chip.  NW waves of 32 query rows each
+  // share every K/V tile the workgroup streams through LDS.
+  constexpr int BM = 32 * NW;            // query rows per workgroup
   constexpr int KSTEPS = D / 16;         // matrix k-steps over the head dim
   constexpr int DT = D / 32;             // 32-row tiles of O^T
   constexpr int TILE = BN * D * 2;       // bytes of one K or V tile
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     const int half = lane >> 5;
     const int bh = tile / n_qtiles;
     const int qt = CAUSAL ? (n_qtiles - 1 - tile % n_qtiles) : (tile % n_qtiles);
-    const int q0 = qt * kBM;
+    const int q0 = qt * BM;
 
     // row strides of Q/O (elements) and LSE: one head's rows are contiguous, or
     // interleaved with the other heads in the packed layout of a prefill
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     auto tile_ids = [&](int t) __attribute__((always_inline)) {
       TileIds r{{-1, -1, -1, -1}};
       if constexpr (PAGED) {
-  #pragma unroll
+#pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int b = 4 * t + q;
           const int v = table_row[min(b, pg.max_blocks - 1)];
@@ -235,34 +236,34 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     // registers, leaving only the ids in flight in vector registers
     auto rotate_ids = [&]() __attribute__((always_inline)) {
       ids_v = ids_k;
-  #pragma unroll
+#pragma unroll
       for (int q = 0; q < 4; ++q) ids_k.b[q] = __builtin_amdgcn_readfirstlane(ids_f.b[q]);
     };
     auto dma_k = [&](unsigned char* dst, int row0) __attribute__((always_inline)) {
       if constexpr (PAGED)
-        dma_rows_paged<D, BN, kThreads / 64>(K, row0 == 0 ? ids_v : ids_k, Nk, pg.num_blocks, kvh,
+        dma_rows_paged<D, BN, NW>(K, row0 == 0 ? ids_v : ids_k, Nk, pg.num_blocks, kvh,
                                              pg.KVH, dst, row0, wave, lane);
       else
-        dma_rows<D, BN, kThreads / 64>(rK, dst, row0, wave, lane);
+        dma_rows<D, BN, NW>(rK, dst, row0, wave, lane);
     };
     auto dma_v = [&](unsigned char* dst, int row0) __attribute__((always_inline)) {
       if constexpr (PAGED)
-        dma_rows_paged<D, BN, kThreads / 64>(V, ids_v, Nk, pg.num_blocks, kvh, pg.KVH, dst, row0,
+        dma_rows_paged<D, BN, NW>(V, ids_v, Nk, pg.num_blocks, kvh, pg.KVH, dst, row0,
                                              wave, lane);
       else
-        dma_rows<D, BN, kThreads / 64>(rV, dst, row0, wave, lane);
+        dma_rows<D, BN, NW>(rV, dst, row0, wave, lane);
     };
 
-    const int kv_end = CAUSAL ? min(Nk, q0 + kBM + delta) : Nk;
+    const int kv_end = CAUSAL ? min(Nk, q0 + BM + delta) : Nk;
     const int n_kv = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
     // tiles [0, n_full) need no masking for any row of this workgroup
     const int n_full = min(CAUSAL ? max(0, q0 + delta + 1) / BN : n_kv, Nk / BN);
     if (n_kv == 0) {
       // no row of this tile sees any key: empty softmax, O = 0 and LSE = -inf
       const int row = q0 + tid / 2;
-      if (tid < 2 * kBM && (!PAGED || row < N)) {
+      if (tid < 2 * BM && (!PAGED || row < N)) {
         const uint32_t prow = (uint32_t)(qrow0 + row);
-  #pragma unroll
+#pragma unroll
         for (int c = 0; c < D / 16; ++c)
           bstore16(u32x4{0u, 0u, 0u, 0u}, rO, (prow * qstride + (tid & 1) * (D / 2) + 8 * c) * 2);
         if ((tid & 1) == 0) bstore4f(kNegInf, rL, prow * lstride * 4);
@@ -276,14 +277,14 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     dma_v(sV0, 0);
     const int my_q_row = q0 + wave * 32 + l32;
     u32x4 qf[KSTEPS];
-  #pragma unroll
+#pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
       qf[s] = bload16(rQ, ((uint32_t)(qrow0 + my_q_row) * qstride + 16 * s + 8 * half) * 2);
     // The softmax takes its maximum over raw scores and folds the scale into one
     // multiply-add, which needs a positive multiplier: for a negative scale,
     // negate Q once (exact in bf16) and use |scale|.
     if (scale_log2 < 0.f) {
-  #pragma unroll
+#pragma unroll
       for (int s = 0; s < KSTEPS; ++s) qf[s] = qf[s] ^ 0x80008000u;
       scale_log2 = -scale_log2;
     }
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
     f32x16 o[DT];
-  #pragma unroll
+#pragma unroll
     for (int t = 0; t < DT; ++t) o[t] = zero16();
     float m_run = kNegInf;   // running max of scale*log2(e)*score (through the last reduced tile)
     float l_run = 0.f;       // this lane's share of the running denominator
@@ -324,18 +325,18 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     // which the LDS instructions take as immediates.  The offsets are re-pinned
     // every iteration so they stay the only live copies.
     uint32_t kofs[KSTEPS], vofs[DT][2];
-  #pragma unroll
+#pragma unroll
     for (int k = 0; k < KSTEPS; ++k) kofs[k] = tile_off<D>(l32, 2 * k + half);
-  #pragma unroll
+#pragma unroll
     for (int t = 0; t < DT; ++t) {
       const int col = t * 32 + tr_col;
       vofs[t][0] = tile_off<D>(tr_row, col >> 3) + (col & 7) * 2;
       vofs[t][1] = tile_off<D>(tr_row + 8, col >> 3) + (col & 7) * 2;
     }
     auto pin_offsets = [&]() {
-  #pragma unroll
+#pragma unroll
       for (int k = 0; k < KSTEPS; ++k) asm volatile("" : "+v"(kofs[k]));
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < DT; ++t) asm volatile("" : "+v"(vofs[t][0]), "+v"(vofs[t][1]));
     };
     auto k_operand = [&](const unsigned char* sK, int idx) {
@@ -352,9 +353,9 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     // keys beyond this lane's row (causal) or beyond N become -inf
     auto mask = [&](f32x16 (&s)[NSUB], int kb) {
       const int lim = min(CAUSAL ? my_q + delta : Nk - 1, Nk - 1) - kb - 4 * half;
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < NSUB; ++t)
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 16; ++i)
           if (t * 32 + 8 * (i >> 2) + (i & 3) > lim) s[t][i] = kNegInf;
     };
@@ -373,9 +374,9 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
       return __builtin_amdgcn_ballot_w64(up) != 0;
     };
     auto rescale = [&]() {
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < DT; ++t)
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
     };
 
@@ -384,16 +385,16 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     if constexpr (PAGED) ids_f = tile_ids(2);
     if (n_kv > 1) dma_k(sK1, BN);
     {
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < NSUB; ++t) sa[t] = zero16();
-  #pragma unroll
+#pragma unroll
       for (int idx = 0; idx < NQ; ++idx)
         sa[idx / KSTEPS] = E::mfma(k_operand(sK0, idx), qf[idx % KSTEPS], sa[idx / KSTEPS]);
       if (0 >= n_full) mask(sa, 0);
       float mx = kNegInf;
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < NSUB; ++t)
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sa[t][i], sa[t][i + 1]));
       update_max(mx);   // O is still zero: no rescale needed
     }
@@ -416,14 +417,14 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
       u32x4 pb[NU];
       float rs = 0.f;
       u32x4 ka[KLEAD];
-  #pragma unroll
+#pragma unroll
       for (int x = 0; x < KLEAD; ++x) ka[x] = k_operand(kcur, x);
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < NSUB; ++t) sn[t] = zero16();
       // probability pair g of the previous tile (scores so), in the slot the
       // schedule gives it
       auto probs = [&](const int slot) __attribute__((always_inline)) {
-  #pragma unroll
+#pragma unroll
         for (int g = 0; g < NPAIR; ++g) {
           if (g * PSLOTS / NPAIR != slot) continue;
           const int t = g / 8, i = 2 * (g % 8);
@@ -434,7 +435,7 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
           pb[2 * t + (i >> 3)][(i & 7) >> 1] = pk;
         }
       };
-  #pragma unroll
+#pragma unroll
       for (int idx = 0; idx < NQ; ++idx) {
         const u32x4 a = ka[idx % KLEAD];
         if (idx + KLEAD < NQ) ka[idx % KLEAD] = k_operand(kcur, idx + KLEAD);
@@ -445,16 +446,16 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
       // P V op ip reads key block ip / DT and writes output column block ip % DT
       auto vidx = [](int ip) { return (ip % DT) * NU + ip / DT; };
       u32x4 va[VLEAD];
-  #pragma unroll
+#pragma unroll
       for (int x = 0; x < VLEAD; ++x) va[x] = v_operand(vprev, vidx(x));
       float mx = kNegInf;
-  #pragma unroll
+#pragma unroll
       for (int ip = 0; ip < NP; ++ip) {
         const u32x4 a = va[ip % VLEAD];
         if (ip + VLEAD < NP) va[ip % VLEAD] = v_operand(vprev, vidx(ip + VLEAD));
         o[ip % DT] = E::mfma(a, pb[ip / DT], o[ip % DT]);
         probs(NQ + ip);
-  #pragma unroll
+#pragma unroll
         for (int e = 0; e < MPER; ++e) {
           const int flat = 2 * (ip * MPER + e);
           mx = fmaxf(mx, fmaxf(sn[flat / 16][flat % 16], sn[flat / 16][flat % 16 + 1]));
@@ -479,9 +480,9 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
       const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
       u32x4 pb[NU];
       float rs = 0.f;
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < NSUB; ++t)
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 16; i += 2) {
           const float p0 = fast_exp2(fmaf(sl[t][i], scale_log2, neg_m));
           const float p1 = fast_exp2(fmaf(sl[t][i + 1], scale_log2, neg_m));
@@ -490,7 +491,7 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
           pb[2 * t + (i >> 3)][(i & 7) >> 1] = pk;
         }
       l_run = fmaf(l_run, alpha, rs);
-  #pragma unroll
+#pragma unroll
       for (int idx = 0; idx < NP; ++idx)
         o[idx / NU] = E::mfma(v_operand(vl, idx), pb[idx % NU], o[idx / NU]);
     };
@@ -512,9 +513,9 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(
     const float l_tot = l_run + swap_half(l_run);
     // a row that saw no key (l = 0) gets O = 0 and LSE = -inf
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  #pragma unroll
+#pragma unroll
     for (int t = 0; t < DT; ++t)
-  #pragma unroll
+#pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = t * 32 + 8 * g + 4 * half;
         u32x2 w;
@@ -705,40 +706,64 @@ __global__ __launch_bounds__(256) void merge_kernel(const T* Oa, const float* La
   if (c == 0) L[row] = empty ? kNegInf : M + fast_log2(tot) * kLn2;
 }
 
-template <class E, int D, bool CAUSAL, int BN = kBNDefault, int OCC = 2>
-hipError_t launch_bf16(const FwdArgs& a, int Nk, int delta) {
+// Launch shape of the contiguous 16-bit forward: waves per workgroup (32
+// query rows each) and whether causal tiles are paired.
+struct FwdPlan {
+  int nw;
+  bool paired;
+};
+
+FwdPlan fwd_plan(long long heads, int N, bool causal) {
+  // Long sequences take 256-row workgroups, which halve the K/V tile
+  // transfers and LDS writes per flop, as long as the grid still gives every
+  // compute unit a workgroup; causal tiles are then always paired.  Below
+  // that, 128-row workgroups, paired when the paired grid keeps four
+  // workgroups per compute unit.
+  const long long t8 = (N + 255) / 256, t4 = (N + 127) / 128;
+  if (N >= 4096 && heads * (causal ? (t8 + 1) / 2 : t8) >= 256) return FwdPlan{8, causal};
+  return FwdPlan{4, causal && heads * ((t4 + 1) / 2) >= 4 * 256};
+}
+
+template <class E, int D, bool CAUSAL, int NW, bool PAIRED>
+hipError_t launch_bf16_as(const FwdArgs& a, int Nk, int delta) {
   using T = typename E::elem;
-  const int n_qtiles = (a.N + kBM - 1) / kBM;
+  constexpr int BM = 32 * NW;
+  const int n_qtiles = (a.N + BM - 1) / BM;
+  const long long units = (long long)a.B * a.H * (PAIRED ? (n_qtiles + 1) / 2 : n_qtiles);
   // causal tiles differ in length: interleave heads so long tiles start first
   const int hg = CAUSAL ? xcd_group((long long)a.B * a.H, (long long)Nk * D * 4) : 0;
-  if constexpr (CAUSAL) {
-    // pair long and short tiles when the paired grid keeps four workgroups
-    // per compute unit
-    const long long pairs = (long long)a.B * a.H * ((n_qtiles + 1) / 2);
-    if (pairs >= 4 * 256) {
-      hipLaunchKernelGGL((fwd_bf16_kernel<E, D, true, BN, OCC, false, true>), dim3((int)pairs),
-                         dim3(kThreads), 0, a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V,
-                         (T*)a.O, a.LSE, a.N, Nk, delta, a.scale * kLog2e, n_qtiles, PagedKV{}, hg);
-      return hipGetLastError();
-    }
-  }
-  hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, BN, OCC>), dim3(a.B * a.H * n_qtiles),
-                     dim3(kThreads), 0, a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V,
-                     (T*)a.O, a.LSE, a.N, Nk, delta, a.scale * kLog2e, n_qtiles, PagedKV{}, hg);
+  // two waves per SIMD whatever the workgroup size
+  hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, kBNDefault, 8 / NW, false, PAIRED, NW>),
+                     dim3((int)units), dim3(64 * NW), 0, a.stream, (const T*)a.Q, (const T*)a.K,
+                     (const T*)a.V, (T*)a.O, a.LSE, a.N, Nk, delta, a.scale * kLog2e, n_qtiles,
+                     PagedKV{}, hg);
   return hipGetLastError();
+}
+
+template <class E, int D, bool CAUSAL>
+hipError_t launch_bf16(const FwdArgs& a, int Nk, int delta) {
+  const FwdPlan p = fwd_plan((long long)a.B * a.H, a.N, CAUSAL);
+  if constexpr (CAUSAL) {
+    if (p.paired)
+      return p.nw == 8 ? launch_bf16_as<E, D, true, 8, true>(a, Nk, delta)
+                       : launch_bf16_as<E, D, true, 4, true>(a, Nk, delta);
+  }
+  return p.nw == 8 ? launch_bf16_as<E, D, CAUSAL, 8, false>(a, Nk, delta)
+                   : launch_bf16_as<E, D, CAUSAL, 4, false>(a, Nk, delta);
 }
 
 template <class E, int D, bool CAUSAL>
 hipError_t launch_paged(const FwdArgs& a) {
   using T = typename E::elem;
-  const int n_qtiles = (a.N + kBM - 1) / kBM;          // a.N: the longest chunk
+  constexpr int NW = 4;                                // 128 query rows per workgroup
+  const int n_qtiles = (a.N + 32 * NW - 1) / (32 * NW);  // a.N: the longest chunk
   const int grid = a.B * a.H * n_qtiles;                // a.B: the number of sequences
   const PagedKV pg{a.table,      a.q_start,    a.seq_lens,  a.H,
                    a.KVH,        a.max_blocks, a.num_blocks, a.total_q};
   const int hg =
       CAUSAL ? xcd_group((long long)a.B * a.H, (long long)a.max_blocks * 16 * D * 4) : 0;
-  hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, kBNDefault, 2, true>), dim3(grid),
-                     dim3(kThreads), 0, a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V,
+  hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, kBNDefault, 2, true, false, NW>), dim3(grid),
+                     dim3(64 * NW), 0, a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V,
                      (T*)a.O, a.LSE, 0, 0, 0, a.scale * kLog2e, n_qtiles, pg, hg);
   return hipGetLastError();
 }

@@ -108,6 +108,25 @@ def test_fwd_maximum_length_sampled(gpu):
     _check(x, o, lse, True, 128 ** -0.5, TOL["bf16"], rows=rows)
 
 
+# Long sequences with enough heads run in 256-row workgroups (causal ones with
+# a long and a short query tile per workgroup).  4096 rows is a whole number of
+# such tiles; 4100 leaves a ragged 4-row tile and an odd tile count, so one
+# workgroup runs the middle tile alone.
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("N", [4096, 4100])
+def test_fwd_256_row_workgroups_sampled(gpu, d, causal, N):
+    H = 32 if causal else 16
+    x = workloads.attention_inputs(1, H, N, d, "bf16", seed=72000 + N + d + causal)
+    scale = d ** -0.5
+    o, lse = _gpu_fwd(gpu, x, causal, scale)
+    _check(x, o, lse, causal, scale, TOL["bf16"], heads=[(0, H - 1)])
+    rng = np.random.default_rng(N + d)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 257, 2047, 2048, 2049, 3839,
+                                      3840, 4095], np.arange(4096, N), rng.integers(0, N, 20)]))
+    _check(x, o, lse, causal, scale, TOL["bf16"], rows=rows)
+
+
 def test_fwd_deterministic(gpu):
     x = workloads.attention_inputs(2, 4, 777, 128, "bf16", seed=77)
     a = _gpu_fwd(gpu, x, True, 0.0884)

@@ -166,3 +166,14 @@ def test_ring_step_long_context_block(gpu):
     rows = np.r_[0:3, 4095:4097, 8189:8192]
     _check_offset(gpu, x, c.N, 0, True, c.scale, TOL["bf16"], heads=[(0, 0), (0, 17), (0, 31)],
                   rows=rows)
+
+
+@pytest.mark.parametrize("Nq,Nk,qo,ko", [(4100, 4100, 1000, 0), (4100, 4096, 0, 1000)])
+def test_fwd_offset_256_row_workgroups(gpu, Nq, Nk, qo, ko):
+    """Offset blocks long enough for 256-row workgroups with paired tiles: the
+    diagonal moved 1000 keys back (every row sees keys before it), and 1000
+    keys ahead (the first 1000 rows see nothing; whole tiles are empty)."""
+    x = _inputs(Nq, Nk, 128, "bf16", seed=3600 + qo, H=32)
+    rows = np.unique(np.r_[0:3, 254:258, 998:1003, 2047:2050, 4095:Nq])
+    _check_offset(gpu, x, qo, ko, True, 128 ** -0.5, TOL["bf16"], heads=[(0, 0), (0, 31)],
+                  rows=rows)
