@@ -320,7 +320,8 @@ def main():
         traffic = load_traffic(P_FWD, src)
         roof = {"bound": "mfma", "achieved": head["tflops"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": head["frac_mfma_peak"], "traffic": traffic,
-                "kernel": "fwd_bf16_kernel<128,causal>", "source_hash": src}
+                "kernel": "fwd_bf16_kernel<d=128, causal, 8 waves, paired tiles>",
+                "source_hash": src}
     dec_res = res.get(P_DEC)
     roof_dec = None
     if dec_res is not None:
