@@ -26,9 +26,11 @@
 //     B operand of O^T += V^T P^T, whose A operand (V^T) comes from transpose
 //     reads of the row-major V tile.
 //   * software pipeline: iteration j runs the matrix ops of S_j interleaved
-//     with the exponentials of tile j-1, then P_{j-1} V_{j-1} interleaved with
-//     the row maximum of S_j.  The accumulated output is rescaled only when a
-//     row's maximum grows by more than a fixed slack (see kSlack).
+//     with the exponentials of tile j-1, then P_{j-1} V_{j-1} with the rest of
+//     those exponentials.  The probabilities are taken against a per-row
+//     reference maximum that moves (and rescales the accumulated output) only
+//     when a probability could exceed 2^kSlack, which the running probability
+//     sum reveals without a per-tile maximum (see kSlack).
 //   * causal: key tiles entirely above the diagonal are never visited; only
 //     tiles that straddle the diagonal (or the ragged end) are masked, in a
 //     separate tail of the loop.
@@ -47,9 +49,12 @@ namespace {
 constexpr int kBNDefault = 64;   // keys per K/V tile
 constexpr int kKLead = 3;        // K operand reads in flight ahead of their matrix op
 constexpr int kVLead = 2;        // V operand read pairs in flight ahead of their matrix op
-// The running reference maximum moves only when a tile's row maximum exceeds
-// it by more than this (base-2 exponent): probabilities stay <= 2^kSlack.
+// Probabilities are exp2(score * scale * log2(e) - m_ref) against a per-row
+// reference m_ref and stay <= 2^kSlack: the reference moves (to the row's
+// exact maximum over the tile at hand) only when a lane's running probability
+// sum over a tile exceeds 2^kSlack, which every larger probability would cause.
 constexpr float kSlack = 8.f;
+constexpr float kSlackPow = 256.f;   // 2^kSlack
 
 // Paged K/V source of a prefill: sequence s's queries are rows
 // [q_start[s], q_start[s+1]) of the packed Q/O/LSE, its seq_lens[s] cached
@@ -110,6 +115,21 @@ constexpr bool probs_before_use(int npair, int pslots, int nq, int dt) {
   for (int g = 0; g < npair; ++g)
     if (g * pslots / npair >= nq + (g / 4) * dt) return false;
   return true;
+}
+
+// Whether the first P V op of key block kb must first check the probability
+// sum: true when some probability pair of block kb was issued after the last
+// check (pairs issued in slots before a check are covered by it; pair g is
+// issued in slot g * pslots / npair, and block b's first P V op sits in slot
+// nq + b * dt).
+constexpr bool check_before_block(int kb, int npair, int pslots, int nq, int dt) {
+  int checked = 0;
+  for (int b = 0; b <= kb; ++b) {
+    const bool need = (4 * b + 3) * pslots / npair >= checked;
+    if (b == kb) return need;
+    if (need) checked = nq + b * dt;
+  }
+  return false;
 }
 
 template <class E, int D, bool CAUSAL, int BN, int OCC, bool PAGED = false, bool PAIRED = false,
@@ -298,9 +318,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     f32x16 o[DT];
 #pragma unroll
     for (int t = 0; t < DT; ++t) o[t] = zero16();
-    float m_run = kNegInf;   // running max of scale*log2(e)*score (through the last reduced tile)
+    float m_run = kNegInf;   // reference maximum of scale*log2(e)*score (see kSlack)
+    float neg_m = 0.f;       // -m_run, or 0 while the row has seen no key (m_run = -inf)
+    float thr = 0.f;         // probability-sum threshold: 2^kSlack, or 0 while m_run = -inf
     float l_run = 0.f;       // this lane's share of the running denominator
-    float alpha = 1.f;       // exp2(m_old - m_new) of the last reduced tile
     constexpr int NQ = NSUB * KSTEPS;     // matrix ops of S = K Q^T per tile
     constexpr int NP = DT * NU;           // matrix ops of O^T += V^T P^T per tile
     constexpr int KLEAD = kKLead;
@@ -310,14 +331,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     // probabilities of the previous tile come in NPAIR pairs, key block kb
     // being pairs [4kb, 4kb + 4); they are spread evenly over the first PSLOTS
     // slots, so block kb is done before the first P V op that reads it (slot
-    // NQ + kb * DT).  The row max of the new tile takes pairs of scores in the
-    // P V slots, after the last S op.
+    // NQ + kb * DT).
     constexpr int NPAIR = NSUB * 8;
     constexpr int PSLOTS = NQ + NP - DT;
     static_assert(NPAIR == 4 * NU, "four probability pairs per key block");
-    static_assert(NPAIR % NP == 0, "row-max pairs per P V op");
     static_assert(probs_before_use(NPAIR, PSLOTS, NQ, DT), "a key block's probabilities come late");
-    constexpr int MPER = NPAIR / NP;      // row-max pairs per P V op
 
     // Per-lane byte offsets of the operand reads inside a tile.  The swizzle
     // makes them differ per k-step (K) and per column block (V); sub-tile,
@@ -359,26 +377,59 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
         for (int i = 0; i < 16; ++i)
           if (t * 32 + 8 * (i >> 2) + (i & 3) > lim) s[t][i] = kNegInf;
     };
-    // Reference maximum from a tile's raw row max.  The reference moves only
-    // when the tile's maximum exceeds it by more than kSlack (base 2), so the
-    // probabilities stay <= 2^kSlack and the accumulated output is rescaled
-    // rarely; numerator and denominator share the reference, so their ratio
-    // and the log-sum-exp are unchanged.  Returns whether any row moved.
-    auto update_max = [&](float mx) {
-      mx = fmaxf(mx, swap_half(mx));
-      const float cand = mx * scale_log2;
-      const bool up = cand > m_run + kSlack;            // always true while m_run = -inf
-      const float m_new = up ? cand : m_run;
-      alpha = up ? fast_exp2(m_run - m_new) : 1.f;     // exp2(-inf) = 0 on the first tile
-      m_run = m_new;
-      return __builtin_amdgcn_ballot_w64(up) != 0;
-    };
-    auto rescale = [&]() {
+    // The row's maximum of a score tile, scaled to base 2 (both half-waves
+    // hold keys of the same query rows, so they agree on it).
+    auto tile_max = [&](const f32x16 (&s)[NSUB]) {
+      float mx = kNegInf;
 #pragma unroll
-      for (int t = 0; t < DT; ++t)
+      for (int t = 0; t < NSUB; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[t][i], s[t][i + 1]));
+      return fmaxf(mx, swap_half(mx)) * scale_log2;
     };
+    auto set_ref = [&](float m) {
+      m_run = m;
+      neg_m = m == kNegInf ? 0.f : -m;
+      thr = m == kNegInf ? 0.f : kSlackPow;
+    };
+    // Probability pair g (keys of score registers s[g/8][2(g%8)], +1) against
+    // the current reference, rounded to the element type; the denominator sums
+    // the rounded values, so numerator and denominator see the same numbers.
+    auto prob_pair = [&](const f32x16 (&s)[NSUB], u32x4 (&pb)[NU], float& rs, const int g)
+        __attribute__((always_inline)) {
+      const int t = g / 8, i = 2 * (g % 8);
+      const float p0 = fast_exp2(fmaf(s[t][i], scale_log2, neg_m));
+      const float p1 = fast_exp2(fmaf(s[t][i + 1], scale_log2, neg_m));
+      const uint32_t pk = E::pack(p0, p1);
+      rs = E::dot2(pk, E::kOnes, rs);
+      pb[2 * t + (i >> 3)][(i & 7) >> 1] = pk;
+    };
+    // Rare path, taken by the whole wave when some lane's probability sum over
+    // the pairs taken so far passed its threshold (a probability may exceed
+    // 2^kSlack, or the row saw its first key).  Every row whose maximum over
+    // the tile lies above its reference moves the reference there, rescales
+    // the output and denominator accumulated so far by exp2(m_old - m_new)
+    // (output already holding part of this tile included: all of it is on the
+    // old reference), and the pairs already taken (issued in slots < upto) are
+    // taken again.  Afterwards every probability of the tile is <= 1.
+    auto raise_ref = [&](const f32x16 (&s)[NSUB], u32x4 (&pb)[NU], float& rs, const int upto)
+        __attribute__((always_inline)) {
+      const float cand = tile_max(s);
+      if (cand > m_run) {
+        const float alpha = fast_exp2(m_run - cand);   // 0 while m_run = -inf
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+        l_run *= alpha;
+        set_ref(cand);
+      }
+      rs = 0.f;
+#pragma unroll
+      for (int g = 0; g < NPAIR; ++g)
+        if (g * PSLOTS / NPAIR < upto) prob_pair(s, pb, rs, g);
+    };
+    auto over = [&](float rs) { return __builtin_amdgcn_ballot_w64(rs > thr) != 0; };
 
     // prologue: S_0, its max; K_1 streams meanwhile
     f32x16 sa[NSUB], sb[NSUB];
@@ -391,20 +442,16 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
       for (int idx = 0; idx < NQ; ++idx)
         sa[idx / KSTEPS] = E::mfma(k_operand(sK0, idx), qf[idx % KSTEPS], sa[idx / KSTEPS]);
       if (0 >= n_full) mask(sa, 0);
-      float mx = kNegInf;
-#pragma unroll
-      for (int t = 0; t < NSUB; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sa[t][i], sa[t][i + 1]));
-      update_max(mx);   // O is still zero: no rescale needed
+      set_ref(tile_max(sa));
     }
     __syncthreads();
     if constexpr (PAGED) rotate_ids();
 
     // Iteration j: S_j = K_j Q^T on the matrix cores interleaved with the
     // probabilities P_{j-1} (exponentials), then O^T += V_{j-1}^T P_{j-1}^T
-    // interleaved with the row max of S_j; O is rescaled (rarely) at the end so
-    // the next P V product adds onto the right base.  K_j is in slot j&1,
+    // with the rest of them.  Before the first P V op of a key block whose
+    // probabilities have not all been checked, the probability sum is tested
+    // against the threshold (raise_ref on the rare hit).  K_j is in slot j&1,
     // V_{j-1} in slot (j-1)&1; K_{j+1} and V_j stream into the other slots.
     auto iter = [&](const int j, const unsigned char* kcur, unsigned char* knxt,
                     const unsigned char* vprev, unsigned char* vcur, f32x16 (&so)[NSUB],
@@ -413,7 +460,6 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
       if constexpr (PAGED) ids_f = tile_ids(j + 2);
       if (j + 1 < n_kv) dma_k(knxt, (j + 1) * BN);
       dma_v(vcur, j * BN);
-      const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
       u32x4 pb[NU];
       float rs = 0.f;
       u32x4 ka[KLEAD];
@@ -425,15 +471,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
       // schedule gives it
       auto probs = [&](const int slot) __attribute__((always_inline)) {
 #pragma unroll
-        for (int g = 0; g < NPAIR; ++g) {
-          if (g * PSLOTS / NPAIR != slot) continue;
-          const int t = g / 8, i = 2 * (g % 8);
-          const float p0 = fast_exp2(fmaf(so[t][i], scale_log2, neg_m));
-          const float p1 = fast_exp2(fmaf(so[t][i + 1], scale_log2, neg_m));
-          const uint32_t pk = E::pack(p0, p1);
-          rs = E::dot2(pk, E::kOnes, rs);
-          pb[2 * t + (i >> 3)][(i & 7) >> 1] = pk;
-        }
+        for (int g = 0; g < NPAIR; ++g)
+          if (g * PSLOTS / NPAIR == slot) prob_pair(so, pb, rs, g);
       };
 #pragma unroll
       for (int idx = 0; idx < NQ; ++idx) {
@@ -448,21 +487,16 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
       u32x4 va[VLEAD];
 #pragma unroll
       for (int x = 0; x < VLEAD; ++x) va[x] = v_operand(vprev, vidx(x));
-      float mx = kNegInf;
 #pragma unroll
       for (int ip = 0; ip < NP; ++ip) {
+        if (ip % DT == 0 && check_before_block(ip / DT, NPAIR, PSLOTS, NQ, DT))
+          if (__builtin_expect(over(rs), 0)) raise_ref(so, pb, rs, NQ + ip);
         const u32x4 a = va[ip % VLEAD];
         if (ip + VLEAD < NP) va[ip % VLEAD] = v_operand(vprev, vidx(ip + VLEAD));
         o[ip % DT] = E::mfma(a, pb[ip / DT], o[ip % DT]);
         probs(NQ + ip);
-#pragma unroll
-        for (int e = 0; e < MPER; ++e) {
-          const int flat = 2 * (ip * MPER + e);
-          mx = fmaxf(mx, fmaxf(sn[flat / 16][flat % 16], sn[flat / 16][flat % 16 + 1]));
-        }
       }
-      l_run = fmaf(l_run, alpha, rs);
-      if (update_max(mx)) rescale();
+      l_run += rs;
       __syncthreads();
       if constexpr (PAGED) rotate_ids();
     };
@@ -477,20 +511,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     // epilogue: P V of the last tile (its V sits in slot (n_kv-1)&1, its
     // scores in sa when n_kv-1 is even, else sb)
     auto last_pv = [&](const f32x16 (&sl)[NSUB], const unsigned char* vl) {
-      const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
       u32x4 pb[NU];
       float rs = 0.f;
 #pragma unroll
-      for (int t = 0; t < NSUB; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const float p0 = fast_exp2(fmaf(sl[t][i], scale_log2, neg_m));
-          const float p1 = fast_exp2(fmaf(sl[t][i + 1], scale_log2, neg_m));
-          const uint32_t pk = E::pack(p0, p1);
-          rs = E::dot2(pk, E::kOnes, rs);
-          pb[2 * t + (i >> 3)][(i & 7) >> 1] = pk;
-        }
-      l_run = fmaf(l_run, alpha, rs);
+      for (int g = 0; g < NPAIR; ++g) prob_pair(sl, pb, rs, g);
+      if (over(rs)) raise_ref(sl, pb, rs, PSLOTS);
+      l_run += rs;
 #pragma unroll
       for (int idx = 0; idx < NP; ++idx)
         o[idx / NU] = E::mfma(v_operand(vl, idx), pb[idx % NU], o[idx / NU]);

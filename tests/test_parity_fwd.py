@@ -172,3 +172,43 @@ def test_fwd_running_max_moves(gpu, d, causal, rise):
     x = workloads.ramp_inputs(1, 2, N, d, "bf16", seed=4242 + d, align=align, ramp=ramp)
     o, lse = _gpu_fwd(gpu, x, causal, scale)
     _check(x, o, lse, causal, scale, TOL["bf16"])
+
+
+# One key far above the rest, placed in each of the four 16-key blocks of a
+# 64-key tile after the first: the kernels take a tile's probabilities against
+# the reference they hold, check the running probability sum before the first
+# product of a key block that uses unchecked probabilities, and on a hit move
+# the reference and rescale what they have accumulated, part of the current
+# tile included.  A rise of 20 (base 2) gives probabilities near 2^20; 150
+# overflows exp2 to inf before the move.  The oracle's max-subtracted softmax
+# is exact either way.
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("key", [64 + 5, 128 + 20, 192 + 40, 256 + 60, 300 + 63])
+@pytest.mark.parametrize("rise", [20.0, 150.0])
+def test_fwd_reference_moves_mid_tile(gpu, d, causal, key, rise):
+    N, align = 400, 4.0
+    scale = 1.0 / math.sqrt(d)
+    spike = rise / (scale * align * math.log2(math.e))
+    x = workloads.spike_inputs(1, 2, N, d, "bf16", seed=5151 + key, align=align, spike=spike,
+                               keys=[key])
+    o, lse = _gpu_fwd(gpu, x, causal, scale)
+    _check(x, o, lse, causal, scale, TOL["bf16"])
+
+
+# Spikes in several tiles, in rising order, on the long-sequence launch
+# (256-row workgroups, paired causal tiles): the reference moves several
+# times per row.
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_reference_moves_long(gpu, causal):
+    B, H, N, d = 1, 8, 4096, 128
+    scale = 1.0 / math.sqrt(d)
+    keys = [70, 1000, 2047, 2100, 4000]
+    x = workloads.spike_inputs(B, H, N, d, "bf16", seed=5252, align=4.0,
+                               spike=30.0 / (scale * 4.0 * math.log2(math.e)), keys=keys)
+    # rising spikes: each later key scores higher than the one before
+    for i, j in enumerate(keys):
+        x["k"][:, :, j, :] *= 1.0 + 0.25 * i
+    o, lse = _gpu_fwd(gpu, x, causal, scale)
+    rows = [0, 69, 70, 71, 999, 1000, 1500, 2047, 2099, 2100, 3000, 3999, 4000, 4095]
+    _check(x, o, lse, causal, scale, TOL["bf16"], rows=rows)

@@ -26,7 +26,7 @@ import torch
 
 __all__ = [
     "AttnConfig", "DecodeConfig", "FP32_SMALL", "GPT2_SHAPE", "LONG_CONTEXT", "FWD_BWD", "DECODE",
-    "WORKLOADS", "attention_inputs", "paged_inputs", "prefill_queries",
+    "WORKLOADS", "attention_inputs", "paged_inputs", "prefill_queries", "ramp_inputs", "spike_inputs",
 ]
 
 _TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
@@ -130,6 +130,27 @@ def ramp_inputs(B: int, H: int, N: int, d: int, dtype: str = "bf16", *, seed: in
     q = noise * torch.randn((B, H, N, d), generator=g, dtype=torch.float32) + align * e
     pos = torch.arange(N, dtype=torch.float32).view(1, 1, N, 1) / 64.0
     k = noise * torch.randn((B, H, N, d), generator=g, dtype=torch.float32) + ramp * pos * e
+    v = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    return {"q": q.to(tdt).contiguous(), "k": k.to(tdt).contiguous(), "v": v.to(tdt).contiguous()}
+
+
+def spike_inputs(B: int, H: int, N: int, d: int, dtype: str = "bf16", *, seed: int,
+                 align: float, spike: float, keys: list, noise: float = 0.1) -> dict:
+    """Q, K, V where a few chosen keys score far above all others.
+
+    q_i = noise*z + align*e and k_j = noise*z + spike*e for j in ``keys``
+    (noise*z alone otherwise), with e one fixed unit direction: the chosen keys
+    score about scale*align*spike above the rest for every query.  V is plain
+    N(0, 1).  CPU tensors, storage dtype.
+    """
+    tdt = _TORCH_DTYPES[dtype]
+    g = _gen(seed)
+    e = torch.randn(d, generator=g, dtype=torch.float32)
+    e = e / e.norm()
+    q = noise * torch.randn((B, H, N, d), generator=g, dtype=torch.float32) + align * e
+    k = noise * torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    for j in keys:
+        k[:, :, j, :] += spike * e
     v = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
     return {"q": q.to(tdt).contiguous(), "k": k.to(tdt).contiguous(), "v": v.to(tdt).contiguous()}
 
