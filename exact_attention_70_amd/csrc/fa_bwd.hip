@@ -22,7 +22,8 @@
 //   3. bwd_dq:   workgroup = 128 queries (wave = 32); loops over 64-key K/V tiles;
 //      recomputes S^T = K Q^T and dP^T = V dO^T (each lane then holds one
 //      query's row, so LSE_i and D_i are per-lane scalars) and accumulates
-//      dQ^T += K^T dS^T.
+//      dQ^T += K^T dS^T.  Within a tile the exponentials run between the dP
+//      matrix ops, and each 16-key step's dS feeds its dQ ops at once.
 // Causal: tiles wholly above the diagonal are skipped; straddling tiles masked.
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -437,39 +438,98 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   for (int t = 0; t < DT; ++t) dq[t] = zero16();
   barrier_all();
 
+  // Per-lane LDS byte offsets: row reads per k-step and transpose reads per
+  // 32-column block (the swizzle repeats every 16 rows, so sub-tile and
+  // key-step offsets are compile-time immediates on top).  Re-pinned every
+  // tile so they stay the only live copies.
+  uint32_t rofs[KSTEPS], tofs[DT][2];
+#pragma unroll
+  for (int k = 0; k < KSTEPS; ++k) rofs[k] = tile_off<D>(l32, 2 * k + half);
+  {
+    const int row = 4 * half + ((lane & 15) >> 2);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      const int col = t * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      tofs[t][0] = tile_off<D>(row, col >> 3) + (col & 7) * 2;
+      tofs[t][1] = tile_off<D>(row + 8, col >> 3) + (col & 7) * 2;
+    }
+  }
+  auto pin_offsets = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < KSTEPS; ++k) asm volatile("" : "+v"(rofs[k]));
+#pragma unroll
+    for (int t = 0; t < DT; ++t) asm volatile("" : "+v"(tofs[t][0]), "+v"(tofs[t][1]));
+  };
+  constexpr int NS = 2 * KSTEPS;   // matrix ops of S^T (and of dP^T) per tile
+  constexpr int LEAD = 3;          // operand reads in flight ahead of their matrix op
+  // row-major operand idx of a 64-key tile: 32-key sub-tile idx % 2, k-step idx / 2
+  auto row_operand = [&](const unsigned char* tile, int idx) __attribute__((always_inline)) {
+    return *(const u32x4*)(tile + rofs[idx / 2] + (idx % 2) * 32 * D * 2);
+  };
+  auto tr_op = [&](const unsigned char* tile, int u, int t) __attribute__((always_inline)) {
+    const u32x2 lo = ds_read_tr16(tile + tofs[t][0] + u * 16 * D * 2);
+    const u32x2 hi = ds_read_tr16(tile + tofs[t][1] + u * 16 * D * 2);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+
+  // One 64-key tile in three overlapping stages:
+  //   A: S^T = K Q^T (the two 32-key sub-tiles' chains in turn);
+  //   B: dP^T = V dO^T, with the probabilities P^T = exp2(scale log2(e) S^T
+  //      - LSE log2(e)) replacing the scores between its matrix ops;
+  //   C: per 16-key step u, dS^T = P^T o (dP^T - D) for the step's scores,
+  //      then its DT products dQ^T += K^T dS^T.
   auto compute = [&](int j, const unsigned char* sK, const unsigned char* sV) {
     const int kb = j * kQBN;
     if (CAUSAL && kb > wave_qlast) return;         // whole tile above this wave's diagonal
+    pin_offsets();
     f32x16 s[2], dp[2];
+    {
+      u32x4 ring[LEAD];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int x = 0; x < LEAD; ++x) ring[x] = row_operand(sK, x);
 #pragma unroll
-      for (int k = 0; k < KSTEPS; ++k) {
-        const u32x4 ak = *(const u32x4*)(sK + tile_off<D>(t * 32 + l32, 2 * k + half));
-        const u32x4 av = *(const u32x4*)(sV + tile_off<D>(t * 32 + l32, 2 * k + half));
-        s[t] = E::mfma(ak, qf[k], k == 0 ? zero16() : s[t]);
-        dp[t] = E::mfma(av, dof[k], k == 0 ? zero16() : dp[t]);
+      for (int idx = 0; idx < NS; ++idx) {
+        const u32x4 a = ring[idx % LEAD];
+        if (idx + LEAD < NS) ring[idx % LEAD] = row_operand(sK, idx + LEAD);
+        const int t = idx % 2, k = idx / 2;
+        s[t] = E::mfma(a, qf[k], k == 0 ? zero16() : s[t]);
       }
+    }
+    {
+      u32x4 ring[LEAD];
+#pragma unroll
+      for (int x = 0; x < LEAD; ++x) ring[x] = row_operand(sV, x);
+#pragma unroll
+      for (int idx = 0; idx < NS; ++idx) {
+        const u32x4 a = ring[idx % LEAD];
+        if (idx + LEAD < NS) ring[idx % LEAD] = row_operand(sV, idx + LEAD);
+        const int t = idx % 2, k = idx / 2;
+        dp[t] = E::mfma(a, dof[k], k == 0 ? zero16() : dp[t]);
+        // score e in slot 2 + e (NS - 2) / 32: two slots after the last S op
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+          if (2 + e * (NS - 2) / 32 == idx)
+            s[e / 16][e % 16] = fast_exp2(fmaf(s[e / 16][e % 16], scale_log2, neg_lse2));
+      }
+    }
     const bool need_mask = (CAUSAL && kb + kQBN - 1 > q0 + wave * 32) || (kb + kQBN > N);
     const int lim = min(CAUSAL ? my_q : N - 1, N - 1) - kb - 4 * half;
-    u32x4 db[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int u = 0; u < 4; ++u) {
+      const int t = u / 2, i0 = (u % 2) * 8;
+      u32x4 db;
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        float p0 = fast_exp2(fmaf(s[t][i], scale_log2, neg_lse2));
-        float p1 = fast_exp2(fmaf(s[t][i + 1], scale_log2, neg_lse2));
+      for (int i = i0; i < i0 + 8; i += 2) {
+        float p0 = s[t][i], p1 = s[t][i + 1];
         if (need_mask) {
           if (t * 32 + 8 * (i >> 2) + (i & 3) > lim) p0 = 0.f;
           if (t * 32 + 8 * ((i + 1) >> 2) + ((i + 1) & 3) > lim) p1 = 0.f;
         }
-        db[2 * t + (i >> 3)][(i & 7) >> 1] = E::pack(p0 * (dp[t][i] - Di), p1 * (dp[t][i + 1] - Di));
+        db[(i & 7) >> 1] = E::pack(p0 * (dp[t][i] - Di), p1 * (dp[t][i + 1] - Di));
       }
-    // dQ^T += K^T dS^T  (contraction over the 64 keys)
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int t = 0; t < DT; ++t) dq[t] = E::mfma(tr_operand<D>(sK, u, t, lane), db[u], dq[t]);
+      for (int t2 = 0; t2 < DT; ++t2) dq[t2] = E::mfma(tr_op(sK, u, t2), db, dq[t2]);
+    }
   };
   for (int j = 0; j < n_kv; j += 2) {
     if (j + 1 < n_kv) load(j + 1, sK1, sV1);
