@@ -83,20 +83,28 @@ __device__ __forceinline__ u32x4 tr_operand(const unsigned char* tile, int u, in
 }
 
 // ---------------------------------------------------------------- dK, dV
-// Workgroup = 128 keys (wave = 32 keys, held in registers as B operands);
-// loops over 64-row query tiles streamed into LDS (Q, dO, -LSE log2 e, D) by
-// buffer->LDS transfers through a four-slot ring, two tiles ahead.  Per tile
-// and wave, three stages:
-//   A: S = Q K^T, dP = dO V^T (rows = queries, columns = this wave's keys);
-//   B: P = exp2(scale log2(e) S - LSE log2(e)), dS = P o (dP - D), both to bf16;
-//   C: dV^T += dO^T P, dK^T += Q^T dS  (dO^T and Q^T from transpose reads).
-// Iteration i runs A of tile i with B of tile i-1 interleaved between its
-// matrix ops, then C of tile i-1, so the exponentials overlap matrix work.
+// Workgroup = 128 keys, eight waves.  Each 32-key block has a dV wave (waves
+// 0-3) and a dK wave (waves 4-7), so a wave holds one of the two gradient
+// accumulators and one of K, V, and two waves share every SIMD.  64-row query
+// tiles (Q, dO, -LSE log2 e, D) stream into a four-slot LDS ring by
+// buffer->LDS transfers, two tiles ahead.  Iteration i:
+//   dV wave, tile i:   S = Q K^T (rows = queries, columns = the block's keys);
+//                      P = exp2(scale log2(e) S - LSE log2(e)), rounded to the
+//                      element type (as P is for P V in the forward) and
+//                      handed to the block's dK wave through LDS;
+//                      dV^T += dO^T P.
+//   dK wave, tile i-1: dP = dO V^T; dS = P o (dP - D) with that P;
+//                      dK^T += Q^T dS.
+// dO^T and Q^T come from transpose reads.  Both waves issue 32 matrix ops per
+// tile.  P passes through one LDS buffer: the dK wave reads the previous
+// tile's P at the start of an iteration, before a barrier after which the dV
+// wave may overwrite it.
 constexpr int kKvBN = 128;   // keys per workgroup
 constexpr int kKvBQ = 64;    // queries per inner tile
+constexpr int kKvWaves = 8;
 
 template <class E, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     const typename E::elem* __restrict__ Q, const typename E::elem* __restrict__ K,
     const typename E::elem* __restrict__ V, const typename E::elem* __restrict__ dO,
     const float* __restrict__ NL, const float* __restrict__ Dvec,
@@ -106,23 +114,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   constexpr int DT = D / 32;
   constexpr int TILE = kKvBQ * D * 2;
   constexpr int NU = kKvBQ / 16;           // 16-query k-steps of the dV / dK products
-  constexpr int NA = 2 * 2 * KSTEPS;       // matrix ops of stage A (2 sub-tiles x {S, dP})
-  constexpr int NC = 2 * NU * DT;          // matrix ops of stage C ({dV, dK})
-  constexpr int NE = 32;                   // score elements per lane per tile
+  constexpr int NA = 2 * KSTEPS;           // matrix ops of S (or dP) per tile
+  constexpr int NC = NU * DT;              // matrix ops of dV (or dK) per tile
   constexpr int LEAD = 4;                  // operand reads in flight ahead of their matrix op
-  constexpr int VM_TILE = 2 * (TILE / 1024 / 4) + 2;   // transfers a wave issues per tile
+  constexpr int VM_TILE = 2 * (TILE / 1024 / kKvWaves) + 2;   // transfers a wave issues per tile
   __shared__ __attribute__((aligned(1024))) unsigned char sQ0[TILE], sQ1[TILE], sQ2[TILE], sQ3[TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char sO0[TILE], sO1[TILE], sO2[TILE], sO3[TILE];
   __shared__ __attribute__((aligned(256))) float sL0[kKvBQ], sL1[kKvBQ], sL2[kKvBQ], sL3[kKvBQ];
   __shared__ __attribute__((aligned(256))) float sD0[kKvBQ], sD1[kKvBQ], sD2[kKvBQ], sD3[kKvBQ];
+  // P of the latest tile for key block b: sP[b][k-step][lane] (16 bytes per
+  // lane and k-step, lane-contiguous: conflict-free 16-byte writes and reads)
+  __shared__ __attribute__((aligned(1024))) u32x4 sP[4][NU][64];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool dk_wave = wave >= 4;
+  const int blk = wave & 3;                       // this wave's 32-key block
   const int l32 = lane & 31, half = lane >> 5;
   const int tile = hgroup > 0 ? xcd_grouped(blockIdx.x, n_ktiles, hgroup)
                              : xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / n_ktiles;
   const int kb = (tile % n_ktiles) * kKvBN;       // low key tiles see the most queries
-  const int my_k = kb + wave * 32 + l32;          // this lane's key (C-layout column)
+  const int my_k = kb + blk * 32 + l32;           // this lane's key (C-layout column)
 
   const size_t head_off = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
@@ -137,36 +150,58 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
   const int q_first = CAUSAL ? kb : 0;            // earlier queries see none of these keys
   const int n_q = (N - q_first + kKvBQ - 1) / kKvBQ;
-  // Tiles past the end read as zeros (buffer range check); every wave copies
-  // the LSE and D rows too, so each wave issues VM_TILE transfers per tile.
-  auto load = [&](int i, unsigned char* sQ, unsigned char* sO, float* sL, float* sD)
-      __attribute__((always_inline)) {
-    const int q0 = q_first + i * kKvBQ;
-    dma_rows<D, kKvBQ, kThreads / 64>(rQ, sQ, q0, wave, lane);
-    dma_rows<D, kKvBQ, kThreads / 64>(rdO, sO, q0, wave, lane);
-    dma4(rL, sL, (uint32_t)(q0 + lane) * 4);
-    dma4(rD, sD, (uint32_t)(q0 + lane) * 4);
+  // the ring slot of tile i is i % 4; slots are separate objects so that reads
+  // of one are never made to wait for transfers into another
+  auto slotQ = [&](auto c) -> unsigned char* {
+    if constexpr (decltype(c)::value == 0) return sQ0;
+    else if constexpr (decltype(c)::value == 1) return sQ1;
+    else if constexpr (decltype(c)::value == 2) return sQ2;
+    else return sQ3;
   };
-  load(0, sQ0, sO0, sL0, sD0);
-  load(1, sQ1, sO1, sL1, sD1);
-  load(2, sQ2, sO2, sL2, sD2);
+  auto slotO = [&](auto c) -> unsigned char* {
+    if constexpr (decltype(c)::value == 0) return sO0;
+    else if constexpr (decltype(c)::value == 1) return sO1;
+    else if constexpr (decltype(c)::value == 2) return sO2;
+    else return sO3;
+  };
+  auto slotL = [&](auto c) -> float* {
+    if constexpr (decltype(c)::value == 0) return sL0;
+    else if constexpr (decltype(c)::value == 1) return sL1;
+    else if constexpr (decltype(c)::value == 2) return sL2;
+    else return sL3;
+  };
+  auto slotD = [&](auto c) -> float* {
+    if constexpr (decltype(c)::value == 0) return sD0;
+    else if constexpr (decltype(c)::value == 1) return sD1;
+    else if constexpr (decltype(c)::value == 2) return sD2;
+    else return sD3;
+  };
+  // Tiles past the end read as zeros (buffer range check); q0 stays far
+  // below 2^31 / (2 D) for any N the library accepts.
+  auto load = [&](int i, auto c) __attribute__((always_inline)) {
+    const int q0 = q_first + i * kKvBQ;
+    dma_rows<D, kKvBQ, kKvWaves>(rQ, slotQ(c), q0, wave, lane);
+    dma_rows<D, kKvBQ, kKvWaves>(rdO, slotO(c), q0, wave, lane);
+    dma4(rL, slotL(c), (uint32_t)(q0 + lane) * 4);
+    dma4(rD, slotD(c), (uint32_t)(q0 + lane) * 4);
+  };
+  load(0, std::integral_constant<int, 0>{});
+  load(1, std::integral_constant<int, 1>{});
 
-  // this wave's 32 keys as B operands: B[k = d][n = key] = K[key][d]
-  u32x4 kf[KSTEPS], vf[KSTEPS];
+  // this wave's 32 keys as B operands (B[k = d][n = key]): K rows for S in a
+  // dV wave, V rows for dP in a dK wave
+  u32x4 kv[KSTEPS];
+  {
+    const auto& r = dk_wave ? rV : rK;
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) {
-    kf[s] = bload16(rK, (uint32_t)(my_k * D + 16 * s + 8 * half) * 2);
-    vf[s] = bload16(rV, (uint32_t)(my_k * D + 16 * s + 8 * half) * 2);
+    for (int s = 0; s < KSTEPS; ++s) kv[s] = bload16(r, (uint32_t)(my_k * D + 16 * s + 8 * half) * 2);
   }
-  f32x16 dk[DT], dv[DT];
+  f32x16 acc[DT];   // dV^T (dV wave) or dK^T (dK wave)
 #pragma unroll
-  for (int t = 0; t < DT; ++t) {
-    dk[t] = zero16();
-    dv[t] = zero16();
-  }
+  for (int t = 0; t < DT; ++t) acc[t] = zero16();
   // per-lane LDS byte offsets: 16-byte row reads (per k-step) and transpose
-  // reads (per 32-column block); sub-tile / row-block / slot offsets are
-  // compile-time immediates on top.  Re-pinned every iteration.
+  // reads (per 32-column block); sub-tile / row-block offsets are compile-time
+  // immediates on top.  Re-pinned every tile.
   uint32_t rofs[KSTEPS], tofs[DT][2];
 #pragma unroll
   for (int k = 0; k < KSTEPS; ++k) rofs[k] = tile_off<D>(l32, 2 * k + half);
@@ -187,191 +222,152 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   };
   barrier_all();
 
-  // stage A operand idx: k-step idx / 4, sub-tile (idx / 2) % 2, {Q -> S, dO -> dP}:
-  // four independent accumulator chains in turn, so that with one wave per
-  // SIMD a matrix op rarely waits for the result of the one before it
-  auto a_operand = [&](const unsigned char* sQ, const unsigned char* sO, int idx)
-      __attribute__((always_inline)) {
-    const int sub = (idx >> 1) & 1, k = idx >> 2;
-    const unsigned char* base = (idx & 1) ? sO : sQ;
-    return *(const u32x4*)(base + rofs[k] + sub * 32 * D * 2);
-  };
-  auto a_op = [&](int idx, u32x4 a, f32x16 (&s)[2], f32x16 (&dp)[2]) __attribute__((always_inline)) {
-    const int sub = (idx >> 1) & 1, k = idx >> 2;
-    if (idx & 1) dp[sub] = E::mfma(a, vf[k], dp[sub]);
-    else s[sub] = E::mfma(a, kf[k], s[sub]);
-  };
-  // stage C operand idx: k-step u, column block t, {dO^T -> dV, Q^T -> dK}
-  auto c_operand = [&](const unsigned char* sQ, const unsigned char* sO, int idx)
-      __attribute__((always_inline)) {
-    const int u = idx / (2 * DT), t = (idx / 2) % DT;
-    const unsigned char* base = (idx & 1) ? sQ : sO;
-    const u32x2 lo = ds_read_tr16(base + tofs[t][0] + u * 16 * D * 2);
-    const u32x2 hi = ds_read_tr16(base + tofs[t][1] + u * 16 * D * 2);
-    return u32x4{lo[0], lo[1], hi[0], hi[1]};
-  };
-  auto stage_c = [&](const unsigned char* sQ, const unsigned char* sO, const u32x4 (&pb)[NU],
-                     const u32x4 (&db)[NU]) __attribute__((always_inline)) {
+  // S (dV wave) or dP (dK wave) of a tile: rows = queries, columns = keys;
+  // operand idx: 32-query sub-tile idx % 2, k-step idx / 2 (two accumulator
+  // chains in turn)
+  auto stage_a = [&](const unsigned char* rows, f32x16 (&s)[2]) __attribute__((always_inline)) {
     u32x4 ring[LEAD];
 #pragma unroll
-    for (int x = 0; x < LEAD; ++x) ring[x] = c_operand(sQ, sO, x);
-#pragma unroll
-    for (int idx = 0; idx < NC; ++idx) {
-      const u32x4 a = ring[idx % LEAD];
-      if (idx + LEAD < NC) ring[idx % LEAD] = c_operand(sQ, sO, idx + LEAD);
-      const int u = idx / (2 * DT), t = (idx / 2) % DT;
-      if (idx & 1) dk[t] = E::mfma(a, db[u], dk[t]);
-      else dv[t] = E::mfma(a, pb[u], dv[t]);
-    }
-  };
-  // stage B for score element e of this lane (sub-tile e/16, C-layout register e%16)
-  struct BState {
-    f32x4 nl4, d4;
-  };
-  auto stage_b_elem = [&](int e, const f32x16 (&s)[2], const f32x16 (&dp)[2], const float* sL,
-                          const float* sD, int q0, BState& st, float (&pv)[2], float (&dsv)[2],
-                          u32x4 (&pb)[NU], u32x4 (&db)[NU], auto masked) __attribute__((always_inline)) {
-    const int sub = e / 16, i = e % 16, g = i / 4, x = i % 4;
-    const int r0 = sub * 32 + 8 * g + 4 * half;   // first of this lane's 4 query rows
-    if (x == 0) {
-      st.nl4 = *(const f32x4*)(sL + r0);
-      st.d4 = *(const f32x4*)(sD + r0);
-    }
-    float p = fast_exp2(fmaf(s[sub][i], scale_log2, st.nl4[x]));
-    if constexpr (decltype(masked)::value) {
-      const int q = q0 + r0 + x;
-      if ((CAUSAL && my_k > q) || q >= N) p = 0.f;
-    }
-    pv[x & 1] = p;
-    dsv[x & 1] = p * (dp[sub][i] - st.d4[x]);
-    if (x & 1) {
-      const int u = 2 * sub + (g >> 1), w = (g & 1) * 2 + (x >> 1);   // B-operand k-step and word
-      pb[u][w] = E::pack(pv[0], pv[1]);
-      db[u][w] = E::pack(dsv[0], dsv[1]);
-    }
-  };
-
-  // iteration i: A(tile i in slot c) with B(tile i-1 in slot p) interleaved,
-  // then C(tile i-1); tile i+2 streams into slot n.
-  auto iter = [&](int i, const unsigned char* sQc, const unsigned char* sOc, const unsigned char* sQp,
-                  const unsigned char* sOp, const float* sLp, const float* sDp, unsigned char* sQn,
-                  unsigned char* sOn, float* sLn, float* sDn, f32x16 (&so)[2], f32x16 (&dpo)[2],
-                  f32x16 (&sn)[2], f32x16 (&dpn)[2], auto masked) __attribute__((always_inline)) {
-    pin_offsets();
-    load(i + 2, sQn, sOn, sLn, sDn);
-    const int q0p = q_first + (i - 1) * kKvBQ;
-    u32x4 pb[NU], db[NU];
-    BState st;
-    float pv[2], dsv[2];
-    u32x4 ring[LEAD];
-#pragma unroll
-    for (int x = 0; x < LEAD; ++x) ring[x] = a_operand(sQc, sOc, x);
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      sn[sub] = zero16();
-      dpn[sub] = zero16();
-    }
+    for (int x = 0; x < LEAD; ++x)
+      ring[x] = *(const u32x4*)(rows + rofs[x / 2] + (x % 2) * 32 * D * 2);
 #pragma unroll
     for (int idx = 0; idx < NA; ++idx) {
       const u32x4 a = ring[idx % LEAD];
-      if (idx + LEAD < NA) ring[idx % LEAD] = a_operand(sQc, sOc, idx + LEAD);
-      a_op(idx, a, sn, dpn);
-#pragma unroll
-      for (int e = idx * NE / NA; e < (idx + 1) * NE / NA; ++e)
-        stage_b_elem(e, so, dpo, sLp, sDp, q0p, st, pv, dsv, pb, db, masked);
+      if (idx + LEAD < NA) {
+        const int nx = idx + LEAD;
+        ring[idx % LEAD] = *(const u32x4*)(rows + rofs[nx / 2] + (nx % 2) * 32 * D * 2);
+      }
+      const int sub = idx % 2, k = idx / 2;
+      s[sub] = E::mfma(a, kv[k], k == 0 ? zero16() : s[sub]);
     }
-    stage_c(sQp, sOp, pb, db);
-    barrier_vm<VM_TILE>();       // tile i+1 has landed; tile i+2 may still stream
   };
-  // last tile: B then C
-  auto fin = [&](int i, const unsigned char* sQp, const unsigned char* sOp, const float* sLp,
-                 const float* sDp, f32x16 (&so)[2], f32x16 (&dpo)[2]) __attribute__((always_inline)) {
-    const int q0p = q_first + i * kKvBQ;
-    u32x4 pb[NU], db[NU];
-    BState st;
-    float pv[2], dsv[2];
+  // acc^T += cols^T B with cols^T from transpose reads; op idx: k-step idx / DT,
+  // column block idx % DT
+  auto stage_c = [&](const unsigned char* cols, const u32x4 (&b)[NU]) __attribute__((always_inline)) {
+    auto op = [&](int idx) {
+      const int u = idx / DT, t = idx % DT;
+      const u32x2 lo = ds_read_tr16(cols + tofs[t][0] + u * 16 * D * 2);
+      const u32x2 hi = ds_read_tr16(cols + tofs[t][1] + u * 16 * D * 2);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4 ring[LEAD];
 #pragma unroll
-    for (int e = 0; e < NE; ++e)
-      stage_b_elem(e, so, dpo, sLp, sDp, q0p, st, pv, dsv, pb, db, std::integral_constant<bool, true>{});
-    stage_c(sQp, sOp, pb, db);
+    for (int x = 0; x < LEAD; ++x) ring[x] = op(x);
+#pragma unroll
+    for (int idx = 0; idx < NC; ++idx) {
+      const u32x4 a = ring[idx % LEAD];
+      if (idx + LEAD < NC) ring[idx % LEAD] = op(idx + LEAD);
+      acc[idx % DT] = E::mfma(a, b[idx / DT], acc[idx % DT]);
+    }
   };
-  using Yes = std::integral_constant<bool, true>;
-  using No = std::integral_constant<bool, false>;
-  f32x16 sa[2], dpa[2], sb[2], dpb[2];   // S, dP of even / odd tiles
-  // slot r = tile index mod 4; S of even tiles in (sa, dpa), odd in (sb, dpb)
-  auto it0 = [&](int i, auto m) __attribute__((always_inline)) {   // i = 0 mod 4
-    iter(i, sQ0, sO0, sQ3, sO3, sL3, sD3, sQ2, sO2, sL2, sD2, sb, dpb, sa, dpa, m);
-  };
-  auto it1 = [&](int i, auto m) __attribute__((always_inline)) {   // i = 1 mod 4
-    iter(i, sQ1, sO1, sQ0, sO0, sL0, sD0, sQ3, sO3, sL3, sD3, sa, dpa, sb, dpb, m);
-  };
-  auto it2 = [&](int i, auto m) __attribute__((always_inline)) {   // i = 2 mod 4
-    iter(i, sQ2, sO2, sQ1, sO1, sL1, sD1, sQ0, sO0, sL0, sD0, sb, dpb, sa, dpa, m);
-  };
-  auto it3 = [&](int i, auto m) __attribute__((always_inline)) {   // i = 3 mod 4
-    iter(i, sQ3, sO3, sQ2, sO2, sL2, sD2, sQ1, sO1, sL1, sD1, sa, dpa, sb, dpb, m);
-  };
+  // score element e of this lane: sub-tile e / 16, C-layout register e % 16,
+  // query row sub * 32 + 8 g + 4 half + x of the tile; its pair sits in word
+  // (g & 1) * 2 + (x >> 1) of B-operand k-step 2 sub + (g >> 1)
 
-  // prologue: A of tile 0
-  pin_offsets();
-  {
+  // dV wave: tile i in ring slot c
+  auto dv_tile = [&](int i, auto c) __attribute__((always_inline)) {
+    pin_offsets();
+    const int q0 = q_first + i * kKvBQ;
+    f32x16 s[2];
+    stage_a(slotQ(c), s);
+    const float* sL = slotL(c);
+    // keys past a query (causal) or queries past N get P = 0
+    const bool masked = (CAUSAL && q0 < kb + blk * 32 + 31) || q0 + kKvBQ > N;
+    u32x4 pb[NU];
+    auto probs = [&](auto mk) __attribute__((always_inline)) {
+      f32x4 nl4;
+      float pv0 = 0.f;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      sa[sub] = zero16();
-      dpa[sub] = zero16();
-    }
-#pragma unroll
-    for (int idx = 0; idx < NA; ++idx) a_op(idx, a_operand(sQ0, sO0, idx), sa, dpa);
-  }
-  if (n_q == 1) {
-    fin(0, sQ0, sO0, sL0, sD0, sa, dpa);
-  } else {
-    it1(1, Yes{});                 // B of tile 0 (causal diagonal) is masked
-    if (n_q == 2) {
-      fin(1, sQ1, sO1, sL1, sD1, sb, dpb);
-    } else {
-      it2(2, Yes{});               // B of tile 1 (causal diagonal) is masked
-      int i = 3;
-      for (; i + 3 < n_q; i += 4) {
-        it3(i, No{});
-        it0(i + 1, No{});
-        it1(i + 2, No{});
-        it2(i + 3, No{});
-      }
-      // the last tile (possibly ragged) is finished masked
-      if (i < n_q) {
-        it3(i, No{});
-        if (i + 1 < n_q) {
-          it0(i + 1, No{});
-          if (i + 2 < n_q) {
-            it1(i + 2, No{});
-            fin(i + 2, sQ1, sO1, sL1, sD1, sb, dpb);
-          } else {
-            fin(i + 1, sQ0, sO0, sL0, sD0, sa, dpa);
-          }
-        } else {
-          fin(i, sQ3, sO3, sL3, sD3, sb, dpb);
+      for (int e = 0; e < 32; ++e) {
+        const int sub = e / 16, i2 = e % 16, g = i2 / 4, x = i2 % 4;
+        const int r0 = sub * 32 + 8 * g + 4 * half;
+        if (x == 0) nl4 = *(const f32x4*)(sL + r0);
+        float p = fast_exp2(fmaf(s[sub][i2], scale_log2, nl4[x]));
+        if constexpr (decltype(mk)::value) {
+          const int q = q0 + r0 + x;
+          if ((CAUSAL && my_k > q) || q >= N) p = 0.f;
         }
-      } else {
-        fin(i - 1, sQ2, sO2, sL2, sD2, sa, dpa);
+        if (x & 1) pb[2 * sub + (g >> 1)][(g & 1) * 2 + (x >> 1)] = E::pack(pv0, p);
+        else pv0 = p;
       }
+    };
+    if (masked) probs(std::integral_constant<bool, true>{});
+    else probs(std::integral_constant<bool, false>{});
+#pragma unroll
+    for (int u = 0; u < NU; ++u) sP[blk][u][lane] = pb[u];
+    stage_c(slotO(c), pb);
+  };
+  // dK wave: tile j (one behind) in ring slot c, with that tile's P in pb
+  auto dk_tile = [&](auto c, const u32x4 (&pb)[NU]) __attribute__((always_inline)) {
+    pin_offsets();
+    f32x16 dp[2];
+    stage_a(slotO(c), dp);
+    u32x4 db[NU];
+    const float* sD = slotD(c);
+    f32x4 d4;
+    float dv0 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int sub = e / 16, i2 = e % 16, g = i2 / 4, x = i2 % 4;
+      const int r0 = sub * 32 + 8 * g + 4 * half;
+      if (x == 0) d4 = *(const f32x4*)(sD + r0);
+      const uint32_t w = pb[2 * sub + (g >> 1)][(g & 1) * 2 + (x >> 1)];
+      const float p = (x & 1) ? E::hi(w) : E::lo(w);
+      const float ds = p * (dp[sub][i2] - d4[x]);
+      if (x & 1) db[2 * sub + (g >> 1)][(g & 1) * 2 + (x >> 1)] = E::pack(dv0, ds);
+      else dv0 = ds;
     }
+    stage_c(slotQ(c), db);
+  };
+  // iteration i: tile i + 2 streams into slot (i + 2) % 4 (which held tile
+  // i - 2, finished last iteration); the dV wave works on tile i (slot i % 4),
+  // the dK wave on tile i - 1 (slot (i + 3) % 4).  The dK wave takes the P of
+  // tile i - 1 into registers before the mid barrier; the dV wave writes the
+  // P of tile i only after it.
+  auto iter = [&](int i, auto c) __attribute__((always_inline)) {
+    constexpr int C = decltype(c)::value;
+    // issued every iteration (past the end it reads zeros), so that each wave
+    // has exactly one younger tile in flight at the barrier below
+    load(i + 2, std::integral_constant<int, (C + 2) % 4>{});
+    if (!dk_wave) {
+      barrier_lds();
+      if (i < n_q) dv_tile(i, c);
+    } else {
+      u32x4 pb[NU];
+#pragma unroll
+      for (int u = 0; u < NU; ++u) pb[u] = sP[blk][u][lane];
+      barrier_lds();
+      if (i >= 1) dk_tile(std::integral_constant<int, (C + 3) % 4>{}, pb);
+    }
+    barrier_vm_lds<VM_TILE>();   // tile i + 1 landed (tile i + 2 may stream); P of tile i written
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C3 = std::integral_constant<int, 3>;
+  int i = 0;
+  for (; i + 3 <= n_q; i += 4) {
+    iter(i, C0{});
+    iter(i + 1, C1{});
+    iter(i + 2, C2{});
+    iter(i + 3, C3{});
   }
+  if (i <= n_q) iter(i, C0{});
+  if (i + 1 <= n_q) iter(i + 1, C1{});
+  if (i + 2 <= n_q) iter(i + 2, C2{});
 
   // store: lane holds key my_k, rows d = 32t + 8g + 4*half + (0..3)
+  const float mul = dk_wave ? scale : 1.f;
+  const auto& rout = dk_wave ? rdK : rdV;
 #pragma unroll
   for (int t = 0; t < DT; ++t)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d0 = t * 32 + 8 * g + 4 * half;
-      u32x4 wk, wv;
+      u32x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        wk[e] = as_u32(dk[t][4 * g + e] * scale);
-        wv[e] = as_u32(dv[t][4 * g + e]);
-      }
-      bstore16(wk, rdK, (uint32_t)(my_k * D + d0) * 4);
-      bstore16(wv, rdV, (uint32_t)(my_k * D + d0) * 4);
+      for (int e = 0; e < 4; ++e) w[e] = as_u32(acc[t][4 * g + e] * mul);
+      bstore16(w, rout, (uint32_t)(my_k * D + d0) * 4);
     }
 }
 
@@ -570,7 +566,7 @@ hipError_t launch(const BwdArgs& a) {
   // causal tiles differ in length: interleave heads so long tiles start first
   // (each tile streams two [N, d] operands of its head)
   const int hg = CAUSAL ? xcd_group((long long)a.B * a.H, (long long)a.N * D * 4) : 0;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL>), dim3(a.B * a.H * n_kt), dim3(kThreads), 0,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL>), dim3(a.B * a.H * n_kt), dim3(kKvWaves * 64), 0,
                      a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V, (const T*)a.dO, NLvec, a.Dvec, a.dK, a.dV, a.N, a.scale, sl2, n_kt, hg);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

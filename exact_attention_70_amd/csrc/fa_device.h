@@ -170,6 +170,13 @@ __device__ __forceinline__ void barrier_vm() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// barrier_vm<N> that also waits for all of this wave's LDS accesses.
+template <int N>
+__device__ __forceinline__ void barrier_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 // Map the hardware workgroup id to a logical tile id so that consecutive
 // logical tiles land on the same XCD: the dispatcher hands workgroups to the
 // 8 XCDs round-robin, so hardware id b runs on XCD b % 8.  The map is a

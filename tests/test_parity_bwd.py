@@ -44,7 +44,7 @@ def _check(x, g, causal, scale, heads):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N", [1, 17, 64, 65, 128, 129, 200, 300])
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 128, 129, 200, 300, 500])
 def test_bwd_small_shapes(gpu, d, causal, N):
     x = workloads.attention_inputs(1, 2, N, d, "bf16", seed=2000 + N + d + causal, with_do=True)
     scale = 1.0 / math.sqrt(d)
