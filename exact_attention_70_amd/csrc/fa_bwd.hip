@@ -88,17 +88,19 @@ __device__ __forceinline__ u32x4 tr_operand(const unsigned char* tile, int u, in
 // accumulators and one of K, V, and two waves share every SIMD.  64-row query
 // tiles (Q, dO, -LSE log2 e, D) stream into a four-slot LDS ring by
 // buffer->LDS transfers, two tiles ahead.  Iteration i:
-//   dV wave, tile i:   S = Q K^T (rows = queries, columns = the block's keys);
-//                      P = exp2(scale log2(e) S - LSE log2(e)), rounded to the
-//                      element type (as P is for P V in the forward) and
-//                      handed to the block's dK wave through LDS;
-//                      dV^T += dO^T P.
-//   dK wave, tile i-1: dP = dO V^T; dS = P o (dP - D) with that P;
-//                      dK^T += Q^T dS.
-// dO^T and Q^T come from transpose reads.  Both waves issue 32 matrix ops per
-// tile.  P passes through one LDS buffer: the dK wave reads the previous
-// tile's P at the start of an iteration, before a barrier after which the dV
-// wave may overwrite it.
+//   dV wave: dV^T += dO^T P of tile i-1 (its P kept in registers), then for
+//            tile i S = Q K^T (rows = queries, columns = the block's keys) and
+//            P = exp2(scale log2(e) S - LSE log2(e)), rounded to the element
+//            type (as P is for P V in the forward) and handed to the block's
+//            dK wave through LDS;
+//   dK wave: for tile i-1 dP = dO V^T, dS = P o (dP - D) with that P, and
+//            dK^T += Q^T dS.
+// So one wave's exponentials run beside the other's matrix ops: matrix,
+// matrix, vector for the dV wave against matrix, vector, matrix for the dK
+// wave.  dO^T and Q^T come from transpose reads.  Both waves issue 32 matrix
+// ops per tile.  P passes through one LDS buffer: the dK wave reads the
+// previous tile's P at the start of an iteration, before a barrier after
+// which the dV wave may overwrite it.
 constexpr int kKvBN = 128;   // keys per workgroup
 constexpr int kKvBQ = 64;    // queries per inner tile
 constexpr int kKvWaves = 8;
@@ -264,8 +266,8 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
   // query row sub * 32 + 8 g + 4 half + x of the tile; its pair sits in word
   // (g & 1) * 2 + (x >> 1) of B-operand k-step 2 sub + (g >> 1)
 
-  // dV wave: tile i in ring slot c
-  auto dv_tile = [&](int i, auto c) __attribute__((always_inline)) {
+  // dV wave: S and P of tile i in ring slot c into pb, and to the dK wave
+  auto dv_probs = [&](int i, auto c, u32x4 (&pb)[NU]) __attribute__((always_inline)) {
     pin_offsets();
     const int q0 = q_first + i * kKvBQ;
     f32x16 s[2];
@@ -273,7 +275,6 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     const float* sL = slotL(c);
     // keys past a query (causal) or queries past N get P = 0
     const bool masked = (CAUSAL && q0 < kb + blk * 32 + 31) || q0 + kKvBQ > N;
-    u32x4 pb[NU];
     auto probs = [&](auto mk) __attribute__((always_inline)) {
       f32x4 nl4;
       float pv0 = 0.f;
@@ -295,7 +296,6 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     else probs(std::integral_constant<bool, false>{});
 #pragma unroll
     for (int u = 0; u < NU; ++u) sP[blk][u][lane] = pb[u];
-    stage_c(slotO(c), pb);
   };
   // dK wave: tile j (one behind) in ring slot c, with that tile's P in pb
   auto dk_tile = [&](auto c, const u32x4 (&pb)[NU]) __attribute__((always_inline)) {
@@ -320,41 +320,54 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     stage_c(slotQ(c), db);
   };
   // iteration i: tile i + 2 streams into slot (i + 2) % 4 (which held tile
-  // i - 2, finished last iteration); the dV wave works on tile i (slot i % 4),
-  // the dK wave on tile i - 1 (slot (i + 3) % 4).  The dK wave takes the P of
-  // tile i - 1 into registers before the mid barrier; the dV wave writes the
-  // P of tile i only after it.
-  auto iter = [&](int i, auto c) __attribute__((always_inline)) {
-    constexpr int C = decltype(c)::value;
-    // issued every iteration (past the end it reads zeros), so that each wave
-    // has exactly one younger tile in flight at the barrier below
-    load(i + 2, std::integral_constant<int, (C + 2) % 4>{});
-    if (!dk_wave) {
-      barrier_lds();
-      if (i < n_q) dv_tile(i, c);
-    } else {
+  // i - 2, finished last iteration); tile i sits in slot i % 4 and tile i - 1
+  // in slot (i + 3) % 4.  The dK wave takes the P of tile i - 1 into registers
+  // before the mid barrier; the dV wave writes the P of tile i only after it.
+  // The two roles run separate loops (so that neither carries the other's
+  // registers) with the same barriers in the same order.
+  auto run = [&](auto body) __attribute__((always_inline)) {
+    auto iter = [&](int i, auto c) __attribute__((always_inline)) {
+      constexpr int C = decltype(c)::value;
+      // issued every iteration (past the end it reads zeros), so that each wave
+      // has exactly one younger tile in flight at the closing barrier
+      load(i + 2, std::integral_constant<int, (C + 2) % 4>{});
+      body(i, c, std::integral_constant<int, (C + 3) % 4>{});
+      barrier_vm_lds<VM_TILE>();   // tile i + 1 landed (tile i + 2 may stream); P of tile i written
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    using C3 = std::integral_constant<int, 3>;
+    int i = 0;
+    for (; i + 3 <= n_q; i += 4) {
+      iter(i, C0{});
+      iter(i + 1, C1{});
+      iter(i + 2, C2{});
+      iter(i + 3, C3{});
+    }
+    if (i <= n_q) iter(i, C0{});
+    if (i + 1 <= n_q) iter(i + 1, C1{});
+    if (i + 2 <= n_q) iter(i + 2, C2{});
+  };
+  if (!dk_wave) {
+    u32x4 pkeep[NU];   // P of the previous tile
+    run([&](int i, auto c, auto cprev) __attribute__((always_inline)) {
+      barrier_lds();   // the dK waves have read the previous P
+      if (i >= 1) {
+        pin_offsets();
+        stage_c(slotO(cprev), pkeep);
+      }
+      if (i < n_q) dv_probs(i, c, pkeep);
+    });
+  } else {
+    run([&](int i, auto c, auto cprev) __attribute__((always_inline)) {
       u32x4 pb[NU];
 #pragma unroll
       for (int u = 0; u < NU; ++u) pb[u] = sP[blk][u][lane];
       barrier_lds();
-      if (i >= 1) dk_tile(std::integral_constant<int, (C + 3) % 4>{}, pb);
-    }
-    barrier_vm_lds<VM_TILE>();   // tile i + 1 landed (tile i + 2 may stream); P of tile i written
-  };
-  using C0 = std::integral_constant<int, 0>;
-  using C1 = std::integral_constant<int, 1>;
-  using C2 = std::integral_constant<int, 2>;
-  using C3 = std::integral_constant<int, 3>;
-  int i = 0;
-  for (; i + 3 <= n_q; i += 4) {
-    iter(i, C0{});
-    iter(i + 1, C1{});
-    iter(i + 2, C2{});
-    iter(i + 3, C3{});
+      if (i >= 1) dk_tile(cprev, pb);
+    });
   }
-  if (i <= n_q) iter(i, C0{});
-  if (i + 1 <= n_q) iter(i + 1, C1{});
-  if (i + 2 <= n_q) iter(i + 2, C2{});
 
   // store: lane holds key my_k, rows d = 32t + 8g + 4*half + (0..3)
   const float mul = dk_wave ? scale : 1.f;
