@@ -142,9 +142,11 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
 size_t fa_paged_decode_workspace_size(int num_seqs, int H, int d, int max_blocks_per_seq,
                                       int block_size) {
   if (num_seqs <= 0 || H <= 0 || d <= 0 || max_blocks_per_seq <= 0 || block_size <= 0) return 0;
-  const size_t parts = (size_t)fa::decode_n_parts(max_blocks_per_seq, block_size);
-  // per (seq, partition, head): m, l, then d output values
-  return round_up((size_t)num_seqs * parts * H * (size_t)(d + 2) * sizeof(float), 256);
+  // per (slot, head): m, l, then d output values (fp32); then the num_seqs + 1
+  // block prefix sums (int64)
+  return round_up(fa::decode_partials_floats(num_seqs, H, d) * sizeof(float) +
+                      ((size_t)num_seqs + 1) * sizeof(long long),
+                  256);
 }
 
 int fa_paged_decode_gqa(const void* q, const void* k_pool, const void* v_pool,
@@ -195,8 +197,7 @@ int fa_paged_decode_gqa(const void* q, const void* k_pool, const void* v_pool,
   }
   fa::DecodeArgs a{q, k_pool, v_pool, block_table, seq_lens, block_size, num_seqs, H, d,
                    max_blocks_per_seq, num_blocks, scale, o, lse,
-                   static_cast<float*>(workspace), fa::kDecodePartTokens,
-                   fa::decode_n_parts(max_blocks_per_seq, block_size), st};
+                   static_cast<float*>(workspace), fa::kDecodeUnits, st};
   a.KVH = KVH;
   a.dtype = dtype;
   return hip_status(fa::launch_decode(a));

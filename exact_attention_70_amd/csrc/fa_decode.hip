@@ -6,7 +6,7 @@
 // and HPC notes "07-16 afternoon", section "Prefill, Decode and inference
 // scheduling" (a decode step feeds one token whose query reads every cached
 // K/V of its sequence, so the step is bound by memory bandwidth).  The split
-// over KV partitions is merged with the rescaling rule of the online softmax
+// over pieces of the KV stream is merged with the rescaling rule of the online softmax
 // (HPC notes, section "Long context and sequence parallelism").
 //
 // Pool layout [num_blocks, block_size = 16, KVH, d = 128]: one physical block
@@ -17,8 +17,14 @@
 // same bytes, which the vector L1 merges, so HBM traffic per token falls by
 // H / KVH.
 //
-// Partial kernel: workgroup = (sequence, KV partition of 256 tokens, group of
-//   32 heads), so at H = 32 every 16-token block is read as one contiguous
+// Work split: the 16-token blocks of all sequences, taken one after another,
+//   are cut into equal shares (prefix sums of the block counts come from a
+//   one-workgroup scan), one share per workgroup and head group.  A share
+//   covers pieces of one or more sequences and writes one partial result per
+//   piece, so every workgroup has the same work whatever the lengths: no
+//   last, nearly empty round of workgroups.
+// Partial kernel: workgroup = (share, group of 32 heads); per sequence piece
+//   it covers, at H = 32 every 16-token block is read as one contiguous
 //   128 KiB stream; wave = 4 heads; 16 lanes per head, each lane owning 8 of
 //   the 128 head-dim values.  Per 16-token block: 16-byte loads of K and V
 //   rows through a buffer resource over that physical block (an out-of-range
@@ -36,9 +42,10 @@
 //   all G queries (packed two-element dot products, reduced across the 16
 //   lanes with DPP); the weights of two rows, rounded to the element type,
 //   meet the V values of those rows in one two-element dot product per d.  The running max is shared by the quarters; their
-//   denominators and outputs stay separate until the partition ends, when
+//   denominators and outputs stay separate until the piece ends, when
 //   two cross-quarter exchanges combine them.
-// Merge kernel: one wave per (sequence, head) combines its partitions.
+// Merge kernel: one wave per (sequence, head) combines its pieces, found
+//   from the prefix sums.
 //   Throughput is bound by HBM: the flops per byte are ~1.
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -53,26 +60,80 @@ constexpr int kDecThreads = 512;
 constexpr int kHeadsPerWave = 4;
 constexpr int kHeadsPerGroup = 32;   // heads per workgroup: whole 8 KiB token rows at H = 32
 
+// prefix[s] = 16-token blocks of sequences 0 .. s-1, a sequence's length
+// clamped to [0, max_blocks_per_seq * 16]; prefix[num_seqs] = all blocks.
+// One workgroup of 256 threads scans the lengths 256 at a time.
+__global__ __launch_bounds__(256) void decode_prefix_kernel(const int32_t* __restrict__ seq_lens,
+                                                            int num_seqs, int max_blocks_per_seq,
+                                                            long long* __restrict__ prefix) {
+  __shared__ long long part[256];
+  const int t = threadIdx.x;
+  long long carry = 0;
+  for (int base = 0; base < num_seqs; base += 256) {
+    const int sq = base + t;
+    long long nb = 0;
+    if (sq < num_seqs) {
+      const int len = min(seq_lens[sq], max_blocks_per_seq * kDecBS);
+      nb = len > 0 ? (len + kDecBS - 1) / kDecBS : 0;
+    }
+    part[t] = nb;
+    __syncthreads();
+#pragma unroll
+    for (int off = 1; off < 256; off <<= 1) {
+      const long long v = t >= off ? part[t - off] : 0;
+      __syncthreads();
+      part[t] += v;
+      __syncthreads();
+    }
+    if (sq < num_seqs) prefix[sq + 1] = carry + part[t];
+    carry += part[255];
+    __syncthreads();
+  }
+  if (t == 0) prefix[0] = 0;
+}
+
+// Shares actually used: kDecodeUnits, or one per block when there are fewer
+// blocks, so that no share is empty.
+__device__ __forceinline__ int decode_shares(const long long* prefix, int num_seqs, int units) {
+  const long long tb = prefix[num_seqs];
+  return (int)min((long long)units, tb);
+}
+
+// Share g of G takes blocks [g TB / G, (g + 1) TB / G) of the concatenated
+// block stream (TB blocks in all) and calls f(s, first block, end block) for
+// every sequence piece in it, blocks counted within the sequence.
+template <class F>
+__device__ __forceinline__ void for_each_piece(const long long* prefix, int num_seqs, int g, int G,
+                                               F f) {
+  const long long tb = prefix[num_seqs];
+  const long long lo = (long long)g * tb / G, hi = (long long)(g + 1) * tb / G;
+  // the first sequence ending after block lo (binary search on the prefix sums)
+  int a = 0, b = num_seqs;
+  while (a < b) {
+    const int m = (a + b) >> 1;
+    if (prefix[m + 1] > lo) b = m;
+    else a = m + 1;
+  }
+  for (int sq = a; sq < num_seqs; ++sq) {
+    const long long p0 = prefix[sq], p1 = prefix[sq + 1];
+    if (p0 >= hi) break;
+    if (p1 > p0) f(sq, (int)(max(lo, p0) - p0), (int)(min(hi, p1) - p0));
+  }
+}
+
+// One sequence piece (tokens [t_begin, t_end) of sequence s) for this
+// workgroup's group of heads; writes the partial result into slot `slot`.
 template <class E>
-__global__ __launch_bounds__(kDecThreads, 1) void decode_partial_kernel(
+__device__ __forceinline__ void decode_piece(
     const typename E::elem* __restrict__ q, const typename E::elem* __restrict__ k_pool,
-    const typename E::elem* __restrict__ v_pool, const int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ seq_lens, int H, int KVH, int max_blocks_per_seq, int num_blocks,
-    float scale_log2, float* __restrict__ part_o, float* __restrict__ part_ml, int part_tokens,
-    int n_parts) {
+    const typename E::elem* __restrict__ v_pool, const int32_t* __restrict__ block_table, int H,
+    int KVH, int max_blocks_per_seq, int num_blocks, float scale_log2, float* __restrict__ part_o,
+    float* __restrict__ part_ml, int s, int t_begin, int t_end, size_t slot) {
   // H query heads; the pools hold KVH key/value heads and query head h reads
   // cached head h / (H / KVH)
-  const int p = blockIdx.x;
   const int hg = blockIdx.y;
-  const int s = blockIdx.z;
-  const int len = min(seq_lens[s], max_blocks_per_seq * kDecBS);
-  const int t_begin = p * part_tokens;
-  if (t_begin >= len) return;                       // partition past this sequence's end
-  const int t_end = min(len, t_begin + part_tokens);
-
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  if (hg * kHeadsPerGroup + wave * kHeadsPerWave >= H) return;   // no head of this wave exists
   const int head = hg * kHeadsPerGroup + wave * kHeadsPerWave + (lane >> 4);
   const int ch = lane & 15;                          // which 8 of the 128 d values
   const bool head_ok = head < H;
@@ -169,7 +230,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_partial_kernel(
     rv = rv2;
   }
   if (!head_ok) return;
-  const size_t entry = ((size_t)s * n_parts + p) * H + head;
+  const size_t entry = slot * H + head;
   u32x4 w0, w1;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -184,27 +245,38 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_partial_kernel(
   }
 }
 
-constexpr int kGqaWaves = 4;   // cached heads per workgroup
-
-template <class E, int G>
-__global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_partial_kernel(
+template <class E>
+__global__ __launch_bounds__(kDecThreads, 1) void decode_partial_kernel(
     const typename E::elem* __restrict__ q, const typename E::elem* __restrict__ k_pool,
     const typename E::elem* __restrict__ v_pool, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int H, int KVH, int max_blocks_per_seq, int num_blocks,
-    float scale_log2, float* __restrict__ part_o, float* __restrict__ part_ml, int part_tokens,
-    int n_parts) {
+    float scale_log2, float* __restrict__ part_o, float* __restrict__ part_ml,
+    const long long* __restrict__ prefix, int num_seqs, int units) {
+  const int G = decode_shares(prefix, num_seqs, units);
+  const int g = blockIdx.x;
+  if (g >= G) return;
+  if ((int)blockIdx.y * kHeadsPerGroup + (int)(threadIdx.x >> 6) * kHeadsPerWave >= H) return;
+  for_each_piece(prefix, num_seqs, g, G, [&](int sq, int b0, int b1) {
+    const int len = min(seq_lens[sq], max_blocks_per_seq * kDecBS);
+    decode_piece<E>(q, k_pool, v_pool, block_table, H, KVH, max_blocks_per_seq, num_blocks,
+                    scale_log2, part_o, part_ml, sq, b0 * kDecBS, min(len, b1 * kDecBS),
+                    (size_t)g + sq);
+  });
+}
+
+constexpr int kGqaWaves = 4;   // cached heads per workgroup
+
+template <class E, int G>
+__device__ __forceinline__ void decode_gqa_piece(
+    const typename E::elem* __restrict__ q, const typename E::elem* __restrict__ k_pool,
+    const typename E::elem* __restrict__ v_pool, const int32_t* __restrict__ block_table, int H,
+    int KVH, int max_blocks_per_seq, int num_blocks, float scale_log2, float* __restrict__ part_o,
+    float* __restrict__ part_ml, int s, int t_begin, int t_end, size_t slot) {
   constexpr int NI = G <= 4 ? 8 : 4;     // token rows per lane per step
   constexpr int STEP = 4 * NI;           // tokens per step: whole blocks
   constexpr int NB = STEP / kDecBS;      // blocks per step
   static_assert(STEP % kDecBS == 0, "a step is whole blocks");
   static_assert(NI % 2 == 0, "rows are weighted in pairs");
-  const int p = blockIdx.x;
-  const int s = blockIdx.z;
-  const int len = min(seq_lens[s], max_blocks_per_seq * kDecBS);
-  const int t_begin = p * part_tokens;              // a multiple of STEP (host-checked)
-  if (t_begin >= len) return;                       // partition past this sequence's end
-  const int t_end = min(len, t_begin + part_tokens);
-
   const int lane = threadIdx.x & 63;
   const int kvh = __builtin_amdgcn_readfirstlane(blockIdx.y * kGqaWaves + (threadIdx.x >> 6));
   if (kvh >= KVH) return;                           // no cached head for this wave
@@ -235,7 +307,7 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_partial_kernel(
 
   const int32_t* table = block_table + (size_t)s * max_blocks_per_seq;
   // resources over the NB blocks of the step starting at t0; a block past the
-  // partition (or an out-of-range id) gets an empty resource and reads zeros
+  // piece (or an out-of-range id) gets an empty resource and reads zeros
   auto step_rsrc = [&](int t0, __amdgpu_buffer_rsrc_t (&rk)[NB], __amdgpu_buffer_rsrc_t (&rv)[NB])
       __attribute__((always_inline)) {
 #pragma unroll
@@ -350,7 +422,7 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_partial_kernel(
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     if (tq != j % 4) continue;
-    const size_t entry = ((size_t)s * n_parts + p) * H + kvh * G + j;
+    const size_t entry = slot * H + kvh * G + j;
     u32x4 w0, w1;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -366,10 +438,29 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_partial_kernel(
   }
 }
 
-// One wave per (sequence, head): rescale every partition's (m, l, o) to the
-// common maximum and sum.  Lanes take the partitions' (m, l) in parallel for
+template <class E, int G>
+__global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_partial_kernel(
+    const typename E::elem* __restrict__ q, const typename E::elem* __restrict__ k_pool,
+    const typename E::elem* __restrict__ v_pool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, int H, int KVH, int max_blocks_per_seq, int num_blocks,
+    float scale_log2, float* __restrict__ part_o, float* __restrict__ part_ml,
+    const long long* __restrict__ prefix, int num_seqs, int units) {
+  const int shares = decode_shares(prefix, num_seqs, units);
+  const int g = blockIdx.x;
+  if (g >= shares) return;
+  if ((int)blockIdx.y * kGqaWaves + (int)(threadIdx.x >> 6) >= KVH) return;   // no cached head
+  for_each_piece(prefix, num_seqs, g, shares, [&](int sq, int b0, int b1) {
+    const int len = min(seq_lens[sq], max_blocks_per_seq * kDecBS);
+    decode_gqa_piece<E, G>(q, k_pool, v_pool, block_table, H, KVH, max_blocks_per_seq, num_blocks,
+                           scale_log2, part_o, part_ml, sq, b0 * kDecBS, min(len, b1 * kDecBS),
+                           (size_t)g + sq);
+  });
+}
+
+// One wave per (sequence, head): rescale every piece's (m, l, o) to the
+// common maximum and sum.  Lanes take the pieces' (m, l) in parallel for
 // the maximum and the weights; then each lane owns 2 of the 128 output values
-// and sums the partitions' contributions with the weights broadcast from the
+// and sums the pieces' contributions with the weights broadcast from the
 // lane that computed them.
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -385,26 +476,32 @@ __device__ __forceinline__ float wave_sum(float x) {
 template <class E>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
-    const int32_t* __restrict__ seq_lens, int num_seqs, int H, int part_tokens, int n_parts,
+    const long long* __restrict__ prefix, int num_seqs, int H, int units,
     typename E::elem* __restrict__ o, float* __restrict__ lse) {
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (gw >= num_seqs * H) return;
   const int lane = threadIdx.x & 63;
   const int s = gw / H, head = gw % H;
-  const int len = seq_lens[s];
-  if (len <= 0) {   // invalid length: defined output, nothing read
+  const long long bs0 = prefix[s], bs1 = prefix[s + 1];   // this sequence's blocks
+  if (bs1 <= bs0) {   // invalid length: defined output, nothing read
     *(uint32_t*)(o + ((size_t)s * H + head) * kDecD + 2 * lane) = 0u;
     if (lane == 0) lse[(size_t)s * H + head] = kNegInf;
     return;
   }
-  const int np = min(n_parts, (len + part_tokens - 1) / part_tokens);
-  const size_t base = (size_t)s * n_parts * H + head;
+  // the shares holding this sequence's first and last block: share g holds
+  // block b iff g is the largest share with g TB / G <= b
+  const long long tb = prefix[num_seqs];
+  const int G = decode_shares(prefix, num_seqs, units);
+  const int g0 = (int)(((bs0 + 1) * G + tb - 1) / tb - 1);
+  const int g1 = (int)((bs1 * G + tb - 1) / tb - 1);
+  const int np = g1 - g0 + 1;          // pieces p = 0 .. np - 1 in slots g0 + p + s
+  const size_t base = ((size_t)g0 + s) * H + head;
   float m_star = kNegInf;
   for (int p = lane; p < np; p += 64) m_star = fmaxf(m_star, part_ml[(base + (size_t)p * H) * 2]);
   m_star = wave_max(m_star);
   float L = 0.f, a0 = 0.f, a1 = 0.f;
   for (int p0 = 0; p0 < np; p0 += 64) {
-    // this lane's partition p0 + lane: weight and its share of the denominator
+    // this lane's piece p0 + lane: weight and its share of the denominator
     float w = 0.f;
     if (p0 + lane < np) {
       const size_t e = base + (size_t)(p0 + lane) * H;
@@ -432,34 +529,38 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 template <class E>
 hipError_t launch_decode_e(const DecodeArgs& a) {
   using T = typename E::elem;
-  const size_t n_entries = (size_t)a.num_seqs * a.n_parts * a.H;
+  const size_t n_floats = decode_partials_floats(a.num_seqs, a.H, kDecD);
+  const size_t n_entries = n_floats / (kDecD + 2);
   float* part_o = a.part;
   float* part_ml = a.part + n_entries * kDecD;
+  long long* prefix = reinterpret_cast<long long*>(a.part + n_floats);
+  hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(256), 0, a.stream, a.seq_lens,
+                     a.num_seqs, a.max_blocks_per_seq, prefix);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int KVH = a.KVH > 0 ? a.KVH : a.H;
   const int g = a.H / KVH;
-  // grouped heads with a group size the grouped kernel is built for (its step,
-  // at most 32 tokens, divides the 256-token partition)
-  if ((g == 2 || g == 4 || g == 8) && a.part_tokens % 32 == 0) {
-    dim3 grid(a.n_parts, (KVH + kGqaWaves - 1) / kGqaWaves, a.num_seqs);
+  // grouped heads with a group size the grouped kernel is built for
+  if (g == 2 || g == 4 || g == 8) {
+    dim3 grid(a.units, (KVH + kGqaWaves - 1) / kGqaWaves);
     auto kern = g == 2 ? decode_gqa_partial_kernel<E, 2>
               : g == 4 ? decode_gqa_partial_kernel<E, 4> : decode_gqa_partial_kernel<E, 8>;
     hipLaunchKernelGGL(kern, grid, dim3(kGqaWaves * 64), 0, a.stream, (const T*)a.q,
                        (const T*)a.k_pool, (const T*)a.v_pool, a.block_table, a.seq_lens, a.H, KVH,
                        a.max_blocks_per_seq, a.num_blocks, a.scale * kLog2e, part_o, part_ml,
-                       a.part_tokens, a.n_parts);
+                       prefix, a.num_seqs, a.units);
   } else {
-    dim3 grid(a.n_parts, (a.H + kHeadsPerGroup - 1) / kHeadsPerGroup, a.num_seqs);
+    dim3 grid(a.units, (a.H + kHeadsPerGroup - 1) / kHeadsPerGroup);
     hipLaunchKernelGGL((decode_partial_kernel<E>), grid, dim3(kDecThreads), 0, a.stream,
                        (const T*)a.q, (const T*)a.k_pool, (const T*)a.v_pool, a.block_table,
                        a.seq_lens, a.H, KVH, a.max_blocks_per_seq, a.num_blocks,
-                       a.scale * kLog2e, part_o, part_ml, a.part_tokens, a.n_parts);
+                       a.scale * kLog2e, part_o, part_ml, prefix, a.num_seqs, a.units);
   }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int waves = a.num_seqs * a.H;
   hipLaunchKernelGGL((decode_merge_kernel<E>), dim3((waves + 3) / 4), dim3(256), 0, a.stream,
-                     part_o, part_ml, a.seq_lens, a.num_seqs, a.H, a.part_tokens, a.n_parts, (T*)a.o,
-                     a.lse);
+                     part_o, part_ml, prefix, a.num_seqs, a.H, a.units, (T*)a.o, a.lse);
   return hipGetLastError();
 }
 

@@ -73,9 +73,8 @@ struct DecodeArgs {
   float scale;
   void* o;
   float* lse;
-  float* part;      // workspace: partial (m, l, o[d]) per (seq, partition, head)
-  int part_tokens;  // tokens per KV partition
-  int n_parts;      // partitions per sequence (max)
+  float* part;      // workspace: partial (m, l, o[d]) per (slot, head), then block prefix sums
+  int units;        // shares of the block stream (kDecodeUnits)
   hipStream_t stream;
   int KVH = 0;      // key/value heads in the pools (0: same as H)
   int dtype = 1;    // 1 = bf16, 2 = fp16
@@ -116,14 +115,20 @@ inline int xcd_group(long long heads, long long bytes_per_head) {
   return g;
 }
 
-// Decode partitioning shared by the workspace query and the launcher.
-#ifndef FA_DECODE_PART_TOKENS
-#define FA_DECODE_PART_TOKENS 256
+// Decode work split shared by the workspace query and the launcher: the
+// concatenated 16-token block stream of all sequences is cut into kDecodeUnits
+// equal shares (fewer when there are fewer blocks), one per workgroup (per
+// head group), so every workgroup has the same work whatever the lengths.  A
+// share writes one partial result per sequence piece it covers, in slot
+// (share + sequence), so at most kDecodeUnits + num_seqs - 1 slots are used.
+#ifndef FA_DECODE_UNITS
+#define FA_DECODE_UNITS 512
 #endif
-constexpr int kDecodePartTokens = FA_DECODE_PART_TOKENS;
-inline int decode_n_parts(int max_blocks_per_seq, int block_size) {
-  const long long max_tokens = (long long)max_blocks_per_seq * block_size;
-  return (int)((max_tokens + kDecodePartTokens - 1) / kDecodePartTokens);
+constexpr int kDecodeUnits = FA_DECODE_UNITS;
+// workspace bytes: per slot and head (m, l, d output values) in fp32, then the
+// num_seqs + 1 block prefix sums (int64)
+inline size_t decode_partials_floats(int num_seqs, int H, int d) {
+  return ((size_t)kDecodeUnits + num_seqs) * H * (size_t)(d + 2);
 }
 
 }  // namespace fa

@@ -170,9 +170,14 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * fa_paged_decode_workspace_size -- bytes of workspace fa_paged_decode needs:
- * per (sequence, head, KV partition) partial results (running max, running
- * denominator and unnormalised output row, fp32).
+ * fa_paged_decode_workspace_size -- bytes of workspace fa_paged_decode needs.
+ * The 16-token blocks of all sequences, taken one after another, are split
+ * into 512 equal shares (one per block when there are fewer blocks).  The
+ * workspace holds a partial result (running max, running denominator and
+ * unnormalised output row, fp32) per head for each piece of a sequence that a
+ * share covers, at most 512 + num_seqs of them, followed by num_seqs + 1
+ * int64 block counts.  The size does not depend on max_blocks_per_seq or
+ * block_size, which are validated as for the decode call.
  */
 size_t fa_paged_decode_workspace_size(int num_seqs, int H, int d, int max_blocks_per_seq,
                                       int block_size);
@@ -187,10 +192,11 @@ size_t fa_paged_decode_workspace_size(int num_seqs, int H, int d, int max_blocks
  * feeds one new query token, which attends to all of its cached tokens,
  * itself included (HPC notes, section "Prefill, Decode and inference
  * scheduling").  Token t of sequence s is slot t % block_size of physical
- * block block_table[s, t / block_size].  Long sequences are split into KV
- * partitions whose partial (max, denominator, output) triples are merged by
- * the rescaling rule of the online softmax (HPC notes, section "Long context
- * and sequence parallelism").
+ * block block_table[s, t / block_size].  The blocks of all sequences are
+ * cut into equal shares of work; a sequence split over several shares has
+ * its partial (max, denominator, output) triples merged by the rescaling
+ * rule of the online softmax (HPC notes, section "Long context and sequence
+ * parallelism").
  *
  *   q            in   [num_seqs, H, d] bf16 or fp16, per `dtype`
  *   k_pool/v_pool in  [num_blocks, block_size, H, d], same dtype

@@ -140,7 +140,10 @@ def test_bwd_validation(lib):
 
 def test_decode_validation(lib):
     ws = lib.fa_paged_decode_workspace_size(64, 32, 128, 256, 16)
-    assert ws >= 64 * 32 * (4096 // 256) * 130 * 4
+    # partials of 512 shares of the block stream plus one per sequence, 32
+    # heads, (m, l, 128 outputs) fp32 each; then 65 int64 prefix sums
+    assert ws >= (512 + 64) * 32 * 130 * 4 + 65 * 8
+    assert ws % 256 == 0
     assert lib.fa_paged_decode_workspace_size(0, 32, 128, 256, 16) == 0
 
     def dec(bs=16, S=4, H=32, d=128, mbps=8, nb=40, dt=1, ws_ptr=P2, ws_bytes=None,

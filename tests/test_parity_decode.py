@@ -109,3 +109,30 @@ def test_decode_debug_validation(gpu, monkeypatch):
     # without the debug check an out-of-range id reads zeros instead of faulting
     o, lse = _run(gpu, bad, 0.1)
     assert torch.isfinite(o[0]).all() and torch.isfinite(o[2]).all()
+
+
+# The decode splits the 16-token blocks of all sequences, taken one after
+# another, into equal shares, each writing one partial per sequence piece it
+# covers.  Many short sequences make shares span several whole sequences and
+# cut others at block boundaries; one long sequence among them is split over
+# many shares; fewer blocks than shares gives one block per share.
+@pytest.mark.parametrize("lens", [
+    "many_short",     # 300 sequences of 1..100 tokens: ~1100 blocks, shares of ~2 blocks
+    "one_long",       # one 4000-token sequence among 40 short ones
+    "few_blocks",     # 5 sequences, 12 blocks in all
+])
+@pytest.mark.parametrize("kvh", [32, 8, 2])
+def test_decode_balanced_shares(gpu, lens, kvh):
+    g = torch.Generator().manual_seed(7777)
+    if lens == "many_short":
+        seq_lens = torch.randint(1, 101, (300,), generator=g).tolist()
+    elif lens == "one_long":
+        seq_lens = torch.randint(1, 60, (40,), generator=g).tolist()
+        seq_lens[17] = 4000
+    else:
+        seq_lens = [1, 16, 17, 100, 31]
+    p = workloads.paged_inputs(len(seq_lens), 32, 128, 16, 1, max(seq_lens), seed=8080,
+                               seq_lens=seq_lens, kv_heads=kvh, pad_value=float("nan"))
+    scale = 1.0 / np.sqrt(128)
+    o, lse = _run(gpu, p, scale)
+    _check(p, o, lse, scale)
