@@ -121,8 +121,10 @@ inline int xcd_group(long long heads, long long bytes_per_head) {
 // head group), so every workgroup has the same work whatever the lengths.  A
 // share writes one partial result per sequence piece it covers, in slot
 // (share + sequence), so at most kDecodeUnits + num_seqs - 1 slots are used.
+// 256 is one share per compute unit of an MI355X: at H = 32 every workgroup
+// of the grid is resident at once and has the same work.
 #ifndef FA_DECODE_UNITS
-#define FA_DECODE_UNITS 512
+#define FA_DECODE_UNITS 256
 #endif
 constexpr int kDecodeUnits = FA_DECODE_UNITS;
 // workspace bytes: per slot and head (m, l, d output values) in fp32, then the

@@ -172,10 +172,11 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
 /*
  * fa_paged_decode_workspace_size -- bytes of workspace fa_paged_decode needs.
  * The 16-token blocks of all sequences, taken one after another, are split
- * into 512 equal shares (one per block when there are fewer blocks).  The
+ * into 256 equal shares, one per compute unit of an MI355X (one per block
+ * when there are fewer blocks).  The
  * workspace holds a partial result (running max, running denominator and
  * unnormalised output row, fp32) per head for each piece of a sequence that a
- * share covers, at most 512 + num_seqs of them, followed by num_seqs + 1
+ * share covers, at most 256 + num_seqs of them, followed by num_seqs + 1
  * int64 block counts.  The size does not depend on max_blocks_per_seq or
  * block_size, which are validated as for the decode call.
  */

@@ -140,9 +140,9 @@ def test_bwd_validation(lib):
 
 def test_decode_validation(lib):
     ws = lib.fa_paged_decode_workspace_size(64, 32, 128, 256, 16)
-    # partials of 512 shares of the block stream plus one per sequence, 32
+    # partials of 256 shares of the block stream plus one per sequence, 32
     # heads, (m, l, 128 outputs) fp32 each; then 65 int64 prefix sums
-    assert ws >= (512 + 64) * 32 * 130 * 4 + 65 * 8
+    assert ws >= (256 + 64) * 32 * 130 * 4 + 65 * 8
     assert ws % 256 == 0
     assert lib.fa_paged_decode_workspace_size(0, 32, 128, 256, 16) == 0
 

@@ -117,7 +117,7 @@ def test_decode_debug_validation(gpu, monkeypatch):
 # cut others at block boundaries; one long sequence among them is split over
 # many shares; fewer blocks than shares gives one block per share.
 @pytest.mark.parametrize("lens", [
-    "many_short",     # 300 sequences of 1..100 tokens: ~1100 blocks, shares of ~2 blocks
+    "many_short",     # 300 sequences of 1..100 tokens: ~1100 blocks, shares of ~4 blocks
     "one_long",       # one 4000-token sequence among 40 short ones
     "few_blocks",     # 5 sequences, 12 blocks in all
 ])
