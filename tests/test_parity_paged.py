@@ -42,8 +42,9 @@ def test_gqa_decode_matches_oracle(gpu, kvh):
 @pytest.mark.parametrize("H,kvh", [(8, 2), (24, 6), (16, 2), (12, 3), (12, 6)])
 def test_gqa_decode_head_counts_and_step_edges(gpu, H, kvh):
     """Cached-head counts that leave waves of a workgroup idle (6 = 4 + 2),
-    group sizes 4, 8, 2, and lengths at the edges of a 32-token step and a
-    256-token partition; pad slots hold NaN."""
+    group sizes 4, 8, 2, and lengths at the edges of a 32-token step and of
+    16-token blocks (the unit the work is split into shares by); pad slots
+    hold NaN."""
     d, bs = 128, 16
     lens = [1, 15, 16, 31, 32, 33, 63, 64, 255, 256, 257, 512, 600]
     p = workloads.paged_inputs(len(lens), H, d, bs, 1, max(lens), seed=5200 + H + kvh,
