@@ -117,9 +117,11 @@ def test_decode_debug_validation(gpu, monkeypatch):
 # cut others at block boundaries; one long sequence among them is split over
 # many shares; fewer blocks than shares gives one block per share.
 @pytest.mark.parametrize("lens", [
-    "many_short",     # 300 sequences of 1..100 tokens: ~1100 blocks, shares of ~4 blocks
+    "many_short",     # 300 sequences of 1..100 tokens: ~1100 blocks, shares of ~4 blocks;
+                      # the prefix scan runs over two chunks of 256
     "one_long",       # one 4000-token sequence among 40 short ones
     "few_blocks",     # 5 sequences, 12 blocks in all
+    "exactly_256",    # one scan chunk of the block-count prefix sums, filled exactly
 ])
 @pytest.mark.parametrize("kvh", [32, 8, 2])
 def test_decode_balanced_shares(gpu, lens, kvh):
@@ -129,6 +131,8 @@ def test_decode_balanced_shares(gpu, lens, kvh):
     elif lens == "one_long":
         seq_lens = torch.randint(1, 60, (40,), generator=g).tolist()
         seq_lens[17] = 4000
+    elif lens == "exactly_256":
+        seq_lens = torch.randint(1, 300, (256,), generator=g).tolist()
     else:
         seq_lens = [1, 16, 17, 100, 31]
     p = workloads.paged_inputs(len(seq_lens), 32, 128, 16, 1, max(seq_lens), seed=8080,
