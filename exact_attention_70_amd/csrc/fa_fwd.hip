@@ -177,6 +177,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     tile0 = hgroup > 0 ? xcd_grouped(blockIdx.x, n_qtiles, hgroup)
                        : xcd_remap(blockIdx.x, gridDim.x);
   }
+  // The softmax takes its maximum over raw scores and folds the scale into one
+  // multiply-add, which needs a positive multiplier: for a negative scale,
+  // each pass negates its Q (exact in bf16) and uses |scale|.
+  const bool neg_scale = scale_log2 < 0.f;
+  scale_log2 = fabsf(scale_log2);
   for (int pass = 0; pass < npass; ++pass) {
     if (pass) __syncthreads();                      // the first tile's LDS reads are done
     const int tile = pass ? tile1 : tile0;
@@ -300,13 +305,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
       qf[s] = bload16(rQ, ((uint32_t)(qrow0 + my_q_row) * qstride + 16 * s + 8 * half) * 2);
-    // The softmax takes its maximum over raw scores and folds the scale into one
-    // multiply-add, which needs a positive multiplier: for a negative scale,
-    // negate Q once (exact in bf16) and use |scale|.
-    if (scale_log2 < 0.f) {
+    if (neg_scale) {
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) qf[s] = qf[s] ^ 0x80008000u;
-      scale_log2 = -scale_log2;
     }
     barrier_all();                                    // K_0, V_0 landed
 

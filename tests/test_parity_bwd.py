@@ -67,6 +67,16 @@ def test_bwd_b4h16n2048d128_sampled_heads(gpu):
     assert float(g["dq"][:, :, 0].abs().max()) <= 1e-3
 
 
+def test_bwd_long_context_b1h32n8192d128_sampled_heads(gpu):
+    """The long-context shape: each key block of the dK/dV kernel meets up to
+    64 query tiles, and each query tile of the dQ kernel up to 128 key tiles.
+    Two heads against the oracle (full 8192 x 8192 gradients in fp64)."""
+    x = workloads.attention_inputs(1, 32, 8192, 128, "bf16", seed=82000, with_do=True)
+    scale = 128 ** -0.5
+    g = _run(gpu, x, True, scale)
+    _check(x, g, True, scale, heads=[(0, 0), (0, 31)])
+
+
 def test_bwd_deterministic(gpu):
     x = workloads.attention_inputs(1, 3, 333, 128, "bf16", seed=7, with_do=True)
     a = _run(gpu, x, True, 0.1)
