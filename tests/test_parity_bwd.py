@@ -68,9 +68,10 @@ def test_bwd_b4h16n2048d128_sampled_heads(gpu):
 
 
 def test_bwd_long_context_b1h32n8192d128_sampled_heads(gpu):
-    """The long-context shape: each key block of the dK/dV kernel meets up to
-    64 query tiles, and each query tile of the dQ kernel up to 128 key tiles.
-    Two heads against the oracle (full 8192 x 8192 gradients in fp64)."""
+    """The long-context shape: a 128-key block of the dK/dV kernel meets up
+    to 128 tiles of 64 queries, and a 128-query block of the dQ kernel up to
+    128 tiles of 64 keys.  Two heads against the oracle (full 8192 x 8192
+    gradients in fp64)."""
     x = workloads.attention_inputs(1, 32, 8192, 128, "bf16", seed=82000, with_do=True)
     scale = 128 ** -0.5
     g = _run(gpu, x, True, scale)

@@ -198,10 +198,12 @@ def test_fwd_reference_moves_mid_tile(gpu, d, causal, key, rise):
 
 # Spikes in several tiles, in rising order, on the long-sequence launch
 # (256-row workgroups, paired causal tiles): the reference moves several
-# times per row.
+# times per row, in both passes of a paired workgroup.  That launch needs at
+# least 256 workgroups: 16 tiles of 256 rows per head, paired to 8 when causal,
+# so 32 heads (causal) or 16 (non-causal).
 @pytest.mark.parametrize("causal", [False, True])
 def test_fwd_reference_moves_long(gpu, causal):
-    B, H, N, d = 1, 8, 4096, 128
+    B, H, N, d = 1, (32 if causal else 16), 4096, 128
     scale = 1.0 / math.sqrt(d)
     keys = [70, 1000, 2047, 2100, 4000]
     x = workloads.spike_inputs(B, H, N, d, "bf16", seed=5252, align=4.0,
