@@ -53,6 +53,30 @@ def test_fwd_f16(gpu, d, causal, N):
     _fwd_check(gpu, x, causal, 1.0 / math.sqrt(d))
 
 
+# The fp16 forward on the two paired launches of longer causal sequences:
+# 256-row workgroups (32 heads x 4100 rows) and 128-row workgroups (128 heads
+# x 1900 rows); both have a ragged last tile and an odd tile count.  Sampled
+# heads and rows.
+@pytest.mark.parametrize("B,H,N", [(1, 32, 4100), (8, 16, 1900)])
+def test_fwd_f16_paired_launches_sampled(gpu, B, H, N):
+    d = 128
+    x = workloads.attention_inputs(B, H, N, d, "f16", seed=6400 + N)
+    scale = d ** -0.5
+    q, k, v = (x[n].to(gpu) for n in "qkv")
+    o, lse = binding.fwd(q, k, v, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    o, lse = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    rows = np.unique(np.array([0, 1, 127, 128, 255, 256, N // 2, N - 2, N - 1]))
+    for heads, rsel in (([(0, 0), (B - 1, H - 1)], None), (None, rows)):
+        ref = oracle.attention_forward(x["q"], x["k"], x["v"], scale, True, heads=heads, rows=rsel)
+        for (b, h), (ro, rl) in ref.items():
+            go, gl = o[b, h], lse[b, h]
+            if rsel is not None:
+                go, gl = go[rsel], gl[rsel]
+            assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))
+            assert max_abs(go, ro) <= TOL and max_abs(gl, rl) <= TOL, (b, h)
+
+
 def test_fwd_f16_scores_beyond_fp16_exp_range(gpu):
     """Scores well past 12 natural units: e^12 alone is beyond fp16's 65504
     (the explainer's softmax appendix), so only the max-subtracted softmax can

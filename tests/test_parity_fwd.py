@@ -127,6 +127,24 @@ def test_fwd_256_row_workgroups_sampled(gpu, d, causal, N):
     _check(x, o, lse, causal, scale, TOL["bf16"], rows=rows)
 
 
+# Shorter sequences with many heads run in 128-row workgroups with paired
+# causal tiles, once the paired grid still leaves four workgroups per compute
+# unit (heads x ceil(query tiles / 2) >= 1024).  1900 rows leave a ragged
+# 108-row tile and an odd tile count (one workgroup runs the middle tile
+# alone); one case takes a negative scale.
+@pytest.mark.parametrize("B,H,N,d,sign", [(8, 16, 2048, 128, 1), (8, 16, 1900, 128, -1),
+                                          (8, 32, 1000, 64, 1)])
+def test_fwd_paired_128_row_workgroups_sampled(gpu, B, H, N, d, sign):
+    x = workloads.attention_inputs(B, H, N, d, "bf16", seed=73000 + N + d)
+    scale = sign * d ** -0.5
+    o, lse = _gpu_fwd(gpu, x, True, scale)
+    _check(x, o, lse, True, scale, TOL["bf16"], heads=[(0, 0), (B - 1, H - 1)])
+    rng = np.random.default_rng(N + d)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 129, N // 2, N - 1],
+                                     rng.integers(0, N, 20)]))
+    _check(x, o, lse, True, scale, TOL["bf16"], rows=rows)
+
+
 def test_fwd_deterministic(gpu):
     x = workloads.attention_inputs(2, 4, 777, 128, "bf16", seed=77)
     a = _gpu_fwd(gpu, x, True, 0.0884)
