@@ -53,22 +53,25 @@ def test_fwd_f16(gpu, d, causal, N):
     _fwd_check(gpu, x, causal, 1.0 / math.sqrt(d))
 
 
-# The fp16 forward on the two paired launches of longer causal sequences:
-# 256-row workgroups (32 heads x 4100 rows) and 128-row workgroups (128 heads
-# x 1900 rows); both have a ragged last tile and an odd tile count.  Sampled
-# heads and rows.
-@pytest.mark.parametrize("B,H,N", [(1, 32, 4100), (8, 16, 1900)])
-def test_fwd_f16_paired_launches_sampled(gpu, B, H, N):
-    d = 128
-    x = workloads.attention_inputs(B, H, N, d, "f16", seed=6400 + N)
+# The fp16 forward on the launches of longer sequences: 256-row workgroups
+# (paired when causal) and, for many heads below 4096 rows, paired 128-row
+# workgroups.  Ragged last tiles and odd tile counts; sampled heads and rows.
+@pytest.mark.parametrize("B,H,N,d,causal", [
+    (1, 32, 4100, 128, True), (8, 16, 1900, 128, True),      # 256-row / 128-row paired
+    (1, 32, 4100, 64, True), (8, 32, 1000, 64, True),
+    (1, 16, 4096, 128, False), (1, 16, 4100, 64, False),     # 256-row, not paired
+])
+def test_fwd_f16_long_launches_sampled(gpu, B, H, N, d, causal):
+    x = workloads.attention_inputs(B, H, N, d, "f16", seed=6400 + N + d)
     scale = d ** -0.5
     q, k, v = (x[n].to(gpu) for n in "qkv")
-    o, lse = binding.fwd(q, k, v, causal=True, scale=scale)
+    o, lse = binding.fwd(q, k, v, causal=causal, scale=scale)
     torch.cuda.synchronize()
     o, lse = o.double().cpu().numpy(), lse.double().cpu().numpy()
     rows = np.unique(np.array([0, 1, 127, 128, 255, 256, N // 2, N - 2, N - 1]))
     for heads, rsel in (([(0, 0), (B - 1, H - 1)], None), (None, rows)):
-        ref = oracle.attention_forward(x["q"], x["k"], x["v"], scale, True, heads=heads, rows=rsel)
+        ref = oracle.attention_forward(x["q"], x["k"], x["v"], scale, causal, heads=heads,
+                                       rows=rsel)
         for (b, h), (ro, rl) in ref.items():
             go, gl = o[b, h], lse[b, h]
             if rsel is not None:
@@ -124,7 +127,7 @@ def test_bwd_f16(gpu, d, causal):
         assert max_abs(dv[b, h].double().cpu().numpy(), r["dv"]) <= TOL_GRAD
 
 
-@pytest.mark.parametrize("kvh", [32, 8])
+@pytest.mark.parametrize("kvh", [32, 16, 8, 4])    # 1, 2, 4 and 8 query heads per cached head
 def test_paged_decode_f16(gpu, kvh):
     p = workloads.paged_inputs(10, 32, 128, 16, 1, 700, seed=6400 + kvh, dtype="f16", kv_heads=kvh,
                                pad_value=float("nan"))

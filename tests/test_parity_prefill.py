@@ -51,8 +51,10 @@ def test_paged_prefill_matches_oracle(gpu, dtype, d, kvh):
     _run(gpu, LENS, CHUNKS, 8, kvh, d, dtype, seed=7000 + d + kvh)
 
 
-def test_paged_prefill_noncausal(gpu):
-    _run(gpu, LENS, CHUNKS, 8, 4, 128, "bf16", seed=7100, causal=False)
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_paged_prefill_noncausal(gpu, dtype, d):
+    _run(gpu, LENS, CHUNKS, 8, 4, d, dtype, seed=7100 + d, causal=False)
 
 
 def test_paged_prefill_long_chunks_gqa(gpu):

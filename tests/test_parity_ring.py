@@ -99,10 +99,11 @@ def _partials(gpu, dtype, B=2, H=3, N=150, d=128, seed=3300):
     return x, qo, (oa, la, ob, lb)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("inplace", [False, True])
-def test_merge_matches_oracle(gpu, dtype, inplace):
-    _, _, (oa, la, ob, lb) = _partials(gpu, dtype)
+def test_merge_matches_oracle(gpu, dtype, d, inplace):
+    _, _, (oa, la, ob, lb) = _partials(gpu, dtype, d=d)
     ref_o, ref_l = oracle.merge_partials(oracle.to_f64(oa), oracle.to_f64(la),
                                          oracle.to_f64(ob), oracle.to_f64(lb))
     if inplace:
@@ -114,7 +115,7 @@ def test_merge_matches_oracle(gpu, dtype, inplace):
     go, gl = o.double().cpu().numpy(), l.double().cpu().numpy()
     empty = ref_l == -np.inf
     assert empty.sum() > 0 and np.all(gl[empty] == -np.inf) and np.all(go[empty] == 0)
-    tol = {"bf16": 1e-2, "f32": 1e-5}[dtype]
+    tol = {"bf16": 1e-2, "f16": 1e-2, "f32": 1e-5}[dtype]
     assert max_abs(go[~empty], ref_o[~empty]) <= tol
     assert max_abs(gl[~empty], ref_l[~empty]) <= 1e-5
 
