@@ -1,5 +1,6 @@
 """C-ABI behaviour with real device buffers: failed validation writes nothing,
-B == 0 is a no-op, and the binding raises on error status."""
+empty inputs are no-ops on every entry point, and the binding raises on
+error status."""
 import ctypes
 
 import pytest
@@ -30,6 +31,41 @@ def test_zero_batch_is_noop(gpu):
                     None)
     torch.cuda.synchronize()
     assert st == 0 and bool((o == 3.0).all())
+
+
+def test_empty_inputs_are_noops_on_every_entry_point(gpu):
+    """B == 0 (fa_fwd_offset, fa_merge, fa_bwd), num_seqs == 0 (decode, GQA
+    decode, prefill, KV append) and total_q == 0 (prefill) return FA_OK and
+    write nothing: every output and in/out argument points at sentinels that
+    keep their values."""
+    lib = binding.load_library()
+    bf = binding.FA_DT_BF16
+    f = torch.full((1024,), 3.0, device=gpu)
+    n = torch.full((64,), 5, dtype=torch.int32, device=gpu)
+    fp, np_ = ctypes.c_void_p(f.data_ptr()), ctypes.c_void_p(n.data_ptr())
+    ws = torch.zeros(4096, dtype=torch.uint8, device=gpu)
+    wp = ctypes.c_void_p(ws.data_ptr())
+    st = {
+        "fa_fwd_offset": lib.fa_fwd_offset(fp, fp, fp, fp, fp, 0, 2, 64, 64, 64, 0, 0, 0.1, 1, bf,
+                                           None),
+        "fa_merge": lib.fa_merge(fp, fp, fp, fp, fp, fp, 0, 2, 64, 64, bf, None),
+        "fa_bwd": lib.fa_bwd(fp, fp, fp, fp, fp, fp, fp, fp, fp, 0, 2, 64, 64, 0.1, 1, bf, wp,
+                             4096, None),
+        "fa_paged_decode": lib.fa_paged_decode(fp, fp, fp, np_, np_, 16, 0, 4, 128, 1, 1, 0.1,
+                                               fp, fp, bf, wp, 4096, None),
+        "fa_paged_decode_gqa": lib.fa_paged_decode_gqa(fp, fp, fp, np_, np_, 16, 0, 4, 2, 128, 1,
+                                                       1, 0.1, fp, fp, bf, wp, 4096, None),
+        "fa_paged_prefill (num_seqs 0)": lib.fa_paged_prefill(
+            fp, np_, fp, fp, np_, np_, 0, 0, 4, 2, 128, 16, 1, 1, 1, 0.1, 1, fp, fp, bf, None),
+        "fa_paged_prefill (total_q 0)": lib.fa_paged_prefill(
+            fp, np_, fp, fp, np_, np_, 3, 0, 4, 2, 128, 16, 1, 1, 1, 0.1, 1, fp, fp, bf, None),
+        "fa_paged_kv_append": lib.fa_paged_kv_append(fp, fp, fp, fp, np_, np_, np_, np_, np_, 0,
+                                                     2, 128, 16, 1, 1, 4, bf, wp, 4096, None),
+    }
+    torch.cuda.synchronize()
+    assert all(v == 0 for v in st.values()), st
+    assert bool((f == 3.0).all()) and bool((n == 5).all())
+    assert bool((ws == 0).all())
 
 
 def test_unsupported_head_dim_raises(gpu):
