@@ -179,9 +179,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   }
   // The softmax takes its maximum over raw scores and folds the scale into one
   // multiply-add, which needs a positive multiplier: for a negative scale,
-  // each pass negates its Q (exact in bf16) and uses |scale|.
+  // each pass negates its Q (exact in bf16) and uses |scale|.  Masked scores
+  // are -inf before that multiply, and -inf * 0 is NaN, so a zero scale is
+  // raised to the smallest normal float: masked keys stay at -inf, and every
+  // finite score below 2^99 in magnitude still gets probability exactly 1.
   const bool neg_scale = scale_log2 < 0.f;
-  scale_log2 = fabsf(scale_log2);
+  scale_log2 = fmaxf(fabsf(scale_log2), __FLT_MIN__);
   for (int pass = 0; pass < npass; ++pass) {
     if (pass) __syncthreads();                      // the first tile's LDS reads are done
     const int tile = pass ? tile1 : tile0;

@@ -78,6 +78,19 @@ def test_bwd_long_context_b1h32n8192d128_sampled_heads(gpu):
     _check(x, g, True, scale, heads=[(0, 0), (0, 31)])
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_zero_scale_closed_form(gpu, d):
+    """scale = 0: S = 0 Q K^T, so dQ = dK = 0 exactly, and with uniform causal
+    weights P_ij = 1/(i+1) for j <= i, dV_j = sum over i >= j of dO_i/(i+1)."""
+    N = 300
+    x = workloads.attention_inputs(1, 2, N, d, "bf16", seed=2400 + d, with_do=True)
+    g = _run(gpu, x, True, 0.0)
+    assert float(g["dq"].abs().max()) == 0.0 and float(g["dk"].abs().max()) == 0.0
+    w = x["do"].double() / torch.arange(1, N + 1, dtype=torch.float64)[None, None, :, None]
+    dv = torch.flip(torch.cumsum(torch.flip(w, [2]), dim=2), [2])
+    assert max_abs(g["dv"].double().numpy(), dv.numpy()) <= TOL_GRAD
+
+
 def test_bwd_deterministic(gpu):
     x = workloads.attention_inputs(1, 3, 333, 128, "bf16", seed=7, with_do=True)
     a = _run(gpu, x, True, 0.1)

@@ -140,3 +140,23 @@ def test_decode_balanced_shares(gpu, lens, kvh):
     scale = 1.0 / np.sqrt(128)
     o, lse = _run(gpu, p, scale)
     _check(p, o, lse, scale)
+
+
+@pytest.mark.parametrize("kvh", [32, 8])
+def test_decode_zero_scale_closed_form(gpu, kvh):
+    """scale = 0 gives every cached token the same weight: o is the mean of the
+    sequence's cached V rows (read through the block table here) and
+    lse = ln(seq_len).  Pad slots hold NaN."""
+    lens = [1, 16, 17, 300, 1000, 4096]
+    H, d, bs = 32, 128, 16
+    p = workloads.paged_inputs(len(lens), H, d, bs, 1, max(lens), seed=9100 + kvh, seq_lens=lens,
+                               kv_heads=kvh, pad_value=float("nan"))
+    o, lse = _run(gpu, p, 0.0)
+    g = H // kvh
+    for s, n in enumerate(lens):
+        t = torch.arange(n)
+        blocks = p["block_table"][s, t // bs].long()
+        v = p["v_pool"][blocks, t % bs].double()               # [n, kvh, d]
+        mean = v.mean(dim=0).repeat_interleave(g, dim=0)       # query head h reads h // g
+        assert max_abs(o[s].double().numpy(), mean.numpy()) <= TOL, s
+        assert max_abs(lse[s].double().numpy(), np.full(H, np.log(n))) <= 1e-3, s

@@ -164,6 +164,26 @@ def test_fwd_closed_forms(gpu):
     assert torch.equal(o[:, :, 0], x["v"][:, :, 0].float())
 
 
+# scale = 0 gives every visible key the same weight: causal O_i is the mean of
+# V_0..V_i and LSE_i = ln(i + 1); non-causal rows all get the mean of V and
+# ln(N).  On the paired 256-row launch (32 heads x 4100 rows) and the 128-row
+# launch with a ragged last key tile.
+@pytest.mark.parametrize("B,H,N,d,causal", [(1, 32, 4100, 128, True), (2, 3, 300, 64, True),
+                                            (2, 3, 300, 128, False)])
+def test_fwd_zero_scale_closed_form(gpu, B, H, N, d, causal):
+    x = workloads.attention_inputs(B, H, N, d, "bf16", seed=74000 + N + d)
+    o, lse = _gpu_fwd(gpu, x, causal, 0.0)
+    v = x["v"].double()
+    if causal:
+        cnt = torch.arange(1, N + 1, dtype=torch.float64)
+        mean = torch.cumsum(v, dim=2) / cnt[None, None, :, None]
+    else:
+        cnt = torch.full((N,), float(N), dtype=torch.float64)
+        mean = v.mean(dim=2, keepdim=True).expand_as(v)
+    assert max_abs(o.double().numpy(), mean.numpy()) <= 2e-2
+    assert max_abs(lse.double().numpy(), np.log(cnt.numpy())[None, None, :]) <= 1e-3
+
+
 def test_fwd_on_side_stream(gpu):
     x = workloads.attention_inputs(1, 2, 130, 128, "bf16", seed=99)
     ref = _gpu_fwd(gpu, x, True, 0.09)
