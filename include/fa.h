@@ -83,7 +83,9 @@ int fa_version(void);
  *   LSE      out  [B,H,N] fp32, natural-log log-sum-exp of the visible scaled scores
  *   B, H, N  >= 0, >= 1, >= 1 (B == 0 is a no-op); N <= 1<<20
  *   d        64 or 128 (else FA_ERR_UNSUPPORTED)
- *   scale    finite; multiplies the raw scores (1/sqrt(d) in the usual setting)
+ *   scale    finite, of either sign or zero; multiplies the raw scores (1/sqrt(d) in
+ *            the usual setting).  scale * q.k must stay inside the fp32 range.
+ *            scale = 0 gives every visible key the same weight.
  *   causal   0 = every key visible; non-zero = key j visible to query i iff j <= i
  *
  * 16-bit inputs (bf16, fp16) are multiplied on the matrix cores with fp32
