@@ -26,6 +26,9 @@ TOL = {"bf16": 2e-2, "f32": 1e-5}
 OFFSET_CASES = [
     (130, 200, 0, 0), (130, 200, 100, 0), (200, 130, 0, 100), (257, 64, 0, 300),
     (64, 300, 1000, 0), (1, 1, 5, 5), (129, 63, 63, 1), (300, 257, 2, 0), (65, 129, 0, 64),
+    # far-apart and extreme positions: every key visible, none visible, and
+    # offsets at the -2^60 limit whose difference (-30) empties the first rows
+    (130, 200, 1 << 40, 0), (130, 200, 0, 1 << 40), (100, 150, -(1 << 60), -(1 << 60) + 30),
 ]
 
 
