@@ -67,6 +67,34 @@ def test_paged_prefill_long_chunks_gqa(gpu):
     _run(gpu, lens, chunks, 32, 8, 128, "bf16", seed=7200, rows=rows)
 
 
+def test_paged_prefill_zero_scale_closed_form(gpu):
+    """scale = 0: chunk row r of a sequence with L cached tokens and an n-token
+    chunk sees keys 0 .. L - n + r, all with the same weight, so its output is
+    the mean of those V rows (read through the block table here) and its LSE
+    the log of their count.  Pad slots hold NaN."""
+    lens, chunks, H, kvh, d = [17, 100, 300], [17, 10, 129], 8, 2, 128
+    p = workloads.paged_inputs(len(lens), H, d, 16, 1, max(lens), seed=7300, seq_lens=lens,
+                               kv_heads=kvh, pad_value=float("nan"))
+    qq = workloads.prefill_queries(chunks, H, d, seed=7301)
+    pd = {k: (v.to(gpu) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+    o, lse = binding.paged_prefill(qq["q"].to(gpu), qq["q_start"].to(gpu), pd["k_pool"],
+                                   pd["v_pool"], pd["block_table"], pd["seq_lens"], block_size=16,
+                                   max_q_len=max(chunks), causal=True, scale=0.0)
+    torch.cuda.synchronize()
+    o, lse = o.double().cpu(), lse.double().cpu()
+    start = 0
+    for s, (L, n) in enumerate(zip(lens, chunks)):
+        t = torch.arange(L)
+        v = p["v_pool"][p["block_table"][s, t // 16].long(), t % 16].double()   # [L, kvh, d]
+        cum = torch.cumsum(v, 0) / torch.arange(1, L + 1, dtype=torch.float64)[:, None, None]
+        last = torch.arange(L - n, L)                           # last visible key of each row
+        ref = cum[last].repeat_interleave(H // kvh, dim=1)      # query head h reads h // g
+        assert max_abs(o[start:start + n].numpy(), ref.numpy()) <= TOL["bf16"], s
+        ref_l = np.log(last.double().numpy() + 1)[:, None].repeat(H, 1)
+        assert max_abs(lse[start:start + n].numpy(), ref_l) <= 1e-3, s
+        start += n
+
+
 def test_paged_prefill_debug_validation(gpu, monkeypatch):
     """FA_DEBUG=1: a chunk longer than its sequence is refused before launch."""
     p = workloads.paged_inputs(2, 4, 128, 16, 1, 40, seed=7300, seq_lens=[10, 40], kv_heads=4)
