@@ -164,29 +164,34 @@ def online_softmax(s: np.ndarray, block: int, values: np.ndarray | None = None):
     return acc / l, traj
 
 
-def _row_chunks(rows: np.ndarray, nk: int, budget_elems: int = 1 << 22):
+ROW_CHUNK_ELEMS = 1 << 22   # score entries held at once per head (32 MiB of fp64)
+
+
+def _row_chunks(rows: np.ndarray, nk: int, budget_elems: int = ROW_CHUNK_ELEMS):
+    """Consecutive pieces of ``rows``, each of at most max(1, budget_elems // nk) rows."""
     step = max(1, budget_elems // max(1, nk))
     for i in range(0, len(rows), step):
         yield rows[i:i + step]
 
 
 def attention_forward_head(q, k, v, scale: float, causal: bool, rows=None, q_offset: int = 0,
-                           k_offset: int = 0):
+                           k_offset: int = 0, budget_elems: int = ROW_CHUNK_ELEMS):
     """Exact attention for one (batch, head).
 
     q [Nq, d], k [Nk, d], v [Nk, dv] float64.  ``rows`` selects a subset of the
     query rows (default: all).  ``q_offset`` / ``k_offset`` are the global
     positions of the first query / key row (they matter only for the causal
     rule).  Returns (O [len(rows), dv], LSE [len(rows)]); a row with no visible
-    key gets O = 0 and LSE = -inf.  Rows are processed in chunks to bound
-    memory; each row is independent.
+    key gets O = 0 and LSE = -inf.  Rows are processed in chunks of at most
+    ``budget_elems`` score entries to bound memory; each row is independent,
+    so the chunking changes nothing but the peak memory.
     """
     nq, nk = q.shape[0], k.shape[0]
     rows = np.arange(nq) if rows is None else np.asarray(rows, dtype=np.int64)
     o = np.zeros((len(rows), v.shape[1]), dtype=np.float64)
     lse = np.full((len(rows),), -np.inf, dtype=np.float64)
-    pos = 0
-    for r in _row_chunks(rows, nk):
+    pos = 0                                        # output index of the chunk's first row
+    for r in _row_chunks(rows, nk, budget_elems):
         vis = visible(r, nk, causal, q_offset, k_offset)
         some = vis.any(axis=1)                     # rows that see at least one key
         if some.any():

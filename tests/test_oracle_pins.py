@@ -191,6 +191,56 @@ def test_forward_invariants():
     check_forward_invariants()
 
 
+def check_forward_row_chunks(seed=2):
+    """The row chunking of the forward changes nothing but peak memory.
+
+    N = 2100 keys puts the default budget at 1997 rows per chunk, so a head is
+    two chunks, the second ragged.  Closed forms hold on every row of both:
+    Q = 0 gives uniform weights (causal O_i = mean of V_0..V_i, LSE_i =
+    ln(i + 1); non-causal O_i = mean of V, LSE_i = ln N), and causal row 0 sees
+    only key 0 (O_0 = V_0).  Budgets of one, two and five rows per chunk
+    (ragged last chunks) give what one chunk over all rows gives, also for a
+    key block ahead of some queries, whose first rows see no key at all.
+    """
+    rng = np.random.default_rng(seed)
+    n, d = 2100, 4
+    k, v = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    z = np.zeros((n, d))
+    assert len(list(A._row_chunks(np.arange(n), n))) == 2
+    oc, lc = A.attention_forward_head(z, k, v, 0.5, True)
+    np.testing.assert_allclose(oc, np.cumsum(v, axis=0) / np.arange(1, n + 1)[:, None],
+                               rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lc, np.log(np.arange(1, n + 1)), rtol=0, atol=1e-12)
+    on, ln_ = A.attention_forward_head(z, k, v, 0.5, False)
+    np.testing.assert_allclose(on, np.broadcast_to(v.mean(axis=0), on.shape), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ln_, math.log(n), rtol=0, atol=1e-12)
+    q = rng.standard_normal((n, d))
+    oq, lq = A.attention_forward_head(q, k, v, 0.5, True)
+    np.testing.assert_array_equal(oq[0], v[0])
+    np.testing.assert_allclose(lq[0], 0.5 * q[0] @ k[0], rtol=1e-15)
+    # small heads under tiny budgets against a single chunk
+    m_, d_ = 37, 3
+    qs, ks, vs = (rng.standard_normal((m_, d_)) for _ in range(3))
+    for causal, q_off in ((False, 0), (True, 0), (True, -10)):
+        whole = A.attention_forward_head(qs, ks, vs, 0.7, causal, q_offset=q_off,
+                                         budget_elems=1 << 30)
+        for budget in (1, 2 * m_, 5 * m_ + 3):
+            part = A.attention_forward_head(qs, ks, vs, 0.7, causal, q_offset=q_off,
+                                            budget_elems=budget)
+            np.testing.assert_allclose(part[0], whole[0], rtol=0, atol=1e-14)
+            np.testing.assert_array_equal(np.isinf(part[1]), np.isinf(whole[1]))
+            fin = np.isfinite(whole[1])
+            np.testing.assert_allclose(part[1][fin], whole[1][fin], rtol=0, atol=1e-14)
+        if q_off < 0:
+            # rows 0..9 sit before key 0: empty softmax
+            assert np.all(whole[0][:10] == 0) and np.all(whole[1][:10] == -np.inf)
+            assert np.all(np.isfinite(whole[1][10:]))
+
+
+def test_forward_row_chunks():
+    check_forward_row_chunks()
+
+
 def test_forward_batched_matches_per_head():
     x = workloads.attention_inputs(2, 3, 19, 8, "bf16", seed=5)
     res = A.attention_forward(x["q"], x["k"], x["v"], 0.3, True, workers=4)
@@ -582,6 +632,7 @@ def _all_forward_pins(golden_dir):
     check_forward_vs_decimal()
     check_forward_large_scores()
     check_forward_invariants()
+    check_forward_row_chunks()
 
 
 def _all_backward_pins():
@@ -607,7 +658,58 @@ def _bad_safe_softmax_nomax(s):
     return e / l, np.zeros(s.shape[:-1]), l[..., 0]
 
 
+def _row_chunks_short(rows, nk, budget_elems=A.ROW_CHUNK_ELEMS):
+    step = max(1, budget_elems // max(1, nk))
+    for i in range(0, len(rows), step):
+        yield rows[i:i + step - 1] if step > 1 else rows[i:i + 1][:0]   # drops a row per chunk
+
+
+_REAL_FORWARD_HEAD = A.attention_forward_head
+
+
+def _forward_head_pos_frozen(q, k, v, scale, causal, rows=None, q_offset=0, k_offset=0,
+                             budget_elems=A.ROW_CHUNK_ELEMS):
+    """The chunked forward with its output index never advancing past chunk 0."""
+    nq, nk = q.shape[0], k.shape[0]
+    rows = np.arange(nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.zeros((len(rows), v.shape[1]))
+    lse = np.full((len(rows),), -np.inf)
+    for r in A._row_chunks(rows, nk, budget_elems):
+        vis = A.visible(r, nk, causal, q_offset, k_offset)
+        some = vis.any(axis=1)
+        if some.any():
+            rs = r[some]
+            s = np.where(vis[some], A.scores(q[rs], k, scale), -np.inf)
+            p, m, l = A.safe_softmax(s)
+            idx = np.nonzero(some)[0]                 # pos missing
+            o[idx] = A.attend(p, v)
+            lse[idx] = A.lse_of(m, l)
+    return o, lse
+
+
+def _forward_head_step_doubled(q, k, v, scale, causal, rows=None, q_offset=0, k_offset=0,
+                               budget_elems=A.ROW_CHUNK_ELEMS):
+    """The chunked forward with its output index advancing twice per chunk."""
+    nq = q.shape[0]
+    rows = np.arange(nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.zeros((len(rows), v.shape[1]))
+    lse = np.full((len(rows),), -np.inf)
+    pos = 0
+    for r in A._row_chunks(rows, k.shape[0], budget_elems):
+        if pos >= len(rows):
+            break
+        oc, lc = _REAL_FORWARD_HEAD(q, k, v, scale, causal, rows=r, q_offset=q_offset,
+                                    k_offset=k_offset, budget_elems=1 << 40)
+        n_ = min(len(r), len(rows) - pos)
+        o[pos:pos + n_], lse[pos:pos + n_] = oc[:n_], lc[:n_]
+        pos += 2 * len(r)
+    return o, lse
+
+
 FORWARD_MUTANTS = {
+    "row_chunks_drop_row": ("_row_chunks", _row_chunks_short),
+    "row_chunks_pos_frozen": ("attention_forward_head", _forward_head_pos_frozen),
+    "row_chunks_step_doubled": ("attention_forward_head", _forward_head_step_doubled),
     "scale_dropped": ("scores", lambda q, k, scale: q @ k.T),
     "scale_squared": ("scores", lambda q, k, scale: scale * scale * (q @ k.T)),
     "transposed_scores": ("scores", lambda q, k, scale: scale * (k @ q.T) if q.shape == k.shape
