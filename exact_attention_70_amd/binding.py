@@ -23,8 +23,11 @@ FA_DT_F16 = 2
 
 EXPORTED = ("fa_status_string", "fa_version", "fa_fwd", "fa_fwd_offset", "fa_merge",
             "fa_bwd_workspace_size", "fa_bwd", "fa_paged_decode_workspace_size", "fa_paged_decode",
-            "fa_paged_decode_gqa", "fa_paged_kv_append_workspace_size", "fa_paged_kv_append",
-            "fa_paged_prefill")
+            "fa_paged_decode_gqa", "fa_paged_decode_gqa_noalloc",
+            "fa_paged_kv_append_workspace_size", "fa_paged_kv_append", "fa_paged_prefill")
+
+# bytes of the static scratch behind fa_paged_decode_gqa_noalloc (FA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _lib = None
 
@@ -72,6 +75,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fa_paged_decode_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, i, vp, sz,
                                         vp]
     lib.fa_paged_decode_gqa.restype = i
+    lib.fa_paged_decode_gqa_noalloc.argtypes = [vp, vp, vp, vp, vp] + [i] * 7 + [f, vp, vp, i, vp]
+    lib.fa_paged_decode_gqa_noalloc.restype = i
     lib.fa_paged_kv_append_workspace_size.argtypes = [i]
     lib.fa_paged_kv_append_workspace_size.restype = sz
     lib.fa_paged_kv_append.argtypes = [vp] * 9 + [i] * 8 + [vp, sz, vp]
@@ -270,6 +275,29 @@ def paged_decode(q, k_pool, v_pool, block_table, seq_lens, *, block_size: int,
             H, KVH, d, mbps, num_blocks, scale, _ptr(o), _ptr(l), _dtype_code(q), _ptr(workspace),
             _nbytes(workspace), _stream(q.device))
         _check(st, "fa_paged_decode_gqa")
+    return o, l
+
+
+def paged_decode_noalloc(q, k_pool, v_pool, block_table, seq_lens, *, block_size: int,
+                         scale: float | None = None, out=None, lse=None):
+    """paged_decode through fa_paged_decode_gqa_noalloc: no workspace, the
+    library's static per-GPU scratch instead.  With ``out`` and ``lse`` given,
+    the call allocates nothing at all."""
+    _need_cuda(q, k_pool, v_pool, block_table, seq_lens)
+    S, H, d = q.shape
+    num_blocks, KVH = k_pool.shape[0], k_pool.shape[2]
+    mbps = block_table.shape[1]
+    _check_pool(k_pool, v_pool, q, block_size, KVH, d)
+    _want(block_table, (S, mbps), torch.int32, q.device, "block_table")
+    _want(seq_lens, (S,), torch.int32, q.device, "seq_lens")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else _want(out, q.shape, q.dtype, q.device, "out")
+    l = (torch.empty((S, H), dtype=torch.float32, device=q.device) if lse is None
+         else _want(lse, (S, H), torch.float32, q.device, "lse"))
+    st = load_library().fa_paged_decode_gqa_noalloc(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), block_size, S, H,
+        KVH, d, mbps, num_blocks, scale, _ptr(o), _ptr(l), _dtype_code(q), _stream(q.device))
+    _check(st, "fa_paged_decode_gqa_noalloc")
     return o, l
 
 

@@ -11,6 +11,9 @@
 #include "../../include/fa.h"
 #include "fa_internal.h"
 
+static_assert(fa::kNoAllocScratchBytes == (size_t)FA_NOALLOC_SCRATCH_BYTES,
+              "the header states the static scratch size");
+
 namespace {
 
 constexpr int kMaxN = 1 << 20;
@@ -53,6 +56,9 @@ const char* fa_status_string(int status) {
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_INVALID: return "FA_ERR_INVALID: invalid contents or overlapping buffers";
     case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error";
+    case FA_ERR_SCRATCH:
+      return "FA_ERR_SCRATCH: the call needs more than the library's static scratch "
+             "(FA_NOALLOC_SCRATCH_BYTES); use the workspace entry point";
     default: return "unknown libfa status";
   }
 }
@@ -149,11 +155,14 @@ size_t fa_paged_decode_workspace_size(int num_seqs, int H, int d, int max_blocks
                   256);
 }
 
-int fa_paged_decode_gqa(const void* q, const void* k_pool, const void* v_pool,
-                        const int32_t* block_table, const int32_t* seq_lens, int block_size,
-                        int num_seqs, int H, int KVH, int d, int max_blocks_per_seq, int num_blocks,
-                        float scale, void* o, float* lse, int dtype, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+namespace {
+
+// Argument checks shared by the decode entry points, before any device work:
+// FA_OK to go on, or the status to return (1: a no-op, num_seqs == 0).
+int check_decode_args(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_table, const int32_t* seq_lens, int block_size,
+                      int num_seqs, int H, int KVH, int d, int max_blocks_per_seq, int num_blocks,
+                      float scale, void* o, float* lse, int dtype) {
   if (dtype != FA_DT_F32 && dtype != FA_DT_BF16 && dtype != FA_DT_F16) return FA_ERR_DTYPE;
   if (num_seqs < 0 || H < 1 || KVH < 1 || d < 1 || max_blocks_per_seq < 1 || num_blocks < 1 ||
       block_size < 1)
@@ -165,17 +174,32 @@ int fa_paged_decode_gqa(const void* q, const void* k_pool, const void* v_pool,
   const long long block_bytes = (long long)block_size * KVH * d * 2;
   if (block_bytes >= (1LL << 31)) return FA_ERR_SHAPE;
   if ((long long)max_blocks_per_seq * block_size > kMaxN) return FA_ERR_SHAPE;
-  if (num_seqs == 0) return FA_OK;
+  if (num_seqs == 0) return 1;
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !o || !lse)
     return FA_ERR_NULL;
-  const size_t need =
-      fa_paged_decode_workspace_size(num_seqs, H, d, max_blocks_per_seq, block_size);
-  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
-  const void* ptrs[] = {q, k_pool, v_pool, o, lse, workspace};
+  const void* ptrs[] = {q, k_pool, v_pool, o, lse};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
     return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+}  // namespace
+
+int fa_paged_decode_gqa(const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* block_table, const int32_t* seq_lens, int block_size,
+                        int num_seqs, int H, int KVH, int d, int max_blocks_per_seq, int num_blocks,
+                        float scale, void* o, float* lse, int dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  const int chk = check_decode_args(q, k_pool, v_pool, block_table, seq_lens, block_size, num_seqs,
+                                    H, KVH, d, max_blocks_per_seq, num_blocks, scale, o, lse, dtype);
+  if (chk == 1) return FA_OK;
+  if (chk != FA_OK) return chk;
+  const size_t need =
+      fa_paged_decode_workspace_size(num_seqs, H, d, max_blocks_per_seq, block_size);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (debug_checks()) {
     std::vector<int32_t> tbl((size_t)num_seqs * max_blocks_per_seq), lens(num_seqs);
@@ -198,6 +222,30 @@ int fa_paged_decode_gqa(const void* q, const void* k_pool, const void* v_pool,
   fa::DecodeArgs a{q, k_pool, v_pool, block_table, seq_lens, block_size, num_seqs, H, d,
                    max_blocks_per_seq, num_blocks, scale, o, lse,
                    static_cast<float*>(workspace), fa::kDecodeUnits, st};
+  a.KVH = KVH;
+  a.dtype = dtype;
+  return hip_status(fa::launch_decode(a));
+}
+
+int fa_paged_decode_gqa_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                int block_size, int num_seqs, int H, int KVH, int d,
+                                int max_blocks_per_seq, int num_blocks, float scale, void* o,
+                                float* lse, int dtype, void* stream) {
+  const int chk = check_decode_args(q, k_pool, v_pool, block_table, seq_lens, block_size, num_seqs,
+                                    H, KVH, d, max_blocks_per_seq, num_blocks, scale, o, lse, dtype);
+  if (chk == 1) return FA_OK;
+  if (chk != FA_OK) return chk;
+  if (fa_paged_decode_workspace_size(num_seqs, H, d, max_blocks_per_seq, block_size) >
+      fa::kNoAllocScratchBytes)
+    return FA_ERR_SCRATCH;
+  void* scratch = nullptr;
+  const hipError_t e = fa::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  fa::DecodeArgs a{q, k_pool, v_pool, block_table, seq_lens, block_size, num_seqs, H, d,
+                   max_blocks_per_seq, num_blocks, scale, o, lse,
+                   static_cast<float*>(scratch), fa::kDecodeUnits,
+                   reinterpret_cast<hipStream_t>(stream)};
   a.KVH = KVH;
   a.dtype = dtype;
   return hip_status(fa::launch_decode(a));

@@ -47,6 +47,8 @@
 // Merge kernel: one wave per (sequence, head) combines its pieces, found
 //   from the prefix sums.
 //   Throughput is bound by HBM: the flops per byte are ~1.
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -566,6 +568,40 @@ hipError_t launch_decode_e(const DecodeArgs& a) {
 
 hipError_t launch_decode(const DecodeArgs& a) {
   return a.dtype == 2 ? launch_decode_e<F16>(a) : launch_decode_e<Bf16>(a);
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of the allocation-free decode: the same partials and prefix
+// sums the workspace holds, in a file-scope device array that every GPU the
+// library runs on keeps for the life of the process.  In host code `scratch`
+// names a host-side stand-in, not device memory: its device address is taken
+// once per device with hipGetSymbolAddress (with that device current) and only
+// that address is handed to kernels.  Every decode kernel fully writes what it
+// later reads (prefix sums, then each piece's partial), so nothing needs
+// clearing between calls.
+namespace {
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace fa

@@ -100,6 +100,9 @@ hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_merge(const MergeArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
+// Device address, on the current device, of the allocation-free decode's
+// static scratch (kNoAllocScratchBytes); taken once per device.
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_append(const AppendArgs& a);
 
 // Heads per group for xcd_grouped over a grid of `heads` heads whose tiles
@@ -129,6 +132,8 @@ inline int xcd_group(long long heads, long long bytes_per_head) {
 constexpr int kDecodeUnits = FA_DECODE_UNITS;
 // workspace bytes: per slot and head (m, l, d output values) in fp32, then the
 // num_seqs + 1 block prefix sums (int64)
+// Bytes of the static scratch behind fa_paged_decode_gqa_noalloc.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
 inline size_t decode_partials_floats(int num_seqs, int H, int d) {
   return ((size_t)kDecodeUnits + num_seqs) * H * (size_t)(d + 2);
 }

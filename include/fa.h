@@ -2,9 +2,12 @@
  * libfa -- exact scaled-dot-product attention for AMD Instinct MI355X (gfx950).
  *
  * C ABI.  Every tensor argument is a DEVICE pointer owned by the caller; the
- * library never allocates, frees or retains caller memory and keeps no device
- * state between calls.  Scratch memory comes only through an explicit
- * workspace argument whose minimum size the *_workspace_size queries return.
+ * library never allocates, frees or retains caller memory.  Scratch memory
+ * comes through an explicit workspace argument whose minimum size the
+ * *_workspace_size queries return; the one exception is
+ * fa_paged_decode_gqa_noalloc, which uses a fixed static device buffer of the
+ * library's own instead (see there).  No other call keeps device state
+ * between calls.
  *
  * Synchrony: each call validates its arguments on the host, enqueues its
  * kernels on `stream` (a hipStream_t passed as void*, NULL = the null stream)
@@ -50,7 +53,8 @@ typedef enum {
   FA_ERR_ALIGN = -5,       /* a tensor pointer is not 16-byte aligned             */
   FA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than the query returns */
   FA_ERR_INVALID = -7,     /* block_table / seq_lens invalid (FA_DEBUG=1), or overlapping buffers */
-  FA_ERR_HIP = -8          /* the HIP runtime reported an error                   */
+  FA_ERR_HIP = -8,         /* the HIP runtime reported an error                   */
+  FA_ERR_SCRATCH = -9      /* needs more than the static scratch of a *_noalloc call */
 } fa_status;
 
 /* Element formats.  FA_DT_F16 is IEEE half: the explainer's mixed-precision
@@ -243,6 +247,36 @@ int fa_paged_decode_gqa(const void* q, const void* k_pool, const void* v_pool,
                         int num_seqs, int H, int KVH, int d, int max_blocks_per_seq,
                         int num_blocks, float scale, void* o, float* lse, int dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_paged_decode_gqa_noalloc -- fa_paged_decode_gqa for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * and harnesses that forbid hipMalloc.  It takes no workspace: the partial
+ * results and block counts that fa_paged_decode_gqa keeps in its workspace go
+ * to a static device buffer of FA_NOALLOC_SCRATCH_BYTES inside the library,
+ * one per GPU, held from the first such call on that GPU until the process
+ * ends.  The call allocates nothing (no hipMalloc, no allocating library
+ * routine); its first call on a GPU looks up that GPU's buffer address.
+ *
+ * Arguments, layouts, arithmetic and results are those of fa_paged_decode_gqa
+ * (KVH = H for plain multi-head decode).  A call whose workspace requirement
+ * (fa_paged_decode_workspace_size) exceeds FA_NOALLOC_SCRATCH_BYTES returns
+ * FA_ERR_SCRATCH and launches nothing: at H = 32, d = 128 that is about 1,750
+ * sequences.  The FA_DEBUG host-side table check is not made (it would copy
+ * the table to the host).
+ *
+ * Every call on one GPU shares that GPU's buffer, which keeps the last call's
+ * contents (nothing in it needs clearing: each call writes what it reads).
+ * Calls that overlap on one GPU -- on different streams, or from different
+ * host threads without ordering -- race on the buffer and give undefined
+ * results; serialise them (one stream, or events).
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int fa_paged_decode_gqa_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                int block_size, int num_seqs, int H, int KVH, int d,
+                                int max_blocks_per_seq, int num_blocks, float scale, void* o,
+                                float* lse, int dtype, void* stream);
 
 /*
  * fa_paged_prefill -- the forward of a chunk of new queries per sequence over

@@ -189,6 +189,32 @@ def test_paged_decode_gqa_validation(lib):
     assert gqa(lib, S=0, q=None) == OK
 
 
+def noalloc(lib, H=32, KVH=32, d=128, bs=16, dt=1, S=4, q=P):
+    return lib.fa_paged_decode_gqa_noalloc(q, P, P, P, P, bs, S, H, KVH, d, 8, 100, 0.1, P2, P2, dt,
+                                           None)
+
+
+def test_paged_decode_noalloc_validation(lib):
+    """The allocation-free decode checks its arguments like the workspace
+    decode, and refuses a call whose partials exceed its static scratch
+    (FA_NOALLOC_SCRATCH_BYTES) before any device work."""
+    ERR_SCRATCH = -9
+    assert "FA_ERR_SCRATCH" in libfa.status_string(ERR_SCRATCH)
+    assert noalloc(lib, KVH=5) == ERR_SHAPE
+    assert noalloc(lib, d=64) == ERR_UNSUP
+    assert noalloc(lib, bs=8) == ERR_UNSUP
+    assert noalloc(lib, dt=3) == ERR_DTYPE
+    assert noalloc(lib, q=None) == ERR_NULL
+    assert noalloc(lib, q=MIS) == ERR_ALIGN
+    assert noalloc(lib, S=0, q=None) == OK
+    # the largest sequence count whose workspace fits the scratch, and one more
+    fits = max(s for s in range(1, 4000)
+               if lib.fa_paged_decode_workspace_size(s, 32, 128, 8, 16) <= libfa.NOALLOC_SCRATCH_BYTES)
+    assert 1500 < fits < 2000
+    assert noalloc(lib, S=fits + 1) == ERR_SCRATCH
+    assert noalloc(lib, S=4000, H=64, KVH=8) == ERR_SCRATCH
+
+
 def append(lib, S=4, KVH=8, d=128, bs=16, mbps=8, nb=100, cap=10, dt=1, kn=P, ws=P2, wsb=None,
            fl=P, fc=P):
     wsb = lib.fa_paged_kv_append_workspace_size(S) if wsb is None else wsb
