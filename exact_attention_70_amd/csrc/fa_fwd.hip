@@ -214,7 +214,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
       const int seq = bh / pg.H, h = bh % pg.H;
       const int qs = pg.q_start[seq];
       N = pg.q_start[seq + 1] - qs;
-      Nk = pg.seq_lens[seq];
+      // a length past the table row is clamped to the row's capacity (as the
+      // decode does), so a corrupt length costs at most one row of blocks
+      Nk = min(pg.seq_lens[seq], pg.max_blocks * 16);
       delta = Nk - N;                                 // the chunk is the sequence's last tokens
       // a chunk outside the packed rows (malformed offsets) is skipped; so is a
       // query tile past the chunk

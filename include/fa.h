@@ -300,7 +300,8 @@ int fa_paged_decode_gqa_noalloc(const void* q, const void* k_pool, const void* v
  *   total_q      rows of q, o and lse; (total_q + 128) * H * d * 2 < 2^31
  *   k_pool/v_pool in  [num_blocks, 16, KVH, d], same dtype
  *   block_table  in   [num_seqs, max_blocks_per_seq] int32
- *   seq_lens     in   [num_seqs] int32, n_s <= seq_lens[s] <= max_blocks_per_seq*16
+ *   seq_lens     in   [num_seqs] int32, n_s <= seq_lens[s] <= max_blocks_per_seq*16;
+ *                     a larger value is taken as max_blocks_per_seq*16 (as in decode)
  *   max_q_len    >= every n_s (sizes the launch), <= 1<<20
  *   o            out  [total_q, H, d], same dtype;  lse out [total_q, H] fp32
  *   block_size 16, d 64 or 128, KVH divides H (else FA_ERR_UNSUPPORTED / FA_ERR_SHAPE)

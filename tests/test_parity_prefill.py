@@ -129,3 +129,28 @@ def test_paged_prefill_chunks_outside_the_packed_rows_are_skipped(gpu):
     assert max_abs(out[:5].double().cpu().numpy(), ro) <= TOL["bf16"]
     assert max_abs(lse[:5].double().cpu().numpy(), rl) <= TOL["bf16"]
     assert bool((out[5:].float() == 3.0).all()) and bool((lse[5:] == 3.0).all())
+
+
+def test_paged_prefill_length_past_the_table_is_clamped(gpu):
+    """A sequence length beyond its table row (max_blocks_per_seq * 16 tokens)
+    is taken as the row's capacity, as the decode takes it: the kernel reads
+    at most the row's blocks.  Sequence 1 claims 2^30 tokens with a 7-block
+    row; its chunk is computed over the row's 112 slots (pad slots hold finite
+    draws here), sequence 0 is unaffected."""
+    lens, chunks, H, kvh, d = [40, 100], [8, 10], 4, 2, 128
+    p = workloads.paged_inputs(2, H, d, 16, 1, max(lens), seed=7500, seq_lens=lens, kv_heads=kvh)
+    qq = workloads.prefill_queries(chunks, H, d, seed=7501)
+    mb = p["block_table"].shape[1]
+    assert mb * 16 == 112
+    bad = p["seq_lens"].clone()
+    bad[1] = 1 << 30
+    pd = {k: (v.to(gpu) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+    o, lse = binding.paged_prefill(qq["q"].to(gpu), qq["q_start"].to(gpu), pd["k_pool"],
+                                   pd["v_pool"], pd["block_table"], bad.to(gpu), block_size=16,
+                                   max_q_len=max(chunks), scale=d ** -0.5)
+    torch.cuda.synchronize()
+    clamped = torch.tensor([lens[0], mb * 16], dtype=torch.int32)
+    ro, rl = oracle.paged_prefill(qq["q"], qq["q_start"], p["k_pool"], p["v_pool"],
+                                  p["block_table"], clamped, 16, d ** -0.5, True)
+    assert max_abs(o.double().cpu().numpy(), ro) <= TOL["bf16"]
+    assert max_abs(lse.double().cpu().numpy(), rl) <= TOL["bf16"]
