@@ -205,8 +205,17 @@ def attention_forward_head(q, k, v, scale: float, causal: bool, rows=None, q_off
     return o, lse
 
 
+def _usable_cpus() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
 def _pool_map(fn, items, workers):
-    workers = workers or min(len(items), os.cpu_count() or 1)
+    # default: one thread per usable core, at most 16 (each holds up to a few
+    # hundred MiB of fp64 score chunks)
+    workers = workers or min(len(items), _usable_cpus(), 16)
     if workers <= 1 or len(items) <= 1:
         return [fn(x) for x in items]
     if threadpool_limits is None:

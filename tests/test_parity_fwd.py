@@ -2,9 +2,9 @@
 
 Tolerances (max-abs): O <= 2e-2 for bf16 inputs, <= 1e-5 for fp32 inputs; the
 same bound is used for LSE.  Sizes span several tiles with ragged tails; the
-full-size workloads are checked on every head (the small fp32 and GPT-2-shaped
-ones) or on sampled heads and rows (the benchmarked long-context launch, and
-the longest sequence the library accepts).
+full-size workloads (small fp32, GPT-2-shaped, long-context) are checked on
+every head and row; the longest sequence the library accepts and the other
+launch variants are checked on sampled heads and rows.
 """
 import math
 
@@ -82,17 +82,14 @@ def test_fwd_gpt2_shape_unscaled_inputs_stress(gpu):
     _check(x, o, lse, c.causal, c.scale, TOL["bf16"], heads=[(b, h) for b in (0, 7) for h in range(12)])
 
 
-def test_fwd_long_context_b1h32n8192d128_sampled(gpu):
+def test_fwd_long_context_b1h32n8192d128_whole(gpu):
+    """The benchmarked long-context launch (256-row paired workgroups), every
+    head and every row against the oracle."""
     c = workloads.LONG_CONTEXT
     x = workloads.attention_inputs(c.B, c.H, c.N, c.d, c.dtype, seed=workloads.LONG_CONTEXT.seed)
     o, lse = _gpu_fwd(gpu, x, c.causal, c.scale)
-    # three whole heads
-    _check(x, o, lse, c.causal, c.scale, TOL["bf16"], heads=[(0, 0), (0, 17), (0, 31)])
-    # sampled rows of every head: tile edges, the ragged diagonal and random rows
-    rng = np.random.default_rng(3)
-    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 4095, 4096, 8190, 8191],
-                                     rng.integers(0, c.N, 54)]))
-    _check(x, o, lse, c.causal, c.scale, TOL["bf16"], rows=rows)
+    worst_o, worst_l = _check(x, o, lse, c.causal, c.scale, TOL["bf16"])
+    print(f"long context B1 H32 N8192 d128: O max-abs {worst_o:.3e}, LSE max-abs {worst_l:.3e}")
 
 
 def test_fwd_maximum_length_sampled(gpu):
