@@ -69,6 +69,40 @@ def source_hash(*names):
     return h.hexdigest()[:16]
 
 
+def load_trace_time(kernel_key, src_hash):
+    """Average kernel duration (us) of a part from the committed rocprofv3
+    kernel trace, if that trace was taken from the current sources."""
+    p = os.path.join(ROOT, "profiles", "kernel_times.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(kernel_key)
+    except Exception:
+        return None
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("avg_us")
+
+
+def host_cpu():
+    """The host's CPU model and core counts (logical CPUs, and those this
+    process may run on)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
 def load_traffic(kernel_key, src_hash):
     """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
@@ -153,8 +187,13 @@ def main():
             qr, kr, vr, q_offset=longctx.N, k_offset=0, causal=True, scale=longctx.scale, out=po,
             lse=pl),
             flops=4 * longctx.B * longctx.H * longctx.N * longctx.N * longctx.d)
+        # the merge reads the partial the offset forward has just written: a
+        # 512 MiB fill between the two (outside the timed region) evicts it
+        # from the 256 MiB Infinity Cache, so the rate is the HBM rate
+        flush = torch.empty(128 << 20, dtype=torch.float32, device=dev)
         parts[P_RING_MERGE] = dict(fn=lambda: binding.merge(acc_o, acc_l, po, pl, out=acc_o,
                                                             lse_out=acc_l),
+                                   pre=lambda: flush.fill_(0.5),
                                    bytes=3 * acc_o.numel() * 2 + 3 * acc_l.numel() * 4)
     if want(P_FWD_GPT2):
         x2 = workloads.attention_inputs(gpt2.B, gpt2.H, gpt2.N, gpt2.d, "bf16", seed=gpt2.seed,
@@ -256,6 +295,8 @@ def main():
              if n in parts]
     for _ in range(args.warmup):
         for n in order:
+            if "pre" in parts[n]:
+                parts[n]["pre"]()
             parts[n]["fn"]()
     torch.cuda.synchronize()
     log("warmup done")
@@ -269,6 +310,8 @@ def main():
     for s in range(args.steps):
         for n in order:
             a, b = evs[n][s]
+            if "pre" in parts[n]:
+                parts[n]["pre"]()
             a.record()
             parts[n]["fn"]()
             b.record()
@@ -297,7 +340,10 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and P_FWD in parts:
         import oracle
-        workers = min(os.cpu_count() or 1, 16)
+        hc = host_cpu()
+        # one worker thread per usable core, at most 16 (one GPU's share of the
+        # host on the machines this runs on)
+        workers = max(1, min(hc["usable_cpus"], 16))
         # whole passes of the fp64 oracle over the headline workload (all 32
         # heads, every row) until at least 10 s of host work, at most 8 passes
         passes, dt = 0, 0.0
@@ -308,7 +354,8 @@ def main():
             passes += 1
         fl = passes * causal_flops(longctx.B, longctx.H, longctx.N, longctx.d)
         cpu = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": workers,
-               "kind": "oracle",
+               "kind": "oracle", "host_cpu_model": hc["model"],
+               "host_logical_cpus": hc["logical_cpus"], "host_usable_cpus": hc["usable_cpus"],
                "sample": f"fp64 oracle forward over the whole causal B=1 H=32 N=8192 d=128 "
                          f"workload, {passes} pass(es), {dt:.1f} s wall on {workers} threads"}
         log("cpu baseline", cpu)
@@ -322,6 +369,13 @@ def main():
                 "unit": "TFLOP/s", "frac": head["frac_mfma_peak"], "traffic": traffic,
                 "kernel": "fwd_bf16_kernel<d=128, causal, 8 waves, paired tiles>",
                 "source_hash": src}
+        # the same fraction from the committed rocprofv3 trace's average
+        # duration of this kernel (null once the sources have changed)
+        t_us = load_trace_time(P_FWD, src)
+        if t_us:
+            fl = parts[P_FWD]["flops"]
+            roof["trace_avg_us"] = t_us
+            roof["frac_from_trace"] = round(fl / (t_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)
     dec_res = res.get(P_DEC)
     roof_dec = None
     if dec_res is not None:
