@@ -144,11 +144,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
   // j <= i + delta.  PAGED: one (sequence, head) per bh; N, Nk and delta are
   // that sequence's chunk length, cached length and cached length - chunk.
   // hgroup > 0: workgroups map to tiles by xcd_grouped with that group size.
-  // PAIRED (causal only): the workgroup runs rank r and rank n_qtiles - 1 - r
-  // of one head one after the other, so every workgroup has the same work and
-  // pays the per-tile start-up once per two tiles.  The host pairs only when
-  // the paired grid still fills the chip.  NW waves of 32 query rows each
-  // share every K/V tile the workgroup streams through LDS.
+  // PAIRED (causal only): the workgroup runs rank n_qtiles - 1 - r (short)
+  // and then rank r (long) of one head, so every workgroup has the same work
+  // and pays the per-tile start-up once per two tiles.  The short tile goes
+  // first: its keys are the first keys of the long tile, which then finds them
+  // in L2 instead of restarting the key stream after its own.  The host pairs
+  // only when the paired grid still fills the chip.  NW waves of 32 query
+  // rows each share every K/V tile the workgroup streams through LDS.
   constexpr int BM = 32 * NW;            // query rows per workgroup
   constexpr int KSTEPS = D / 16;         // matrix k-steps over the head dim
   constexpr int DT = D / 32;             // 32-row tiles of O^T
@@ -170,8 +172,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const int t = hgroup > 0 ? xcd_grouped(blockIdx.x, n_ranks, hgroup)
                              : xcd_remap(blockIdx.x, gridDim.x);
     const int r = t % n_ranks, base = t / n_ranks * n_qtiles;
-    tile0 = base + r;
-    tile1 = base + n_qtiles - 1 - r;
+    tile0 = base + n_qtiles - 1 - r;
+    tile1 = base + r;
     npass = tile1 != tile0 ? 2 : 1;
   } else {
     tile0 = hgroup > 0 ? xcd_grouped(blockIdx.x, n_qtiles, hgroup)
@@ -545,16 +547,36 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const float l_tot = l_run + swap_half(l_run);
     // a row that saw no key (l = 0) gets O = 0 and LSE = -inf
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    // O leaves through LDS so that every store instruction writes whole rows:
+    // a lane holds one query's values spread over the head dim, and storing
+    // them directly would write 16-byte pieces of 32 rows per instruction.
+    // Each wave stages its 32 x D tile (swizzled 16-byte chunks) in a quarter
+    // of the K/V rings, once every wave is done reading them, and then stores
+    // it row-major with 16 bytes per lane.
+    constexpr int CPR = D * 2 / 16;       // 16-byte chunks per row
+    constexpr int RPS = 64 / CPR;         // rows per store instruction
+    constexpr int SW = 32 * D * 2;        // staging bytes per wave (half a ring slot)
+    static_assert(2 * SW == TILE && NW <= 8, "two waves' staging per ring slot");
+    barrier_lds();
+    unsigned char* stage = ((wave >> 1) == 0 ? sK0 : (wave >> 1) == 1 ? sK1
+                            : (wave >> 1) == 2 ? sV0 : sV1) + (wave & 1) * SW;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d0 = t * 32 + 8 * g + 4 * half;
         u32x2 w;
         w[0] = E::pack(o[t][4 * g] * inv, o[t][4 * g + 1] * inv);
         w[1] = E::pack(o[t][4 * g + 2] * inv, o[t][4 * g + 3] * inv);
-        if (!PAGED || my_q < N) bstore8(w, rO, ((uint32_t)(qrow0 + my_q) * qstride + d0) * 2);
+        const int c = t * 4 + g;          // chunk of d0 = t * 32 + 8 * g + 4 * half
+        *(u32x2*)(stage + l32 * (D * 2) + ((c ^ (l32 % CPR)) << 4) + 8 * half) = w;
       }
+#pragma unroll
+    for (int k = 0; k < 32 / RPS; ++k) {
+      const int r = k * RPS + lane / CPR, c = lane % CPR;
+      const u32x4 w = *(const u32x4*)(stage + r * (D * 2) + ((c ^ (r % CPR)) << 4));
+      const int row = q0 + wave * 32 + r;
+      if (!PAGED || row < N) bstore16(w, rO, ((uint32_t)(qrow0 + row) * qstride + 8 * c) * 2);
+    }
     if (half == 0 && (!PAGED || my_q < N))
       bstore4f(l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf, rL,
                (uint32_t)(qrow0 + my_q) * lstride * 4);
