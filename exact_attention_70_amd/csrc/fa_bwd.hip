@@ -369,19 +369,16 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     });
   }
 
-  // store: lane holds key my_k, rows d = 32t + 8g + 4*half + (0..3)
-  const float mul = dk_wave ? scale : 1.f;
-  const auto& rout = dk_wave ? rdK : rdV;
-#pragma unroll
-  for (int t = 0; t < DT; ++t)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = t * 32 + 8 * g + 4 * half;
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = as_u32(acc[t][4 * g + e] * mul);
-      bstore16(w, rout, (uint32_t)(my_k * D + d0) * 4);
-    }
+  // store: lane holds key my_k, rows d = 32t + 8g + 4*half + (0..3).  Once
+  // the last transfers have landed and every wave is done with the rings, each
+  // wave stages its 32 x D tile in one ring slot (sQ0..3 for the dV waves,
+  // sO0..3 for the dK waves) and stores it as whole rows.
+  static_assert(32 * D * 4 == TILE, "one wave's fp32 tile per ring slot");
+  barrier_all();
+  unsigned char* stage = dk_wave ? (blk == 0 ? sO0 : blk == 1 ? sO1 : blk == 2 ? sO2 : sO3)
+                                 : (blk == 0 ? sQ0 : blk == 1 ? sQ1 : blk == 2 ? sQ2 : sQ3);
+  store_rows_f32<D, DT>(acc, dk_wave ? scale : 1.f, stage, dk_wave ? rdK : rdV,
+                        kb + blk * 32, lane);
 }
 
 // ---------------------------------------------------------------- dQ
@@ -551,16 +548,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     }
   }
 
-#pragma unroll
-  for (int t = 0; t < DT; ++t)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = t * 32 + 8 * g + 4 * half;
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = as_u32(dq[t][4 * g + e] * scale);
-      bstore16(w, rdQ, (uint32_t)(my_q * D + d0) * 4);
-    }
+  // dQ rows through LDS as whole-row stores (one ring slot per wave)
+  static_assert(32 * D * 4 == TILE, "one wave's fp32 tile per ring slot");
+  barrier_all();
+  unsigned char* stage = wave == 0 ? sK0 : wave == 1 ? sK1 : wave == 2 ? sV0 : sV1;
+  store_rows_f32<D, DT>(dq, scale, stage, rdQ, q0 + wave * 32, lane);
 }
 
 template <class E, int D, bool CAUSAL>

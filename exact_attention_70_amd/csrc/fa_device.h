@@ -293,6 +293,37 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, unsigned char
   }
 }
 
+// Store a wave's 32 x D fp32 accumulator tile (MFMA C layout: lane l holds
+// row l % 32 and, in register 4g + e of 32-column block t, column
+// 32t + 8g + 4(l / 32) + e), scaled by `mul`, as whole rows: the tile is
+// staged in `stage` (32 * D * 4 bytes of LDS that no other wave touches) with
+// swizzled 16-byte chunks, then stored 16 bytes per lane, each instruction
+// covering whole rows.  Row r goes to byte (row0 + r) * D * 4 of `r_out`.
+template <int D, int DT>
+__device__ __forceinline__ void store_rows_f32(const f32x16 (&acc)[DT], float mul,
+                                               unsigned char* stage, __amdgpu_buffer_rsrc_t r_out,
+                                               int row0, int lane) {
+  constexpr int CPR = D / 4;            // 16-byte chunks per row
+  constexpr int RPS = 64 / CPR;         // rows per store instruction
+  const int l32 = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = as_u32(acc[t][4 * g + e] * mul);
+      const int c = t * 8 + 2 * g + half;
+      *(u32x4*)(stage + l32 * (D * 4) + ((c ^ (l32 & 15)) << 4)) = w;
+    }
+#pragma unroll
+  for (int k = 0; k < 32 / RPS; ++k) {
+    const int r = k * RPS + lane / CPR, c = lane % CPR;
+    const u32x4 w = *(const u32x4*)(stage + r * (D * 4) + ((c ^ (r & 15)) << 4));
+    bstore16(w, r_out, (uint32_t)((row0 + r) * D + 4 * c) * 4);
+  }
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
