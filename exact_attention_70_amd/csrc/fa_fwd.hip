@@ -65,7 +65,8 @@ struct PagedKV {
   const int32_t* q_start;
   const int32_t* seq_lens;
   int H, KVH, max_blocks, num_blocks;
-  int total_q;   // rows of the packed Q/O/LSE
+  int total_q;          // rows of the packed Q/O/LSE
+  uint32_t pool_bytes;  // bytes of one pool when at most 2^31 (one resource per pool), else 0
 };
 
 // Physical ids of the four 16-token blocks one 64-key tile spans (-1: past
@@ -108,6 +109,37 @@ __device__ __forceinline__ void dma_rows_paged(const T* pool, TileIds ids, int n
   }
 }
 
+// dma_rows_paged through one buffer resource over the whole pool (pools of
+// at most 2 GiB): every lane's offset is its row's place in its physical
+// block, or 2^31, past the pool (which reads zeros), for a slot past the
+// sequence's last token or a block id outside the pool.  No per-block
+// resources are built, so the transfers cost a few vector operations per
+// instruction instead of scalar address arithmetic per block.
+template <int D, int ROWS, int NWAVES>
+__device__ __forceinline__ void dma_rows_paged_flat(__amdgpu_buffer_rsrc_t pool, TileIds ids,
+                                                    int n_tok, int num_blocks, int kvh, int KVH,
+                                                    unsigned char* lds, int row0, int wave,
+                                                    int lane) {
+  constexpr int DCH = D / 8;
+  constexpr int RPI = 64 / DCH;
+  constexpr int NI = ROWS / RPI;
+  static_assert(16 % RPI == 0 && NI % NWAVES == 0, "instruction rows must stay inside a block");
+  static_assert(ROWS == 64, "a tile spans four blocks");
+  const uint32_t blk_bytes = (uint32_t)16 * KVH * D * 2;
+#pragma unroll
+  for (int ii = 0; ii < NI / NWAVES; ++ii) {
+    const int ins = ii * NWAVES + wave;
+    const int bi = (ins * RPI) >> 4;                // block of this instruction within the tile
+    const int phys = bi == 0 ? ids.b[0] : bi == 1 ? ids.b[1] : bi == 2 ? ids.b[2] : ids.b[3];
+    const int rr = ins * RPI + lane / DCH;          // LDS row written by this lane
+    const int tok = row0 + rr;
+    const int c = (lane % DCH) ^ tile_swz<D>(rr);
+    const bool ok = (unsigned)phys < (unsigned)num_blocks && tok < n_tok;
+    const uint32_t off = (uint32_t)phys * blk_bytes + (uint32_t)(((tok & 15) * KVH + kvh) * D + c * 8) * 2;
+    dma16(pool, lds + ins * 1024, ok ? off : 0x80000000u);
+  }
+}
+
 // True when every probability pair g (key block g / 4), issued in slot
 // g * pslots / npair, precedes the first P V op that reads its block (slot
 // nq + (g / 4) * dt).
@@ -133,7 +165,7 @@ constexpr bool check_before_block(int kb, int npair, int pslots, int nq, int dt)
 }
 
 template <class E, int D, bool CAUSAL, int BN, int OCC, bool PAGED = false, bool PAIRED = false,
-          int NW = 4>
+          int NW = 4, bool FLAT = false>
 __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const typename E::elem* __restrict__ Q, const typename E::elem* __restrict__ K,
     const typename E::elem* __restrict__ V, typename E::elem* __restrict__ O,
@@ -243,8 +275,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const size_t khead_off = (size_t)bh * (size_t)Nk * D;
     const uint32_t khead_bytes = (uint32_t)Nk * D * 2;
     const auto rQ = make_rsrc(Q + head_off, head_bytes);
-    const auto rK = make_rsrc(K + (PAGED ? 0 : khead_off), PAGED ? 0u : khead_bytes);
-    const auto rV = make_rsrc(V + (PAGED ? 0 : khead_off), PAGED ? 0u : khead_bytes);
+    // paged: one resource over each whole pool when FLAT, else none (each
+    // transfer builds one over its block)
+    const uint32_t kv_bytes = PAGED ? (FLAT ? pg.pool_bytes : 0u) : khead_bytes;
+    const auto rK = make_rsrc(K + (PAGED ? 0 : khead_off), kv_bytes);
+    const auto rV = make_rsrc(V + (PAGED ? 0 : khead_off), kv_bytes);
     const auto rO = make_rsrc(O + head_off, head_bytes);
     const auto rL = make_rsrc(LSE + lse_off, lse_bytes);
     // Paged: a tile's block ids are read from the table one iteration before
@@ -273,14 +308,20 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
       for (int q = 0; q < 4; ++q) ids_k.b[q] = __builtin_amdgcn_readfirstlane(ids_f.b[q]);
     };
     auto dma_k = [&](unsigned char* dst, int row0) __attribute__((always_inline)) {
-      if constexpr (PAGED)
+      if constexpr (PAGED && FLAT)
+        dma_rows_paged_flat<D, BN, NW>(rK, row0 == 0 ? ids_v : ids_k, Nk, pg.num_blocks, kvh,
+                                       pg.KVH, dst, row0, wave, lane);
+      else if constexpr (PAGED)
         dma_rows_paged<D, BN, NW>(K, row0 == 0 ? ids_v : ids_k, Nk, pg.num_blocks, kvh,
                                              pg.KVH, dst, row0, wave, lane);
       else
         dma_rows<D, BN, NW>(rK, dst, row0, wave, lane);
     };
     auto dma_v = [&](unsigned char* dst, int row0) __attribute__((always_inline)) {
-      if constexpr (PAGED)
+      if constexpr (PAGED && FLAT)
+        dma_rows_paged_flat<D, BN, NW>(rV, ids_v, Nk, pg.num_blocks, kvh, pg.KVH, dst, row0,
+                                       wave, lane);
+      else if constexpr (PAGED)
         dma_rows_paged<D, BN, NW>(V, ids_v, Nk, pg.num_blocks, kvh, pg.KVH, dst, row0,
                                              wave, lane);
       else
@@ -813,13 +854,23 @@ hipError_t launch_paged(const FwdArgs& a) {
   constexpr int NW = 4;                                // 128 query rows per workgroup
   const int n_qtiles = (a.N + 32 * NW - 1) / (32 * NW);  // a.N: the longest chunk
   const int grid = a.B * a.H * n_qtiles;                // a.B: the number of sequences
+  // pools of at most 2 GiB are read through one resource each (offsets of
+  // 2^31 then read zeros)
+  const unsigned long long pool_bytes = (unsigned long long)a.num_blocks * 16 * a.KVH * D * 2;
+  const bool flat = pool_bytes <= 0x80000000ull;
   const PagedKV pg{a.table,      a.q_start,    a.seq_lens,  a.H,
-                   a.KVH,        a.max_blocks, a.num_blocks, a.total_q};
+                   a.KVH,        a.max_blocks, a.num_blocks, a.total_q,
+                   flat ? (uint32_t)pool_bytes : 0u};
   const int hg =
       CAUSAL ? xcd_group((long long)a.B * a.H, (long long)a.max_blocks * 16 * D * 4) : 0;
-  hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, kBNDefault, 2, true, false, NW>), dim3(grid),
-                     dim3(64 * NW), 0, a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V,
-                     (T*)a.O, a.LSE, 0, 0, 0, a.scale * kLog2e, n_qtiles, pg, hg);
+  if (flat)
+    hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, kBNDefault, 2, true, false, NW, true>),
+                       dim3(grid), dim3(64 * NW), 0, a.stream, (const T*)a.Q, (const T*)a.K,
+                       (const T*)a.V, (T*)a.O, a.LSE, 0, 0, 0, a.scale * kLog2e, n_qtiles, pg, hg);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, kBNDefault, 2, true, false, NW>), dim3(grid),
+                       dim3(64 * NW), 0, a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V,
+                       (T*)a.O, a.LSE, 0, 0, 0, a.scale * kLog2e, n_qtiles, pg, hg);
   return hipGetLastError();
 }
 

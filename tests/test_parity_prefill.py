@@ -154,3 +154,39 @@ def test_paged_prefill_length_past_the_table_is_clamped(gpu):
                                   p["block_table"], clamped, 16, d ** -0.5, True)
     assert max_abs(o.double().cpu().numpy(), ro) <= TOL["bf16"]
     assert max_abs(lse.double().cpu().numpy(), rl) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_paged_prefill_pool_above_2gib(gpu, d):
+    """Pools of at most 2 GiB are read through one buffer resource each;
+    larger ones through one resource per physical block.  This case takes
+    the second path: the blocks the sequences use sit at the top of a pool
+    of more than 2 GiB (32 cached heads), the rest of which is never
+    written.  Pad slots hold NaN."""
+    lens, chunks, H, kvh = [17, 100, 300], [17, 10, 129], 32, 32
+    p = workloads.paged_inputs(len(lens), H, d, 16, 1, max(lens), seed=7600 + d, seq_lens=lens,
+                               kv_heads=kvh, pad_value=float("nan"))
+    qq = workloads.prefill_queries(chunks, H, d, seed=7601 + d)
+    n_small = p["k_pool"].shape[0]
+    blk_bytes = 16 * kvh * d * 2
+    n_big = (2 ** 31) // blk_bytes + 64                     # just past 2 GiB per pool
+    top = n_big - 1
+    big_k = torch.empty((n_big, 16, kvh, d), dtype=torch.bfloat16, device=gpu)
+    big_v = torch.empty_like(big_k)
+    ids = torch.arange(n_small)
+    big_k[(top - ids).to(gpu)] = p["k_pool"].to(gpu)
+    big_v[(top - ids).to(gpu)] = p["v_pool"].to(gpu)
+    table = p["block_table"].clone()
+    table = torch.where(table >= 0, top - table, table)   # block i lives at top - i
+    o, lse = binding.paged_prefill(qq["q"].to(gpu), qq["q_start"].to(gpu), big_k, big_v,
+                                   table.to(gpu), p["seq_lens"].to(gpu), block_size=16,
+                                   max_q_len=max(chunks), scale=d ** -0.5)
+    torch.cuda.synchronize()
+    ro, rl = oracle.paged_prefill(qq["q"], qq["q_start"], p["k_pool"], p["v_pool"],
+                                  p["block_table"], p["seq_lens"], 16, d ** -0.5, True)
+    go, gl = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))
+    assert max_abs(go, ro) <= TOL["bf16"]
+    assert max_abs(gl, rl) <= TOL["bf16"]
+    del big_k, big_v
+    torch.cuda.empty_cache()
