@@ -144,9 +144,15 @@ struct F16 {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Exchange with the lane 32 positions away (the other half of the wave).
+// Exchange with the lane 32 positions away (the other half of the wave).  The
+// lane index is formed at each call and hidden from the optimizer, so that
+// its permute address is not computed once and held (or spilled) across a
+// whole kernel for the few places that need it.
 __device__ __forceinline__ float swap_half(float x) {
-  return __shfl_xor(x, 32, 64);
+  int l = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  asm volatile("" : "+v"(l));
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_ds_bpermute((l ^ 32) << 2, __builtin_bit_cast(int, x)));
 }
 
 // Workgroup barriers for LDS producer/consumer phases.  barrier_lds() waits

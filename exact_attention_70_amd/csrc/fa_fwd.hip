@@ -602,6 +602,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     barrier_lds();
     unsigned char* stage = ((wave >> 1) == 0 ? sK0 : (wave >> 1) == 1 ? sK1
                             : (wave >> 1) == 2 ? sV0 : sV1) + (wave & 1) * SW;
+    // the lane index again, hidden from the optimizer: values derived from it
+    // here are formed here rather than held across the loop
+    int elane = threadIdx.x & 63;
+    asm volatile("" : "+v"(elane));
+    const int el32 = elane & 31, ehalf = elane >> 5;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -610,11 +615,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
         w[0] = E::pack(o[t][4 * g] * inv, o[t][4 * g + 1] * inv);
         w[1] = E::pack(o[t][4 * g + 2] * inv, o[t][4 * g + 3] * inv);
         const int c = t * 4 + g;          // chunk of d0 = t * 32 + 8 * g + 4 * half
-        *(u32x2*)(stage + l32 * (D * 2) + ((c ^ (l32 % CPR)) << 4) + 8 * half) = w;
+        *(u32x2*)(stage + el32 * (D * 2) + ((c ^ (el32 % CPR)) << 4) + 8 * ehalf) = w;
       }
 #pragma unroll
     for (int k = 0; k < 32 / RPS; ++k) {
-      const int r = k * RPS + lane / CPR, c = lane % CPR;
+      const int r = k * RPS + elane / CPR, c = elane % CPR;
       const u32x4 w = *(const u32x4*)(stage + r * (D * 2) + ((c ^ (r % CPR)) << 4));
       const int row = q0 + wave * 32 + r;
       if (!PAGED || row < N) bstore16(w, rO, ((uint32_t)(qrow0 + row) * qstride + 8 * c) * 2);
