@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(const typename E::ele
   const int c = threadIdx.x % LPR;
   const bool ok = row < rows;
   const long long r = ok ? row : 0;
-  const u32x4 a = *(const u32x4*)(O + r * D + c * 8);
+  const u32x4 a = __builtin_nontemporal_load((const u32x4*)(O + r * D + c * 8));   // read once
   const u32x4 b = *(const u32x4*)(dO + r * D + c * 8);
   float acc = 0.f;
 #pragma unroll

@@ -49,9 +49,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
-// 16-byte load at a per-lane offset plus a wave-uniform (scalar) offset
-__device__ __forceinline__ u32x4 bload16s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+// Cache-policy operand of a buffer access: bit 1 is the non-temporal hint
+// (NT) on gfx950, for data that is read or written once.
+constexpr int kCpolNT = 2;
+// 16-byte streaming load at a per-lane offset plus a wave-uniform (scalar)
+// offset, with the non-temporal hint: for bytes read exactly once (the cached
+// keys and values of a decode step), so they do not displace reused lines.
+__device__ __forceinline__ u32x4 bload16s_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kCpolNT);
 }
 __device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
@@ -61,6 +66,9 @@ __device__ __forceinline__ float bload4f(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 __device__ __forceinline__ void bstore16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void bstore16_nt(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kCpolNT);
 }
 __device__ __forceinline__ void bstore8(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
@@ -305,6 +313,7 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, unsigned char
 // staged in `stage` (32 * D * 4 bytes of LDS that no other wave touches) with
 // swizzled 16-byte chunks, then stored 16 bytes per lane, each instruction
 // covering whole rows.  Row r goes to byte (row0 + r) * D * 4 of `r_out`.
+// The stores carry the non-temporal hint: the gradients are written once.
 template <int D, int DT>
 __device__ __forceinline__ void store_rows_f32(const f32x16 (&acc)[DT], float mul,
                                                unsigned char* stage, __amdgpu_buffer_rsrc_t r_out,
@@ -326,7 +335,7 @@ __device__ __forceinline__ void store_rows_f32(const f32x16 (&acc)[DT], float mu
   for (int k = 0; k < 32 / RPS; ++k) {
     const int r = k * RPS + lane / CPR, c = lane % CPR;
     const u32x4 w = *(const u32x4*)(stage + r * (D * 4) + ((c ^ (r & 15)) << 4));
-    bstore16(w, r_out, (uint32_t)((row0 + r) * D + 4 * c) * 4);
+    bstore16_nt(w, r_out, (uint32_t)((row0 + r) * D + 4 * c) * 4);
   }
 }
 
