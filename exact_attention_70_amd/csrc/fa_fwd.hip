@@ -573,17 +573,42 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     };
     // The rest (at most one unmasked tile plus the tiles that straddle the
     // diagonal or the ragged end) runs with the mask on.  j is odd here, so
-    // pairs keep the ring slots and score arrays static.
-    for (; j + 1 < n_kv; j += 2) {
+    // pairs keep the ring slots and score arrays static.  Causal: no row of
+    // this wave sees a key past tile n_wave - 1 (its last row's diagonal), so
+    // the wave computes up to that tile only; for the workgroup's remaining
+    // tiles it just issues its share of the transfers and joins the barriers.
+    // n_wave >= n_plain, as the unmasked tiles are seen by every row.
+    int n_wave = n_kv;
+    if constexpr (CAUSAL) {
+      const int last_key = q0 + wave * 32 + 31 + delta;   // last key a row of the wave sees
+      n_wave = min(n_kv, last_key >= 0 ? last_key / BN + 1 : 1);
+    }
+    for (; j + 1 < n_wave; j += 2) {
       iter(j, sK1, sK0, sV0, sV1, sa, sb, Masked{});
       iter(j + 1, sK0, sK1, sV1, sV0, sb, sa, Masked{});
     }
-    if (j < n_kv) {
+    if (j < n_wave) {
       iter(j, sK1, sK0, sV0, sV1, sa, sb, Masked{});
       last_pv(sb, sV1);          // last tile j is odd
     } else {
       last_pv(sa, sV0);          // last tile j-1 is even
     }
+    // transfers and barriers of tiles [n_wave, n_kv): K_{i+1} into slot
+    // (i+1)&1 and V_i into slot i&1, as iteration i issues them
+    auto idle_iter = [&](const int i, unsigned char* knxt, unsigned char* vcur) {
+      if constexpr (PAGED) ids_f = tile_ids(i + 2);
+      if (i + 1 < n_kv) dma_k(knxt, (i + 1) * BN);
+      dma_v(vcur, i * BN);
+      __syncthreads();
+      if constexpr (PAGED) rotate_ids();
+    };
+    int i = n_wave;
+    if (i < n_kv && (i & 1)) idle_iter(i++, sK0, sV1);
+    for (; i + 1 < n_kv; i += 2) {
+      idle_iter(i, sK1, sV0);
+      idle_iter(i + 1, sK0, sV1);
+    }
+    if (i < n_kv) idle_iter(i, sK1, sV0);
 
     // ---- epilogue: O = O^T / l, LSE = ln(sum exp) = (m + log2 l) ln 2
     const float l_tot = l_run + swap_half(l_run);
