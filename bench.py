@@ -11,7 +11,8 @@ benchmark shapes:
     and one paged KV append of a token per sequence
   * chunked prefill over a paged cache: 8 sequences x 1024 new tokens
   * one ring-attention step at the long-context shape: fa_fwd_offset of the
-    8192 queries against the previous 8192-token block, then fa_merge
+    8192 queries against the previous 8192-token block, then fa_merge; and the
+    same step as one fa_fwd_offset_accumulate call
 Inputs are resident in HBM before timing starts.  Each call is bracketed by
 HIP events on the stream it runs on; `value` is the headline forward's
 algorithmic TFLOP/s (causal pairs only) over its average kernel time.
@@ -51,6 +52,7 @@ P_PREFILL = "prefill_gqa_s8x1024h32kv8d128"
 P_RING = "ring_h32n8192d128"
 P_RING_FWD = "ring_fwd_h32n8192d128"
 P_RING_MERGE = "ring_merge_h32n8192d128"
+P_RING_FUSED = "ring_fused_h32n8192d128"
 
 
 def log(*a):
@@ -130,7 +132,7 @@ def main():
                          "decode_s64h32d128, decode_gqa_s64h32kv8d128 (8 cached heads), "
                          "append_s64kv8d128 (paged KV append), prefill_gqa_s8x1024h32kv8d128 "
                          "(chunked prefill over a paged cache), ring_h32n8192d128 (offset "
-                         "forward + merge of one ring step), copy_calib (a 1 GiB device copy "
+                         "forward + merge of one ring step, and the fused step), copy_calib (a 1 GiB device copy "
                          "used to scale the HBM-traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -195,6 +197,14 @@ def main():
                                                             lse_out=acc_l),
                                    pre=lambda: flush.fill_(0.5),
                                    bytes=3 * acc_o.numel() * 2 + 3 * acc_l.numel() * 4)
+        # the same step in one call: the block's forward merged into the
+        # running result in its epilogue (the running result read from HBM,
+        # as after the fill)
+        fo, fl = acc_o.clone(), acc_l.clone()
+        parts[P_RING_FUSED] = dict(fn=lambda: binding.fwd_offset_accumulate(
+            qr, kr, vr, fo, fl, q_offset=longctx.N, k_offset=0, causal=True, scale=longctx.scale),
+            pre=lambda: flush.fill_(0.5),
+            flops=4 * longctx.B * longctx.H * longctx.N * longctx.N * longctx.d)
     if want(P_FWD_GPT2):
         x2 = workloads.attention_inputs(gpt2.B, gpt2.H, gpt2.N, gpt2.d, "bf16", seed=gpt2.seed,
                                         in_scale=gpt2.in_scale)
@@ -291,7 +301,7 @@ def main():
     log(f"inputs ready: {list(parts)}")
 
     order = [n for n in (P_FWD, P_FWD16, P_FWD_GPT2, P_FWD4, P_BWD4, P_DEC, P_DEC_GQA, P_APPEND,
-                         P_PREFILL, P_RING_FWD, P_RING_MERGE, P_COPY)
+                         P_PREFILL, P_RING_FWD, P_RING_MERGE, P_RING_FUSED, P_COPY)
              if n in parts]
     for _ in range(args.warmup):
         for n in order:
@@ -396,7 +406,8 @@ def main():
                                "(one step also runs fwd B=8 H=12 N=1024 d=64, fwd+bwd "
                                "B=4 H=16 N=2048 d=128, paged decode 64x32x128 with 32 and "
                                "with 8 cached heads, a paged KV append, and one "
-                               "ring-attention step: offset fwd + merge at 32x8192x128)",
+                               "ring-attention step: offset fwd + merge, and fused, at "
+                               "32x8192x128)",
                    "global_batch": 1, "seq_len": 8192, "parallelism": "single-gpu"},
         "roofline": roof,
         "roofline_decode": roof_dec,

@@ -22,6 +22,7 @@ FA_DT_BF16 = 1
 FA_DT_F16 = 2
 
 EXPORTED = ("fa_status_string", "fa_version", "fa_fwd", "fa_fwd_offset", "fa_merge",
+            "fa_fwd_offset_accumulate",
             "fa_bwd_workspace_size", "fa_bwd", "fa_paged_decode_workspace_size", "fa_paged_decode",
             "fa_paged_decode_gqa", "fa_paged_decode_gqa_noalloc",
             "fa_paged_kv_append_workspace_size", "fa_paged_kv_append", "fa_paged_prefill")
@@ -62,6 +63,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     ll = ctypes.c_longlong
     lib.fa_fwd_offset.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, ll, ll, f, i, i, vp]
     lib.fa_fwd_offset.restype = i
+    lib.fa_fwd_offset_accumulate.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, ll, ll, f, i, i, vp]
+    lib.fa_fwd_offset_accumulate.restype = i
     lib.fa_merge.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.fa_merge.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
@@ -189,6 +192,27 @@ def fwd_offset(q, k, v, *, q_offset: int, k_offset: int, causal: bool, scale: fl
                                       _dtype_code(q), _stream(q.device))
     _check(st, "fa_fwd_offset")
     return o, l
+
+
+def fwd_offset_accumulate(q, k, v, o, lse, *, q_offset: int, k_offset: int, causal: bool,
+                          scale: float | None = None):
+    """Merge the attention of q [B, H, Nq, d] against the key/value block k, v
+    [B, H, Nk, d] (rows at global positions q_offset + i, k_offset + j) into the
+    running result o [B, H, Nq, d], lse [B, H, Nq] (fp32), in place."""
+    _need_cuda(q, k, v, o, lse)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if (k.shape[:2] != q.shape[:2] or k.shape[3] != d or v.shape != k.shape
+            or k.dtype != q.dtype or v.dtype != q.dtype):
+        raise ValueError("q [B,H,Nq,d], k and v [B,H,Nk,d] must share B, H, d and dtype")
+    _want(o, q.shape, q.dtype, q.device, "o")
+    _want(lse, (B, H, Nq), torch.float32, q.device, "lse")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = load_library().fa_fwd_offset_accumulate(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, int(q_offset),
+        int(k_offset), scale, int(bool(causal)), _dtype_code(q), _stream(q.device))
+    _check(st, "fa_fwd_offset_accumulate")
+    return o, lse
 
 
 def merge(o_a, lse_a, o_b, lse_b, *, out=None, lse_out=None):

@@ -65,9 +65,10 @@ const char* fa_status_string(int status) {
 
 int fa_version(void) { return 100; }
 
-int fa_fwd_offset(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
-                  int Nq, int Nk, int d, long long q_offset, long long k_offset, float scale,
-                  int causal, int dtype, void* stream) {
+namespace {
+int fwd_offset_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                    int Nq, int Nk, int d, long long q_offset, long long k_offset, float scale,
+                    int causal, int dtype, void* stream, bool accumulate) {
   if (dtype != FA_DT_F32 && dtype != FA_DT_BF16 && dtype != FA_DT_F16) return FA_ERR_DTYPE;
   if (B < 0 || H < 1 || Nq < 1 || Nq > kMaxN || Nk < 1 || Nk > kMaxN || d < 1) return FA_ERR_SHAPE;
   if (q_offset < -kMaxOffset || q_offset > kMaxOffset || k_offset < -kMaxOffset ||
@@ -86,7 +87,24 @@ int fa_fwd_offset(const void* Q, const void* K, const void* V, void* O, float* L
                 reinterpret_cast<hipStream_t>(stream)};
   a.Nk = Nk;
   a.delta = q_offset - k_offset;
+  a.accumulate = accumulate;
   return hip_status(fa::launch_fwd(a));
+}
+}  // namespace
+
+int fa_fwd_offset(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                  int Nq, int Nk, int d, long long q_offset, long long k_offset, float scale,
+                  int causal, int dtype, void* stream) {
+  return fwd_offset_impl(Q, K, V, O, LSE, B, H, Nq, Nk, d, q_offset, k_offset, scale, causal,
+                         dtype, stream, false);
+}
+
+int fa_fwd_offset_accumulate(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                             int B, int H, int Nq, int Nk, int d, long long q_offset,
+                             long long k_offset, float scale, int causal, int dtype,
+                             void* stream) {
+  return fwd_offset_impl(Q, K, V, O, LSE, B, H, Nq, Nk, d, q_offset, k_offset, scale, causal,
+                         dtype, stream, true);
 }
 
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N,

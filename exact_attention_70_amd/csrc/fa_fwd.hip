@@ -170,12 +170,15 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const typename E::elem* __restrict__ Q, const typename E::elem* __restrict__ K,
     const typename E::elem* __restrict__ V, typename E::elem* __restrict__ O,
     float* __restrict__ LSE, int N, int Nk, int delta, float scale_log2, int n_qtiles, PagedKV pg,
-    int hgroup) {
+    int hgroup, int acc) {
   // scale_log2 = scale * log2(e): scores are handled in base 2.  N query rows
   // and Nk key rows per head; with CAUSAL, key j is visible to row i iff
   // j <= i + delta.  PAGED: one (sequence, head) per bh; N, Nk and delta are
   // that sequence's chunk length, cached length and cached length - chunk.
   // hgroup > 0: workgroups map to tiles by xcd_grouped with that group size.
+  // acc != 0 (contiguous layout only): O and LSE hold on entry the running
+  // result over other keys, and the epilogue merges this block's result into
+  // them by the rescale rule instead of overwriting them.
   // PAIRED (causal only): the workgroup runs rank r (long) and then rank
   // n_qtiles - 1 - r (short) of one head, so every workgroup has the same work
   // and pays the per-tile start-up once per two tiles.  The long tiles of a
@@ -334,8 +337,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const int n_full = min(CAUSAL ? max(0, q0 + delta + 1) / BN : n_kv, Nk / BN);
     if (n_kv == 0) {
       // no row of this tile sees any key: empty softmax, O = 0 and LSE = -inf
+      // (merged into a running result, an empty block changes nothing)
       const int row = q0 + tid / 2;
-      if (tid < 2 * BM && (!PAGED || row < N)) {
+      if (!acc && tid < 2 * BM && (!PAGED || row < N)) {
         const uint32_t prow = (uint32_t)(qrow0 + row);
 #pragma unroll
         for (int c = 0; c < D / 16; ++c)
@@ -617,7 +621,26 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     // ---- epilogue: O = O^T / l, LSE = ln(sum exp) = (m + log2 l) ln 2
     const float l_tot = l_run + swap_half(l_run);
     // a row that saw no key (l = 0) gets O = 0 and LSE = -inf
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float lse_out = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+    // acc: weights of the running result (a) and of this block (b) in base 2,
+    // w = exp2(LSE2 - max); O = c_a O_a + c_b O_b with c = w / (w_a + w_b),
+    // LSE = max + log2(w_a + w_b); a side at -inf weighs nothing
+    float ca = 0.f;
+    if (acc) {
+      const float la = bload4f(rL, (uint32_t)(qrow0 + my_q) * lstride * 4);
+      const float la2 = la * kLog2e;
+      const float lb2 = l_tot > 0.f ? m_run + fast_log2(l_tot) : kNegInf;
+      const float M = fmaxf(la2, lb2);
+      const bool empty = M == kNegInf;
+      const float wa = empty ? 0.f : fast_exp2(la2 - M);
+      const float wb = empty ? 0.f : fast_exp2(lb2 - M);
+      const float itot = empty ? 0.f : 1.f / (wa + wb);
+      ca = wa * itot;
+      inv *= wb * itot;
+      // a block of weight 0 leaves the running LSE exactly as it was
+      lse_out = empty ? kNegInf : wb == 0.f ? la : (M + fast_log2(wa + wb)) * kLn2;
+    }
     // O leaves through LDS so that every store instruction writes whole rows:
     // a lane holds one query's values spread over the head dim, and storing
     // them directly would write 16-byte pieces of 32 rows per instruction.
@@ -646,16 +669,41 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
         const int c = t * 4 + g;          // chunk of d0 = t * 32 + 8 * g + 4 * half
         *(u32x2*)(stage + el32 * (D * 2) + ((c ^ (el32 % CPR)) << 4) + 8 * ehalf) = w;
       }
+    if (!acc) {
 #pragma unroll
-    for (int k = 0; k < 32 / RPS; ++k) {
-      const int r = k * RPS + elane / CPR, c = elane % CPR;
-      const u32x4 w = *(const u32x4*)(stage + r * (D * 2) + ((c ^ (r % CPR)) << 4));
-      const int row = q0 + wave * 32 + r;
-      if (!PAGED || row < N) bstore16(w, rO, ((uint32_t)(qrow0 + row) * qstride + 8 * c) * 2);
+      for (int k = 0; k < 32 / RPS; ++k) {
+        const int r = k * RPS + elane / CPR, c = elane % CPR;
+        const u32x4 w = *(const u32x4*)(stage + r * (D * 2) + ((c ^ (r % CPR)) << 4));
+        const int row = q0 + wave * 32 + r;
+        if (!PAGED || row < N) bstore16(w, rO, ((uint32_t)(qrow0 + row) * qstride + 8 * c) * 2);
+      }
+    } else {
+      // the running rows first (all loads in flight together), then
+      // c_a O_a + (c_b O_b as staged), with c_a of row r from lane r
+      u32x4 old[32 / RPS];
+#pragma unroll
+      for (int k = 0; k < 32 / RPS; ++k) {
+        const int r = k * RPS + elane / CPR, c = elane % CPR;
+        old[k] = bload16(rO, ((uint32_t)(qrow0 + q0 + wave * 32 + r) * qstride + 8 * c) * 2);
+      }
+#pragma unroll
+      for (int k = 0; k < 32 / RPS; ++k) {
+        const int r = k * RPS + elane / CPR, c = elane % CPR;
+        const u32x4 w = *(const u32x4*)(stage + r * (D * 2) + ((c ^ (r % CPR)) << 4));
+        const float car = __shfl(ca, r, 64);
+        // a running row of weight 0 (LSE -inf on entry) is not read into the
+        // result, whatever its O holds
+        if (car == 0.f) old[k] = u32x4{0u, 0u, 0u, 0u};
+        u32x4 m;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          m[e] = E::pack(fmaf(car, E::lo(old[k][e]), E::lo(w[e])),
+                         fmaf(car, E::hi(old[k][e]), E::hi(w[e])));
+        bstore16(m, rO, ((uint32_t)(qrow0 + q0 + wave * 32 + r) * qstride + 8 * c) * 2);
+      }
     }
     if (half == 0 && (!PAGED || my_q < N))
-      bstore4f(l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf, rL,
-               (uint32_t)(qrow0 + my_q) * lstride * 4);
+      bstore4f(lse_out, rL, (uint32_t)(qrow0 + my_q) * lstride * 4);
   }
 }
 
@@ -672,7 +720,7 @@ template <int D>
 __global__ __launch_bounds__(64) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int N, int Nk, int delta, float scale_log2,
-    int causal, int n_qtiles) {
+    int causal, int n_qtiles, int acc) {
   constexpr int KSTEPS = D / 2;
   constexpr int DT = D / 32;
   constexpr int PAD = 1;                         // one-float row pad: conflict-free column reads
@@ -762,19 +810,41 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(
   }
 
   const float l_tot = l_run + swap_half(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // no visible key: O = 0
+  float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // no visible key: O = 0
+  float lse_out = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+  float ca = 0.f;   // acc: the running result's weight (as in the 16-bit kernel)
+  if (acc) {
+    const float la = bload4f(rL, (uint32_t)my_q * 4);
+    const float la2 = la * kLog2e;
+    const float lb2 = l_tot > 0.f ? m_run + fast_log2(l_tot) : kNegInf;
+    const float M = fmaxf(la2, lb2);
+    const bool empty = M == kNegInf;
+    const float wa = empty ? 0.f : fast_exp2(la2 - M);
+    const float wb = empty ? 0.f : fast_exp2(lb2 - M);
+    const float itot = empty ? 0.f : 1.f / (wa + wb);
+    ca = wa * itot;
+    inv *= wb * itot;
+    lse_out = empty ? kNegInf : wb == 0.f ? la : (M + fast_log2(wa + wb)) * kLn2;
+  }
 #pragma unroll
   for (int t = 0; t < DT; ++t)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d0 = t * 32 + 8 * g + 4 * half;
+      const uint32_t off = (uint32_t)(my_q * D + d0) * 4;
       u32x4 w;
+      if (acc) {
+        u32x4 old = bload16(rO, off);
+        if (ca == 0.f) old = u32x4{0u, 0u, 0u, 0u};   // weight 0: O not read in
 #pragma unroll
-      for (int x = 0; x < 4; ++x) w[x] = as_u32(o[t][4 * g + x] * inv);
-      bstore16(w, rO, (uint32_t)(my_q * D + d0) * 4);
+        for (int x = 0; x < 4; ++x) w[x] = as_u32(fmaf(ca, as_f32(old[x]), o[t][4 * g + x] * inv));
+      } else {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) w[x] = as_u32(o[t][4 * g + x] * inv);
+      }
+      bstore16(w, rO, off);
     }
-  if (half == 0)
-    bstore4f(l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf, rL, (uint32_t)my_q * 4);
+  if (half == 0) bstore4f(lse_out, rL, (uint32_t)my_q * 4);
 }
 
 // ---------------------------------------------------------------------------
@@ -821,8 +891,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const T* Oa, const float* La
   const float inv = empty ? 0.f : 1.f / tot;
   const float ca = wa * inv, cb = wb * inv;
   const long long off = row * D + (long long)c * EPT;
-  const u32x4 a = __builtin_nontemporal_load((const u32x4*)(Oa + off));
-  const u32x4 b = __builtin_nontemporal_load((const u32x4*)(Ob + off));
+  u32x4 a = __builtin_nontemporal_load((const u32x4*)(Oa + off));
+  u32x4 b = __builtin_nontemporal_load((const u32x4*)(Ob + off));
+  // a side of weight 0 is not read into the result, whatever its O holds
+  if (ca == 0.f) a = u32x4{0u, 0u, 0u, 0u};
+  if (cb == 0.f) b = u32x4{0u, 0u, 0u, 0u};
   u32x4 r;
   if constexpr (sizeof(T) == 2) {
 #pragma unroll
@@ -869,7 +942,7 @@ hipError_t launch_bf16_as(const FwdArgs& a, int Nk, int delta) {
   hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, kBNDefault, 8 / NW, false, PAIRED, NW>),
                      dim3((int)units), dim3(64 * NW), 0, a.stream, (const T*)a.Q, (const T*)a.K,
                      (const T*)a.V, (T*)a.O, a.LSE, a.N, Nk, delta, a.scale * kLog2e, n_qtiles,
-                     PagedKV{}, hg);
+                     PagedKV{}, hg, a.accumulate ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -903,11 +976,11 @@ hipError_t launch_paged(const FwdArgs& a) {
   if (flat)
     hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, kBNDefault, 2, true, false, NW, true>),
                        dim3(grid), dim3(64 * NW), 0, a.stream, (const T*)a.Q, (const T*)a.K,
-                       (const T*)a.V, (T*)a.O, a.LSE, 0, 0, 0, a.scale * kLog2e, n_qtiles, pg, hg);
+                       (const T*)a.V, (T*)a.O, a.LSE, 0, 0, 0, a.scale * kLog2e, n_qtiles, pg, hg, 0);
   else
     hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, kBNDefault, 2, true, false, NW>), dim3(grid),
                        dim3(64 * NW), 0, a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V,
-                       (T*)a.O, a.LSE, 0, 0, 0, a.scale * kLog2e, n_qtiles, pg, hg);
+                       (T*)a.O, a.LSE, 0, 0, 0, a.scale * kLog2e, n_qtiles, pg, hg, 0);
   return hipGetLastError();
 }
 
@@ -930,7 +1003,7 @@ hipError_t launch_f32(const FwdArgs& a, int Nk, int delta, bool causal) {
   const int grid = a.B * a.H * n_qtiles;
   hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3(grid), dim3(64), 0, a.stream,
                      (const float*)a.Q, (const float*)a.K, (const float*)a.V, (float*)a.O, a.LSE,
-                     a.N, Nk, delta, a.scale * kLog2e, causal ? 1 : 0, n_qtiles);
+                     a.N, Nk, delta, a.scale * kLog2e, causal ? 1 : 0, n_qtiles, a.accumulate ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -943,7 +1016,8 @@ hipError_t launch_fwd(const FwdArgs& a) {
   // every key at or before every query: the mask is void
   if (causal && a.delta >= (long long)Nk - 1) causal = false;
   if (causal && a.delta + a.N - 1 < 0) {
-    // no query sees any key
+    // no query sees any key: merged into a running result, nothing changes
+    if (a.accumulate) return hipSuccess;
     const long long rows = (long long)a.B * a.H * a.N;
     const long long n = rows * a.d;
     const int grid = (int)std::min<long long>((n + 255) / 256, 65536);

@@ -21,6 +21,9 @@ struct FwdArgs {
   hipStream_t stream;
   int Nk = 0;       // key/value rows per head (0: same as N)
   long long delta = 0;   // q_offset - k_offset: key j is visible to row i iff j <= i + delta
+  // O and LSE hold a running result on entry, which this block is merged
+  // into (contiguous layout only)
+  bool accumulate = false;
   // paged prefill: K/V are pools read through a block table, Q/O/LSE are
   // packed [total_q, H, ...] with per-sequence start offsets; B is the number
   // of sequences and N the longest chunk

@@ -145,6 +145,29 @@ int fa_merge(const void* O_a, const float* LSE_a, const void* O_b, const float* 
              void* O, float* LSE, int B, int H, int N, int d, int dtype, void* stream);
 
 /*
+ * fa_fwd_offset_accumulate -- one ring-attention step in one call: the
+ * forward of fa_fwd_offset for this key/value block, merged at once into a
+ * running result by the rule of fa_merge (HPC notes "07-16 afternoon",
+ * section "Long context and sequence parallelism").  Equivalent to
+ * fa_fwd_offset into a temporary followed by fa_merge(O, LSE, temporary ->
+ * O, LSE), without the temporary: the block's output never reaches HBM.
+ *
+ *   Q, K, V, B, H, Nq, Nk, d, offsets, scale, causal, dtype: as fa_fwd_offset
+ *   O        in/out [B,H,Nq,d] dtype `dtype`: on entry the running output over
+ *            the key blocks merged so far, on return the output over those
+ *            blocks and this one (16-bit results round to nearest even)
+ *   LSE      in/out [B,H,Nq] fp32, likewise; a row at -inf on entry has no
+ *            keys yet and its O is not read into the result
+ *
+ * A row that sees no key of this block keeps its running result (its weight
+ * is 0).  Errors as fa_fwd_offset; on an error nothing is written.
+ */
+int fa_fwd_offset_accumulate(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                             int B, int H, int Nq, int Nk, int d, long long q_offset,
+                             long long k_offset, float scale, int causal, int dtype,
+                             void* stream);
+
+/*
  * fa_bwd_workspace_size -- bytes of workspace fa_bwd needs for this shape:
  * two fp32 [B,H,N] row vectors, D_i = sum_d dO_id O_id and -LSE_i log2(e),
  * rounded up to 256 bytes.

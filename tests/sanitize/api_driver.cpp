@@ -75,6 +75,16 @@ int main() {
                        nullptr),
          FA_OK);
   EXPECT(fa_fwd_offset(P, P, P, P2, F, 1, 1, 64, 0, 64, 0, 0, 0.1f, 1, 1, nullptr), FA_ERR_SHAPE);
+  // ---- fa_fwd_offset_accumulate (same checks, one launch when valid)
+  EXPECT(fa_fwd_offset_accumulate(P, P, P, P2, F, 1, 1, 64, 32, 64, big, 0, 0.1f, 1, 1, nullptr),
+         FA_ERR_SHAPE);
+  EXPECT(fa_fwd_offset_accumulate(P, P, P, nullptr, F, 1, 1, 64, 32, 64, 0, 0, 0.1f, 1, 1,
+                                  nullptr),
+         FA_ERR_NULL);
+  before = g_launches;
+  EXPECT(fa_fwd_offset_accumulate(P, P, P, P2, F, 1, 2, 64, 32, 64, 100, 0, 0.1f, 1, 1, nullptr),
+         FA_OK);
+  EXPECT(g_launches - before, 1);
 
   // ---- fa_merge
   EXPECT(fa_merge(P, F, P, F, P2, F, 1, 1, 64, 64, 9, nullptr), FA_ERR_DTYPE);

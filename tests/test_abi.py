@@ -35,7 +35,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_fwd_offset", "fa_merge", "fa_bwd", "fa_paged_decode",
+    for n in ("fa_fwd", "fa_fwd_offset", "fa_fwd_offset_accumulate", "fa_merge", "fa_bwd",
+              "fa_paged_decode",
               "fa_paged_decode_gqa", "fa_paged_kv_append", "fa_paged_kv_append_workspace_size",
               "fa_paged_prefill",
               "fa_bwd_workspace_size", "fa_paged_decode_workspace_size", "fa_status_string",
@@ -98,6 +99,26 @@ def test_fwd_offset_validation(lib):
     assert fwd_off(lib, v=MIS) == ERR_ALIGN
     # B == 0 is a no-op even with NULL pointers
     assert fwd_off(lib, B=0, q=None, k=None, v=None, o=None, lse=None) == OK
+
+
+def fwd_acc(lib, q=P, k=P, v=P, o=P2, lse=P2, B=1, H=1, Nq=64, Nk=96, d=64, qo=0, ko=0,
+            scale=0.125, causal=1, dt=1):
+    return lib.fa_fwd_offset_accumulate(q, k, v, o, lse, B, H, Nq, Nk, d, qo, ko, scale, causal,
+                                        dt, None)
+
+
+def test_fwd_offset_accumulate_validation(lib):
+    """The fused ring step takes the arguments of fa_fwd_offset (O and LSE in
+    and out) and refuses the same things, before any launch."""
+    assert fwd_acc(lib, dt=3) == ERR_DTYPE
+    assert fwd_acc(lib, Nq=0) == ERR_SHAPE
+    assert fwd_acc(lib, Nk=(1 << 20) + 1) == ERR_SHAPE
+    assert fwd_acc(lib, qo=(1 << 60) + 1) == ERR_SHAPE
+    assert fwd_acc(lib, scale=float("inf")) == ERR_SHAPE
+    assert fwd_acc(lib, d=96) == ERR_UNSUP
+    assert fwd_acc(lib, lse=None) == ERR_NULL
+    assert fwd_acc(lib, o=MIS) == ERR_ALIGN
+    assert fwd_acc(lib, B=0, q=None, k=None, v=None, o=None, lse=None) == OK
 
 
 def merge(lib, oa=P, la=P, ob=P2, lb=P2, o=ctypes.c_void_p(0x40000), l=ctypes.c_void_p(0x80000),

@@ -181,3 +181,130 @@ def test_fwd_offset_256_row_workgroups(gpu, Nq, Nk, qo, ko):
     rows = np.unique(np.r_[0:3, 254:258, 998:1003, 2047:2050, 4095:Nq])
     _check_offset(gpu, x, qo, ko, True, 128 ** -0.5, TOL["bf16"], heads=[(0, 0), (0, 31)],
                   rows=rows)
+
+
+# ---------------------------------------------------------------- fused step
+# fa_fwd_offset_accumulate: the forward of one key/value block merged at once
+# into a running result.  A contiguous key block split in two (A, then B at
+# k_offset + n1) must give attention over the whole block, the rows that see
+# no key of either half coming out O = 0, LSE = -inf.
+ACC_CASES = [c for c in OFFSET_CASES if c[1] >= 2]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", ACC_CASES)
+def test_fwd_offset_accumulate_two_halves(gpu, dtype, d, case):
+    Nq, Nk, qo, ko = case
+    x = _inputs(Nq, Nk, d, dtype, seed=3700 + Nq + 7 * Nk + d)
+    q, k, v = (x[n].to(gpu) for n in "qkv")
+    n1 = max(1, Nk // 3)
+    ka, va = k[:, :, :n1].contiguous(), v[:, :, :n1].contiguous()
+    kb, vb = k[:, :, n1:].contiguous(), v[:, :, n1:].contiguous()
+    scale = 1.0 / math.sqrt(d)
+    o, lse = binding.fwd_offset(q, ka, va, q_offset=qo, k_offset=ko, causal=True, scale=scale)
+    binding.fwd_offset_accumulate(q, kb, vb, o, lse, q_offset=qo, k_offset=ko + n1, causal=True,
+                                  scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.attention_forward(x["q"], x["k"], x["v"], scale, True, q_offset=qo, k_offset=ko)
+    tol = {"bf16": 2e-2, "f16": 2e-2, "f32": 1e-5}[dtype]
+    for (b, h), (ro, rl) in ref.items():
+        go, gl = o[b, h].double().cpu().numpy(), lse[b, h].double().cpu().numpy()
+        empty = rl == -np.inf
+        assert np.all(gl[empty] == -np.inf) and np.all(go[empty] == 0.0)
+        assert np.all(np.isfinite(gl[~empty])) and np.all(np.isfinite(go))
+        if (~empty).any():
+            assert max_abs(go[~empty], ro[~empty]) <= tol
+            assert max_abs(gl[~empty], rl[~empty]) <= tol
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fwd_offset_accumulate_weightless_sides(gpu, dtype):
+    """A running row at LSE = -inf is not read into the result (its O may hold
+    NaN): it comes out bit-identical to fa_fwd_offset of the block alone.  A
+    row that sees no key of the block keeps its running O and LSE bit for bit."""
+    Nq, Nk, d = 200, 300, 128
+    x = _inputs(Nq, Nk, d, dtype, seed=3800)
+    q, k, v = (x[n].to(gpu) for n in "qkv")
+    qo, ko = 100, 150            # key j visible to row i iff j <= i - 50: rows 0..49 see none
+    o_blk, l_blk = binding.fwd_offset(q, k, v, q_offset=qo, k_offset=ko, causal=True)
+    run_o = torch.randn(q.shape, device=gpu).to(q.dtype)
+    run_l = torch.randn(l_blk.shape, device=gpu)
+    run_o[:, :, 60:90] = float("nan")
+    run_l[:, :, 60:90] = -math.inf
+    o, l = run_o.clone(), run_l.clone()
+    binding.fwd_offset_accumulate(q, k, v, o, l, q_offset=qo, k_offset=ko, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :, 60:90], o_blk[:, :, 60:90])
+    assert torch.equal(l[:, :, 60:90], l_blk[:, :, 60:90])
+    assert torch.equal(o[:, :, :50], run_o[:, :, :50]) and torch.equal(l[:, :, :50], run_l[:, :, :50])
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(l).all())
+    # everything else is the merge of the two
+    ref_o, ref_l = oracle.merge_partials(oracle.to_f64(run_o[:, :, 90:]), oracle.to_f64(run_l[:, :, 90:]),
+                                         oracle.to_f64(o_blk[:, :, 90:]), oracle.to_f64(l_blk[:, :, 90:]))
+    tol = 2e-2 if dtype == "bf16" else 1e-5
+    assert max_abs(o[:, :, 90:].double().cpu().numpy(), ref_o) <= tol
+    assert max_abs(l[:, :, 90:].double().cpu().numpy(), ref_l) <= 1e-5
+
+
+def test_fwd_offset_accumulate_empty_block_is_a_no_op(gpu):
+    """A key block wholly ahead of every query leaves the running result as it was."""
+    x = _inputs(130, 200, 128, "bf16", seed=3900)
+    q, k, v = (x[n].to(gpu) for n in "qkv")
+    run_o = torch.randn(q.shape, device=gpu).to(q.dtype)
+    run_l = torch.randn(q.shape[:3], device=gpu)
+    o, l = run_o.clone(), run_l.clone()
+    binding.fwd_offset_accumulate(q, k, v, o, l, q_offset=0, k_offset=1 << 40, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, run_o) and torch.equal(l, run_l)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_ring_of_four_ranks_fused_steps(gpu, d):
+    """Four ranks of 256 queries each meet the key/value blocks in ring order,
+    fa_fwd for the diagonal block then fa_fwd_offset_accumulate for each later
+    one: the result equals causal attention over the 1024-token sequence."""
+    n, R, H = 256, 4, 3
+    x = workloads.attention_inputs(1, H, R * n, d, "bf16", seed=4000 + d)
+    q, k, v = (x[t].to(gpu) for t in "qkv")
+    outs = []
+    for r in range(R):
+        qr = q[:, :, r * n:(r + 1) * n].contiguous()
+        kr, vr = k[:, :, r * n:(r + 1) * n].contiguous(), v[:, :, r * n:(r + 1) * n].contiguous()
+        acc_o, acc_l = binding.fwd(qr, kr, vr, causal=True)
+        for step in range(1, R):
+            src = (r - step) % R
+            kb = k[:, :, src * n:(src + 1) * n].contiguous()
+            vb = v[:, :, src * n:(src + 1) * n].contiguous()
+            binding.fwd_offset_accumulate(qr, kb, vb, acc_o, acc_l, q_offset=r * n,
+                                          k_offset=src * n, causal=True)
+        outs.append((acc_o, acc_l))
+    torch.cuda.synchronize()
+    ring_o = torch.cat([o for o, _ in outs], dim=2).float().cpu()
+    ring_l = torch.cat([l for _, l in outs], dim=2).cpu()
+    ref = oracle.attention_forward(x["q"], x["k"], x["v"], 1.0 / math.sqrt(d), True)
+    for (b, h), (ro, rl) in ref.items():
+        assert max_abs(ring_o[b, h].double().numpy(), ro) <= 2e-2
+        assert max_abs(ring_l[b, h].double().numpy(), rl) <= 2e-2
+
+
+def test_ring_step_long_context_fused(gpu):
+    """The long-context ring step (32 heads x 8192 queries against the 8192
+    keys just before them) accumulated into the diagonal block's result:
+    sampled heads and rows against the oracle over all 16384 keys."""
+    c = workloads.LONG_CONTEXT
+    x = workloads.attention_inputs(c.B, c.H, 2 * c.N, c.d, c.dtype, seed=c.seed + 2)
+    q, k, v = (x[t].to(gpu) for t in "qkv")
+    q2 = q[:, :, c.N:].contiguous()
+    k1, v1 = k[:, :, :c.N].contiguous(), v[:, :, :c.N].contiguous()
+    k2, v2 = k[:, :, c.N:].contiguous(), v[:, :, c.N:].contiguous()
+    o, l = binding.fwd(q2, k2, v2, causal=True, scale=c.scale)
+    binding.fwd_offset_accumulate(q2, k1, v1, o, l, q_offset=c.N, k_offset=0, causal=True,
+                                  scale=c.scale)
+    torch.cuda.synchronize()
+    rows = np.r_[0:3, 4095:4097, 8189:8192]
+    ref = oracle.attention_forward(x["q"], x["k"], x["v"], c.scale, True, heads=[(0, 0), (0, 31)],
+                                   rows=rows + c.N)
+    for (b, h), (ro, rl) in ref.items():
+        assert max_abs(o[b, h].double().cpu().numpy()[rows], ro) <= 2e-2
+        assert max_abs(l[b, h].double().cpu().numpy()[rows], rl) <= 2e-2
