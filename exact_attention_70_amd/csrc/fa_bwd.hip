@@ -10,8 +10,14 @@
 //   dV = P^T dO,  dP = dO V^T,  D_i = sum_d dO_id O_id,  dS = P o (dP - D),
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
-// Three kernels, all on the caller's stream, deterministic (no atomics):
-//   1. bwd_dot:  D_i = rowsum(dO o O) and -LSE_i log2(e) into the workspace.
+// Two kernels, both on the caller's stream, deterministic (no atomics):
+//   1. bwd_dq:   workgroup = 128 queries (wave = 32); loops over 64-key K/V tiles;
+//      recomputes S^T = K Q^T and dP^T = V dO^T (each lane then holds one
+//      query's row, so LSE_i and D_i are per-lane scalars) and accumulates
+//      dQ^T += K^T dS^T.  Within a tile the exponentials run between the dP
+//      matrix ops, and each 16-key step's dS feeds its dQ ops at once.  Its
+//      prologue forms D_i = rowsum(dO o O) and -LSE_i log2(e) for its rows
+//      and writes them into the workspace for the second kernel.
 //   2. bwd_dkdv: workgroup = 128 keys (wave = 32 keys); loops over 64-row
 //      query tiles; recomputes S = Q K^T and dP = dO V^T with this wave's K
 //      and V rows held in registers, and accumulates dV^T += dO^T P and
@@ -19,11 +25,6 @@
 //      LDS by buffer->LDS transfers through a four-slot ring, two tiles ahead;
 //      Q^T and dO^T come from transpose reads.  Iteration i overlaps the
 //      exponentials of tile i-1 with the S / dP matrix ops of tile i.
-//   3. bwd_dq:   workgroup = 128 queries (wave = 32); loops over 64-key K/V tiles;
-//      recomputes S^T = K Q^T and dP^T = V dO^T (each lane then holds one
-//      query's row, so LSE_i and D_i are per-lane scalars) and accumulates
-//      dQ^T += K^T dS^T.  Within a tile the exponentials run between the dP
-//      matrix ops, and each 16-key step's dS feeds its dQ ops at once.
 // Causal: tiles wholly above the diagonal are skipped; straddling tiles masked.
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -34,34 +35,6 @@ namespace fa {
 namespace {
 
 constexpr int kThreads = 256;
-
-// ---------------------------------------------------------------- D = rowsum(dO o O)
-template <class E, int D>
-__global__ __launch_bounds__(kThreads) void bwd_dot_kernel(const typename E::elem* __restrict__ O,
-                                                           const typename E::elem* __restrict__ dO,
-                                                           const float* __restrict__ LSE,
-                                                           float* __restrict__ Dvec,
-                                                           float* __restrict__ NL,
-                                                           long long rows) {
-  constexpr int LPR = D / 8;                      // lanes per row, 8 values each
-  const long long row = (long long)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR;
-  const int c = threadIdx.x % LPR;
-  const bool ok = row < rows;
-  const long long r = ok ? row : 0;
-  const u32x4 a = __builtin_nontemporal_load((const u32x4*)(O + r * D + c * 8));   // read once
-  const u32x4 b = *(const u32x4*)(dO + r * D + c * 8);
-  float acc = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    acc = fmaf(E::lo(a[e]), E::lo(b[e]), acc);
-    acc = fmaf(E::hi(a[e]), E::hi(b[e]), acc);
-  }
-  acc = group_sum<LPR>(acc);
-  if (ok && c == 0) {
-    Dvec[row] = acc;
-    NL[row] = -LSE[row] * kLog2e;   // exp(scale s - LSE) = exp2(scale log2(e) s + NL)
-  }
-}
 
 // Direct buffer -> LDS copy of one dword per lane (lane i lands at lds + 4 i).
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
@@ -390,11 +363,16 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
 constexpr int kQBM = 128;   // queries per workgroup
 constexpr int kQBN = 64;    // keys per tile
 
+// The dQ kernel runs first and also forms, for its rows, D = rowsum(dO o O)
+// and -LSE log2(e), which it writes for the dK/dV kernel: each lane holds half
+// of its row's dO as B operands, loads the same half of O, and the two halves
+// meet in one cross-lane exchange.
 template <class E, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const typename E::elem* __restrict__ Q, const typename E::elem* __restrict__ K,
-    const typename E::elem* __restrict__ V, const typename E::elem* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Dvec,
+    const typename E::elem* __restrict__ V, const typename E::elem* __restrict__ O,
+    const typename E::elem* __restrict__ dO, const float* __restrict__ LSE,
+    float* __restrict__ Dvec, float* __restrict__ NLvec,
     float* __restrict__ dQ, int N, float scale, float scale_log2, int n_qtiles, int hgroup) {
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;
@@ -420,8 +398,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const auto rK = make_rsrc(K + head_off, head_bytes);
   const auto rV = make_rsrc(V + head_off, head_bytes);
   const auto rdO = make_rsrc(dO + head_off, head_bytes);
+  const auto rO = make_rsrc(O + head_off, head_bytes);
   const auto rL = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
   const auto rD = make_rsrc(Dvec + (size_t)bh * N, (uint32_t)N * 4);
+  const auto rNL = make_rsrc(NLvec + (size_t)bh * N, (uint32_t)N * 4);
   const auto rdQ = make_rsrc(dQ + head_off, (uint32_t)N * D * 4);
 
   const int kv_end = CAUSAL ? min(N, q0 + kQBM) : N;
@@ -432,13 +412,30 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   };
   load(0, sK0, sV0);
   u32x4 qf[KSTEPS], dof[KSTEPS];
+  float Di = 0.f;
+  {
+    u32x4 of[KSTEPS];
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) {
-    qf[s] = bload16(rQ, (uint32_t)(my_q * D + 16 * s + 8 * half) * 2);
-    dof[s] = bload16(rdO, (uint32_t)(my_q * D + 16 * s + 8 * half) * 2);
+    for (int s = 0; s < KSTEPS; ++s) {
+      qf[s] = bload16(rQ, (uint32_t)(my_q * D + 16 * s + 8 * half) * 2);
+      dof[s] = bload16(rdO, (uint32_t)(my_q * D + 16 * s + 8 * half) * 2);
+      of[s] = __builtin_amdgcn_raw_buffer_load_b128(rO, (int)((my_q * D + 16 * s + 8 * half) * 2),
+                                                    0, kCpolNT);   // O is read once
+    }
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Di = fmaf(E::lo(of[s][e]), E::lo(dof[s][e]), Di);
+        Di = fmaf(E::hi(of[s][e]), E::hi(dof[s][e]), Di);
+      }
+    Di += swap_half(Di);              // the other half of the row's head dim
   }
-  const float neg_lse2 = bload4f(rL, (uint32_t)my_q * 4);   // -LSE log2(e)
-  const float Di = bload4f(rD, (uint32_t)my_q * 4);
+  const float neg_lse2 = -bload4f(rL, (uint32_t)my_q * 4) * kLog2e;
+  if (half == 0) {                    // rows past N fall outside the resources
+    bstore4f(Di, rD, (uint32_t)my_q * 4);
+    bstore4f(neg_lse2, rNL, (uint32_t)my_q * 4);
+  }
   f32x16 dq[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) dq[t] = zero16();
@@ -559,25 +556,21 @@ template <class E, int D, bool CAUSAL>
 hipError_t launch(const BwdArgs& a) {
   using T = typename E::elem;
   const long long rows = (long long)a.B * a.H * a.N;
-  constexpr int rows_per_block = kThreads / (D / 8);
   float* NLvec = a.Dvec + rows;   // -LSE log2(e), after D in the workspace
-  hipLaunchKernelGGL((bwd_dot_kernel<E, D>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
-                     dim3(kThreads), 0, a.stream, (const T*)a.O, (const T*)a.dO, a.LSE,
-                     a.Dvec, NLvec, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const float sl2 = a.scale * kLog2e;
-  const int n_kt = (a.N + kKvBN - 1) / kKvBN;
   // causal tiles differ in length: interleave heads so long tiles start first
   // (each tile streams two [N, d] operands of its head)
   const int hg = CAUSAL ? xcd_group((long long)a.B * a.H, (long long)a.N * D * 4) : 0;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL>), dim3(a.B * a.H * n_kt), dim3(kKvWaves * 64), 0,
-                     a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V, (const T*)a.dO, NLvec, a.Dvec, a.dK, a.dV, a.N, a.scale, sl2, n_kt, hg);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // dQ first: it also writes D and -LSE log2(e), which the dK/dV kernel reads
   const int n_qt = (a.N + kQBM - 1) / kQBM;
   hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL>), dim3(a.B * a.H * n_qt), dim3(kThreads), 0,
-                     a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V, (const T*)a.dO, NLvec, a.Dvec, a.dQ, a.N, a.scale, sl2, n_qt, hg);
+                     a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V, (const T*)a.O,
+                     (const T*)a.dO, a.LSE, a.Dvec, NLvec, a.dQ, a.N, a.scale, sl2, n_qt, hg);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_kt = (a.N + kKvBN - 1) / kKvBN;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL>), dim3(a.B * a.H * n_kt), dim3(kKvWaves * 64), 0,
+                     a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V, (const T*)a.dO, NLvec, a.Dvec, a.dK, a.dV, a.N, a.scale, sl2, n_kt, hg);
   return hipGetLastError();
 }
 
