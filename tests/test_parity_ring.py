@@ -308,3 +308,29 @@ def test_ring_step_long_context_fused(gpu):
     for (b, h), (ro, rl) in ref.items():
         assert max_abs(o[b, h].double().cpu().numpy()[rows], ro) <= 2e-2
         assert max_abs(l[b, h].double().cpu().numpy()[rows], rl) <= 2e-2
+
+
+@pytest.mark.parametrize("Nq,Nk,qo,ko", [(4100, 4100, 1000, 0), (4100, 4096, 0, 1000)])
+def test_fwd_offset_accumulate_256_row_workgroups(gpu, Nq, Nk, qo, ko):
+    """The fused step on the paired 256-row causal kernel: the key block split
+    in two halves, the second accumulated into the first's result, against the
+    oracle over the whole block on sampled heads and rows."""
+    x = _inputs(Nq, Nk, 128, "bf16", seed=4100 + qo, H=32)
+    q, k, v = (x[n].to(gpu) for n in "qkv")
+    n1 = Nk // 2
+    scale = 128 ** -0.5
+    o, lse = binding.fwd_offset(q, k[:, :, :n1].contiguous(), v[:, :, :n1].contiguous(),
+                                q_offset=qo, k_offset=ko, causal=True, scale=scale)
+    binding.fwd_offset_accumulate(q, k[:, :, n1:].contiguous(), v[:, :, n1:].contiguous(), o, lse,
+                                  q_offset=qo, k_offset=ko + n1, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    rows = np.unique(np.r_[0:3, 254:258, 998:1003, 2047:2052, 3095:3100, 4095:Nq])
+    ref = oracle.attention_forward(x["q"], x["k"], x["v"], scale, True, heads=[(0, 0), (0, 31)],
+                                   rows=rows, q_offset=qo, k_offset=ko)
+    for (b, h), (ro, rl) in ref.items():
+        go, gl = o[b, h].double().cpu().numpy()[rows], lse[b, h].double().cpu().numpy()[rows]
+        empty = rl == -np.inf
+        assert np.all(gl[empty] == -np.inf) and np.all(go[empty] == 0.0)
+        if (~empty).any():
+            assert max_abs(go[~empty], ro[~empty]) <= 2e-2
+            assert max_abs(gl[~empty], rl[~empty]) <= 2e-2
