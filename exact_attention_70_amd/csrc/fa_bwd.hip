@@ -429,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         Di = fmaf(E::lo(of[s][e]), E::lo(dof[s][e]), Di);
         Di = fmaf(E::hi(of[s][e]), E::hi(dof[s][e]), Di);
       }
-    Di += swap_half(Di);              // the other half of the row's head dim
+    Di = half_sum(Di);                // with the other half of the row's head dim
   }
   const float neg_lse2 = -bload4f(rL, (uint32_t)my_q * 4) * kLog2e;
   if (half == 0) {                    // rows past N fall outside the resources

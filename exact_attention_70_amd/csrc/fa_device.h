@@ -152,16 +152,20 @@ struct F16 {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Exchange with the lane 32 positions away (the other half of the wave).  The
-// lane index is formed at each call and hidden from the optimizer, so that
-// its permute address is not computed once and held (or spilled) across a
-// whole kernel for the few places that need it.
+// x of the lane 32 positions away (the other half of the wave), and the sum
+// and maximum over lanes l and l ^ 32, which both halves get alike.  The lane
+// index is formed by an asm block at each call, so the compiler can neither
+// compute it once and hold it (or spill it) across a kernel nor merge calls.
+// (v_permlane32_swap would need no index, but this compiler folds its two
+// results into one when both are used.)
 __device__ __forceinline__ float swap_half(float x) {
-  int l = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-  asm volatile("" : "+v"(l));
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
   return __builtin_bit_cast(float,
                             __builtin_amdgcn_ds_bpermute((l ^ 32) << 2, __builtin_bit_cast(int, x)));
 }
+__device__ __forceinline__ float half_sum(float x) { return x + swap_half(x); }
+__device__ __forceinline__ float half_max(float x) { return fmaxf(x, swap_half(x)); }
 
 // Workgroup barriers for LDS producer/consumer phases.  barrier_lds() waits
 // only for this wave's LDS accesses (so buffer->LDS transfers it issued may

@@ -439,7 +439,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
       for (int t = 0; t < NSUB; ++t)
 #pragma unroll
         for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[t][i], s[t][i + 1]));
-      return fmaxf(mx, swap_half(mx)) * scale_log2;
+      return half_max(mx) * scale_log2;
     };
     auto set_ref = [&](float m) {
       m_run = m;
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     if (i < n_kv) idle_iter(i, sK1, sV0);
 
     // ---- epilogue: O = O^T / l, LSE = ln(sum exp) = (m + log2 l) ln 2
-    const float l_tot = l_run + swap_half(l_run);
+    const float l_tot = half_sum(l_run);
     // a row that saw no key (l = 0) gets O = 0 and LSE = -inf
     float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     float lse_out = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
@@ -690,7 +690,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
       for (int k = 0; k < 32 / RPS; ++k) {
         const int r = k * RPS + elane / CPR, c = elane % CPR;
         const u32x4 w = *(const u32x4*)(stage + r * (D * 2) + ((c ^ (r % CPR)) << 4));
-        const float car = __shfl(ca, r, 64);
+        const float car = __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_bpermute(r << 2, __builtin_bit_cast(int, ca)));
         // a running row of weight 0 (LSE -inf on entry) is not read into the
         // result, whatever its O holds
         if (car == 0.f) old[k] = u32x4{0u, 0u, 0u, 0u};
@@ -782,7 +783,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(
       s[i] = x;
       mx = fmaxf(mx, x);
     }
-    mx = fmaxf(mx, swap_half(mx));
+    mx = half_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
@@ -809,7 +810,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(
       }
   }
 
-  const float l_tot = l_run + swap_half(l_run);
+  const float l_tot = half_sum(l_run);
   float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // no visible key: O = 0
   float lse_out = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
   float ca = 0.f;   // acc: the running result's weight (as in the 16-bit kernel)
