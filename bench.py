@@ -42,6 +42,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak (published)
 P_APPEND = "append_s64kv8d128"
 P_BWD4 = "bwd_causal_b4h16n2048d128"
 P_COPY = "copy_calib"
+P_GEMM = "ref_gemm_bf16_m8192n8192k8192"
 P_DEC = "decode_s64h32d128"
 P_DEC_GQA = "decode_gqa_s64h32kv8d128"
 P_FWD = "fwd_causal_b1h32n8192d128"
@@ -132,7 +133,8 @@ def main():
                          "decode_s64h32d128, decode_gqa_s64h32kv8d128 (8 cached heads), "
                          "append_s64kv8d128 (paged KV append), prefill_gqa_s8x1024h32kv8d128 "
                          "(chunked prefill over a paged cache), ring_h32n8192d128 (offset "
-                         "forward + merge of one ring step, and the fused step), copy_calib (a 1 GiB device copy "
+                         "forward + merge of one ring step, and the fused step), ref_gemm_bf16_m8192n8192k8192 (the "
+                         "vendor library's bf16 GEMM on random operands, a reference point), copy_calib (a 1 GiB device copy "
                          "used to scale the HBM-traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -297,11 +299,20 @@ def main():
         src.fill_(1.0)
         dst = torch.empty_like(src)
         parts[P_COPY] = dict(fn=lambda: dst.copy_(src), bytes=2 * src.numel() * 4)
+    if P_GEMM in only:
+        # reference point, not the hot path: the vendor library's dense bf16
+        # GEMM on N(0,1) operands (torch.mm on contiguous 2-D tensors), whose
+        # rate on this data bounds what a matrix-bound kernel can expect
+        gen = torch.Generator(device="cpu").manual_seed(70100)
+        ga = torch.randn(8192, 8192, generator=gen).to(torch.bfloat16).to(dev)
+        gb = torch.randn(8192, 8192, generator=gen).to(torch.bfloat16).to(dev)
+        gc = torch.empty(8192, 8192, dtype=torch.bfloat16, device=dev)
+        parts[P_GEMM] = dict(fn=lambda: torch.mm(ga, gb, out=gc), flops=2 * 8192 ** 3)
     torch.cuda.synchronize()
     log(f"inputs ready: {list(parts)}")
 
     order = [n for n in (P_FWD, P_FWD16, P_FWD_GPT2, P_FWD4, P_BWD4, P_DEC, P_DEC_GQA, P_APPEND,
-                         P_PREFILL, P_RING_FWD, P_RING_MERGE, P_RING_FUSED, P_COPY)
+                         P_PREFILL, P_RING_FWD, P_RING_MERGE, P_RING_FUSED, P_COPY, P_GEMM)
              if n in parts]
     for _ in range(args.warmup):
         for n in order:
