@@ -9,8 +9,8 @@
 // over pieces of the KV stream is merged with the rescaling rule of the online softmax
 // (HPC notes, section "Long context and sequence parallelism").
 //
-// Pool layout [num_blocks, block_size = 16, KVH, d = 128]: one physical block
-// is a contiguous 16 * KVH * 256-byte chunk, so a workgroup that reads all
+// Pool layout [num_blocks, block_size = 16, KVH, d], d = 64 or 128: one physical block
+// is a contiguous 16 * KVH * 2d-byte chunk, so a workgroup that reads all
 // heads of a block streams contiguous memory.  With grouped-query attention
 // (KVH < H; HPC notes, "Prefill, Decode and inference scheduling", KV-cache
 // size) consecutive query heads share one cached head: their lanes load the
@@ -23,29 +23,31 @@
 //   covers pieces of one or more sequences and writes one partial result per
 //   piece, so every workgroup has the same work whatever the lengths: no
 //   last, nearly empty round of workgroups.
-// Partial kernel: workgroup = (share, group of 32 heads); per sequence piece
-//   it covers, at H = 32 every 16-token block is read as one contiguous
-//   128 KiB stream; wave = 4 heads; 16 lanes per head, each lane owning 8 of
-//   the 128 head-dim values.  Per 16-token block: 16-byte loads of K and V
+// Partial kernel: workgroup = (share, group of heads); a lane owns 8 of a
+//   head's d values, so d / 8 lanes serve a head and a wave 64 / (d / 8)
+//   heads (4 at d = 128, 8 at d = 64).  Per sequence piece it covers, at
+//   H = 32, d = 128 every 16-token block is read as one contiguous 128 KiB
+//   stream.  Per 16-token block: 16-byte loads of K and V
 //   rows through a buffer resource over that physical block (an out-of-range
 //   block id therefore reads zeros instead of faulting), the token stride in
 //   the wave-uniform offset, with the non-temporal hint (each cached byte is
 //   read once per step; on MI355X the hint took the 64 x 32 x 128 decode
-//   from 392 to 360 us); q.k partial dot products reduced across the 16
+//   from 392 to 360 us); q.k partial dot products reduced across the head's
 //   lanes with DPP, one online-softmax update per block, and the P V
 //   accumulation.  K and V are separate load batches: the scores of block t
 //   run while V_t streams in, and K_{t+1} streams in while V_t is accumulated.
 //   Writes (m, l, unnormalised o).
 // Grouped-query partial kernel (G = H / KVH in {2, 4, 8}): a wave serves one
 //   cached head and the G query heads that read it, so each cached row is
-//   loaded once.  Lane = (token phase tq = lane / 16, 8 of the 128 d values);
-//   the four quarter-waves take interleaved tokens (4i + tq), so one 16-byte
-//   load instruction brings 4 token rows.  Each lane scores its rows against
-//   all G queries (packed two-element dot products, reduced across the 16
-//   lanes with DPP); the weights of two rows, rounded to the element type,
-//   meet the V values of those rows in one two-element dot product per d.  The running max is shared by the quarters; their
-//   denominators and outputs stay separate until the piece ends, when
-//   two cross-quarter exchanges combine them.
+//   loaded once.  Lane = (token phase tq = lane / (d / 8), 8 of the d
+//   values); the TQ = 64 / (d / 8) phases take interleaved tokens
+//   (TQ i + tq), so one 16-byte load instruction brings TQ token rows (4 at
+//   d = 128, 8 at d = 64).  Each lane scores its rows against all G queries
+//   (packed two-element dot products, reduced across the row's lanes with
+//   DPP); the weights of two rows, rounded to the element type, meet the V
+//   values of those rows in one two-element dot product per d.  The running
+//   max is shared by the phases; their denominators and outputs stay
+//   separate until the piece ends, when cross-phase exchanges combine them.
 // Merge kernel: one wave per (sequence, head) combines its pieces, found
 //   from the prefix sums.
 //   Throughput is bound by HBM: the flops per byte are ~1.
@@ -58,11 +60,18 @@ namespace fa {
 
 namespace {
 
-constexpr int kDecD = 128;
 constexpr int kDecBS = 16;
 constexpr int kDecThreads = 512;
-constexpr int kHeadsPerWave = 4;
-constexpr int kHeadsPerGroup = 32;   // heads per workgroup: whole 8 KiB token rows at H = 32
+// Head dims 64 and 128: a lane owns 8 of a row's d values, so D / 8 lanes
+// cover a row, a wave serves 64 / (D / 8) heads (4 at d = 128, 8 at d = 64)
+// and a workgroup 8 times that (32: whole 8 KiB token rows at H = 32, d = 128).
+template <int D>
+struct DecShape {
+  static_assert(D == 64 || D == 128, "head dim 64 or 128");
+  static constexpr int kLanesPerRow = D / 8;
+  static constexpr int kHeadsPerWave = 64 / kLanesPerRow;
+  static constexpr int kHeadsPerGroup = (kDecThreads / 64) * kHeadsPerWave;
+};
 
 // prefix[s] = 16-token blocks of sequences 0 .. s-1, a sequence's length
 // clamped to [0, max_blocks_per_seq * 16]; prefix[num_seqs] = all blocks.
@@ -127,7 +136,7 @@ __device__ __forceinline__ void for_each_piece(const long long* prefix, int num_
 
 // One sequence piece (tokens [t_begin, t_end) of sequence s) for this
 // workgroup's group of heads; writes the partial result into slot `slot`.
-template <class E>
+template <class E, int D>
 __device__ __forceinline__ void decode_piece(
     const typename E::elem* __restrict__ q, const typename E::elem* __restrict__ k_pool,
     const typename E::elem* __restrict__ v_pool, const int32_t* __restrict__ block_table, int H,
@@ -138,21 +147,23 @@ __device__ __forceinline__ void decode_piece(
   const int hg = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int head = hg * kHeadsPerGroup + wave * kHeadsPerWave + (lane >> 4);
-  const int ch = lane & 15;                          // which 8 of the 128 d values
+  using S = DecShape<D>;
+  constexpr int LPR = S::kLanesPerRow;
+  const int head = hg * S::kHeadsPerGroup + wave * S::kHeadsPerWave + lane / LPR;
+  const int ch = lane % LPR;                         // which 8 of the D values
   const bool head_ok = head < H;
   const int hh = head_ok ? head : 0;
   const int kvh = hh / (H / KVH);                   // the cached head this query head reads
 
-  const uint32_t blk_bytes = (uint32_t)kDecBS * KVH * kDecD * 2;
-  const uint32_t row_off = (uint32_t)(kvh * kDecD + ch * 8) * 2;   // within one token row
-  const uint32_t tok_stride = (uint32_t)KVH * kDecD * 2;
+  const uint32_t blk_bytes = (uint32_t)kDecBS * KVH * D * 2;
+  const uint32_t row_off = (uint32_t)(kvh * D + ch * 8) * 2;   // within one token row
+  const uint32_t tok_stride = (uint32_t)KVH * D * 2;
 
   // this lane's 8 query values, fp32
   float qv[8];
   {
-    const auto rq = make_rsrc(q + (size_t)s * H * kDecD, (uint32_t)H * kDecD * 2);
-    const u32x4 w = bload16(rq, (uint32_t)(hh * kDecD + ch * 8) * 2);   // this query head
+    const auto rq = make_rsrc(q + (size_t)s * H * D, (uint32_t)H * D * 2);
+    const u32x4 w = bload16(rq, (uint32_t)(hh * D + ch * 8) * 2);   // this query head
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       qv[2 * e] = E::lo(w[e]);
@@ -172,7 +183,7 @@ __device__ __forceinline__ void decode_piece(
   auto block_rsrc = [&](int t0, __amdgpu_buffer_rsrc_t& rk, __amdgpu_buffer_rsrc_t& rv) {
     const int32_t phys = table[t0 / kDecBS];
     const bool phys_ok = (uint32_t)phys < (uint32_t)num_blocks;
-    const size_t boff = (size_t)(phys_ok ? phys : 0) * kDecBS * KVH * kDecD;
+    const size_t boff = (size_t)(phys_ok ? phys : 0) * kDecBS * KVH * D;
     rk = make_rsrc(k_pool + boff, phys_ok ? blk_bytes : 0u);
     rv = make_rsrc(v_pool + boff, phys_ok ? blk_bytes : 0u);
   };
@@ -198,7 +209,7 @@ __device__ __forceinline__ void decode_piece(
         part = fmaf(qv[2 * e], E::lo(kr[u][e]), part);
         part = fmaf(qv[2 * e + 1], E::hi(kr[u][e]), part);
       }
-      float x = group_sum<16>(part) * scale_log2;
+      float x = group_sum<LPR>(part) * scale_log2;
       if (u >= n_valid) x = kNegInf;
       sc[u] = x;
       mx = fmaxf(mx, x);
@@ -241,15 +252,15 @@ __device__ __forceinline__ void decode_piece(
     w0[e] = as_u32(acc[e]);
     w1[e] = as_u32(acc[4 + e]);
   }
-  *(u32x4*)(part_o + entry * kDecD + ch * 8) = w0;
-  *(u32x4*)(part_o + entry * kDecD + ch * 8 + 4) = w1;
+  *(u32x4*)(part_o + entry * D + ch * 8) = w0;
+  *(u32x4*)(part_o + entry * D + ch * 8 + 4) = w1;
   if (ch == 0) {
     part_ml[entry * 2] = m_run;
     part_ml[entry * 2 + 1] = l_run;
   }
 }
 
-template <class E>
+template <class E, int D>
 __global__ __launch_bounds__(kDecThreads, 1) void decode_partial_kernel(
     const typename E::elem* __restrict__ q, const typename E::elem* __restrict__ k_pool,
     const typename E::elem* __restrict__ v_pool, const int32_t* __restrict__ block_table,
@@ -259,10 +270,12 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_partial_kernel(
   const int G = decode_shares(prefix, num_seqs, units);
   const int g = blockIdx.x;
   if (g >= G) return;
-  if ((int)blockIdx.y * kHeadsPerGroup + (int)(threadIdx.x >> 6) * kHeadsPerWave >= H) return;
+  if ((int)blockIdx.y * DecShape<D>::kHeadsPerGroup +
+          (int)(threadIdx.x >> 6) * DecShape<D>::kHeadsPerWave >= H)
+    return;
   for_each_piece(prefix, num_seqs, g, G, [&](int sq, int b0, int b1) {
     const int len = min(seq_lens[sq], max_blocks_per_seq * kDecBS);
-    decode_piece<E>(q, k_pool, v_pool, block_table, H, KVH, max_blocks_per_seq, num_blocks,
+    decode_piece<E, D>(q, k_pool, v_pool, block_table, H, KVH, max_blocks_per_seq, num_blocks,
                     scale_log2, part_o, part_ml, sq, b0 * kDecBS, min(len, b1 * kDecBS),
                     (size_t)g + sq);
   });
@@ -270,34 +283,37 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_partial_kernel(
 
 constexpr int kGqaWaves = 4;   // cached heads per workgroup
 
-template <class E, int G>
+template <class E, int G, int D>
 __device__ __forceinline__ void decode_gqa_piece(
     const typename E::elem* __restrict__ q, const typename E::elem* __restrict__ k_pool,
     const typename E::elem* __restrict__ v_pool, const int32_t* __restrict__ block_table, int H,
     int KVH, int max_blocks_per_seq, int num_blocks, float scale_log2, float* __restrict__ part_o,
     float* __restrict__ part_ml, int s, int t_begin, int t_end, size_t slot) {
-  constexpr int NI = G <= 4 ? 8 : 4;     // token rows per lane per step
-  constexpr int STEP = 4 * NI;           // tokens per step: whole blocks
+  constexpr int CH = D / 8;              // lanes per cached row (8 d values each)
+  constexpr int TQ = 64 / CH;            // token phases: rows one load instruction brings
+  constexpr int NI = (G <= 4 ? 8 : 4) * 4 / TQ;   // token rows per lane per step
+  constexpr int STEP = TQ * NI;          // tokens per step: whole blocks
   constexpr int NB = STEP / kDecBS;      // blocks per step
+  constexpr int RPB = kDecBS / TQ;       // a lane's rows per block
   static_assert(STEP % kDecBS == 0, "a step is whole blocks");
   static_assert(NI % 2 == 0, "rows are weighted in pairs");
   const int lane = threadIdx.x & 63;
   const int kvh = __builtin_amdgcn_readfirstlane(blockIdx.y * kGqaWaves + (threadIdx.x >> 6));
   if (kvh >= KVH) return;                           // no cached head for this wave
-  const int tq = lane >> 4;                         // token phase within 4 consecutive tokens
-  const int ch = lane & 15;                         // which 8 of the 128 d values
+  const int tq = lane / CH;                         // token phase within TQ consecutive tokens
+  const int ch = lane % CH;                         // which 8 of the D values
 
-  const uint32_t blk_bytes = (uint32_t)kDecBS * KVH * kDecD * 2;
-  const uint32_t tok_stride = (uint32_t)KVH * kDecD * 2;
-  // row (4i + tq) of a step: block i / 4, slot 4 (i % 4) + tq
-  const uint32_t lane_off = tq * tok_stride + (uint32_t)(kvh * kDecD + ch * 8) * 2;
+  const uint32_t blk_bytes = (uint32_t)kDecBS * KVH * D * 2;
+  const uint32_t tok_stride = (uint32_t)KVH * D * 2;
+  // row (TQ i + tq) of a step: block i / RPB, slot TQ (i % RPB) + tq
+  const uint32_t lane_off = tq * tok_stride + (uint32_t)(kvh * D + ch * 8) * 2;
 
   // the G query heads' 8 values of this lane, packed pairs
   u32x4 qv[G];
   {
-    const auto rq = make_rsrc(q + (size_t)s * H * kDecD, (uint32_t)H * kDecD * 2);
+    const auto rq = make_rsrc(q + (size_t)s * H * D, (uint32_t)H * D * 2);
 #pragma unroll
-    for (int j = 0; j < G; ++j) qv[j] = bload16(rq, (uint32_t)((kvh * G + j) * kDecD + ch * 8) * 2);
+    for (int j = 0; j < G; ++j) qv[j] = bload16(rq, (uint32_t)((kvh * G + j) * D + ch * 8) * 2);
   }
 
   float m_run[G], l_run[G], acc[G][8];
@@ -319,7 +335,7 @@ __device__ __forceinline__ void decode_gqa_piece(
       const int tb = t0 + b * kDecBS;
       const int32_t phys = tb < t_end ? table[tb / kDecBS] : -1;
       const bool ok = (uint32_t)phys < (uint32_t)num_blocks;
-      const size_t boff = (size_t)(ok ? phys : 0) * kDecBS * KVH * kDecD;
+      const size_t boff = (size_t)(ok ? phys : 0) * kDecBS * KVH * D;
       rk[b] = make_rsrc(k_pool + boff, ok ? blk_bytes : 0u);
       rv[b] = make_rsrc(v_pool + boff, ok ? blk_bytes : 0u);
     }
@@ -327,7 +343,8 @@ __device__ __forceinline__ void decode_gqa_piece(
   auto load_rows = [&](const __amdgpu_buffer_rsrc_t (&r)[NB], u32x4 (&dst)[NI])
       __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dst[i] = bload16s_nt(r[i / 4], lane_off, (i % 4) * 4 * tok_stride);
+    for (int i = 0; i < NI; ++i)
+      dst[i] = bload16s_nt(r[i / RPB], lane_off, (i % RPB) * TQ * tok_stride);
   };
 
   // One step over tokens [t0, t0 + STEP): K of the next step streams in while
@@ -350,13 +367,13 @@ __device__ __forceinline__ void decode_gqa_piece(
     for (int j = 0; j < G; ++j) mx[j] = kNegInf;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const bool valid = !MASKED || t0 + 4 * i + tq < t_end;
+      const bool valid = !MASKED || t0 + TQ * i + tq < t_end;
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         float part = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) part = E::dot2(qv[j][e], kr[i][e], part);
-        float x = group_sum<16>(part) * scale_log2;
+        float x = group_sum<CH>(part) * scale_log2;
         if constexpr (MASKED) x = valid ? x : kNegInf;
         sc[i][j] = x;
         mx[j] = fmaxf(mx[j], x);
@@ -366,8 +383,10 @@ __device__ __forceinline__ void decode_gqa_piece(
     float alpha[G], m_new[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      float m = fmaxf(mx[j], __shfl_xor(mx[j], 16, 64));
-      m = fmaxf(m, __shfl_xor(m, 32, 64));          // the step's max over all four quarters
+      float m = mx[j];
+#pragma unroll
+      for (int off = CH; off < 64; off *= 2)          // the step's max over all TQ phases
+        m = fmaxf(m, __shfl_xor(m, off, 64));
       m_new[j] = fmaxf(m_run[j], m);
       alpha[j] = fast_exp2(m_run[j] - m_new[j]);
       m_run[j] = m_new[j];
@@ -380,7 +399,7 @@ __device__ __forceinline__ void decode_gqa_piece(
     if constexpr (MASKED) {
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        if (t0 + 4 * i + tq >= t_end) vr[i] = u32x4{0u, 0u, 0u, 0u};
+        if (t0 + TQ * i + tq >= t_end) vr[i] = u32x4{0u, 0u, 0u, 0u};
     }
     // Two rows at a time: the pair's weights, rounded to the element type
     // (as the forward rounds P), weight the pair of V values of each d
@@ -411,21 +430,20 @@ __device__ __forceinline__ void decode_gqa_piece(
   for (; t0 + STEP <= t_end; t0 += STEP) step(t0, Plain{});
   if (t0 < t_end) step(t0, Masked{});
 
-  // combine the four quarters' denominators and outputs
+  // combine the TQ phases' denominators and outputs
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    l_run[j] += __shfl_xor(l_run[j], 16, 64);
-    l_run[j] += __shfl_xor(l_run[j], 32, 64);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      acc[j][e] += __shfl_xor(acc[j][e], 16, 64);
-      acc[j][e] += __shfl_xor(acc[j][e], 32, 64);
+    for (int off = CH; off < 64; off *= 2) {
+      l_run[j] += __shfl_xor(l_run[j], off, 64);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[j][e] += __shfl_xor(acc[j][e], off, 64);
     }
   }
-  // quarter j % 4 writes query head kvh * G + j
+  // phase j % TQ writes query head kvh * G + j
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    if (tq != j % 4) continue;
+    if (tq != j % TQ) continue;
     const size_t entry = slot * H + kvh * G + j;
     u32x4 w0, w1;
 #pragma unroll
@@ -433,8 +451,8 @@ __device__ __forceinline__ void decode_gqa_piece(
       w0[e] = as_u32(acc[j][e]);
       w1[e] = as_u32(acc[j][4 + e]);
     }
-    *(u32x4*)(part_o + entry * kDecD + ch * 8) = w0;
-    *(u32x4*)(part_o + entry * kDecD + ch * 8 + 4) = w1;
+    *(u32x4*)(part_o + entry * D + ch * 8) = w0;
+    *(u32x4*)(part_o + entry * D + ch * 8 + 4) = w1;
     if (ch == 0) {
       part_ml[entry * 2] = m_run[j];
       part_ml[entry * 2 + 1] = l_run[j];
@@ -442,7 +460,7 @@ __device__ __forceinline__ void decode_gqa_piece(
   }
 }
 
-template <class E, int G>
+template <class E, int G, int D>
 __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_partial_kernel(
     const typename E::elem* __restrict__ q, const typename E::elem* __restrict__ k_pool,
     const typename E::elem* __restrict__ v_pool, const int32_t* __restrict__ block_table,
@@ -455,7 +473,7 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_partial_kernel(
   if ((int)blockIdx.y * kGqaWaves + (int)(threadIdx.x >> 6) >= KVH) return;   // no cached head
   for_each_piece(prefix, num_seqs, g, shares, [&](int sq, int b0, int b1) {
     const int len = min(seq_lens[sq], max_blocks_per_seq * kDecBS);
-    decode_gqa_piece<E, G>(q, k_pool, v_pool, block_table, H, KVH, max_blocks_per_seq, num_blocks,
+    decode_gqa_piece<E, G, D>(q, k_pool, v_pool, block_table, H, KVH, max_blocks_per_seq, num_blocks,
                            scale_log2, part_o, part_ml, sq, b0 * kDecBS, min(len, b1 * kDecBS),
                            (size_t)g + sq);
   });
@@ -463,9 +481,9 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_partial_kernel(
 
 // One wave per (sequence, head): rescale every piece's (m, l, o) to the
 // common maximum and sum.  Lanes take the pieces' (m, l) in parallel for
-// the maximum and the weights; then each lane owns 2 of the 128 output values
-// and sums the pieces' contributions with the weights broadcast from the
-// lane that computed them.
+// the maximum and the weights; then each of the first D / 2 lanes owns 2 of
+// the D output values and sums the pieces' contributions with the weights
+// broadcast from the lane that computed them.
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
@@ -477,7 +495,7 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-template <class E>
+template <class E, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const long long* __restrict__ prefix, int num_seqs, int H, int units,
@@ -487,8 +505,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   const int lane = threadIdx.x & 63;
   const int s = gw / H, head = gw % H;
   const long long bs0 = prefix[s], bs1 = prefix[s + 1];   // this sequence's blocks
+  const bool owner = 2 * lane < D;    // this lane owns output values 2 lane, 2 lane + 1
   if (bs1 <= bs0) {   // invalid length: defined output, nothing read
-    *(uint32_t*)(o + ((size_t)s * H + head) * kDecD + 2 * lane) = 0u;
+    if (owner) *(uint32_t*)(o + ((size_t)s * H + head) * D + 2 * lane) = 0u;
     if (lane == 0) lse[(size_t)s * H + head] = kNegInf;
     return;
   }
@@ -516,27 +535,29 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 #pragma unroll 4
     for (int q = 0; q < cnt; ++q) {
       const float wq = __shfl(w, q, 64);
-      const size_t e = base + (size_t)(p0 + q) * H;
-      const float2 v = *(const float2*)(part_o + e * kDecD + 2 * lane);
-      a0 = fmaf(wq, v.x, a0);
-      a1 = fmaf(wq, v.y, a1);
+      if (owner) {
+        const size_t e = base + (size_t)(p0 + q) * H;
+        const float2 v = *(const float2*)(part_o + e * D + 2 * lane);
+        a0 = fmaf(wq, v.x, a0);
+        a1 = fmaf(wq, v.y, a1);
+      }
     }
   }
   L = wave_sum(L);
   const float inv = 1.f / L;
-  *(uint32_t*)(o + ((size_t)s * H + head) * kDecD + 2 * lane) = E::pack(a0 * inv, a1 * inv);
+  if (owner) *(uint32_t*)(o + ((size_t)s * H + head) * D + 2 * lane) = E::pack(a0 * inv, a1 * inv);
   if (lane == 0) lse[(size_t)s * H + head] = (m_star + fast_log2(L)) * kLn2;
 }
 
 }  // namespace
 
-template <class E>
-hipError_t launch_decode_e(const DecodeArgs& a) {
+template <class E, int D>
+hipError_t launch_decode_ed(const DecodeArgs& a) {
   using T = typename E::elem;
-  const size_t n_floats = decode_partials_floats(a.num_seqs, a.H, kDecD);
-  const size_t n_entries = n_floats / (kDecD + 2);
+  const size_t n_floats = decode_partials_floats(a.num_seqs, a.H, D);
+  const size_t n_entries = n_floats / (D + 2);
   float* part_o = a.part;
-  float* part_ml = a.part + n_entries * kDecD;
+  float* part_ml = a.part + n_entries * D;
   long long* prefix = reinterpret_cast<long long*>(a.part + n_floats);
   hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(256), 0, a.stream, a.seq_lens,
                      a.num_seqs, a.max_blocks_per_seq, prefix);
@@ -547,15 +568,16 @@ hipError_t launch_decode_e(const DecodeArgs& a) {
   // grouped heads with a group size the grouped kernel is built for
   if (g == 2 || g == 4 || g == 8) {
     dim3 grid(a.units, (KVH + kGqaWaves - 1) / kGqaWaves);
-    auto kern = g == 2 ? decode_gqa_partial_kernel<E, 2>
-              : g == 4 ? decode_gqa_partial_kernel<E, 4> : decode_gqa_partial_kernel<E, 8>;
+    auto kern = g == 2 ? decode_gqa_partial_kernel<E, 2, D>
+              : g == 4 ? decode_gqa_partial_kernel<E, 4, D> : decode_gqa_partial_kernel<E, 8, D>;
     hipLaunchKernelGGL(kern, grid, dim3(kGqaWaves * 64), 0, a.stream, (const T*)a.q,
                        (const T*)a.k_pool, (const T*)a.v_pool, a.block_table, a.seq_lens, a.H, KVH,
                        a.max_blocks_per_seq, a.num_blocks, a.scale * kLog2e, part_o, part_ml,
                        prefix, a.num_seqs, a.units);
   } else {
-    dim3 grid(a.units, (a.H + kHeadsPerGroup - 1) / kHeadsPerGroup);
-    hipLaunchKernelGGL((decode_partial_kernel<E>), grid, dim3(kDecThreads), 0, a.stream,
+    constexpr int HPG = DecShape<D>::kHeadsPerGroup;
+    dim3 grid(a.units, (a.H + HPG - 1) / HPG);
+    hipLaunchKernelGGL((decode_partial_kernel<E, D>), grid, dim3(kDecThreads), 0, a.stream,
                        (const T*)a.q, (const T*)a.k_pool, (const T*)a.v_pool, a.block_table,
                        a.seq_lens, a.H, KVH, a.max_blocks_per_seq, a.num_blocks,
                        a.scale * kLog2e, part_o, part_ml, prefix, a.num_seqs, a.units);
@@ -563,9 +585,14 @@ hipError_t launch_decode_e(const DecodeArgs& a) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int waves = a.num_seqs * a.H;
-  hipLaunchKernelGGL((decode_merge_kernel<E>), dim3((waves + 3) / 4), dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((decode_merge_kernel<E, D>), dim3((waves + 3) / 4), dim3(256), 0, a.stream,
                      part_o, part_ml, prefix, a.num_seqs, a.H, a.units, (T*)a.o, a.lse);
   return hipGetLastError();
+}
+
+template <class E>
+hipError_t launch_decode_e(const DecodeArgs& a) {
+  return a.d == 64 ? launch_decode_ed<E, 64>(a) : launch_decode_ed<E, 128>(a);
 }
 
 hipError_t launch_decode(const DecodeArgs& a) {

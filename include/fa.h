@@ -235,7 +235,7 @@ size_t fa_paged_decode_workspace_size(int num_seqs, int H, int d, int max_blocks
  *   seq_lens     in   [num_seqs] int32, 1 <= seq_lens[s] <= max_blocks_per_seq*block_size
  *   o            out  [num_seqs, H, d], same dtype
  *   lse          out  [num_seqs, H] fp32 (natural log)
- *   block_size   16 (else FA_ERR_UNSUPPORTED); d 128 (else FA_ERR_UNSUPPORTED)
+ *   block_size   16 (else FA_ERR_UNSUPPORTED); d 64 or 128 (else FA_ERR_UNSUPPORTED)
  *   H            a multiple of 4
  *   workspace    >= fa_paged_decode_workspace_size() bytes, 16-B aligned
  * The contents of block_table and seq_lens are trusted like a page table.

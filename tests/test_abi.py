@@ -174,7 +174,8 @@ def test_decode_validation(lib):
         return lib.fa_paged_decode(q, P, P, table, P, bs, S, H, d, mbps, nb, 0.1, P2, P2, dt,
                                    ws_ptr, wsb, None)
     assert dec(bs=32) == ERR_UNSUP
-    assert dec(d=64) == ERR_UNSUP
+    assert dec(d=96) == ERR_UNSUP
+    assert dec(d=64, S=0) == OK                  # head dims 64 and 128
     assert dec(H=6) == ERR_UNSUP
     assert dec(dt=0) == ERR_UNSUP
     assert dec(dt=3) == ERR_DTYPE
@@ -205,7 +206,7 @@ def test_paged_decode_gqa_validation(lib):
     assert gqa(lib, KVH=0) == ERR_SHAPE
     assert gqa(lib, KVH=5) == ERR_SHAPE          # must divide H
     assert gqa(lib, KVH=64) == ERR_SHAPE
-    assert gqa(lib, d=64) == ERR_UNSUP
+    assert gqa(lib, d=80) == ERR_UNSUP
     assert gqa(lib, q=None) == ERR_NULL
     assert gqa(lib, S=0, q=None) == OK
 
@@ -222,7 +223,7 @@ def test_paged_decode_noalloc_validation(lib):
     ERR_SCRATCH = -9
     assert "FA_ERR_SCRATCH" in libfa.status_string(ERR_SCRATCH)
     assert noalloc(lib, KVH=5) == ERR_SHAPE
-    assert noalloc(lib, d=64) == ERR_UNSUP
+    assert noalloc(lib, d=32) == ERR_UNSUP
     assert noalloc(lib, bs=8) == ERR_UNSUP
     assert noalloc(lib, dt=3) == ERR_DTYPE
     assert noalloc(lib, q=None) == ERR_NULL

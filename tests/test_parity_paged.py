@@ -59,6 +59,44 @@ def test_gqa_decode_head_counts_and_step_edges(gpu, H, kvh):
     assert max_abs(lse.double().cpu().numpy(), rl) <= TOL
 
 
+@pytest.mark.parametrize("H,kvh", [(12, 12), (12, 6), (12, 3), (16, 4), (16, 2), (32, 32)])
+def test_decode_head_dim_64(gpu, H, kvh):
+    """Head dim 64 (a GPT-2-sized head): multi-head decode (8 heads a wave,
+    H = 12 leaving half of the second wave idle), the grouped kernel at group
+    sizes 2, 4 and 8 (8 token rows per load instruction), and a group size
+    (4 of 12 = 3) the grouped kernel is not built for; lengths at the edges of
+    16-token blocks and 32-token steps, pad slots NaN."""
+    d, bs = 64, 16
+    lens = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 255, 256, 257, 600]
+    p = workloads.paged_inputs(len(lens), H, d, bs, 1, max(lens), seed=5300 + H + kvh,
+                               seq_lens=lens, kv_heads=kvh, pad_value=float("nan"))
+    pd = _to_dev(p, gpu)
+    o, lse = binding.paged_decode(pd["q"], pd["k_pool"], pd["v_pool"], pd["block_table"],
+                                  pd["seq_lens"], block_size=bs, scale=d ** -0.5)
+    torch.cuda.synchronize()
+    ro, rl = oracle.paged_decode(p["q"], p["k_pool"], p["v_pool"], p["block_table"], p["seq_lens"],
+                                 bs, d ** -0.5)
+    assert np.all(np.isfinite(o.float().cpu().numpy()))
+    assert max_abs(o.double().cpu().numpy(), ro) <= TOL
+    assert max_abs(lse.double().cpu().numpy(), rl) <= TOL
+
+
+def test_decode_head_dim_64_many_sequences(gpu):
+    """d = 64 over more blocks than shares (64 sequences of 128..4096 tokens),
+    so that sequences are split over several shares and merged."""
+    d, bs, H, kvh = 64, 16, 12, 12
+    p = workloads.paged_inputs(64, H, d, bs, 128, 4096, seed=5400, kv_heads=kvh)
+    pd = _to_dev(p, gpu)
+    o, lse = binding.paged_decode(pd["q"], pd["k_pool"], pd["v_pool"], pd["block_table"],
+                                  pd["seq_lens"], block_size=bs, scale=d ** -0.5)
+    torch.cuda.synchronize()
+    seqs = [0, 1, 17, 40, 63]
+    ro, rl = oracle.paged_decode(p["q"], p["k_pool"], p["v_pool"], p["block_table"], p["seq_lens"],
+                                 bs, d ** -0.5, seqs=seqs)
+    assert max_abs(o[seqs].double().cpu().numpy(), ro) <= TOL
+    assert max_abs(lse[seqs].double().cpu().numpy(), rl) <= TOL
+
+
 def test_gqa_decode_maximum_length(gpu):
     """One sequence of 2^20 cached tokens, the longest a table may describe
     (65536 blocks of 16), 4 query heads on one cached head; pad slots NaN."""
