@@ -187,8 +187,7 @@ int check_decode_args(const void* q, const void* k_pool, const void* v_pool,
     return FA_ERR_SHAPE;
   if (H % KVH != 0) return FA_ERR_SHAPE;
   if (!std::isfinite(scale)) return FA_ERR_SHAPE;
-  if (dtype == FA_DT_F32 || block_size != 16 || (d != 64 && d != 128) || (H % 4) != 0)
-    return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_DT_F32 || block_size != 16 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
   const long long block_bytes = (long long)block_size * KVH * d * 2;
   if (block_bytes >= (1LL << 31)) return FA_ERR_SHAPE;
   if ((long long)max_blocks_per_seq * block_size > kMaxN) return FA_ERR_SHAPE;

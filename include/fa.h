@@ -236,7 +236,7 @@ size_t fa_paged_decode_workspace_size(int num_seqs, int H, int d, int max_blocks
  *   o            out  [num_seqs, H, d], same dtype
  *   lse          out  [num_seqs, H] fp32 (natural log)
  *   block_size   16 (else FA_ERR_UNSUPPORTED); d 64 or 128 (else FA_ERR_UNSUPPORTED)
- *   H            a multiple of 4
+ *   H            >= 1 (any count; a wave's lanes past H idle)
  *   workspace    >= fa_paged_decode_workspace_size() bytes, 16-B aligned
  * The contents of block_table and seq_lens are trusted like a page table.
  * With the environment variable FA_DEBUG=1 they are copied to the host and

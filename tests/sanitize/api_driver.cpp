@@ -127,9 +127,13 @@ int main() {
   EXPECT(fa_paged_decode(P, P, P, I, I, 8, 64, 32, 128, 256, 9000, 0.088f, P2, F, 1, W, dws,
                          nullptr),
          FA_ERR_UNSUPPORTED);
-  EXPECT(fa_paged_decode(P, P, P, I, I, 16, 64, 30, 128, 256, 9000, 0.088f, P2, F, 1, W, dws,
+  EXPECT(fa_paged_decode(P, P, P, I, I, 16, 64, 32, 96, 256, 9000, 0.088f, P2, F, 1, W, dws,
                          nullptr),
          FA_ERR_UNSUPPORTED);
+  // any head count (here 30) and head dim 64 are accepted
+  EXPECT(fa_paged_decode(P, P, P, I, I, 16, 64, 30, 64, 256, 9000, 0.088f, P2, F, 1, W, dws,
+                         nullptr),
+         FA_OK);
   EXPECT(fa_paged_decode(P, P, P, IMIS, I, 16, 64, 32, 128, 256, 9000, 0.088f, P2, F, 1, W, dws,
                          nullptr),
          FA_ERR_ALIGN);

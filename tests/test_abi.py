@@ -176,7 +176,7 @@ def test_decode_validation(lib):
     assert dec(bs=32) == ERR_UNSUP
     assert dec(d=96) == ERR_UNSUP
     assert dec(d=64, S=0) == OK                  # head dims 64 and 128
-    assert dec(H=6) == ERR_UNSUP
+    assert dec(H=6, S=0) == OK                   # any head count
     assert dec(dt=0) == ERR_UNSUP
     assert dec(dt=3) == ERR_DTYPE
     assert dec(nb=0) == ERR_SHAPE

@@ -81,6 +81,26 @@ def test_decode_head_dim_64(gpu, H, kvh):
     assert max_abs(lse.double().cpu().numpy(), rl) <= TOL
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("H,kvh", [(1, 1), (3, 3), (6, 6), (7, 7), (6, 3), (10, 5), (14, 7)])
+def test_decode_any_head_count(gpu, d, H, kvh):
+    """Head counts that are not a multiple of a wave's heads (lanes past H
+    idle), including one head, odd counts, and odd cached-head counts with
+    group size 2 (grouped kernel) on odd KVH."""
+    bs = 16
+    lens = [1, 16, 17, 33, 100, 257]
+    p = workloads.paged_inputs(len(lens), H, d, bs, 1, max(lens), seed=5500 + 13 * H + kvh + d,
+                               seq_lens=lens, kv_heads=kvh, pad_value=float("nan"))
+    pd = _to_dev(p, gpu)
+    o, lse = binding.paged_decode(pd["q"], pd["k_pool"], pd["v_pool"], pd["block_table"],
+                                  pd["seq_lens"], block_size=bs, scale=d ** -0.5)
+    torch.cuda.synchronize()
+    ro, rl = oracle.paged_decode(p["q"], p["k_pool"], p["v_pool"], p["block_table"], p["seq_lens"],
+                                 bs, d ** -0.5)
+    assert max_abs(o.double().cpu().numpy(), ro) <= TOL
+    assert max_abs(lse.double().cpu().numpy(), rl) <= TOL
+
+
 def test_decode_head_dim_64_many_sequences(gpu):
     """d = 64 over more blocks than shares (64 sequences of 128..4096 tokens),
     so that sequences are split over several shares and merged."""
