@@ -43,10 +43,12 @@ P_APPEND = "append_s64kv8d128"
 P_BWD4 = "bwd_causal_b4h16n2048d128"
 P_COPY = "copy_calib"
 P_GEMM = "ref_gemm_bf16_m8192n8192k8192"
+P_GEMM_ZERO = "ref_gemm_bf16_m8192n8192k8192_zero_inputs"
 P_DEC = "decode_s64h32d128"
 P_DEC_GQA = "decode_gqa_s64h32kv8d128"
 P_FWD = "fwd_causal_b1h32n8192d128"
 P_FWD16 = "fwd_causal_f16_b1h32n8192d128"
+P_FWD_ZERO = "fwd_causal_b1h32n8192d128_zero_inputs"
 P_FWD4 = "fwd_causal_b4h16n2048d128"
 P_FWD_GPT2 = "fwd_causal_b8h12n1024d64"
 P_PREFILL = "prefill_gqa_s8x1024h32kv8d128"
@@ -135,7 +137,10 @@ def main():
                          "(chunked prefill over a paged cache), ring_h32n8192d128 (offset "
                          "forward + merge of one ring step, and the fused step), ref_gemm_bf16_m8192n8192k8192 (the "
                          "vendor library's bf16 GEMM on random operands, a reference point), copy_calib (a 1 GiB device copy "
-                         "used to scale the HBM-traffic counters)")
+                         "used to scale the HBM-traffic counters); and, to show how the rate depends on the "
+                         "operand data, fwd_causal_b1h32n8192d128_zero_inputs and "
+                         "ref_gemm_bf16_m8192n8192k8192_zero_inputs (the same work on all-zero inputs). "
+                         "The reference and zero-input parts run only when named here.")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -308,11 +313,27 @@ def main():
         gb = torch.randn(8192, 8192, generator=gen).to(torch.bfloat16).to(dev)
         gc = torch.empty(8192, 8192, dtype=torch.bfloat16, device=dev)
         parts[P_GEMM] = dict(fn=lambda: torch.mm(ga, gb, out=gc), flops=2 * 8192 ** 3)
+    if P_GEMM_ZERO in only:
+        za = torch.zeros(8192, 8192, dtype=torch.bfloat16, device=dev)
+        zb = torch.zeros_like(za)
+        zc = torch.empty_like(za)
+        parts[P_GEMM_ZERO] = dict(fn=lambda: torch.mm(za, zb, out=zc), flops=2 * 8192 ** 3)
+    if P_FWD_ZERO in only:
+        # the headline forward's instructions on all-zero Q, K, V: matrix
+        # operands that never toggle draw less power, so the clock runs higher
+        zq = torch.zeros(longctx.B, longctx.H, longctx.N, longctx.d, dtype=torch.bfloat16,
+                         device=dev)
+        zk, zv, zo = torch.zeros_like(zq), torch.zeros_like(zq), torch.empty_like(zq)
+        zl = torch.empty(longctx.B, longctx.H, longctx.N, device=dev)
+        parts[P_FWD_ZERO] = dict(fn=lambda: binding.fwd(zq, zk, zv, causal=True,
+                                                        scale=longctx.scale, out=zo, lse=zl),
+                                 flops=causal_flops(longctx.B, longctx.H, longctx.N, longctx.d))
     torch.cuda.synchronize()
     log(f"inputs ready: {list(parts)}")
 
     order = [n for n in (P_FWD, P_FWD16, P_FWD_GPT2, P_FWD4, P_BWD4, P_DEC, P_DEC_GQA, P_APPEND,
-                         P_PREFILL, P_RING_FWD, P_RING_MERGE, P_RING_FUSED, P_COPY, P_GEMM)
+                         P_PREFILL, P_RING_FWD, P_RING_MERGE, P_RING_FUSED, P_COPY, P_GEMM,
+                         P_FWD_ZERO, P_GEMM_ZERO)
              if n in parts]
     for _ in range(args.warmup):
         for n in order:
