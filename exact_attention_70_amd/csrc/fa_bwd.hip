@@ -22,7 +22,7 @@
 //      query tiles; recomputes S = Q K^T and dP = dO V^T with this wave's K
 //      and V rows held in registers, and accumulates dV^T += dO^T P and
 //      dK^T += Q^T dS on the matrix cores.  Q, dO, LSE and D tiles stream into
-//      LDS by buffer->LDS transfers through a four-slot ring, two tiles ahead;
+//      LDS by buffer->LDS transfers through a three-slot ring, one tile ahead;
 //      Q^T and dO^T come from transpose reads.  Iteration i overlaps the
 //      exponentials of tile i-1 with the S / dP matrix ops of tile i.
 // Causal: tiles wholly above the diagonal are skipped; straddling tiles masked.
@@ -59,8 +59,8 @@ __device__ __forceinline__ u32x4 tr_operand(const unsigned char* tile, int u, in
 // Workgroup = 128 keys, eight waves.  Each 32-key block has a dV wave (waves
 // 0-3) and a dK wave (waves 4-7), so a wave holds one of the two gradient
 // accumulators and one of K, V, and two waves share every SIMD.  64-row query
-// tiles (Q, dO, -LSE log2 e, D) stream into a four-slot LDS ring by
-// buffer->LDS transfers, two tiles ahead.  Iteration i:
+// tiles (Q, dO, -LSE log2 e, D) stream into a three-slot LDS ring by
+// buffer->LDS transfers, one tile ahead.  Iteration i:
 //   dV wave: dV^T += dO^T P of tile i-1 (its P kept in registers), then for
 //            tile i S = Q K^T (rows = queries, columns = the block's keys) and
 //            P = exp2(scale log2(e) S - LSE log2(e)), rounded to the element
@@ -71,9 +71,9 @@ __device__ __forceinline__ u32x4 tr_operand(const unsigned char* tile, int u, in
 // So one wave's exponentials run beside the other's matrix ops: matrix,
 // matrix, vector for the dV wave against matrix, vector, matrix for the dK
 // wave.  dO^T and Q^T come from transpose reads.  Both waves issue 32 matrix
-// ops per tile.  P passes through one LDS buffer: the dK wave reads the
-// previous tile's P at the start of an iteration, before a barrier after
-// which the dV wave may overwrite it.
+// ops per tile.  P passes through two LDS buffers (by tile parity), so the
+// dK wave reads tile i-1's while the dV wave writes tile i's and the roles
+// meet at one barrier per iteration.
 constexpr int kKvBN = 128;   // keys per workgroup
 constexpr int kKvBQ = 64;    // queries per inner tile
 constexpr int kKvWaves = 8;
@@ -92,14 +92,15 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
   constexpr int NA = 2 * KSTEPS;           // matrix ops of S (or dP) per tile
   constexpr int NC = NU * DT;              // matrix ops of dV (or dK) per tile
   constexpr int LEAD = 4;                  // operand reads in flight ahead of their matrix op
-  constexpr int VM_TILE = 2 * (TILE / 1024 / kKvWaves) + 2;   // transfers a wave issues per tile
-  __shared__ __attribute__((aligned(1024))) unsigned char sQ0[TILE], sQ1[TILE], sQ2[TILE], sQ3[TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char sO0[TILE], sO1[TILE], sO2[TILE], sO3[TILE];
-  __shared__ __attribute__((aligned(256))) float sL0[kKvBQ], sL1[kKvBQ], sL2[kKvBQ], sL3[kKvBQ];
-  __shared__ __attribute__((aligned(256))) float sD0[kKvBQ], sD1[kKvBQ], sD2[kKvBQ], sD3[kKvBQ];
-  // P of the latest tile for key block b: sP[b][k-step][lane] (16 bytes per
-  // lane and k-step, lane-contiguous: conflict-free 16-byte writes and reads)
-  __shared__ __attribute__((aligned(1024))) u32x4 sP[4][NU][64];
+  __shared__ __attribute__((aligned(1024))) unsigned char sQ0[TILE], sQ1[TILE], sQ2[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char sO0[TILE], sO1[TILE], sO2[TILE];
+  __shared__ __attribute__((aligned(256))) float sL0[kKvBQ], sL1[kKvBQ], sL2[kKvBQ];
+  __shared__ __attribute__((aligned(256))) float sD0[kKvBQ], sD1[kKvBQ], sD2[kKvBQ];
+  // P of tile i for key block b: sPi[b][k-step][lane] with sPi = sP0 for
+  // even i, sP1 for odd i (16 bytes per lane and k-step, lane-contiguous:
+  // conflict-free 16-byte writes and reads).  Two buffers let the dV wave
+  // write tile i's P while the dK wave still reads tile i-1's.
+  __shared__ __attribute__((aligned(1024))) u32x4 sP0[4][NU][64], sP1[4][NU][64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -125,31 +126,27 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
 
   const int q_first = CAUSAL ? kb : 0;            // earlier queries see none of these keys
   const int n_q = (N - q_first + kKvBQ - 1) / kKvBQ;
-  // the ring slot of tile i is i % 4; slots are separate objects so that reads
+  // the ring slot of tile i is i % 3; slots are separate objects so that reads
   // of one are never made to wait for transfers into another
   auto slotQ = [&](auto c) -> unsigned char* {
     if constexpr (decltype(c)::value == 0) return sQ0;
     else if constexpr (decltype(c)::value == 1) return sQ1;
-    else if constexpr (decltype(c)::value == 2) return sQ2;
-    else return sQ3;
+    else return sQ2;
   };
   auto slotO = [&](auto c) -> unsigned char* {
     if constexpr (decltype(c)::value == 0) return sO0;
     else if constexpr (decltype(c)::value == 1) return sO1;
-    else if constexpr (decltype(c)::value == 2) return sO2;
-    else return sO3;
+    else return sO2;
   };
   auto slotL = [&](auto c) -> float* {
     if constexpr (decltype(c)::value == 0) return sL0;
     else if constexpr (decltype(c)::value == 1) return sL1;
-    else if constexpr (decltype(c)::value == 2) return sL2;
-    else return sL3;
+    else return sL2;
   };
   auto slotD = [&](auto c) -> float* {
     if constexpr (decltype(c)::value == 0) return sD0;
     else if constexpr (decltype(c)::value == 1) return sD1;
-    else if constexpr (decltype(c)::value == 2) return sD2;
-    else return sD3;
+    else return sD2;
   };
   // Tiles past the end read as zeros (buffer range check); q0 stays far
   // below 2^31 / (2 D) for any N the library accepts.
@@ -161,7 +158,6 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     dma4(rD, slotD(c), (uint32_t)(q0 + lane) * 4);
   };
   load(0, std::integral_constant<int, 0>{});
-  load(1, std::integral_constant<int, 1>{});
 
   // this wave's 32 keys as B operands (B[k = d][n = key]): K rows for S in a
   // dV wave, V rows for dP in a dK wave
@@ -268,7 +264,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     if (masked) probs(std::integral_constant<bool, true>{});
     else probs(std::integral_constant<bool, false>{});
 #pragma unroll
-    for (int u = 0; u < NU; ++u) sP[blk][u][lane] = pb[u];
+    for (int u = 0; u < NU; ++u) ((i & 1) ? sP1 : sP0)[blk][u][lane] = pb[u];
   };
   // dK wave: tile j (one behind) in ring slot c, with that tile's P in pb
   auto dk_tile = [&](auto c, const u32x4 (&pb)[NU]) __attribute__((always_inline)) {
@@ -292,40 +288,38 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     }
     stage_c(slotQ(c), db);
   };
-  // iteration i: tile i + 2 streams into slot (i + 2) % 4 (which held tile
-  // i - 2, finished last iteration); tile i sits in slot i % 4 and tile i - 1
-  // in slot (i + 3) % 4.  The dK wave takes the P of tile i - 1 into registers
-  // before the mid barrier; the dV wave writes the P of tile i only after it.
-  // The two roles run separate loops (so that neither carries the other's
-  // registers) with the same barriers in the same order.
+  // iteration i: tile i + 1 streams into slot (i + 1) % 3 (which held tile
+  // i - 2, finished last iteration); tile i sits in slot i % 3 and tile i - 1
+  // in slot (i + 2) % 3.  The dV wave writes the P of tile i into the buffer
+  // of i's parity while the dK wave reads that of tile i - 1 from the other,
+  // so the two roles meet only at the barrier that closes an iteration (with
+  // a single P buffer a mid-iteration barrier kept the matrix pipe idle while
+  // the dK wave read P, about a quarter of each iteration).  The two roles
+  // run separate loops (so that neither carries the other's registers) with
+  // the same barriers.
   auto run = [&](auto body) __attribute__((always_inline)) {
     auto iter = [&](int i, auto c) __attribute__((always_inline)) {
       constexpr int C = decltype(c)::value;
-      // issued every iteration (past the end it reads zeros), so that each wave
-      // has exactly one younger tile in flight at the closing barrier
-      load(i + 2, std::integral_constant<int, (C + 2) % 4>{});
-      body(i, c, std::integral_constant<int, (C + 3) % 4>{});
-      barrier_vm_lds<VM_TILE>();   // tile i + 1 landed (tile i + 2 may stream); P of tile i written
+      // issued every iteration (past the end it reads zeros)
+      load(i + 1, std::integral_constant<int, (C + 1) % 3>{});
+      body(i, c, std::integral_constant<int, (C + 2) % 3>{});
+      barrier_all();   // tile i + 1 landed; P of tile i written; slot of tile i - 1 free
     };
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
     using C2 = std::integral_constant<int, 2>;
-    using C3 = std::integral_constant<int, 3>;
     int i = 0;
-    for (; i + 3 <= n_q; i += 4) {
+    for (; i + 2 <= n_q; i += 3) {
       iter(i, C0{});
       iter(i + 1, C1{});
       iter(i + 2, C2{});
-      iter(i + 3, C3{});
     }
     if (i <= n_q) iter(i, C0{});
     if (i + 1 <= n_q) iter(i + 1, C1{});
-    if (i + 2 <= n_q) iter(i + 2, C2{});
   };
   if (!dk_wave) {
     u32x4 pkeep[NU];   // P of the previous tile
     run([&](int i, auto c, auto cprev) __attribute__((always_inline)) {
-      barrier_lds();   // the dK waves have read the previous P
       if (i >= 1) {
         pin_offsets();
         stage_c(slotO(cprev), pkeep);
@@ -334,22 +328,26 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     });
   } else {
     run([&](int i, auto c, auto cprev) __attribute__((always_inline)) {
-      u32x4 pb[NU];
+      if (i >= 1) {
+        u32x4 pb[NU];
 #pragma unroll
-      for (int u = 0; u < NU; ++u) pb[u] = sP[blk][u][lane];
-      barrier_lds();
-      if (i >= 1) dk_tile(cprev, pb);
+        for (int u = 0; u < NU; ++u) pb[u] = ((i & 1) ? sP0 : sP1)[blk][u][lane];
+        dk_tile(cprev, pb);
+      }
     });
   }
 
   // store: lane holds key my_k, rows d = 32t + 8g + 4*half + (0..3).  Once
   // the last transfers have landed and every wave is done with the rings, each
-  // wave stages its 32 x D tile in one ring slot (sQ0..3 for the dV waves,
-  // sO0..3 for the dK waves) and stores it as whole rows.
+  // wave stages its 32 x D tile in one ring slot or P buffer (sQ0..2 and sP0
+  // for the dV waves, sO0..2 and sP1 for the dK waves) and stores it as whole
+  // rows.
   static_assert(32 * D * 4 == TILE, "one wave's fp32 tile per ring slot");
+  static_assert(sizeof(sP0) >= 32 * D * 4, "one wave's fp32 tile per P buffer");
   barrier_all();
-  unsigned char* stage = dk_wave ? (blk == 0 ? sO0 : blk == 1 ? sO1 : blk == 2 ? sO2 : sO3)
-                                 : (blk == 0 ? sQ0 : blk == 1 ? sQ1 : blk == 2 ? sQ2 : sQ3);
+  unsigned char* stage =
+      dk_wave ? (blk == 0 ? sO0 : blk == 1 ? sO1 : blk == 2 ? sO2 : (unsigned char*)sP1)
+              : (blk == 0 ? sQ0 : blk == 1 ? sQ1 : blk == 2 ? sQ2 : (unsigned char*)sP0);
   store_rows_f32<D, DT>(acc, dk_wave ? scale : 1.f, stage, dk_wave ? rdK : rdV,
                         kb + blk * 32, lane);
 }
