@@ -171,7 +171,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const typename E::elem* __restrict__ Q, const typename E::elem* __restrict__ K,
     const typename E::elem* __restrict__ V, typename E::elem* __restrict__ O,
     float* __restrict__ LSE, int N, int Nk, int delta, float scale_log2, int n_qtiles, PagedKV pg,
-    int hgroup, int acc) {
+    int hgroup, int acc, int snake) {
   // scale_log2 = scale * log2(e): scores are handled in base 2.  N query rows
   // and Nk key rows per head; with CAUSAL, key j is visible to row i iff
   // j <= i + delta.  PAGED: one (sequence, head) per bh; N, Nk and delta are
@@ -219,8 +219,16 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     tile1 = base + n_qtiles - 1 - r;
     npass = tile1 != tile0 ? 2 : 1;
   } else {
-    tile0 = hgroup > 0 ? xcd_grouped(blockIdx.x, n_qtiles, hgroup)
-                       : xcd_remap(blockIdx.x, gridDim.x);
+    // snake != 0 (grouped order, whole grid resident, 32 k slots per XCD):
+    // compute unit j of an XCD holds that XCD's slots j, j + 32, j + 64, ...,
+    // so every other round of 32 slots is taken in reverse, and each unit
+    // gets long and short tiles instead of all long or all short ones
+    int b = blockIdx.x;
+    if (snake) {
+      const int xs = b >> 3, r = xs >> 5, p = xs & 31;
+      b = (((r & 1) ? (r << 5) + 31 - p : xs) << 3) | (b & 7);
+    }
+    tile0 = hgroup > 0 ? xcd_grouped(b, n_qtiles, hgroup) : xcd_remap(b, gridDim.x);
   }
   // The softmax takes its maximum over raw scores and folds the scale into one
   // multiply-add, which needs a positive multiplier: for a negative scale,
@@ -1006,10 +1014,12 @@ hipError_t launch_bf16_as(const FwdArgs& a, int Nk, int delta) {
   // and 4096 keys)
   if constexpr (D == 64 && NW == 4 && !PAIRED) {
     if (Nk <= 1024) {
+      // three workgroups per CU: a grid of at most 768 is resident at once
+      const int snake = hg > 0 && units % 256 == 0 && units <= 3 * 256;
       hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, kBNDefault, 3, false, false, 4, false, true>),
                          dim3((int)units), dim3(64 * NW), 0, a.stream, (const T*)a.Q, (const T*)a.K,
                          (const T*)a.V, (T*)a.O, a.LSE, a.N, Nk, delta, a.scale * kLog2e, n_qtiles,
-                         PagedKV{}, hg, a.accumulate ? 1 : 0);
+                         PagedKV{}, hg, a.accumulate ? 1 : 0, snake);
       return hipGetLastError();
     }
   }
@@ -1017,7 +1027,7 @@ hipError_t launch_bf16_as(const FwdArgs& a, int Nk, int delta) {
   hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, kBNDefault, 8 / NW, false, PAIRED, NW>),
                      dim3((int)units), dim3(64 * NW), 0, a.stream, (const T*)a.Q, (const T*)a.K,
                      (const T*)a.V, (T*)a.O, a.LSE, a.N, Nk, delta, a.scale * kLog2e, n_qtiles,
-                     PagedKV{}, hg, a.accumulate ? 1 : 0);
+                     PagedKV{}, hg, a.accumulate ? 1 : 0, 0);
   return hipGetLastError();
 }
 
@@ -1051,11 +1061,11 @@ hipError_t launch_paged(const FwdArgs& a) {
   if (flat)
     hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, kBNDefault, 2, true, false, NW, true>),
                        dim3(grid), dim3(64 * NW), 0, a.stream, (const T*)a.Q, (const T*)a.K,
-                       (const T*)a.V, (T*)a.O, a.LSE, 0, 0, 0, a.scale * kLog2e, n_qtiles, pg, hg, 0);
+                       (const T*)a.V, (T*)a.O, a.LSE, 0, 0, 0, a.scale * kLog2e, n_qtiles, pg, hg, 0, 0);
   else
     hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, kBNDefault, 2, true, false, NW>), dim3(grid),
                        dim3(64 * NW), 0, a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V,
-                       (T*)a.O, a.LSE, 0, 0, 0, a.scale * kLog2e, n_qtiles, pg, hg, 0);
+                       (T*)a.O, a.LSE, 0, 0, 0, a.scale * kLog2e, n_qtiles, pg, hg, 0, 0);
   return hipGetLastError();
 }
 
