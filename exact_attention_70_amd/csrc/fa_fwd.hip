@@ -1035,7 +1035,11 @@ template <class E, int D, bool CAUSAL>
 hipError_t launch_bf16(const FwdArgs& a, int Nk, int delta) {
   const FwdPlan p = fwd_plan((long long)a.B * a.H, a.N, CAUSAL);
   if constexpr (CAUSAL) {
-    if (p.paired)
+    // d = 64 rows of at most 1024 keys take the unpaired one-stage kernel
+    // even where 4-wave tiles would pair: 7-15% faster at B16-B64 H12-H16
+    // N512-N1024 (three workgroups per CU balance the tile lengths well)
+    const bool one_stage = D == 64 && p.nw == 4 && Nk <= 1024;
+    if (p.paired && !one_stage)
       return p.nw == 8 ? launch_bf16_as<E, D, true, 8, true>(a, Nk, delta)
                        : launch_bf16_as<E, D, true, 4, true>(a, Nk, delta);
   }

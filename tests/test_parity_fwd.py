@@ -126,11 +126,12 @@ def test_fwd_256_row_workgroups_sampled(gpu, d, causal, N):
 
 # Shorter sequences with many heads run in 128-row workgroups with paired
 # causal tiles, once the paired grid still leaves four workgroups per compute
-# unit (heads x ceil(query tiles / 2) >= 1024).  1900 rows leave a ragged
-# 108-row tile and an odd tile count (one workgroup runs the middle tile
-# alone); one case takes a negative scale.
+# unit (heads x ceil(query tiles / 2) >= 1024); at d = 64 only above 1024 keys
+# (shorter rows take the unpaired one-stage kernel, as the next test checks).
+# 1900 and 1100 rows leave ragged tiles and odd tile counts (one workgroup
+# runs the middle tile alone); one case takes a negative scale.
 @pytest.mark.parametrize("B,H,N,d,sign", [(8, 16, 2048, 128, 1), (8, 16, 1900, 128, -1),
-                                          (8, 32, 1000, 64, 1)])
+                                          (8, 32, 1100, 64, 1)])
 def test_fwd_paired_128_row_workgroups_sampled(gpu, B, H, N, d, sign):
     x = workloads.attention_inputs(B, H, N, d, "bf16", seed=73000 + N + d)
     scale = sign * d ** -0.5
@@ -140,6 +141,23 @@ def test_fwd_paired_128_row_workgroups_sampled(gpu, B, H, N, d, sign):
     rows = np.unique(np.concatenate([[0, 1, 127, 128, 129, N // 2, N - 1],
                                      rng.integers(0, N, 20)]))
     _check(x, o, lse, True, scale, TOL["bf16"], rows=rows)
+
+
+# d = 64 rows of at most 1024 keys: the unpaired one-stage kernel at three
+# workgroups per compute unit, also where 128-row tiles would pair; 768
+# workgroups (a whole grid resident at once) take the reversed-round order.
+@pytest.mark.parametrize("B,H,N,causal", [(8, 32, 1000, True), (8, 12, 1024, True),
+                                          (2, 12, 1024, False), (64, 12, 128, True)])
+def test_fwd_one_stage_d64_sampled(gpu, B, H, N, causal):
+    d = 64
+    x = workloads.attention_inputs(B, H, N, d, "bf16", seed=74000 + N + B)
+    scale = d ** -0.5
+    o, lse = _gpu_fwd(gpu, x, causal, scale)
+    _check(x, o, lse, causal, scale, TOL["bf16"], heads=[(0, 0), (B - 1, H - 1), (B // 2, H // 2)])
+    rng = np.random.default_rng(N + B)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, N // 2, N - 1],
+                                     rng.integers(0, N, 16)]))
+    _check(x, o, lse, causal, scale, TOL["bf16"], rows=rows[rows < N])
 
 
 def test_fwd_deterministic(gpu):
