@@ -47,6 +47,7 @@ namespace fa {
 namespace {
 
 constexpr int kBNDefault = 64;   // keys per K/V tile
+constexpr int kOneStageMaxKeys = 4096;   // d = 64 rows up to this many keys: one-stage loop
 
 constexpr int kKLead = 3;        // K operand reads in flight ahead of their matrix op
 constexpr int kVLead = 2;        // V operand read pairs in flight ahead of their matrix op
@@ -1008,12 +1009,11 @@ hipError_t launch_bf16_as(const FwdArgs& a, int Nk, int delta) {
   const long long units = (long long)a.B * a.H * (PAIRED ? (n_qtiles + 1) / 2 : n_qtiles);
   // causal tiles differ in length: interleave heads so long tiles start first
   const int hg = CAUSAL ? xcd_group((long long)a.B * a.H, (long long)Nk * D * 4) : 0;
-  // d = 64 with at most 1024 keys: the one-stage loop at three waves per
-  // SIMD (122 registers), 7-18% faster on such shapes; with longer rows the
-  // two-stage loop's own overlap is worth more (1-2% the other way at 2048
-  // and 4096 keys)
+  // d = 64 with at most 4096 keys: the one-stage loop at three waves per
+  // SIMD (122 registers), 3-18% faster on such shapes (B8 H32 N2048 causal
+  // 215 -> 198 us); longer rows keep the two-stage loop
   if constexpr (D == 64 && NW == 4 && !PAIRED) {
-    if (Nk <= 1024) {
+    if (Nk <= kOneStageMaxKeys) {
       // three workgroups per CU: a grid of at most 768 is resident at once
       const int snake = hg > 0 && units % 256 == 0 && units <= 3 * 256;
       hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, kBNDefault, 3, false, false, 4, false, true>),
@@ -1035,10 +1035,10 @@ template <class E, int D, bool CAUSAL>
 hipError_t launch_bf16(const FwdArgs& a, int Nk, int delta) {
   const FwdPlan p = fwd_plan((long long)a.B * a.H, a.N, CAUSAL);
   if constexpr (CAUSAL) {
-    // d = 64 rows of at most 1024 keys take the unpaired one-stage kernel
+    // d = 64 rows of at most 4096 keys take the unpaired one-stage kernel
     // even where 4-wave tiles would pair: 7-15% faster at B16-B64 H12-H16
     // N512-N1024 (three workgroups per CU balance the tile lengths well)
-    const bool one_stage = D == 64 && p.nw == 4 && Nk <= 1024;
+    const bool one_stage = D == 64 && p.nw == 4 && Nk <= kOneStageMaxKeys;
     if (p.paired && !one_stage)
       return p.nw == 8 ? launch_bf16_as<E, D, true, 8, true>(a, Nk, delta)
                        : launch_bf16_as<E, D, true, 4, true>(a, Nk, delta);

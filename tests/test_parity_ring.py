@@ -183,6 +183,16 @@ def test_fwd_offset_256_row_workgroups(gpu, Nq, Nk, qo, ko):
                   rows=rows)
 
 
+def test_fwd_offset_paired_d64_long_keys(gpu):
+    """d = 64 queries over more than 4096 keys with many heads: 128-row
+    workgroups with paired causal tiles (the one-stage kernel stops at 4096
+    keys); every row sees the 4000 keys before its own block."""
+    x = _inputs(1100, 5000, 64, "bf16", seed=3700, B=8, H=32)
+    rows = np.unique(np.r_[0:3, 127:130, 549:552, 1023:1026, 1097:1100])
+    _check_offset(gpu, x, 3900, 0, True, 64 ** -0.5, TOL["bf16"], heads=[(0, 0), (7, 31), (3, 17)],
+                  rows=rows)
+
+
 # ---------------------------------------------------------------- fused step
 # fa_fwd_offset_accumulate: the forward of one key/value block merged at once
 # into a running result.  A contiguous key block split in two (A, then B at
