@@ -365,8 +365,10 @@ constexpr int kQBN = 64;    // keys per tile
 // and -LSE log2(e), which it writes for the dK/dV kernel: each lane holds half
 // of its row's dO as B operands, loads the same half of O, and the two halves
 // meet in one cross-lane exchange.
+// d = 64 fits in 168 registers (160-166), so three workgroups share a CU
+// (the d = 64 backward 1-7% faster); d = 128 needs all 256 for two.
 template <class E, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 2)) void bwd_dq_kernel(
     const typename E::elem* __restrict__ Q, const typename E::elem* __restrict__ K,
     const typename E::elem* __restrict__ V, const typename E::elem* __restrict__ O,
     const typename E::elem* __restrict__ dO, const float* __restrict__ LSE,
