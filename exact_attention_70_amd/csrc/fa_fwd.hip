@@ -11,7 +11,8 @@
 // HBM).  The tiling itself is this file's own design for CDNA4.
 //
 // Work decomposition (bf16 kernel)
-//   * one workgroup = 4 waves = a 128-row query tile of one (batch, head);
+//   * one workgroup = 4 or 8 waves = a 128- or 256-row query tile of one
+//     (batch, head) (8 waves for long sequences, causal tiles then paired);
 //     wave w owns query rows [32w, 32w + 32) of the tile and keeps them in
 //     registers as the B operands of S^T = K Q^T (loaded once from HBM).
 //   * K/V stream through LDS in 64-key tiles by buffer-to-LDS DMA, one tile
@@ -30,7 +31,10 @@
 //     those exponentials.  The probabilities are taken against a per-row
 //     reference maximum that moves (and rescales the accumulated output) only
 //     when a probability could exceed 2^kSlack, which the running probability
-//     sum reveals without a per-tile maximum (see kSlack).
+//     sum reveals without a per-tile maximum (see kSlack).  At d = 64 most
+//     launches use a one-stage loop instead (each tile's scores, probabilities
+//     and P V in turn), whose smaller register set lets more waves share a
+//     SIMD (see SIMPLE).
 //   * causal: key tiles entirely above the diagonal are never visited; only
 //     tiles that straddle the diagonal (or the ragged end) are masked, in a
 //     separate tail of the loop.
