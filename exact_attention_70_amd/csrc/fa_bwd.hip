@@ -11,7 +11,8 @@
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Two kernels, both on the caller's stream, deterministic (no atomics):
-//   1. bwd_dq:   workgroup = 128 queries (wave = 32); loops over 64-key K/V tiles;
+//   1. bwd_dq:   workgroup = 128 queries (wave = 32; two workgroups per CU,
+//      three at d = 64); loops over 64-key K/V tiles;
 //      recomputes S^T = K Q^T and dP^T = V dO^T (each lane then holds one
 //      query's row, so LSE_i and D_i are per-lane scalars) and accumulates
 //      dQ^T += K^T dS^T.  Within a tile the exponentials run between the dP
@@ -23,8 +24,9 @@
 //      and V rows held in registers, and accumulates dV^T += dO^T P and
 //      dK^T += Q^T dS on the matrix cores.  Q, dO, LSE and D tiles stream into
 //      LDS by buffer->LDS transfers through a three-slot ring, one tile ahead;
-//      Q^T and dO^T come from transpose reads.  Iteration i overlaps the
-//      exponentials of tile i-1 with the S / dP matrix ops of tile i.
+//      Q^T and dO^T come from transpose reads.  Each 32-key block has a dV
+//      wave and a dK wave on one SIMD (P passes between them through LDS),
+//      so one wave's exponentials run beside the other's matrix ops.
 // Causal: tiles wholly above the diagonal are skipped; straddling tiles masked.
 #include "fa_device.h"
 #include "fa_internal.h"
