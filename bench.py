@@ -44,6 +44,7 @@ P_BWD4 = "bwd_causal_b4h16n2048d128"
 P_COPY = "copy_calib"
 P_GEMM = "ref_gemm_bf16_m8192n8192k8192"
 P_GEMM_ZERO = "ref_gemm_bf16_m8192n8192k8192_zero_inputs"
+P_READ = "ref_rowmax_bf16_4gib"
 P_DEC = "decode_s64h32d128"
 P_DEC_GQA = "decode_gqa_s64h32kv8d128"
 P_FWD = "fwd_causal_b1h32n8192d128"
@@ -139,7 +140,9 @@ def main():
                          "vendor library's bf16 GEMM on random operands, a reference point), copy_calib (a 1 GiB device copy "
                          "used to scale the HBM-traffic counters); and, to show how the rate depends on the "
                          "operand data, fwd_causal_b1h32n8192d128_zero_inputs and "
-                         "ref_gemm_bf16_m8192n8192k8192_zero_inputs (the same work on all-zero inputs). "
+                         "ref_gemm_bf16_m8192n8192k8192_zero_inputs (the same work on all-zero inputs); "
+                         "ref_rowmax_bf16_4gib (the library's row maximum over 4 GiB of bf16, a plain "
+                         "streaming read for comparison with the decode). "
                          "The reference and zero-input parts run only when named here.")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -313,6 +316,11 @@ def main():
         gb = torch.randn(8192, 8192, generator=gen).to(torch.bfloat16).to(dev)
         gc = torch.empty(8192, 8192, dtype=torch.bfloat16, device=dev)
         parts[P_GEMM] = dict(fn=lambda: torch.mm(ga, gb, out=gc), flops=2 * 8192 ** 3)
+    if P_READ in only:
+        # reference point, not the hot path: a plain streaming read by the
+        # vendor library (torch.amax over rows of a 4 GiB bf16 tensor)
+        rx = torch.ones(1 << 31, dtype=torch.bfloat16, device=dev).view(-1, 4096)
+        parts[P_READ] = dict(fn=lambda: torch.amax(rx, dim=1), bytes=rx.numel() * 2)
     if P_GEMM_ZERO in only:
         za = torch.zeros(8192, 8192, dtype=torch.bfloat16, device=dev)
         zb = torch.zeros_like(za)
@@ -333,7 +341,7 @@ def main():
 
     order = [n for n in (P_FWD, P_FWD16, P_FWD_GPT2, P_FWD4, P_BWD4, P_DEC, P_DEC_GQA, P_APPEND,
                          P_PREFILL, P_RING_FWD, P_RING_MERGE, P_RING_FUSED, P_COPY, P_GEMM,
-                         P_FWD_ZERO, P_GEMM_ZERO)
+                         P_FWD_ZERO, P_GEMM_ZERO, P_READ)
              if n in parts]
     for _ in range(args.warmup):
         for n in order:
