@@ -320,15 +320,17 @@ def test_ring_step_long_context_fused(gpu):
         assert max_abs(l[b, h].double().cpu().numpy()[rows], rl) <= 2e-2
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("Nq,Nk,qo,ko", [(4100, 4100, 1000, 0), (4100, 4096, 0, 1000)])
-def test_fwd_offset_accumulate_256_row_workgroups(gpu, Nq, Nk, qo, ko):
-    """The fused step on the paired 256-row causal kernel: the key block split
-    in two halves, the second accumulated into the first's result, against the
-    oracle over the whole block on sampled heads and rows."""
-    x = _inputs(Nq, Nk, 128, "bf16", seed=4100 + qo, H=32)
+def test_fwd_offset_accumulate_256_row_workgroups(gpu, Nq, Nk, qo, ko, d):
+    """The fused step on the paired 256-row causal kernel (at d = 64 its
+    one-stage form, four waves per SIMD): the key block split in two halves,
+    the second accumulated into the first's result, against the oracle over
+    the whole block on sampled heads and rows."""
+    x = _inputs(Nq, Nk, d, "bf16", seed=4100 + qo + d, H=32)
     q, k, v = (x[n].to(gpu) for n in "qkv")
     n1 = Nk // 2
-    scale = 128 ** -0.5
+    scale = d ** -0.5
     o, lse = binding.fwd_offset(q, k[:, :, :n1].contiguous(), v[:, :, :n1].contiguous(),
                                 q_offset=qo, k_offset=ko, causal=True, scale=scale)
     binding.fwd_offset_accumulate(q, k[:, :, n1:].contiguous(), v[:, :, n1:].contiguous(), o, lse,
