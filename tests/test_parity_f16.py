@@ -55,10 +55,12 @@ def test_fwd_f16(gpu, d, causal, N):
 
 # The fp16 forward on the launches of longer sequences: 256-row workgroups
 # (paired when causal) and, for many heads below 4096 rows, paired 128-row
-# workgroups.  Ragged last tiles and odd tile counts; sampled heads and rows.
+# workgroups at d = 128; at d = 64 the one-stage kernel (256-row workgroups
+# paired, 128-row ones never).  Ragged last tiles and odd tile counts; sampled
+# heads and rows.
 @pytest.mark.parametrize("B,H,N,d,causal", [
     (1, 32, 4100, 128, True), (8, 16, 1900, 128, True),      # 256-row / 128-row paired
-    (1, 32, 4100, 64, True), (8, 32, 1000, 64, True),
+    (1, 32, 4100, 64, True), (8, 32, 1000, 64, True),        # one-stage: 256-row paired / 128-row
     (1, 16, 4096, 128, False), (1, 16, 4100, 64, False),     # 256-row, not paired
 ])
 def test_fwd_f16_long_launches_sampled(gpu, B, H, N, d, causal):
