@@ -132,17 +132,26 @@ __device__ __forceinline__ void dma_rows_paged_flat(__amdgpu_buffer_rsrc_t pool,
   static_assert(16 % RPI == 0 && NI % NWAVES == 0, "instruction rows must stay inside a block");
   static_assert(ROWS == 64, "a tile spans four blocks");
   const uint32_t blk_bytes = (uint32_t)16 * KVH * D * 2;
+  // the tile's four block bases, once per call: an id outside the pool maps
+  // to 2^31, past the pool (the flat path serves pools of at most 2^31
+  // bytes), and stays there with the lane's in-block offset added
+  uint32_t base[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    base[q] = (unsigned)ids.b[q] < (unsigned)num_blocks ? (uint32_t)ids.b[q] * blk_bytes : 0x80000000u;
+  // with the wave index known to be below NWAVES, each instruction's block
+  // is a constant (or a choice of two) instead of a select over all four
+  __builtin_assume(wave >= 0 && wave < NWAVES);
 #pragma unroll
   for (int ii = 0; ii < NI / NWAVES; ++ii) {
     const int ins = ii * NWAVES + wave;
     const int bi = (ins * RPI) >> 4;                // block of this instruction within the tile
-    const int phys = bi == 0 ? ids.b[0] : bi == 1 ? ids.b[1] : bi == 2 ? ids.b[2] : ids.b[3];
+    const uint32_t bb = bi == 0 ? base[0] : bi == 1 ? base[1] : bi == 2 ? base[2] : base[3];
     const int rr = ins * RPI + lane / DCH;          // LDS row written by this lane
     const int tok = row0 + rr;
     const int c = (lane % DCH) ^ tile_swz<D>(rr);
-    const bool ok = (unsigned)phys < (unsigned)num_blocks && tok < n_tok;
-    const uint32_t off = (uint32_t)phys * blk_bytes + (uint32_t)(((tok & 15) * KVH + kvh) * D + c * 8) * 2;
-    dma16(pool, lds + ins * 1024, ok ? off : 0x80000000u);
+    const uint32_t off = bb + (uint32_t)(((tok & 15) * KVH + kvh) * D + c * 8) * 2;
+    dma16(pool, lds + ins * 1024, tok < n_tok ? off : 0x80000000u);
   }
 }
 
