@@ -98,11 +98,15 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) unsigned char sO0[TILE], sO1[TILE], sO2[TILE];
   __shared__ __attribute__((aligned(256))) float sL0[kKvBQ], sL1[kKvBQ], sL2[kKvBQ];
   __shared__ __attribute__((aligned(256))) float sD0[kKvBQ], sD1[kKvBQ], sD2[kKvBQ];
-  // P of tile i for key block b: sPi[b][k-step][lane] with sPi = sP0 for
-  // even i, sP1 for odd i (16 bytes per lane and k-step, lane-contiguous:
+  // P of tile i for key block b: sP[i & 1][b][k-step][lane] (16 bytes per
+  // lane and k-step, lane-contiguous:
   // conflict-free 16-byte writes and reads).  Two buffers let the dV wave
   // write tile i's P while the dK wave still reads tile i-1's.
-  __shared__ __attribute__((aligned(1024))) u32x4 sP0[4][NU][64], sP1[4][NU][64];
+  // One object indexed by the tile's parity, not two chosen by a select: a
+  // pointer chosen between two objects may point at either, so the compiler
+  // cannot tell it from the ring slots and made the P accesses wait for every
+  // transfer in flight (the next tile's included).
+  __shared__ __attribute__((aligned(1024))) u32x4 sP[2][4][NU][64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -266,7 +270,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     if (masked) probs(std::integral_constant<bool, true>{});
     else probs(std::integral_constant<bool, false>{});
 #pragma unroll
-    for (int u = 0; u < NU; ++u) ((i & 1) ? sP1 : sP0)[blk][u][lane] = pb[u];
+    for (int u = 0; u < NU; ++u) sP[i & 1][blk][u][lane] = pb[u];
   };
   // dK wave: tile j (one behind) in ring slot c, with that tile's P in pb
   auto dk_tile = [&](auto c, const u32x4 (&pb)[NU]) __attribute__((always_inline)) {
@@ -333,7 +337,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
       if (i >= 1) {
         u32x4 pb[NU];
 #pragma unroll
-        for (int u = 0; u < NU; ++u) pb[u] = ((i & 1) ? sP0 : sP1)[blk][u][lane];
+        for (int u = 0; u < NU; ++u) pb[u] = sP[(i & 1) ^ 1][blk][u][lane];
         dk_tile(cprev, pb);
       }
     });
@@ -341,15 +345,15 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
 
   // store: lane holds key my_k, rows d = 32t + 8g + 4*half + (0..3).  Once
   // the last transfers have landed and every wave is done with the rings, each
-  // wave stages its 32 x D tile in one ring slot or P buffer (sQ0..2 and sP0
-  // for the dV waves, sO0..2 and sP1 for the dK waves) and stores it as whole
+  // wave stages its 32 x D tile in one ring slot or P buffer (sQ0..2 and sP[0]
+  // for the dV waves, sO0..2 and sP[1] for the dK waves) and stores it as whole
   // rows.
   static_assert(32 * D * 4 == TILE, "one wave's fp32 tile per ring slot");
-  static_assert(sizeof(sP0) >= 32 * D * 4, "one wave's fp32 tile per P buffer");
+  static_assert(sizeof(sP[0]) >= 32 * D * 4, "one wave's fp32 tile per P buffer");
   barrier_all();
   unsigned char* stage =
-      dk_wave ? (blk == 0 ? sO0 : blk == 1 ? sO1 : blk == 2 ? sO2 : (unsigned char*)sP1)
-              : (blk == 0 ? sQ0 : blk == 1 ? sQ1 : blk == 2 ? sQ2 : (unsigned char*)sP0);
+      dk_wave ? (blk == 0 ? sO0 : blk == 1 ? sO1 : blk == 2 ? sO2 : (unsigned char*)sP[1])
+              : (blk == 0 ? sQ0 : blk == 1 ? sQ1 : blk == 2 ? sQ2 : (unsigned char*)sP[0]);
   store_rows_f32<D, DT>(acc, dk_wave ? scale : 1.f, stage, dk_wave ? rdK : rdV,
                         kb + blk * 32, lane);
 }
