@@ -151,6 +151,8 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
   if (dtype == FA_DT_F32) return FA_ERR_UNSUPPORTED;   // 16-bit inputs only
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (!head_fits(N, d, 4)) return FA_ERR_SHAPE;
+  // one workgroup per 128-row tile of every head in each of the two kernels
+  if ((long long)B * H * ((N + 127) / 128) >= (1LL << 31)) return FA_ERR_SHAPE;
   if (B == 0) return FA_OK;
   if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL;
   if (!workspace || workspace_bytes < fa_bwd_workspace_size(B, H, N, d)) return FA_ERR_WORKSPACE;
@@ -186,6 +188,8 @@ int check_decode_args(const void* q, const void* k_pool, const void* v_pool,
       block_size < 1)
     return FA_ERR_SHAPE;
   if (H % KVH != 0) return FA_ERR_SHAPE;
+  // (sequence, head) pairs are counted in 32-bit integers by the launches
+  if ((long long)num_seqs * H >= (1LL << 30)) return FA_ERR_SHAPE;
   if (!std::isfinite(scale)) return FA_ERR_SHAPE;
   if (dtype == FA_DT_F32 || block_size != 16 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
   const long long block_bytes = (long long)block_size * KVH * d * 2;

@@ -191,6 +191,7 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  *   dQ, dK, dV      out  [B,H,N,d] fp32 (fully overwritten)
  *   d               64 or 128; dtype FA_DT_BF16 or FA_DT_F16 (16-bit inputs)
  *   workspace       device buffer of >= fa_bwd_workspace_size() bytes, 16-B aligned
+ *   B * H * ceil(N / 128) < 2^31 (workgroups per kernel), else FA_ERR_SHAPE
  * The result is deterministic (no atomics).
  */
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
@@ -236,7 +237,8 @@ size_t fa_paged_decode_workspace_size(int num_seqs, int H, int d, int max_blocks
  *   o            out  [num_seqs, H, d], same dtype
  *   lse          out  [num_seqs, H] fp32 (natural log)
  *   block_size   16 (else FA_ERR_UNSUPPORTED); d 64 or 128 (else FA_ERR_UNSUPPORTED)
- *   H            >= 1 (any count; a wave's lanes past H idle)
+ *   H            >= 1 (any count; a wave's lanes past H idle); num_seqs * H < 2^30
+ *                (else FA_ERR_SHAPE)
  *   workspace    >= fa_paged_decode_workspace_size() bytes, 16-B aligned
  * The contents of block_table and seq_lens are trusted like a page table.
  * With the environment variable FA_DEBUG=1 they are copied to the host and

@@ -113,6 +113,9 @@ int main() {
          FA_ERR_SHAPE);
   EXPECT(fa_bwd(P, P, P, MIS, P, F, g, g, g, 2, 3, 100, 128, 0.1f, 1, 1, W, ws, nullptr),
          FA_ERR_ALIGN);
+  EXPECT(fa_bwd(P, P, P, P, P, F, g, g, g, 1 << 12, 1 << 12, 128 * 128, 128, 0.1f, 1, 1, W, ws,
+                nullptr),
+         FA_ERR_SHAPE);   // 2^31 workgroups per kernel
 
   // ---- decode (workspace and static-scratch entry points)
   const size_t dws = fa_paged_decode_workspace_size(64, 32, 128, 256, 16);
@@ -140,6 +143,9 @@ int main() {
   EXPECT(fa_paged_decode_gqa(P, P, P, I, I, 16, 64, 32, 5, 128, 256, 9000, 0.088f, P2, F, 1, W,
                              dws, nullptr),
          FA_ERR_SHAPE);
+  EXPECT(fa_paged_decode_gqa(P, P, P, I, I, 16, 1 << 25, 32, 8, 128, 256, 9000, 0.088f, P2, F, 1,
+                             W, dws, nullptr),
+         FA_ERR_SHAPE);   // num_seqs * H >= 2^30
   EXPECT(fa_paged_decode_gqa(P, P, P, I, I, 16, 64, 32, 8, 128, 256, 9000, 0.088f, P2, F, 1, W,
                              dws, nullptr),
          FA_OK);

@@ -144,8 +144,8 @@ def test_bwd_validation(lib):
     assert ws >= 2 * (2 * 3 * 100 * 4) and ws % 256 == 0
     assert lib.fa_bwd_workspace_size(0, 3, 100, 128) == 0
 
-    def bwd(dt=1, d=128, N=100, ws_ptr=P2, ws_bytes=ws, dq=P2, B=2, scale=0.1):
-        return lib.fa_bwd(P, P, P, P, P, P, dq, P2, P2, B, 3, N, d, scale, 1, dt, ws_ptr,
+    def bwd(dt=1, d=128, N=100, ws_ptr=P2, ws_bytes=ws, dq=P2, B=2, H=3, scale=0.1):
+        return lib.fa_bwd(P, P, P, P, P, P, dq, P2, P2, B, H, N, d, scale, 1, dt, ws_ptr,
                           ws_bytes, None)
     assert bwd(dt=0) == ERR_UNSUP          # fp32 backward not provided
     assert bwd(dt=5) == ERR_DTYPE
@@ -156,6 +156,8 @@ def test_bwd_validation(lib):
     assert bwd(dq=None) == ERR_NULL
     assert bwd(dq=MIS) == ERR_ALIGN
     assert bwd(scale=float("nan")) == ERR_SHAPE
+    # workgroup counts past 2^31 are refused before the workspace is looked at
+    assert bwd(B=1 << 12, H=1 << 12, N=128 * 128) == ERR_SHAPE
     assert bwd(B=0) == OK
 
 
@@ -209,6 +211,7 @@ def test_paged_decode_gqa_validation(lib):
     assert gqa(lib, d=80) == ERR_UNSUP
     assert gqa(lib, q=None) == ERR_NULL
     assert gqa(lib, S=0, q=None) == OK
+    assert gqa(lib, S=1 << 25, H=32, KVH=8) == ERR_SHAPE    # num_seqs * H >= 2^30
 
 
 def noalloc(lib, H=32, KVH=32, d=128, bs=16, dt=1, S=4, q=P):
