@@ -73,7 +73,43 @@ struct PagedKV {
   int H, KVH, max_blocks, num_blocks;
   int total_q;          // rows of the packed Q/O/LSE
   uint32_t pool_bytes;  // bytes of one pool when at most 2^31 (one resource per pool), else 0
+  int num_seqs;
 };
+
+// Up to this many sequences, a prefill takes them longest first.
+constexpr int kOrderSeqs = 64;
+
+// The sequence at position p of a prefill's work order, and its chunk's first
+// packed row, chunk length and cached length.  With at most kOrderSeqs
+// sequences the order is by the keys an average query tile of the chunk reads
+// (cached tokens minus half the chunk), most first, ties by index, so that the
+// workgroups of the longest sequences start first rather than leave a tail
+// behind them; lane i of the wave reads sequence i's entries and ranks it
+// against the others, so the ranking costs no memory round trip beyond the
+// one that fetches the chosen sequence's entries.  With more sequences they
+// keep their own order.
+struct SeqPick {
+  int seq, q_begin, q_end, len;
+};
+__device__ __forceinline__ SeqPick pick_sequence(const PagedKV& pg, int p, int lane) {
+  if (pg.num_seqs > kOrderSeqs)
+    return SeqPick{p, pg.q_start[p], pg.q_start[p + 1], pg.seq_lens[p]};
+  const bool live = lane < pg.num_seqs;
+  const int qb = live ? pg.q_start[lane] : 0;
+  const int qe = live ? pg.q_start[lane + 1] : 0;
+  const int L = live ? pg.seq_lens[lane] : 0;
+  const int key = L - (qe - qb) / 2;
+  int rank = 0;
+  for (int j = 0; j < pg.num_seqs; ++j) {
+    const int kj = __builtin_amdgcn_readlane(key, j);
+    rank += (kj > key || (kj == key && j < lane)) ? 1 : 0;
+  }
+  // the ranks of the live lanes are 0 .. num_seqs - 1, each once
+  const unsigned long long hit = __ballot(live && rank == p);
+  const int s = hit ? (int)__builtin_ctzll(hit) : p;
+  return SeqPick{s, __builtin_amdgcn_readlane(qb, s), __builtin_amdgcn_readlane(qe, s),
+                 __builtin_amdgcn_readlane(L, s)};
+}
 
 // Physical ids of the four 16-token blocks one 64-key tile spans (-1: past
 // the sequence's table row).
@@ -278,12 +314,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const int32_t* table_row = nullptr;
     int kvh = 0;
     if constexpr (PAGED) {
-      const int seq = bh / pg.H, h = bh % pg.H;
-      const int qs = pg.q_start[seq];
-      N = pg.q_start[seq + 1] - qs;
+      const int h = bh % pg.H;
+      const SeqPick sp = pick_sequence(pg, bh / pg.H, lane);
+      const int seq = sp.seq, qs = sp.q_begin;
+      N = sp.q_end - qs;
       // a length past the table row is clamped to the row's capacity (as the
       // decode does), so a corrupt length costs at most one row of blocks
-      Nk = min(pg.seq_lens[seq], pg.max_blocks * 16);
+      Nk = min(sp.len, pg.max_blocks * 16);
       delta = Nk - N;                                 // the chunk is the sequence's last tokens
       // a chunk outside the packed rows (malformed offsets) is skipped; so is a
       // query tile past the chunk
@@ -1083,7 +1120,7 @@ hipError_t launch_paged(const FwdArgs& a) {
   const bool flat = pool_bytes <= 0x80000000ull;
   const PagedKV pg{a.table,      a.q_start,    a.seq_lens,  a.H,
                    a.KVH,        a.max_blocks, a.num_blocks, a.total_q,
-                   flat ? (uint32_t)pool_bytes : 0u};
+                   flat ? (uint32_t)pool_bytes : 0u, a.B};
   const int hg =
       CAUSAL ? xcd_group((long long)a.B * a.H, (long long)a.max_blocks * 16 * D * 4) : 0;
   if (flat)

@@ -62,6 +62,7 @@ def test_fwd_f16(gpu, d, causal, N):
     (1, 32, 4100, 128, True), (8, 16, 1900, 128, True),      # 256-row / 128-row paired
     (1, 32, 4100, 64, True), (8, 32, 1000, 64, True),        # one-stage: 256-row paired / 128-row
     (1, 16, 4096, 128, False), (1, 16, 4100, 64, False),     # 256-row, not paired
+    (1, 32, 8192, 128, True),                                # the fp16 long-context launch
 ])
 def test_fwd_f16_long_launches_sampled(gpu, B, H, N, d, causal):
     x = workloads.attention_inputs(B, H, N, d, "f16", seed=6400 + N + d)

@@ -67,6 +67,29 @@ def test_paged_prefill_long_chunks_gqa(gpu):
     _run(gpu, lens, chunks, 32, 8, 128, "bf16", seed=7200, rows=rows)
 
 
+@pytest.mark.parametrize("n_seqs", [64, 65])
+def test_paged_prefill_many_sequences_in_any_order(gpu, n_seqs):
+    """Workgroups take the sequences of a call longest first (by the keys an
+    average query tile reads) when there are at most 64 of them, and in their
+    own order beyond: 64 and 65 sequences whose lengths, chunk lengths and tie
+    patterns are mixed (equal keys included), every row checked."""
+    rng = np.random.default_rng(7300 + n_seqs)
+    lens = [int(x) for x in rng.integers(1, 400, n_seqs)]
+    lens[3] = lens[7] = 250                       # equal keys: ties broken by index
+    chunks = [int(rng.integers(1, L + 1)) for L in lens]
+    chunks[3] = chunks[7] = 40
+    _run(gpu, lens, chunks, 8, 4, 128, "bf16", seed=7300 + n_seqs)
+
+
+def test_paged_prefill_longest_sequences_last(gpu):
+    """Sequences in ascending order of work, so that the longest-first order
+    reverses them; causal and non-causal."""
+    lens = [40, 90, 200, 333, 500, 700]
+    chunks = [40, 64, 100, 129, 200, 256]
+    _run(gpu, lens, chunks, 8, 2, 64, "bf16", seed=7350)
+    _run(gpu, lens, chunks, 8, 2, 64, "bf16", seed=7351, causal=False)
+
+
 def test_paged_prefill_zero_scale_closed_form(gpu):
     """scale = 0: chunk row r of a sequence with L cached tokens and an n-token
     chunk sees keys 0 .. L - n + r, all with the same weight, so its output is
