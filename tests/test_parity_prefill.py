@@ -58,13 +58,12 @@ def test_paged_prefill_noncausal(gpu, dtype, d):
 
 
 def test_paged_prefill_long_chunks_gqa(gpu):
-    """Eight sequences with 1024-token chunks over 1500..4000 cached tokens,
-    32 query heads on 8 cached heads; sampled rows."""
+    """The benchmark's prefill shape: eight sequences with 1024-token chunks
+    over 1500..4000 cached tokens, 32 query heads on 8 cached heads; every row
+    and head."""
     lens = [1500, 2048, 2500, 3000, 3333, 3700, 4000, 1024]
     chunks = [1024] * 8
-    starts = np.cumsum([0] + chunks)
-    rows = np.concatenate([np.r_[a:a + 3, b - 3:b] for a, b in zip(starts[:-1], starts[1:])])
-    _run(gpu, lens, chunks, 32, 8, 128, "bf16", seed=7200, rows=rows)
+    _run(gpu, lens, chunks, 32, 8, 128, "bf16", seed=7200)
 
 
 @pytest.mark.parametrize("n_seqs", [64, 65])
