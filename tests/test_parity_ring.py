@@ -164,12 +164,10 @@ def test_ring_of_two_ranks_equals_full_causal(gpu, d):
 def test_ring_step_long_context_block(gpu):
     """One rank's non-diagonal step at the long-context shape: 32 heads x 8192
     queries against the 8192-token key/value block just before them (every key
-    visible).  Sampled heads and rows against the oracle."""
+    visible).  Every head and row against the oracle."""
     c = workloads.LONG_CONTEXT
     x = workloads.attention_inputs(c.B, c.H, c.N, c.d, c.dtype, seed=workloads.LONG_CONTEXT.seed + 1)
-    rows = np.r_[0:3, 4095:4097, 8189:8192]
-    _check_offset(gpu, x, c.N, 0, True, c.scale, TOL["bf16"], heads=[(0, 0), (0, 17), (0, 31)],
-                  rows=rows)
+    _check_offset(gpu, x, c.N, 0, True, c.scale, TOL["bf16"])
 
 
 @pytest.mark.parametrize("Nq,Nk,qo,ko", [(4100, 4100, 1000, 0), (4100, 4096, 0, 1000)])
@@ -301,7 +299,7 @@ def test_ring_of_four_ranks_fused_steps(gpu, d):
 def test_ring_step_long_context_fused(gpu):
     """The long-context ring step (32 heads x 8192 queries against the 8192
     keys just before them) accumulated into the diagonal block's result:
-    sampled heads and rows against the oracle over all 16384 keys."""
+    every head and row against the oracle over all 16384 keys."""
     c = workloads.LONG_CONTEXT
     x = workloads.attention_inputs(c.B, c.H, 2 * c.N, c.d, c.dtype, seed=c.seed + 2)
     q, k, v = (x[t].to(gpu) for t in "qkv")
@@ -312,12 +310,12 @@ def test_ring_step_long_context_fused(gpu):
     binding.fwd_offset_accumulate(q2, k1, v1, o, l, q_offset=c.N, k_offset=0, causal=True,
                                   scale=c.scale)
     torch.cuda.synchronize()
-    rows = np.r_[0:3, 4095:4097, 8189:8192]
-    ref = oracle.attention_forward(x["q"], x["k"], x["v"], c.scale, True, heads=[(0, 0), (0, 31)],
-                                   rows=rows + c.N)
+    ref = oracle.attention_forward(x["q"], x["k"], x["v"], c.scale, True,
+                                   rows=np.arange(c.N, 2 * c.N))
+    o, l = o.double().cpu().numpy(), l.double().cpu().numpy()
     for (b, h), (ro, rl) in ref.items():
-        assert max_abs(o[b, h].double().cpu().numpy()[rows], ro) <= 2e-2
-        assert max_abs(l[b, h].double().cpu().numpy()[rows], rl) <= 2e-2
+        assert max_abs(o[b, h], ro) <= 2e-2
+        assert max_abs(l[b, h], rl) <= 2e-2
 
 
 @pytest.mark.parametrize("d", [64, 128])
