@@ -62,7 +62,6 @@ def test_fwd_f16(gpu, d, causal, N):
     (1, 32, 4100, 128, True), (8, 16, 1900, 128, True),      # 256-row / 128-row paired
     (1, 32, 4100, 64, True), (8, 32, 1000, 64, True),        # one-stage: 256-row paired / 128-row
     (1, 16, 4096, 128, False), (1, 16, 4100, 64, False),     # 256-row, not paired
-    (1, 32, 8192, 128, True),                                # the fp16 long-context launch
 ])
 def test_fwd_f16_long_launches_sampled(gpu, B, H, N, d, causal):
     x = workloads.attention_inputs(B, H, N, d, "f16", seed=6400 + N + d)
@@ -81,6 +80,13 @@ def test_fwd_f16_long_launches_sampled(gpu, B, H, N, d, causal):
                 go, gl = go[rsel], gl[rsel]
             assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))
             assert max_abs(go, ro) <= TOL and max_abs(gl, rl) <= TOL, (b, h)
+
+
+def test_fwd_f16_long_context_every_row(gpu):
+    """The benchmark's fp16 forward, causal B1 H32 N8192 d128, on every head
+    and row."""
+    x = workloads.attention_inputs(1, 32, 8192, 128, "f16", seed=6500)
+    _fwd_check(gpu, x, True, 128 ** -0.5)
 
 
 def test_fwd_f16_scores_beyond_fp16_exp_range(gpu):
