@@ -314,7 +314,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void fwd_bf16_kernel(
     const int32_t* table_row = nullptr;
     int kvh = 0;
     if constexpr (PAGED) {
-      const int h = bh % pg.H;
+      // workgroups of head position x run on XCD x % 8; query heads that read
+      // one cached head are consecutive, so the position is transposed over
+      // the 8 XCDs to keep a cached head's query heads on one XCD (one L2)
+      const int hx = bh % pg.H;
+      const int h = (pg.H & 7) == 0 ? (hx & 7) * (pg.H >> 3) + (hx >> 3) : hx;
       const SeqPick sp = pick_sequence(pg, bh / pg.H, lane);
       const int seq = sp.seq, qs = sp.q_begin;
       N = sp.q_end - qs;
