@@ -1125,8 +1125,11 @@ hipError_t launch_paged(const FwdArgs& a) {
   const PagedKV pg{a.table,      a.q_start,    a.seq_lens,  a.H,
                    a.KVH,        a.max_blocks, a.num_blocks, a.total_q,
                    flat ? (uint32_t)pool_bytes : 0u, a.B};
+  // the query heads of one cached head share its K/V stream in one L2 (the
+  // kernel keeps them on one XCD when H is a multiple of 8)
+  const long long share = (a.H % 8 == 0) ? a.H / a.KVH : 1;
   const int hg =
-      CAUSAL ? xcd_group((long long)a.B * a.H, (long long)a.max_blocks * 16 * D * 4) : 0;
+      CAUSAL ? xcd_group((long long)a.B * a.H, (long long)a.max_blocks * 16 * D * 4 / share) : 0;
   if (flat)
     hipLaunchKernelGGL((fwd_bf16_kernel<E, D, CAUSAL, kBNDefault, 2, true, false, NW, true>),
                        dim3(grid), dim3(64 * NW), 0, a.stream, (const T*)a.Q, (const T*)a.K,
